@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-diffusion denoising round on one MI355X.
+
+A step is one full round on a 32-position block: RMSNorm, router and top-8 of
+256 experts, union-of-experts SwiGLU plus the shared expert and the weighted
+combine (one Clover-shaped MoE layer: hidden 2048, intermediate 512, flat
+routing, no coreset), the final RMSNorm, the LM head over a 248320-token
+vocabulary with the fused softmax-confidence/argmax, and the LowConfidence
+commit.  Inputs are seeded synthetic tensors, resident in HBM before timing.
+
+Prints one JSON line: microseconds per round, achieved HBM bandwidth on the
+round's algorithmic bytes, the roofline of the dominant kernel (its duration
+measured with hipEvents on its launch stream during the timed region), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per 32-token block-denoise round; achieved HBM GB/s & % of roofline"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = ("clover_block_round: 1 MoE layer (hidden 2048, 256 routed experts top-8, expert "
+            "intermediate 512, shared expert 512, flat routing, no coreset) + final RMSNorm + LM head "
+            "(vocab 248320) + LowConfidence commit (threshold 0.95), block 32, bf16 weights / fp32 accumulate")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build targets a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_diffusion_decode_amd as bdd
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    d = W.C1
+    R = 8
+    log(f"[bench] generating inputs (seed {args.seed})")
+    x, info = W.planted_round_inputs(args.seed, d, rounds=R, p=0.3, amp_pass=24.0, amp_fail=(10.0, 14.0))
+    x = x.to(dev)
+    layer = W.layer_weights(args.seed, 0, d, device=dev)
+    w_lm = W.lm_head_weight(args.seed, d, device=dev, unit_rows=info["unit_rows"])
+    dims = bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16)
+    plan = bdd.RoundPlan(dims, [layer], w_lm, 1.0, 0.95)
+    T = d.T
+    tok = torch.full((T,), bdd.MASK, dtype=torch.int32, device=dev)
+    conf = torch.empty(T, dtype=torch.float32, device=dev)
+    choice = torch.empty(T, dtype=torch.int32, device=dev)
+    ri = torch.empty(4, dtype=torch.int32, device=dev)
+    nd = torch.empty((R, 1), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    # distinct experts of each stub round (the GPU's own routing)
+    for r in range(R):
+        plan(x[r], tok, conf, choice, ri, None, nd[r])
+    torch.cuda.synchronize()
+    n_distinct = nd[:, 0].cpu().numpy().astype(np.int64)
+
+    # warmup, with every kernel timed to find the dominant one
+    bdd.timing_enable(True, None)
+    for i in range(args.warmup):
+        plan(x[i % R], tok, conf, choice, ri)
+    torch.cuda.synchronize()
+    warm = bdd.timing_read()
+    bdd.timing_enable(False)
+    dominant = max(warm, key=lambda k: warm[k][0])
+    log("[bench] warmup per-kernel avg us: " +
+        ", ".join(f"{k}={1e3 * v[0] / v[1]:.1f}" for k, v in warm.items()))
+
+    # timed region: events on torch's current stream (the library launches
+    # there); the dominant kernel is bracketed by its own events
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bdd.timing_enable(True, dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        plan(x[i % R], tok, conf, choice, ri)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom = bdd.timing_read()
+    bdd.timing_enable(False)
+    ms = start.elapsed_time(stop) / args.steps
+    log(f"[bench] {args.steps} rounds: {ms * 1e3:.1f} us/round (wall {wall * 1e3 / args.steps:.1f} us/round)")
+
+    # algorithmic bytes: union experts + shared expert + router + LM head + block activations
+    eb = 3 * d.H * d.I * 2
+    mean_u = float(np.mean([n_distinct[i % R] for i in range(args.steps)]))
+    lm_bytes = d.V * d.H * 2 + T * d.H * 2
+    round_bytes = mean_u * eb + 3 * d.H * d.I_s * 2 + d.E * d.H * 2 + lm_bytes + T * d.H * 4 * 2
+    gbps = round_bytes / (ms * 1e-3) / 1e9
+
+    dom_ms = dom[dominant][0] / dom[dominant][1]
+    dom_bytes = {"lmhead": lm_bytes,
+                 "routed_gateup": mean_u * 2 * d.I * d.H * 2 + T * d.K * d.H * 2,
+                 "routed_down": mean_u * d.H * d.I * 2 + T * d.K * (d.I + d.H) * 4}.get(dominant)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_bytes else None
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS if achieved else None,
+                "traffic": None, "avg_us": dom_ms * 1e3, "algorithmic_bytes": dom_bytes}
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms * 1e3, 2),
+        "unit": "us/round",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded counter-based inputs, random-init weights of the Clover shape",
+        "config": {"workload": WORKLOAD, "global_batch": T, "seq_len": T, "parallelism": "single GPU",
+                   "distinct_experts_mean": mean_u},
+        "round_bytes": round_bytes,
+        "hbm_gbps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "per_kernel_warmup_us": {k: 1e3 * v[0] / v[1] for k, v in warm.items()},
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, d, x, layer, w_lm, info, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, d, x, layer, w_lm, info, budget_s):
+    """The CPU oracle (float64 NumPy) on the same round, inputs already in host
+    memory as float64; rounds run until the time budget is spent."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count()
+    log("[bench] preparing float64 host copies for the CPU oracle")
+    L = {"w_router": layer["w_router"].double().cpu().numpy(),
+         "router_bias": layer["router_bias"].double().cpu().numpy(),
+         "ws_gate_up": layer["ws_gate_up"].double().cpu().numpy(),
+         "ws_down": layer["ws_down"].double().cpu().numpy()}
+    gu, dn = layer["w_gate_up"], layer["w_down"]
+    L["experts"] = {e: (gu[e].double().cpu().numpy(), dn[e].double().cpu().numpy()) for e in range(d.E)}
+    wl = w_lm.double().cpu().numpy()
+    xs = x.double().cpu().numpy()
+    tok = np.full(d.T, O.MASK)
+    times = []
+    t_end = time.perf_counter() + budget_s
+    r = 0
+    while time.perf_counter() < t_end or r == 0:
+        t0 = time.perf_counter()
+        hh, _ = O.moe_stack(xs[r % xs.shape[0]], [L], d.K, 1.0)
+        c, ch, _ = O.lm_head_confidence(hh, wl)
+        tok, *_ = O.commit(tok, c, ch, 0.95)
+        times.append(time.perf_counter() - t0)
+        r += 1
+    us = 1e6 * float(np.median(times))
+    log(f"[bench] cpu oracle: {len(times)} rounds, median {us / 1e3:.1f} ms/round on {cores} threads")
+    return {"value": round(us, 1), "unit": "us/round", "cores": cores, "kind": "oracle",
+            "sample": f"{len(times)} full rounds of the same workload (float64 NumPy oracle, "
+                      f"median), inputs prepared as float64 host arrays before timing"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,403 @@
+// C ABI of the denoising round: argument checks, workspace planning and the
+// launch sequences.  Every step runs in the kernels of this library.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/bdd.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace bdd;
+
+thread_local char g_err[512] = "";
+
+bdd_status fail(bdd_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess) return fail(BDD_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// ----------------------------------------------------------------- kernel timing
+// Optional hipEvent pairs around every launch whose name contains the filter
+// (measurement tools only; not thread-safe; off by default).
+struct TimingRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::string g_filter;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+bool timing_wants(const char *name) {
+  return g_timing && (g_filter.empty() || strstr(name, g_filter.c_str()) != nullptr);
+}
+
+#define LAUNCH(name, stream, expr)                                               \
+  do {                                                                           \
+    const bool rec_ = timing_wants(name);                                        \
+    hipEvent_t a_ = nullptr, b_ = nullptr;                                       \
+    if (rec_ && (a_ = pool_event()) != nullptr) HIP_TRY(hipEventRecord(a_, stream)); \
+    HIP_TRY(expr);                                                               \
+    if (a_ && (b_ = pool_event()) != nullptr) {                                  \
+      HIP_TRY(hipEventRecord(b_, stream));                                       \
+      g_recs.push_back({name, a_, b_});                                          \
+    }                                                                            \
+  } while (0)
+
+constexpr int kMaxLmGrid = 1024;
+constexpr int kExpertWgPerCu = 4;
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+int esize(int wdtype) { return wdtype == BDD_BF16 ? 2 : 4; }
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bdd_status check_dims(const bdd_moe_dims *d) {
+  if (!d) return fail(BDD_ERR_INVALID_ARG, "dims is NULL");
+  if (d->wdtype != BDD_F32 && d->wdtype != BDD_BF16)
+    return fail(BDD_ERR_INVALID_ARG, "wdtype %d is not BDD_F32 or BDD_BF16", d->wdtype);
+  if (d->T < 1 || d->H < 1 || d->E < 1 || d->K < 1 || d->I < 1 || d->I_shared < 0)
+    return fail(BDD_ERR_INVALID_ARG, "non-positive size in dims (T=%d H=%d E=%d K=%d I=%d I_shared=%d)",
+                d->T, d->H, d->E, d->K, d->I, d->I_shared);
+  if (d->K > d->E) return fail(BDD_ERR_INVALID_ARG, "K=%d exceeds E=%d", d->K, d->E);
+  if (d->T > kMaxT) return fail(BDD_ERR_UNSUPPORTED, "T=%d exceeds %d", d->T, kMaxT);
+  if (d->E > kMaxE) return fail(BDD_ERR_UNSUPPORTED, "E=%d exceeds %d", d->E, kMaxE);
+  if (d->K > 32) return fail(BDD_ERR_UNSUPPORTED, "K=%d exceeds 32", d->K);
+  if (d->H % 32 || d->I % 32 || d->I_shared % 32)
+    return fail(BDD_ERR_UNSUPPORTED, "H=%d, I=%d, I_shared=%d must be multiples of 32", d->H, d->I,
+                d->I_shared);
+  if (d->H > 8192 || d->I > 8192 || d->I_shared > 8192)
+    return fail(BDD_ERR_UNSUPPORTED, "H, I, I_shared must be <= 8192");
+  return BDD_OK;
+}
+
+struct MoePlan {
+  size_t logits, prob, idx, wgt, meta, ulist, slot_n, slot_asg, bits, mass, xhat, A, A_s, P, P_s;
+  size_t end;
+};
+
+MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
+  MoePlan p;
+  size_t o = base;
+  auto take = [&o](size_t bytes) { size_t at = o; o = a256(o + bytes); return at; };
+  const size_t T = d.T, E = d.E, K = d.K, H = d.H, I = d.I, Is = d.I_shared;
+  p.logits = take(T * E * 4);
+  p.prob = take(T * E * 4);
+  p.idx = take(T * K * 4);
+  p.wgt = take(T * K * 4);
+  p.meta = take(64);
+  p.ulist = take(E * 4);
+  p.slot_n = take(E * 4);
+  p.slot_asg = take(E * kMaxT * 4);
+  p.bits = take(32);
+  p.mass = take(E * 4);
+  p.xhat = take(T * H * esize(d.wdtype));
+  p.A = take(T * K * I * 4);
+  p.A_s = take(T * (Is ? Is : 1) * 4);
+  p.P = take(T * K * H * 4);
+  p.P_s = take(T * H * 4);
+  p.end = o;
+  return p;
+}
+
+struct LmPlan {
+  size_t m, s, i, end;
+};
+
+LmPlan plan_lm(int T, size_t base) {
+  LmPlan p;
+  size_t o = base;
+  auto take = [&o](size_t bytes) { size_t at = o; o = a256(o + bytes); return at; };
+  p.m = take((size_t)kMaxLmGrid * T * 4);
+  p.s = take((size_t)kMaxLmGrid * T * 4);
+  p.i = take((size_t)kMaxLmGrid * T * 4);
+  p.end = o;
+  return p;
+}
+
+template <typename P>
+P *at(void *ws, size_t off) { return reinterpret_cast<P *>(static_cast<char *>(ws) + off); }
+
+bdd_status check_ws(void *ws, size_t have, size_t need) {
+  if (need && !ws) return fail(BDD_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (have < need) return fail(BDD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(BDD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return BDD_OK;
+}
+
+bdd_status check_weights(const bdd_moe_dims &d, const bdd_moe_weights *w, int layer) {
+  if (!w) return fail(BDD_ERR_INVALID_ARG, "weights of layer %d are NULL", layer);
+  if (!w->w_router || !w->w_gate_up || !w->w_down)
+    return fail(BDD_ERR_INVALID_ARG, "layer %d: w_router, w_gate_up and w_down are required", layer);
+  if (d.I_shared > 0 && (!w->ws_gate_up || !w->ws_down))
+    return fail(BDD_ERR_INVALID_ARG, "layer %d: shared-expert weights are NULL but I_shared=%d", layer,
+                d.I_shared);
+  return BDD_OK;
+}
+
+bdd_status check_lm(int T, int H, int V, int dtype, float threshold) {
+  if (dtype != BDD_F32 && dtype != BDD_BF16) return fail(BDD_ERR_INVALID_ARG, "dtype %d", dtype);
+  if (T < 1 || H < 1 || V < 1) return fail(BDD_ERR_INVALID_ARG, "T=%d H=%d V=%d", T, H, V);
+  if (T > kMaxT) return fail(BDD_ERR_UNSUPPORTED, "T=%d exceeds %d", T, kMaxT);
+  if (H % 32) return fail(BDD_ERR_UNSUPPORTED, "H=%d must be a multiple of 32", H);
+  if (!(threshold > 0.0f && threshold <= 1.0f))
+    return fail(BDD_ERR_INVALID_ARG, "threshold %g outside (0, 1]", (double)threshold);
+  if (lmhead_lds_bytes(dtype, T, H) > 144 * 1024)
+    return fail(BDD_ERR_UNSUPPORTED, "T=%d, H=%d: block hidden states exceed the LDS budget", T, H);
+  if ((long long)V * H >= (1ll << 40)) return fail(BDD_ERR_UNSUPPORTED, "V*H too large");
+  return BDD_OK;
+}
+
+RouteBufs route_bufs(void *ws, const MoePlan &p) {
+  RouteBufs r;
+  r.logits = at<float>(ws, p.logits);
+  r.prob = at<float>(ws, p.prob);
+  r.idx = at<int32_t>(ws, p.idx);
+  r.wgt = at<float>(ws, p.wgt);
+  r.meta = at<int32_t>(ws, p.meta);
+  r.union_list = at<int32_t>(ws, p.ulist);
+  r.slot_n = at<int32_t>(ws, p.slot_n);
+  r.slot_asg = at<int32_t>(ws, p.slot_asg);
+  r.cs_bits = at<uint32_t>(ws, p.bits);
+  r.mass = at<float>(ws, p.mass);
+  r.n_distinct_out = nullptr;
+  r.coreset_size_out = nullptr;
+  return r;
+}
+
+// One MoE layer from xhat (already normalised).  combine: h += y and the next
+// normalisation when h != nullptr, else y_out = y.
+bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_p, const void *xhat,
+                     RouteBufs r, const MoePlan &p, void *ws, float *h, float *y_out,
+                     void *xhat_next, hipStream_t s) {
+  const int T = d.T, H = d.H, E = d.E, K = d.K, I = d.I, Is = d.I_shared;
+  const int cus = device_cus();
+  float *A = at<float>(ws, p.A), *A_s = at<float>(ws, p.A_s);
+  float *P = at<float>(ws, p.P), *P_s = at<float>(ws, p.P_s);
+  LAUNCH("router_logits", s, launch_router_logits(d.wdtype, xhat, w.w_router, w.router_bias, r.logits, T, H, E, s));
+  LAUNCH("route_select", s, launch_route_select(r, T, E, K, top_p, s));
+  if (Is > 0) LAUNCH("shared_gateup", s, launch_shared_gateup(d.wdtype, xhat, w.ws_gate_up, A_s, T, H, Is, s));
+  const int union_max = E < T * K ? E : T * K;
+  int g1 = union_max * (I / 16), g2 = union_max * (H / 32);
+  const int cap = cus * kExpertWgPerCu;
+  g1 = g1 < cap ? g1 : cap;
+  g2 = g2 < cap ? g2 : cap;
+  LAUNCH("routed_gateup", s, launch_routed_gateup(d.wdtype, xhat, w.w_gate_up, r, A, T, H, E, K, I, g1, s));
+  if (Is > 0) LAUNCH("shared_down", s, launch_shared_down(d.wdtype, A_s, w.ws_down, P_s, T, H, Is, s));
+  LAUNCH("routed_down", s, launch_routed_down(d.wdtype, A, w.w_down, r, P, H, E, K, I, g2, s));
+  LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P_s : nullptr, r.idx, h, y_out, xhat_next, T, H, K, s));
+  return BDD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bdd_status_string(int32_t st) {
+  switch (st) {
+    case BDD_OK: return "BDD_OK";
+    case BDD_ERR_INVALID_ARG: return "BDD_ERR_INVALID_ARG";
+    case BDD_ERR_UNSUPPORTED: return "BDD_ERR_UNSUPPORTED";
+    case BDD_ERR_WORKSPACE: return "BDD_ERR_WORKSPACE";
+    case BDD_ERR_HIP: return "BDD_ERR_HIP";
+    default: return "unknown bdd_status";
+  }
+}
+
+const char *bdd_last_error(void) { return g_err; }
+
+int32_t bdd_device_cus(void) { return device_cus(); }
+
+bdd_status bdd_timing_enable(int32_t on, const char *filter) {
+  g_timing = on != 0;
+  g_filter = filter ? filter : "";
+  return BDD_OK;
+}
+
+int32_t bdd_timing_read(int32_t max_kernels, char *names, double *total_ms, int32_t *count) {
+  if (max_kernels < 0 || (max_kernels > 0 && (!names || !total_ms || !count)))
+    return fail(BDD_ERR_INVALID_ARG, "timing_read: bad output buffers");
+  std::vector<std::string> seen;
+  std::vector<double> tot;
+  std::vector<int> cnt;
+  hipError_t err = hipSuccess;
+  for (const TimingRec &r : g_recs) {
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventSynchronize(r.b);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, r.a, r.b);
+    size_t k = 0;
+    while (k < seen.size() && seen[k] != r.name) ++k;
+    if (k == seen.size()) { seen.push_back(r.name); tot.push_back(0.0); cnt.push_back(0); }
+    tot[k] += ms;
+    cnt[k] += 1;
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  if (err != hipSuccess) return fail(BDD_ERR_HIP, "timing_read: %s", hipGetErrorString(err));
+  const int n = (int)seen.size() < max_kernels ? (int)seen.size() : max_kernels;
+  for (int k = 0; k < n; ++k) {
+    snprintf(names + 64 * k, 64, "%s", seen[k].c_str());
+    total_ms[k] = tot[k];
+    count[k] = cnt[k];
+  }
+  return (int32_t)seen.size();
+}
+
+size_t bdd_moe_workspace_bytes(const bdd_moe_dims *d) {
+  if (check_dims(d) != BDD_OK) return 0;
+  return plan_moe(*d, 0).end;
+}
+
+bdd_status bdd_moe_block_forward(const bdd_moe_dims *d, const bdd_moe_weights *w, const float *h,
+                                 float coreset_top_p, float *y, void *xhat_out, int32_t *topk_idx,
+                                 float *topk_w, int32_t *n_distinct, uint32_t *coreset_bits,
+                                 int32_t *coreset_size, void *ws, size_t ws_bytes, void *stream) {
+  bdd_status st = check_dims(d);
+  if (st != BDD_OK) return st;
+  if ((st = check_weights(*d, w, 0)) != BDD_OK) return st;
+  if (!h || !y || !topk_idx || !topk_w || !n_distinct)
+    return fail(BDD_ERR_INVALID_ARG, "h, y, topk_idx, topk_w and n_distinct are required");
+  if (!(coreset_top_p > 0.0f)) return fail(BDD_ERR_INVALID_ARG, "coreset_top_p %g must be > 0", (double)coreset_top_p);
+  const MoePlan p = plan_moe(*d, 0);
+  if ((st = check_ws(ws, ws_bytes, p.end)) != BDD_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  RouteBufs r = route_bufs(ws, p);
+  r.idx = topk_idx;
+  r.wgt = topk_w;
+  if (coreset_bits) r.cs_bits = coreset_bits;
+  r.n_distinct_out = n_distinct;
+  r.coreset_size_out = coreset_size;
+  void *xhat = xhat_out ? xhat_out : at<void>(ws, p.xhat);
+  LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, h, nullptr, xhat, d->T, d->H, s));
+  return moe_layer(*d, *w, coreset_top_p >= 1.0f ? 1.0f : coreset_top_p, xhat, r, p, ws, nullptr, y,
+                   nullptr, s);
+}
+
+bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx, int32_t T, int32_t E,
+                              int32_t K, float top_p, uint32_t *coreset_bits, int32_t *coreset_size,
+                              float *expert_mass, void *stream) {
+  if (!router_prob || !topk_idx || !coreset_bits || !coreset_size)
+    return fail(BDD_ERR_INVALID_ARG, "router_prob, topk_idx, coreset_bits and coreset_size are required");
+  if (T < 1 || E < 1 || K < 1 || K > E) return fail(BDD_ERR_INVALID_ARG, "T=%d E=%d K=%d", T, E, K);
+  if (T > kMaxT || E > kMaxE || K > 32) return fail(BDD_ERR_UNSUPPORTED, "T=%d E=%d K=%d", T, E, K);
+  if (!(top_p > 0.0f)) return fail(BDD_ERR_INVALID_ARG, "top_p %g must be > 0", (double)top_p);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  LAUNCH("coreset", s, launch_coreset(router_prob, topk_idx, T, E, K, top_p >= 1.0f ? 1.0f : top_p,
+                                      coreset_bits, coreset_size, expert_mass, s));
+  return BDD_OK;
+}
+
+size_t bdd_lmhead_workspace_bytes(int32_t T, int32_t H, int32_t V) {
+  if (T < 1 || T > kMaxT || H < 1 || V < 1) return 0;
+  return plan_lm(T, 0).end;
+}
+
+bdd_status bdd_lmhead_confidence_commit(const void *hhat, const void *w_lm, int32_t T, int32_t H,
+                                        int32_t V, int32_t dtype, float threshold, int32_t *tokens,
+                                        float *conf, int32_t *choice, int32_t *round_info, void *ws,
+                                        size_t ws_bytes, void *stream) {
+  bdd_status st = check_lm(T, H, V, dtype, threshold);
+  if (st != BDD_OK) return st;
+  if (!hhat || !w_lm || !tokens || !conf || !choice || !round_info)
+    return fail(BDD_ERR_INVALID_ARG, "hhat, w_lm, tokens, conf, choice and round_info are required");
+  const LmPlan p = plan_lm(T, 0);
+  if ((st = check_ws(ws, ws_bytes, p.end)) != BDD_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int cus = device_cus();
+  const int grid = lmhead_grid(cus) < kMaxLmGrid ? lmhead_grid(cus) : kMaxLmGrid;
+  float *pm = at<float>(ws, p.m), *ps = at<float>(ws, p.s);
+  int32_t *pi = at<int32_t>(ws, p.i);
+  LAUNCH("lmhead", s, launch_lmhead(dtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, s));
+  LAUNCH("commit", s, launch_commit(pm, ps, pi, grid, T, threshold, tokens, conf, choice, round_info, s));
+  return BDD_OK;
+}
+
+size_t bdd_round_workspace_bytes(const bdd_moe_dims *d, int32_t V) {
+  if (check_dims(d) != BDD_OK || V < 1) return 0;
+  const MoePlan m = plan_moe(*d, 0);
+  const size_t h_off = m.end;
+  const LmPlan l = plan_lm(d->T, a256(h_off + (size_t)d->T * d->H * 4));
+  return l.end;
+}
+
+bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
+                                   const bdd_moe_weights *layers, float coreset_top_p,
+                                   const void *w_lm, int32_t V, float threshold, const float *x_in,
+                                   int32_t *tokens, float *conf, int32_t *choice, int32_t *round_info,
+                                   int32_t *layer_topk_idx, int32_t *layer_n_distinct,
+                                   void *hhat_out, void *ws, size_t ws_bytes, void *stream) {
+  bdd_status st = check_dims(d);
+  if (st != BDD_OK) return st;
+  if (n_layers < 0) return fail(BDD_ERR_INVALID_ARG, "n_layers=%d", n_layers);
+  if (n_layers > 0 && !layers) return fail(BDD_ERR_INVALID_ARG, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l)
+    if ((st = check_weights(*d, &layers[l], l)) != BDD_OK) return st;
+  if ((st = check_lm(d->T, d->H, V, d->wdtype, threshold)) != BDD_OK) return st;
+  if (!w_lm || !x_in || !tokens || !conf || !choice || !round_info)
+    return fail(BDD_ERR_INVALID_ARG, "w_lm, x_in, tokens, conf, choice and round_info are required");
+  if (!(coreset_top_p > 0.0f)) return fail(BDD_ERR_INVALID_ARG, "coreset_top_p %g must be > 0", (double)coreset_top_p);
+  const MoePlan p = plan_moe(*d, 0);
+  const size_t h_off = p.end;
+  const LmPlan lp = plan_lm(d->T, a256(h_off + (size_t)d->T * d->H * 4));
+  if ((st = check_ws(ws, ws_bytes, lp.end)) != BDD_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int T = d->T, H = d->H, K = d->K;
+  float *h = at<float>(ws, h_off);
+  void *xhat = at<void>(ws, p.xhat);
+  void *hhat = hhat_out ? hhat_out : xhat;
+  const float tp = coreset_top_p >= 1.0f ? 1.0f : coreset_top_p;
+  LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, n_layers == 0 ? hhat : xhat, T, H, s));
+  for (int l = 0; l < n_layers; ++l) {
+    RouteBufs r = route_bufs(ws, p);
+    if (layer_topk_idx) r.idx = layer_topk_idx + (size_t)l * T * K;
+    if (layer_n_distinct) r.n_distinct_out = layer_n_distinct + l;
+    void *next = l + 1 == n_layers ? hhat : xhat;
+    if ((st = moe_layer(*d, layers[l], tp, xhat, r, p, ws, h, nullptr, next, s)) != BDD_OK) return st;
+  }
+  const int cus = device_cus();
+  const int grid = lmhead_grid(cus) < kMaxLmGrid ? lmhead_grid(cus) : kMaxLmGrid;
+  float *pm = at<float>(ws, lp.m), *ps = at<float>(ws, lp.s);
+  int32_t *pi = at<int32_t>(ws, lp.i);
+  LAUNCH("lmhead", s, launch_lmhead(d->wdtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, s));
+  LAUNCH("commit", s, launch_commit(pm, ps, pi, grid, T, threshold, tokens, conf, choice, round_info, s));
+  return BDD_OK;
+}
+
+}  // extern "C"

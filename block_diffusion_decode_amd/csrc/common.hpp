@@ -1,0 +1,148 @@
+// Device helpers shared by the round's kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bdd {
+
+constexpr int kWave = 64;
+constexpr int kMaxT = 32;        // block positions handled per call
+constexpr int kMaxE = 256;       // routed experts
+constexpr int kTokGroup = 4;     // positions per pass of the routed-expert kernels
+
+typedef uint16_t bf16_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct WBf16 { typedef bf16_t T; static constexpr int kChunk = 8; };   // 16-byte chunk = 8 elements
+struct WF32  { typedef float  T; static constexpr int kChunk = 4; };   // 16-byte chunk = 4 elements
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN -> quiet NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void unpack8(const uint4 &v, float (&f)[8]) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) {
+  return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
+
+// ---------------------------------------------------------------- memory
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+// Streaming load of weights that are read once per call.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  return v;
+}
+
+// Reduce N partial values per lane across the 64 lanes of a wave, leaving
+// lane l with the total of value index (l >> (6 - log2 N)).  N is a power of
+// two <= 64.  Halving exchange: at each step (partner distance S = 32, 16,
+// ...) lanes keep one half of their values and add the partner's copy of that
+// half; once one value is left the remaining steps are a plain butterfly.
+// All register indices are compile-time constants.
+template <int N, int S>
+__device__ __forceinline__ void reduce_scatter_step(float *v, int lane) {
+  if constexpr (S >= 1) {
+    if constexpr (N > 1) {
+      constexpr int half = N / 2;
+      const bool upper = (lane & S) != 0;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float send = upper ? v[i] : v[i + half];
+        const float keep = upper ? v[i + half] : v[i];
+        v[i] = keep + __shfl_xor(send, S);
+      }
+      reduce_scatter_step<half, S / 2>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], S);
+      reduce_scatter_step<1, S / 2>(v, lane);
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+  reduce_scatter_step<N, 32>(v, lane);
+  return v[0];
+}
+template <int N>
+constexpr int log2i() { return N <= 1 ? 0 : 1 + log2i<N / 2>(); }
+
+// ---------------------------------------------------------------- math
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4_f32.  For both, lane l holds
+// A row (l & 15) and B column (l & 15) for k-group (l >> 4), and the 16x16
+// result as rows 4*(l >> 4) + r, column (l & 15), r = 0..3.  Any consistent
+// assignment of k values to (k-group, item) gives the same dot products.
+
+__device__ __forceinline__ f32x4 mfma_bf16(const uint4 &a, const uint4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Split 8 fp32 values into bf16 high parts and bf16 residuals, so that a
+// bf16 MFMA pass over each reproduces fp32-accurate products with bf16 weights.
+__device__ __forceinline__ void split_hi_lo(const float (&x)[8], uint4 &hi, uint4 &lo) {
+  bf16_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f2bf(x[i]);
+    l[i] = f2bf(x[i] - bf2f(h[i]));
+  }
+  hi = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+  lo = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+}
+
+}  // namespace bdd

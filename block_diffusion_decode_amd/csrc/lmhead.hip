@@ -1,0 +1,283 @@
+// LM head with a fused softmax-confidence/argmax epilogue, and the
+// LowConfidence commit.
+//
+// Pages: [P1] aitujian.cn article on Clover-35B-A3B-Preview, section 三: each
+// round runs one forward over the block, takes every position's argmax and its
+// probability (the confidence), writes positions with confidence >= 0.95 for
+// good, and when none reaches it forces the single most confident one; written
+// tokens are never revised.  [P2] goremy.ai "What Is Clover-35B-A3B? Block
+// Diffusion on a Qwen3.6 MoE", "How does confidence-threshold block decoding
+// work?" (same loop; scores each masked position).
+//
+// conf = max_v softmax(z)_v = 1 / sum_v exp(z_v - max z), so the kernel keeps,
+// per position, a running (max, sum of exp(z - max), argmax) over vocabulary
+// tiles and never stores a logit.
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bdd {
+
+constexpr int kLmWaves = 16;
+
+// Online-softmax merge of (m2, s2, i2) into (m, s, i): max, rescaled sum,
+// lowest index among equal maxima.
+__device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, float s2, int i2) {
+  if (s2 == 0.f) return;
+  if (s == 0.f) { m = m2; s = s2; i = i2; return; }
+  if (m2 > m) {
+    s = s * __expf(m - m2) + s2;
+    m = m2;
+    i = i2;
+  } else if (m2 < m) {
+    s += s2 * __expf(m2 - m);
+  } else {
+    s += s2;
+    i = min(i, i2);
+  }
+}
+
+// One workgroup (16 waves) per CU.  The block's normalised hidden states are
+// staged once in LDS as [chunk][position] 16-byte entries; each wave takes
+// 16-row vocabulary tiles round-robin, streams the rows with 16-byte loads,
+// multiplies them by the staged positions on MFMA, and folds the 16 x 32
+// logits into its running (max, sum, argmax).
+template <class W, int NT>
+__global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__restrict__ hhat,
+                                                      const typename W::T *__restrict__ wlm, int T,
+                                                      int H, int V, float *__restrict__ part_m,
+                                                      float *__restrict__ part_s,
+                                                      int32_t *__restrict__ part_i) {
+  extern __shared__ uint4 xs[];  // [H / kChunk][16 * NT]
+  __shared__ float sm[kLmWaves][kMaxT], ssum[kLmWaves][kMaxT];
+  __shared__ int si[kLmWaves][kMaxT];
+  constexpr int CH = W::kChunk;
+  constexpr int TP = 16 * NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NC = H / CH;
+  for (int idx = tid; idx < TP * NC; idx += blockDim.x) {
+    const int t = idx / NC, c = idx - t * NC;
+    xs[c * TP + t] = t < T ? ld16(hhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  const int li = lane & 15, g = lane >> 4;
+  float m[NT], s[NT];
+  int am[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) { m[n] = -FLT_MAX; s[n] = 0.f; am[n] = INT_MAX; }
+
+  const int ntiles = (V + 15) / 16;
+  for (int tile = blockIdx.x * kLmWaves + wave; tile < ntiles; tile += gridDim.x * kLmWaves) {
+    const int row0 = tile * 16;
+    const bool ok = row0 + li < V;
+    const typename W::T *wrow = wlm + (size_t)(ok ? row0 + li : 0) * H;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (std::is_same<W, WBf16>::value) {
+#pragma unroll 8
+      for (int c0 = 0; c0 < NC; c0 += 4) {
+        const int c = c0 + g;
+        const uint4 a = ok ? ld16_stream(wrow + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = mfma_bf16(a, xs[c * TP + n * 16 + li], acc[n]);
+      }
+    } else {
+#pragma unroll 8
+      for (int c0 = 0; c0 < NC; c0 += 4) {
+        const int c = c0 + g;
+        const float4 a = ok ? *reinterpret_cast<const float4 *>(wrow + (size_t)c * 4)
+                            : make_float4(0, 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const uint4 bv = xs[c * TP + n * 16 + li];
+          acc[n] = mfma_f32(a.x, __uint_as_float(bv.x), acc[n]);
+          acc[n] = mfma_f32(a.y, __uint_as_float(bv.y), acc[n]);
+          acc[n] = mfma_f32(a.z, __uint_as_float(bv.z), acc[n]);
+          acc[n] = mfma_f32(a.w, __uint_as_float(bv.w), acc[n]);
+        }
+      }
+    }
+    // epilogue: lane holds rows row0 + 4g + r (r = 0..3) of column li + 16n
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float tmax = -FLT_MAX;
+      int targ = INT_MAX;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = row0 + 4 * g + r;
+        if (v < V && (targ == INT_MAX || acc[n][r] > tmax)) { tmax = acc[n][r]; targ = v; }
+      }
+#pragma unroll
+      for (int sft = 16; sft <= 32; sft <<= 1) {
+        const float m2 = __shfl_xor(tmax, sft);
+        const int a2 = __shfl_xor(targ, sft);
+        if (a2 != INT_MAX && (targ == INT_MAX || m2 > tmax || (m2 == tmax && a2 < targ))) {
+          tmax = m2;
+          targ = a2;
+        }
+      }
+      float tsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = row0 + 4 * g + r;
+        if (v < V) tsum += __expf(acc[n][r] - tmax);
+      }
+      tsum += __shfl_xor(tsum, 16);
+      tsum += __shfl_xor(tsum, 32);
+      sm_merge(m[n], s[n], am[n], tmax, tsum, targ);
+    }
+  }
+
+  if (lane < 16) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      sm[wave][n * 16 + lane] = m[n];
+      ssum[wave][n * 16 + lane] = s[n];
+      si[wave][n * 16 + lane] = am[n];
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    float mm = -FLT_MAX, ss = 0.f;
+    int ii = INT_MAX;
+    for (int w = 0; w < kLmWaves; ++w) sm_merge(mm, ss, ii, sm[w][tid], ssum[w][tid], si[w][tid]);
+    part_m[(size_t)blockIdx.x * T + tid] = mm;
+    part_s[(size_t)blockIdx.x * T + tid] = ss;
+    part_i[(size_t)blockIdx.x * T + tid] = ii;
+  }
+}
+
+// Merge the per-workgroup partials of every position (fixed order), then the
+// commit rule on the still-masked positions.
+__global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ part_m,
+                                                      const float *__restrict__ part_s,
+                                                      const int32_t *__restrict__ part_i,
+                                                      int nparts, int T, float threshold,
+                                                      int32_t *__restrict__ tokens,
+                                                      float *__restrict__ conf,
+                                                      int32_t *__restrict__ choice,
+                                                      int32_t *__restrict__ round_info) {
+  __shared__ float s_conf[kMaxT];
+  __shared__ int s_choice[kMaxT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  for (int t = wave; t < T; t += nw) {
+    float m = -FLT_MAX, s = 0.f;
+    int i = INT_MAX;
+    for (int p = lane; p < nparts; p += 64)
+      sm_merge(m, s, i, part_m[(size_t)p * T + t], part_s[(size_t)p * T + t], part_i[(size_t)p * T + t]);
+#pragma unroll
+    for (int sft = 1; sft <= 32; sft <<= 1) {
+      const float m2 = __shfl_xor(m, sft), s2 = __shfl_xor(s, sft);
+      const int i2 = __shfl_xor(i, sft);
+      // both partners merge the same pair in the same order: lower lane first
+      if (lane & sft) {
+        float mm = m2, ss = s2;
+        int ii = i2;
+        sm_merge(mm, ss, ii, m, s, i);
+        m = mm; s = ss; i = ii;
+      } else {
+        sm_merge(m, s, i, m2, s2, i2);
+      }
+    }
+    if (lane == 0) {
+      const float c = 1.0f / s;
+      s_conf[t] = c;
+      s_choice[t] = i;
+      conf[t] = c;
+      choice[t] = i;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool in = lane < T;
+    const int tok = in ? tokens[lane] : 0;
+    const bool masked = in && tok == -1;
+    const float c = in ? s_conf[lane] : 0.f;
+    const unsigned long long pass = __ballot(masked && c >= threshold);
+    const unsigned long long msk = __ballot(masked);
+    int committed = 0, fallback = 0;
+    bool write = false;
+    if (pass) {
+      write = (pass >> lane) & 1ull;
+      committed = __popcll(pass);
+    } else if (msk) {
+      float bv = masked ? c : -FLT_MAX;
+      int bi = masked ? lane : INT_MAX;
+#pragma unroll
+      for (int sft = 32; sft >= 1; sft >>= 1) {
+        const float v2 = __shfl_xor(bv, sft);
+        const int i2 = __shfl_xor(bi, sft);
+        if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
+      }
+      write = lane == bi;
+      committed = 1;
+      fallback = 1;
+    }
+    if (write) tokens[lane] = s_choice[lane];
+    const int left = __popcll(msk) - committed;
+    if (lane == 0) {
+      round_info[0] = committed;
+      round_info[1] = fallback;
+      round_info[2] = left;
+      round_info[3] = left == 0 ? 1 : 0;
+    }
+  }
+}
+
+int lmhead_grid(int cus) { return cus; }
+
+size_t lmhead_lds_bytes(int wdtype, int T, int H) {
+  const int tp = T <= 16 ? 16 : 32;
+  const int ch = wdtype == 1 ? 8 : 4;
+  return (size_t)(H / ch) * tp * 16;
+}
+
+template <typename F>
+static hipError_t allow_lds(F *fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,
+                         float *part_m, float *part_s, int32_t *part_i, int grid, hipStream_t s) {
+  const size_t lds = lmhead_lds_bytes(wdtype, T, H);
+  hipError_t err;
+  if (wdtype == 1) {
+    if (T <= 16) {
+      if ((err = allow_lds(lmhead_kernel<WBf16, 1>, lds)) != hipSuccess) return err;
+      lmhead_kernel<WBf16, 1><<<grid, 1024, lds, s>>>((const bf16_t *)hhat, (const bf16_t *)w_lm, T,
+                                                      H, V, part_m, part_s, part_i);
+    } else {
+      if ((err = allow_lds(lmhead_kernel<WBf16, 2>, lds)) != hipSuccess) return err;
+      lmhead_kernel<WBf16, 2><<<grid, 1024, lds, s>>>((const bf16_t *)hhat, (const bf16_t *)w_lm, T,
+                                                      H, V, part_m, part_s, part_i);
+    }
+  } else {
+    if (T <= 16) {
+      if ((err = allow_lds(lmhead_kernel<WF32, 1>, lds)) != hipSuccess) return err;
+      lmhead_kernel<WF32, 1><<<grid, 1024, lds, s>>>((const float *)hhat, (const float *)w_lm, T, H,
+                                                     V, part_m, part_s, part_i);
+    } else {
+      if ((err = allow_lds(lmhead_kernel<WF32, 2>, lds)) != hipSuccess) return err;
+      lmhead_kernel<WF32, 2><<<grid, 1024, lds, s>>>((const float *)hhat, (const float *)w_lm, T, H,
+                                                     V, part_m, part_s, part_i);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,
+                         int nparts, int T, float threshold, int32_t *tokens, float *conf,
+                         int32_t *choice, int32_t *round_info, hipStream_t s) {
+  commit_kernel<<<1, 1024, 0, s>>>(part_m, part_s, part_i, nparts, T, threshold, tokens, conf,
+                                   choice, round_info);
+  return hipGetLastError();
+}
+
+}  // namespace bdd

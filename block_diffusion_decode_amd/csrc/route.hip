@@ -1,0 +1,431 @@
+// Normalisation, router, top-K selection, block coreset and expert work lists.
+//
+// Pages: [P1] aitujian.cn article on Clover-35B-A3B-Preview, section 四 (256
+// routed experts, top-8, one shared expert) and section 五 (a block of 32
+// positions touches a union of experts); [P2] goremy.ai "What Is
+// Clover-35B-A3B? Block Diffusion on a Qwen3.6 MoE", section "What is the MoE
+// coreset and why does it matter?" (aggregate each position's top-8 scores,
+// rank experts, keep enough to cover top_p of the mass).
+#include <float.h>
+#include <limits.h>
+
+#include "dense.hpp"
+#include "kernels.hpp"
+
+namespace bdd {
+
+constexpr int kMaxK = 32;
+
+__device__ __forceinline__ float block_sum_256(float v, float *red4) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) red4[wave] = v;
+  __syncthreads();
+  v = red4[0] + red4[1] + red4[2] + red4[3];
+  __syncthreads();
+  return v;
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// x_hat = h / sqrt(mean(h^2) + eps), unit gain, one workgroup per position.
+template <typename OT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ in,
+                                                      float *__restrict__ copy_out,
+                                                      OT *__restrict__ out, int H, float eps) {
+  __shared__ float red[4];
+  const size_t base = (size_t)blockIdx.x * H;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < H; k += 256) {
+    const float v = in[base + k];
+    ss += v * v;
+  }
+  ss = block_sum_256(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int k = threadIdx.x; k < H; k += 256) {
+    const float v = in[base + k];
+    if (copy_out) copy_out[base + k] = v;
+    out[base + k] = from_f32<OT>(v * inv);
+  }
+}
+
+// ------------------------------------------------------------------ router logits
+// logits[t][e] = xhat_t . W_r[e] + b_e.  One workgroup per 16 experts; its
+// waves split the hidden dimension and sum through LDS.
+template <class W, int NT>
+__global__ __launch_bounds__(512) void router_logits_kernel(const typename W::T *__restrict__ xhat,
+                                                            const typename W::T *__restrict__ wr,
+                                                            const float *__restrict__ bias,
+                                                            float *__restrict__ logits, int T, int H,
+                                                            int E) {
+  __shared__ float red[8 * NT * 4 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int row0 = blockIdx.x * 16;
+  const int row = row0 + (lane & 15);
+  const bool ok = row < E;
+  int k0, k1;
+  k_slice(H, mfma_kstep<W>(), wave, nw, k0, k1);
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  dense_acc_global<W, typename W::T, NT>(wr + (size_t)(ok ? row : 0) * H, ok, xhat, H, T, k0, k1,
+                                         lane, acc);
+  splitk_sum<NT>(acc, red, wave, nw, lane);
+  if (wave == 0) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = row0 + 4 * (lane >> 4) + r;
+        const int t = n * 16 + (lane & 15);
+        if (e < E && t < T) logits[(size_t)t * E + e] = acc[n][r] + (bias ? bias[e] : 0.f);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ selection helpers
+
+// Wave-wide best (largest value, lowest id on ties).
+__device__ __forceinline__ void wave_argbest(float &v, int &id) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    const float v2 = __shfl_xor(v, s);
+    const int i2 = __shfl_xor(id, s);
+    if (v2 > v || (v2 == v && i2 < id)) { v = v2; id = i2; }
+  }
+}
+
+// One wave picks up to K experts for one position by descending logit (ties to
+// the lower id) among those allowed (allowed == nullptr: all).  lv / pv hold
+// the lane's logits and softmax scores for experts lane + 64j.  Writes the
+// picks and their scores to idx_row / psel_row (-1 / 0 where fewer than K are
+// allowed) and returns nothing; all lanes take part.
+__device__ void wave_topk(const float (&lv)[4], const float (&pv)[4], int E, int K,
+                          const int32_t *allowed, int lane, int32_t *idx_row, float *psel_row) {
+  bool avail[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    avail[j] = e < E && (allowed == nullptr || allowed[e] != 0);
+  }
+  for (int k = 0; k < K; ++k) {
+    float bv = -FLT_MAX;
+    int be = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (avail[j] && (be == INT_MAX || lv[j] > bv)) { bv = lv[j]; be = e; }
+    }
+    wave_argbest(bv, be);
+    float ps = 0.f;
+    if (be != INT_MAX) {
+      const int j = be >> 6;                      // uniform across the wave
+      const float pj = j == 0 ? pv[0] : j == 1 ? pv[1] : j == 2 ? pv[2] : pv[3];
+      ps = __shfl(pj, be & 63);
+      if ((be & 63) == lane) avail[j] = false;
+    }
+    if (lane == 0) {
+      idx_row[k] = be == INT_MAX ? -1 : be;
+      psel_row[k] = ps;
+    }
+  }
+}
+
+struct SelShared {
+  int32_t idx[kMaxT][kMaxK];
+  float psel[kMaxT][kMaxK];
+  double mass[kMaxE];
+  int32_t sorted[kMaxE];
+  int32_t member[kMaxE];
+  int32_t cnt[kMaxE];
+  int32_t wtot[16];
+  int32_t csize;
+};
+
+// Block expert mass, ranking and coreset cut ([P2] coreset section).  Needs
+// sh.idx / sh.psel filled for T positions.  Fills sh.mass, sh.sorted,
+// sh.member and sh.csize.  Called by every thread of a workgroup of >= E
+// threads.
+__device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    double m = 0.0;
+    for (int t = 0; t < T; ++t)
+      for (int k = 0; k < K; ++k)
+        if (sh.idx[t][k] == tid) m += (double)sh.psel[t][k];
+    sh.mass[tid] = m;
+  }
+  __syncthreads();
+  if (tid < E) {
+    const double m = sh.mass[tid];
+    int r = 0;
+    for (int e = 0; e < E; ++e) {
+      const double o = sh.mass[e];
+      r += (o > m) || (o == m && e < tid);
+    }
+    sh.sorted[r] = tid;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double total = 0.0;
+    int npos = 0;
+    for (int r = 0; r < E; ++r) {
+      const double m = sh.mass[sh.sorted[r]];
+      total += m;
+      npos += m > 0.0;
+    }
+    int k = npos;
+    if (top_p < 1.0f) {
+      const double target = (double)top_p * total;
+      double cum = 0.0;
+      k = E;
+      for (int r = 0; r < E; ++r) {
+        cum += sh.mass[sh.sorted[r]];
+        if (cum >= target) { k = r + 1; break; }
+      }
+      k = max(1, min(k, npos));
+    }
+    sh.csize = k;
+  }
+  __syncthreads();
+  if (tid < E) sh.member[tid] = 0;
+  __syncthreads();
+  if (tid < sh.csize) sh.member[sh.sorted[tid]] = 1;
+  __syncthreads();
+}
+
+__device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
+  const int tid = threadIdx.x;
+  if (tid < (E + 31) / 32) {
+    uint32_t b = 0;
+    for (int j = 0; j < 32; ++j) {
+      const int e = tid * 32 + j;
+      if (e < E && sh.member[e]) b |= 1u << j;
+    }
+    bits[tid] = b;
+  }
+}
+
+// ------------------------------------------------------------------ route + select
+// One workgroup of 1024 threads: per-position softmax and top-K, optional
+// coreset and re-routing, then the union of experts and each union expert's
+// list of (position, pick) assignments.
+__global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, int E, int K,
+                                                            float top_p) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  constexpr int kTokPerWave = kMaxT / 16;
+  float lv[kTokPerWave][4], pv[kTokPerWave][4];
+
+  // softmax over all experts and top-K by logit
+  for (int q = 0; q < kTokPerWave; ++q) {
+    const int t = wave + q * nw;
+    if (t >= T) continue;
+    float m = -FLT_MAX;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      lv[q][j] = e < E ? r.logits[(size_t)t * E + e] : -FLT_MAX;
+      m = fmaxf(m, lv[q][j]);
+    }
+    m = wave_max(m);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      pv[q][j] = e < E ? expf(lv[q][j] - m) : 0.f;
+      s += pv[q][j];
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      pv[q][j] = pv[q][j] / s;
+      if (e < E) r.prob[(size_t)t * E + e] = pv[q][j];
+    }
+    wave_topk(lv[q], pv[q], E, K, nullptr, lane, sh.idx[t], sh.psel[t]);
+  }
+  __syncthreads();
+
+  // block mass and coreset (also run without coreset: it reports the union)
+  coreset_core(sh, T, E, K, top_p);
+  if (top_p < 1.0f) {
+    const int kk = min(K, sh.csize);
+    for (int q = 0; q < kTokPerWave; ++q) {
+      const int t = wave + q * nw;
+      if (t >= T) continue;
+      wave_topk(lv[q], pv[q], E, kk, sh.member, lane, sh.idx[t], sh.psel[t]);
+      if (lane == 0)
+        for (int k = kk; k < K; ++k) { sh.idx[t][k] = -1; sh.psel[t][k] = 0.f; }
+    }
+    __syncthreads();
+  }
+
+  // renormalised weights, outputs
+  if (tid < T * K) {
+    const int t = tid / K, k = tid % K;
+    float s = 0.f;
+    for (int j = 0; j < K; ++j) s += sh.psel[t][j];
+    const int e = sh.idx[t][k];
+    r.idx[tid] = e;
+    r.wgt[tid] = e >= 0 ? sh.psel[t][k] / s : 0.f;
+  }
+  if (tid < E) r.mass[tid] = (float)sh.mass[tid];
+  write_bits(sh, E, r.cs_bits);
+
+  // union of experts and assignment lists
+  int n = 0;
+  if (tid < E) {
+    for (int t = 0; t < T; ++t)
+      for (int k = 0; k < K; ++k) n += sh.idx[t][k] == tid;
+  }
+  // exclusive prefix over experts of (n > 0)
+  const int flag = (tid < E && n > 0) ? 1 : 0;
+  int incl = flag;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int o = __shfl_up(incl, s);
+    if (lane >= s) incl += o;
+  }
+  if (lane == 63) sh.wtot[wave] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wave; ++w) off += sh.wtot[w];
+  const int slot = off + incl - flag;
+  if (flag) {
+    r.union_list[slot] = tid;
+    r.slot_n[slot] = n;
+    int j = 0;
+    for (int t = 0; t < T; ++t)
+      for (int k = 0; k < K; ++k)
+        if (sh.idx[t][k] == tid) r.slot_asg[slot * kMaxT + j++] = t * K + k;
+  }
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += sh.wtot[w];
+    r.meta[0] = tot;
+    r.meta[1] = sh.csize;
+    if (r.n_distinct_out) *r.n_distinct_out = tot;
+    if (r.coreset_size_out) *r.coreset_size_out = sh.csize;
+  }
+}
+
+// ------------------------------------------------------------------ coreset alone
+__global__ __launch_bounds__(256) void coreset_kernel(const float *__restrict__ prob,
+                                                      const int32_t *__restrict__ idx, int T,
+                                                      int E, int K, float top_p,
+                                                      uint32_t *__restrict__ bits,
+                                                      int32_t *__restrict__ size,
+                                                      float *__restrict__ mass) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < T * K; i += blockDim.x) {
+    const int t = i / K, k = i % K;
+    const int e = idx[i];
+    const bool ok = e >= 0 && e < E;
+    sh.idx[t][k] = ok ? e : -1;
+    sh.psel[t][k] = ok ? prob[(size_t)t * E + e] : 0.f;
+  }
+  __syncthreads();
+  coreset_core(sh, T, E, K, top_p);
+  write_bits(sh, E, bits);
+  if (tid == 0) *size = sh.csize;
+  if (mass && tid < E) mass[tid] = (float)sh.mass[tid];
+}
+
+// ------------------------------------------------------------------ combine
+// y_t = sum_k P[t*K+k] (live slots) + P_s[t]; h += y; xhat = RMSNorm(h).
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ P,
+                                                      const float *__restrict__ P_s,
+                                                      const int32_t *__restrict__ idx,
+                                                      float *__restrict__ h,
+                                                      float *__restrict__ y_out,
+                                                      OT *__restrict__ xhat_out, int H, int K,
+                                                      float eps) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  uint32_t live = 0;
+  for (int k = 0; k < K; ++k) live |= (idx[t * K + k] >= 0 ? 1u : 0u) << k;
+  const size_t base = (size_t)t * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += 256) {
+    float y = 0.f;
+    for (int k = 0; k < K; ++k)
+      if (live >> k & 1u) y += P[((size_t)t * K + k) * H + c];
+    if (P_s) y += P_s[base + c];
+    if (y_out) y_out[base + c] = y;
+    if (h) {
+      const float v = h[base + c] + y;
+      h[base + c] = v;
+      ss += v * v;
+    }
+  }
+  if (h && xhat_out) {
+    ss = block_sum_256(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int c = threadIdx.x; c < H; c += 256) xhat_out[base + c] = from_f32<OT>(h[base + c] * inv);
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, int T, int H,
+                          hipStream_t s) {
+  if (wdtype == 1)
+    rmsnorm_kernel<bf16_t><<<T, 256, 0, s>>>(in, copy_out, (bf16_t *)out, H, 1e-6f);
+  else
+    rmsnorm_kernel<float><<<T, 256, 0, s>>>(in, copy_out, (float *)out, H, 1e-6f);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(int wdtype, const void *xhat, const void *w_router,
+                                const float *bias, float *logits, int T, int H, int E,
+                                hipStream_t s) {
+  const int grid = (E + 15) / 16;
+  if (wdtype == 1) {
+    if (T <= 16)
+      router_logits_kernel<WBf16, 1><<<grid, 512, 0, s>>>((const bf16_t *)xhat,
+                                                           (const bf16_t *)w_router, bias, logits,
+                                                           T, H, E);
+    else
+      router_logits_kernel<WBf16, 2><<<grid, 512, 0, s>>>((const bf16_t *)xhat,
+                                                           (const bf16_t *)w_router, bias, logits,
+                                                           T, H, E);
+  } else {
+    if (T <= 16)
+      router_logits_kernel<WF32, 1><<<grid, 512, 0, s>>>((const float *)xhat,
+                                                          (const float *)w_router, bias, logits, T,
+                                                          H, E);
+    else
+      router_logits_kernel<WF32, 2><<<grid, 512, 0, s>>>((const float *)xhat,
+                                                          (const float *)w_router, bias, logits, T,
+                                                          H, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_select(const RouteBufs &r, int T, int E, int K, float top_p,
+                               hipStream_t s) {
+  route_select_kernel<<<1, 1024, 0, s>>>(r, T, E, K, top_p);
+  return hipGetLastError();
+}
+
+hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, int K, float top_p,
+                          uint32_t *bits, int32_t *size, float *mass, hipStream_t s) {
+  coreset_kernel<<<1, 256, 0, s>>>(prob, idx, T, E, K, top_p, bits, size, mass);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const int32_t *idx,
+                          float *h, float *y_out, void *xhat_out, int T, int H, int K,
+                          hipStream_t s) {
+  if (wdtype == 1)
+    combine_kernel<bf16_t><<<T, 256, 0, s>>>(P, P_s, idx, h, y_out, (bf16_t *)xhat_out, H, K,
+                                             1e-6f);
+  else
+    combine_kernel<float><<<T, 256, 0, s>>>(P, P_s, idx, h, y_out, (float *)xhat_out, H, K,
+                                            1e-6f);
+  return hipGetLastError();
+}
+
+}  // namespace bdd

@@ -1,0 +1,210 @@
+/*
+ * bdd.h -- C ABI of the block-diffusion decode round on AMD MI355X (gfx950).
+ *
+ * One denoising round of a masked block, as the pages describe it:
+ *   [P1] aitujian.cn article on Clover-35B-A3B-Preview (Chinese):
+ *        section 三 (LowConfidence decoding loop: rules and pseudocode),
+ *        section 四 (40 layers, 256 routed experts, top-8, one shared expert),
+ *        section 五 (a 32-position block touches a union of experts).
+ *   [P2] goremy.ai, "What Is Clover-35B-A3B? Block Diffusion on a Qwen3.6 MoE":
+ *        "How does confidence-threshold block decoding work?" and
+ *        "What is the MoE coreset and why does it matter?".
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a DEVICE pointer owned by the caller, dense
+ *     and row-major in the layout stated.  The library keeps no pointer
+ *     after a call returns and allocates no device memory: scratch space
+ *     comes from the caller's workspace, sized by the *_workspace_bytes
+ *     queries (256-byte aligned base required).
+ *   - Weights are stored [out][in] (input dimension contiguous), in bf16
+ *     (BDD_BF16) or fp32 (BDD_F32); arithmetic accumulates in fp32.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and return without waiting.  Outputs are valid once the stream has
+ *     reached that point.  Calls that share a workspace must not overlap.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     failed check returns a negative status and enqueues nothing.  A
+ *     launch failure returns BDD_ERR_HIP.  bdd_last_error() describes the
+ *     last failure of the calling thread.  No exception crosses the ABI.
+ *   - MASK is -1 and is never a vocabulary candidate.
+ *   - Supported shapes: 1 <= T <= 32; H, I, I_shared multiples of 32;
+ *     1 <= K <= E <= 256; H <= 2048 for the LM head when T > 16 (the block's
+ *     normalised hidden states are kept in the 160 KiB LDS of one CU).
+ */
+#ifndef BDD_H
+#define BDD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BDD_MASK (-1)
+
+typedef enum {
+  BDD_OK = 0,
+  BDD_ERR_INVALID_ARG = -1, /* null pointer, out-of-range size or parameter */
+  BDD_ERR_UNSUPPORTED = -2, /* valid but outside the supported shapes      */
+  BDD_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned  */
+  BDD_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
+} bdd_status;
+
+typedef enum { BDD_F32 = 0, BDD_BF16 = 1 } bdd_dtype;
+
+/* Shapes of one MoE layer and the block.  T block positions, H hidden, E
+ * routed experts, K experts per token, I routed-expert intermediate,
+ * I_shared shared-expert intermediate (0: no shared expert), wdtype the
+ * storage type of every weight (a bdd_dtype). */
+typedef struct {
+  int32_t T, H, E, K, I, I_shared;
+  int32_t wdtype;
+} bdd_moe_dims;
+
+/* Device pointers to one MoE layer's weights ([P1] section 四).
+ *   w_router    [E][H]          router logits l = xhat W_r^T + b
+ *   router_bias [E] fp32        may be NULL (no bias)
+ *   w_gate_up   [E][2I][H]      expert e: rows 0..I-1 gate, I..2I-1 up
+ *   w_down      [E][H][I]
+ *   ws_gate_up  [2I_shared][H]  shared expert (ignored when I_shared == 0)
+ *   ws_down     [H][I_shared] */
+typedef struct {
+  const void *w_router;
+  const float *router_bias;
+  const void *w_gate_up;
+  const void *w_down;
+  const void *ws_gate_up;
+  const void *ws_down;
+} bdd_moe_weights;
+
+/* round_info[4] written by the commit: number of positions written this
+ * round, fallback flag (1 when no masked position reached the threshold and
+ * the most confident one was forced), masked positions left, resolved flag. */
+enum { BDD_RI_COMMITTED = 0, BDD_RI_FALLBACK = 1, BDD_RI_MASKED_LEFT = 2, BDD_RI_RESOLVED = 3 };
+
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes bdd_moe_block_forward needs for these dims (0 if the dims
+ * are invalid). */
+size_t bdd_moe_workspace_bytes(const bdd_moe_dims *d);
+
+/* One MoE FFN layer on a block ([P1] sections 四 and 五; [P2] coreset section).
+ *   h        [T][H] fp32   block hidden states entering the layer (read only)
+ *   The layer normalises h (RMSNorm, eps 1e-6, unit gain; stored as wdtype),
+ *   routes each position to its top-K experts (softmax over all E router
+ *   logits, K largest logits, ties to the lower expert id, weights
+ *   renormalised over the K picks), optionally restricts routing to the
+ *   block coreset, runs each expert of the union once over all positions
+ *   routed to it (SwiGLU: silu(x W_g^T) * (x W_u^T), then W_d), adds the
+ *   ungated shared expert, and combines:
+ *     y_t = sum_k w_tk * Expert_{idx_tk}(xhat_t) + Shared(xhat_t).
+ *   coreset_top_p  >= 1: no coreset.  In (0,1): each expert's mass is the sum
+ *                  of the softmax scores of the positions that picked it; the
+ *                  coreset is the shortest prefix of experts ranked by mass
+ *                  (ties to the lower id) whose mass reaches top_p of the
+ *                  total; each position then re-takes its min(K,|C|) largest
+ *                  logits inside the coreset and renormalises.
+ *   y          [T][H] fp32 out    the layer output (residual not added)
+ *   xhat_out   [T][H] wdtype out  normalised input (may be NULL)
+ *   topk_idx   [T][K] int32 out   picked experts in descending-logit order;
+ *                                 -1 in slots beyond min(K,|C|)
+ *   topk_w     [T][K] fp32 out    their weights (0 in unused slots)
+ *   n_distinct [1] int32 out      size of the union of experts read
+ *   coreset_bits [ceil(E/32)] uint32 out, coreset_size [1] int32 out:
+ *                                 coreset membership bitset and size (both
+ *                                 may be NULL; without coreset every expert
+ *                                 with positive mass is reported) */
+bdd_status bdd_moe_block_forward(const bdd_moe_dims *d, const bdd_moe_weights *w,
+                                 const float *h, float coreset_top_p, float *y,
+                                 void *xhat_out, int32_t *topk_idx, float *topk_w,
+                                 int32_t *n_distinct, uint32_t *coreset_bits,
+                                 int32_t *coreset_size, void *ws, size_t ws_bytes,
+                                 void *stream);
+
+/* Block coreset selection alone ([P2] "What is the MoE coreset"): from the
+ * routing of a block, sum each expert's softmax scores over the positions
+ * that picked it, rank experts by that mass (descending, ties to the lower
+ * id) and keep the shortest ranked prefix reaching top_p of the total mass
+ * (top_p >= 1: every expert with positive mass).
+ *   router_prob [T][E] fp32   softmax scores p_te
+ *   topk_idx    [T][K] int32  each position's picks (entries < 0 ignored)
+ *   coreset_bits [ceil(E/32)] uint32 out, coreset_size [1] int32 out,
+ *   expert_mass [E] fp32 out (may be NULL).
+ * Needs no workspace. */
+bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx,
+                              int32_t T, int32_t E, int32_t K, float top_p,
+                              uint32_t *coreset_bits, int32_t *coreset_size,
+                              float *expert_mass, void *stream);
+
+/* Workspace bytes bdd_lmhead_confidence_commit needs. */
+size_t bdd_lmhead_workspace_bytes(int32_t T, int32_t H, int32_t V);
+
+/* LM head, confidence and LowConfidence commit ([P1] section 三 pseudocode
+ * and rules; [P2] decoding-loop steps 2-4).
+ *   hhat   [T][H] dtype     normalised final hidden states
+ *   w_lm   [V][H] dtype     output embedding rows
+ *   For each position: logits z = hhat W_lm^T (never stored), conf = max
+ *   softmax probability = 1 / sum_v exp(z_v - max z), choice = argmax (lowest
+ *   token id on ties).  Then among positions whose token is MASK: every one
+ *   with conf >= threshold is written with its choice; if none qualifies, the
+ *   single most confident masked position (lowest index on ties) is written.
+ *   Written tokens never change.
+ *   tokens     [T] int32 in/out   MASK (-1) = not yet written
+ *   conf       [T] fp32 out, choice [T] int32 out (all positions)
+ *   round_info [4] int32 out      see BDD_RI_*
+ *   threshold in (0, 1]. */
+bdd_status bdd_lmhead_confidence_commit(const void *hhat, const void *w_lm, int32_t T,
+                                        int32_t H, int32_t V, int32_t dtype,
+                                        float threshold, int32_t *tokens, float *conf,
+                                        int32_t *choice, int32_t *round_info, void *ws,
+                                        size_t ws_bytes, void *stream);
+
+/* Workspace bytes bdd_block_denoise_round needs. */
+size_t bdd_round_workspace_bytes(const bdd_moe_dims *d, int32_t V);
+
+/* One full denoising round ([P1] section 三 pseudocode, one pass of the inner
+ * loop): the block's hidden states go through n_layers MoE layers with the
+ * mixer replaced by identity (h <- h + MoE(RMSNorm(h)), as in
+ * bdd_moe_block_forward), a final RMSNorm stored as wdtype, the LM head and
+ * the commit (as in bdd_lmhead_confidence_commit).
+ *   layers       HOST array [n_layers] of device weight pointers
+ *   x_in         [T][H] fp32 hidden states entering layer 0 (read only)
+ *   w_lm         [V][H] wdtype
+ *   tokens, conf, choice, round_info as in bdd_lmhead_confidence_commit
+ *   layer_topk_idx   [n_layers][T][K] int32 out (may be NULL)
+ *   layer_n_distinct [n_layers] int32 out (may be NULL)
+ *   hhat_out     [T][H] wdtype out: the LM-head input (may be NULL) */
+bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
+                                   const bdd_moe_weights *layers, float coreset_top_p,
+                                   const void *w_lm, int32_t V, float threshold,
+                                   const float *x_in, int32_t *tokens, float *conf,
+                                   int32_t *choice, int32_t *round_info,
+                                   int32_t *layer_topk_idx, int32_t *layer_n_distinct,
+                                   void *hhat_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Human-readable name of a status, and the calling thread's last error. */
+const char *bdd_status_string(int32_t status);
+const char *bdd_last_error(void);
+
+/* Number of compute units of the current HIP device that the kernels size
+ * their grids for. */
+int32_t bdd_device_cus(void);
+
+/* Kernel timing for measurement tools.  While enabled, every kernel launch of
+ * this library whose name contains `filter` (NULL or "": all) is bracketed by
+ * a pair of hipEvents recorded on the launching stream.  Kernel names:
+ * rmsnorm, router_logits, route_select, coreset, shared_gateup, routed_gateup,
+ * shared_down, routed_down, combine, lmhead, commit.  Not thread-safe. */
+bdd_status bdd_timing_enable(int32_t on, const char *filter);
+
+/* Waits for the recorded events, then for up to max_kernels distinct kernel
+ * names writes the name (64-byte slots in `names`), the summed duration in ms
+ * and the launch count, clears the records and returns the number of distinct
+ * names (negative status on failure). */
+int32_t bdd_timing_read(int32_t max_kernels, char *names, double *total_ms, int32_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDD_H */

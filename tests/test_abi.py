@@ -1,0 +1,106 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/bdd.h declares, sizes workspaces, and rejects bad arguments on the
+host before touching a GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_diffusion_decode_amd as bdd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bdd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bdd.LIB_PATH),
+                                reason="libbdd.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bdd_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared()
+    for n in ("bdd_moe_block_forward", "bdd_coreset_select", "bdd_lmhead_confidence_commit",
+              "bdd_block_denoise_round"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bdd.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert sorted(bdd.EXPORTS) == sorted(_declared())
+
+
+def test_status_strings():
+    L = bdd.lib()
+    assert L.bdd_status_string(0) == b"BDD_OK"
+    assert L.bdd_status_string(-1) == b"BDD_ERR_INVALID_ARG"
+    assert L.bdd_status_string(-3) == b"BDD_ERR_WORKSPACE"
+
+
+def test_workspace_queries():
+    d = bdd.MoEDims(32, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    m = bdd.moe_workspace_bytes(d)
+    # at least the per-pick activations and outputs: T*K*(I + H) fp32
+    assert m >= 32 * 8 * (512 + 2048) * 4
+    assert bdd.round_workspace_bytes(d, 248320) > m
+    assert bdd.lmhead_workspace_bytes(32, 2048, 248320) > 0
+    bad = bdd.MoEDims(33, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    assert bdd.moe_workspace_bytes(bad) == 0
+    assert bdd.lmhead_workspace_bytes(0, 2048, 10) == 0
+
+
+def _call_moe(d):
+    L = bdd.lib()
+    w = bdd._Weights(1, None, 1, 1, 1, 1)
+    return L.bdd_moe_block_forward(ctypes.byref(d.c()), ctypes.byref(w), ctypes.c_void_p(1), 1.0,
+                                   ctypes.c_void_p(1), None, ctypes.c_void_p(1), ctypes.c_void_p(1),
+                                   ctypes.c_void_p(1), None, None, None, 0, None)
+
+
+@pytest.mark.parametrize("dims,status", [
+    ((0, 256, 16, 4, 128, 128, 0), -1),       # T < 1
+    ((33, 256, 16, 4, 128, 128, 0), -2),      # T > 32
+    ((8, 256, 16, 17, 128, 128, 0), -1),      # K > E
+    ((8, 250, 16, 4, 128, 128, 0), -2),       # H not a multiple of 32
+    ((8, 256, 300, 4, 128, 128, 0), -2),      # E > 256
+    ((8, 256, 16, 4, 128, 128, 7), -1),       # bad dtype
+    ((8, 256, 16, 4, 128, 128, 0), -3),       # valid dims, missing workspace
+])
+def test_moe_forward_rejects_on_host(dims, status):
+    assert _call_moe(bdd.MoEDims(*dims)) == status
+    assert bdd.lib().bdd_last_error()
+
+
+def test_lmhead_rejects_bad_threshold_and_shapes():
+    L = bdd.lib()
+    p = ctypes.c_void_p(1)
+    args = lambda T, H, V, dt, thr: (p, p, T, H, V, dt, thr, p, p, p, p, None, 0, None)
+    assert L.bdd_lmhead_confidence_commit(*args(32, 2048, 1000, 1, 0.0)) == -1
+    assert L.bdd_lmhead_confidence_commit(*args(32, 2048, 1000, 1, 1.5)) == -1
+    assert L.bdd_lmhead_confidence_commit(*args(32, 4096, 1000, 1, 0.95)) == -2   # LDS budget
+    assert L.bdd_lmhead_confidence_commit(*args(32, 2048, 1000, 1, 0.95)) == -3   # no workspace
+    assert L.bdd_lmhead_confidence_commit(None, p, 32, 2048, 10, 1, 0.95, p, p, p, p, p, 1 << 30, None) == -1
+
+
+def test_coreset_rejects_on_host():
+    L = bdd.lib()
+    p = ctypes.c_void_p(1)
+    assert L.bdd_coreset_select(p, p, 4, 16, 4, 0.0, p, p, None, None) == -1
+    assert L.bdd_coreset_select(p, p, 4, 16, 20, 0.9, p, p, None, None) == -1
+    assert L.bdd_coreset_select(None, p, 4, 16, 4, 0.9, p, p, None, None) == -1
+
+
+def test_round_rejects_null_layers():
+    L = bdd.lib()
+    d = bdd.MoEDims(8, 256, 16, 4, 128, 128, 0)
+    p = ctypes.c_void_p(1)
+    st = L.bdd_block_denoise_round(ctypes.byref(d.c()), 2, None, 1.0, p, 1024, 0.95, p, p, p, p, p,
+                                   None, None, None, None, 0, None)
+    assert st == -1

@@ -1,0 +1,129 @@
+"""GPU parity at the full Clover shapes (hidden 2048, 256 experts top-8,
+intermediate 512, vocab 248320, block 32), in the launch configuration the
+benchmark times, against the CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_decode_amd as bdd
+import oracle as O
+import workloads as W
+from gpu_helpers import (BAND, TAU, assert_close, bf16_ulp, commit_in_band, coreset_in_band, dims_of,
+                         f64, oracle_layer, top2_gap, topk_gap)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+C1 = W.C1
+
+
+def _phase1_idx(l, K):
+    return np.argsort(-l, axis=1, kind="stable")[:, :K]
+
+
+@pytest.mark.parametrize("bias,top_p", [("flat", 1.0), ("zipf", 1.0), ("zipf", 0.9), ("zipf", 0.7)])
+def test_moe_layer_full_shape(bias, top_p):
+    seed = 0
+    layer = W.layer_weights(seed, 0, C1, device=DEV, bias=bias, gamma=1.0)
+    h = W.block_hidden(seed, C1, device=DEV)
+    out = bdd.moe_block_forward(dims_of(C1), layer, h, top_p)
+    torch.cuda.synchronize()
+    xh = O.bf16_round(O.rmsnorm(f64(h)))
+    y_ref, info = O.moe_layer(xh, oracle_layer(layer), C1.K, top_p)
+    gx = f64(out["xhat"])
+    assert np.all(np.abs(gx - xh) <= bf16_ulp(xh) * 1.0001)
+    band = topk_gap(info["logits"], C1.K) < BAND
+    if info["coreset"] is not None:
+        m = info["coreset"]
+        band |= topk_gap(info["logits"][:, m], min(C1.K, len(m))) < BAND
+    cband = coreset_in_band(info["p"], _phase1_idx(info["logits"], C1.K), top_p)
+    print(f"{bias} top_p={top_p}: union {len(info['union'])} experts, "
+          f"coreset {None if info['coreset'] is None else len(info['coreset'])}, band positions {int(band.sum())}")
+    if cband or (band.any() and top_p < 1.0):
+        pytest.skip("coreset decision inside the margin band")
+    gi = out["topk_idx"].cpu().numpy()
+    for t in np.nonzero(~band)[0]:
+        assert set(int(e) for e in gi[t] if e >= 0) == set(int(e) for e in info["idx"][t]), t
+    if not band.any():
+        assert int(out["n_distinct"].item()) == len(info["union"])
+    assert_close(f64(out["y"])[~band], y_ref[~band], "y")
+
+
+@pytest.fixture(scope="module")
+def lm_full():
+    seed = 0
+    w_lm = W.lm_head_weight(seed, C1, device=DEV)
+    wl = f64(w_lm)       # float64 copy on the host for the oracle (4 GB)
+    return seed, w_lm, wl
+
+
+@pytest.mark.parametrize("p", [0.5, 0.2, 0.05])
+def test_lmhead_commit_full_resolve(lm_full, p):
+    seed, w_lm, wl = lm_full
+    R = 32
+    h, _ = W.lmhead_stub_inputs(seed, C1, R, p=p)
+    tok = torch.full((C1.T,), bdd.MASK, dtype=torch.int32, device=DEV)
+    tok_ref = np.full(C1.T, O.MASK)
+    ws = torch.empty(bdd.lmhead_workspace_bytes(C1.T, C1.H, C1.V), dtype=torch.uint8, device=DEV)
+    rounds = fallbacks = 0
+    for r in range(R):
+        hr = h[r].contiguous().to(DEV)
+        prev = tok.cpu().numpy().copy()
+        conf, choice, ri = bdd.lmhead_confidence_commit(hr, w_lm, tok, ws=ws)
+        torch.cuda.synchronize()
+        c_ref, ch_ref, z = O.lm_head_confidence(f64(hr), wl)
+        assert_close(conf.cpu().numpy(), c_ref, f"conf round {r}")
+        ok = top2_gap(z) >= BAND
+        assert np.array_equal(choice.cpu().numpy()[ok], ch_ref[ok])
+        assert not commit_in_band(tok_ref, c_ref), f"round {r}: stub landed in the margin band"
+        tok_ref, acc, fb, left, done = O.commit(tok_ref, c_ref, ch_ref, TAU)
+        got = tok.cpu().numpy()
+        assert np.array_equal(got, tok_ref), (r, got, tok_ref)
+        assert ri.cpu().tolist() == [len(acc), int(fb), left, int(done)]
+        assert np.all(got[prev != O.MASK] == prev[prev != O.MASK])
+        rounds += 1
+        fallbacks += int(fb)
+        if done:
+            break
+    assert done
+    print(f"p={p}: resolved in {rounds} rounds with {fallbacks} fallback rounds")
+
+
+def test_full_round_clover_layer_plus_lm_head(lm_full):
+    """The benchmark's round: one Clover-shaped MoE layer (flat routing), final
+    RMSNorm, the full LM head and the commit; two rounds checked."""
+    seed, _, _ = lm_full
+    x, info = W.planted_round_inputs(seed, C1, rounds=2, p=0.3, amp_pass=24.0, amp_fail=(10.0, 14.0))
+    layer = W.layer_weights(seed, 0, C1, device=DEV)
+    w_lm = W.lm_head_weight(seed, C1, device=DEV, unit_rows=info["unit_rows"])
+    wl = f64(w_lm)
+    plan = bdd.RoundPlan(dims_of(C1), [layer], w_lm, 1.0)
+    T = C1.T
+    tok = torch.full((T,), bdd.MASK, dtype=torch.int32, device=DEV)
+    conf = torch.empty(T, dtype=torch.float32, device=DEV)
+    choice = torch.empty(T, dtype=torch.int32, device=DEV)
+    ri = torch.empty(4, dtype=torch.int32, device=DEV)
+    ltk = torch.empty((1, T, C1.K), dtype=torch.int32, device=DEV)
+    hh_gpu = torch.empty((T, C1.H), dtype=torch.bfloat16, device=DEV)
+    ol = [oracle_layer(layer)]
+    tok_ref = np.full(T, O.MASK)
+    for r in range(2):
+        plan(x[r].to(DEV), tok, conf, choice, ri, ltk, None, hh_gpu)
+        torch.cuda.synchronize()
+        hh, infos = O.moe_stack(x[r].double().numpy(), ol, C1.K, 1.0)
+        band = topk_gap(infos[0]["logits"], C1.K) < BAND
+        g = ltk.cpu().numpy()[0]
+        for t in np.nonzero(~band)[0]:
+            assert set(g[t].tolist()) == set(int(e) for e in infos[0]["idx"][t])
+        keep = ~band
+        assert np.all(np.abs(f64(hh_gpu)[keep] - hh[keep]) <= 2 * bf16_ulp(hh[keep]) + 1e-6)
+        c_ref, ch_ref, z = O.lm_head_confidence(hh, wl)
+        assert_close(conf.cpu().numpy()[keep], c_ref[keep], f"conf round {r}")
+        ok = keep & (top2_gap(z) >= BAND)
+        assert np.array_equal(choice.cpu().numpy()[ok], ch_ref[ok])
+        if band.any() or commit_in_band(tok_ref, c_ref):
+            pytest.skip(f"round {r}: a decision inside the margin band")
+        tok_ref, acc, fb, left, done = O.commit(tok_ref, c_ref, ch_ref, TAU)
+        assert np.array_equal(tok.cpu().numpy(), tok_ref)
+        assert ri.cpu().tolist() == [len(acc), int(fb), left, int(done)]
+        print(f"round {r}: committed {len(acc)} fallback {fb}")

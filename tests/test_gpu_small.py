@@ -1,0 +1,277 @@
+"""GPU parity at small sizes: every entry point through the C ABI against the
+CPU oracle on the same seeded inputs, element by element.  Sizes span several
+tiles with ragged tails (T=13 of 16/32, V=5003 = 312 tiles of 16 + 11, E=40
+of 64-lane groups)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_decode_amd as bdd
+import oracle as O
+import workloads as W
+from gpu_helpers import (BAND, TAU, assert_close, bf16_ulp, commit_in_band, coreset_in_band, dims_of,
+                         f64, oracle_layer, top2_gap, topk_gap)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+SMALL_BF16 = W.Dims("small_bf16", T=13, H=256, E=40, K=6, I=96, I_s=64, V=5003, wdtype="bf16",
+                    w_std=0.05, lm_std=256 ** -0.5)
+SMALL_F32 = W.C0
+
+
+def _moe_case(d, seed, bias, top_p):
+    layer = W.layer_weights(seed, 0, d, device=DEV, bias=bias, gamma=1.0)
+    h = W.block_hidden(seed, d, device=DEV)
+    out = bdd.moe_block_forward(dims_of(d), layer, h, top_p)
+    torch.cuda.synchronize()
+    hn = O.rmsnorm(f64(h))
+    xh = O.bf16_round(hn) if d.wdtype == "bf16" else hn
+    y_ref, info = O.moe_layer(xh, oracle_layer(layer), d.K, top_p)
+    return out, y_ref, info, xh
+
+
+def _check_moe(d, out, y_ref, info, xh, top_p):
+    # normalised input: bf16 values within one unit in the last place (rounding
+    # of an fp32 vs fp64 norm can differ only next to a rounding midpoint)
+    gx = f64(out["xhat"])
+    if d.wdtype == "bf16":
+        diff = np.abs(gx - xh)
+        assert np.all(diff <= bf16_ulp(xh) * 1.0001)
+        assert int((diff > 0).sum()) <= max(2, gx.size // 1000)
+    else:
+        assert_close(gx, xh, "xhat", abs_=1e-6, rel=1e-5)
+
+    l = info["logits"]
+    band_tok = topk_gap(l, d.K) < BAND
+    if info["coreset"] is not None:
+        m = info["coreset"]
+        band_tok |= topk_gap(l[:, m], min(d.K, len(m))) < BAND
+    glob_band = bool(band_tok.any()) and top_p < 1.0 or coreset_in_band(info["p"], _phase1_idx(l, d.K), top_p)
+    gi = out["topk_idx"].cpu().numpy()
+    gw = out["topk_w"].cpu().numpy()
+    if not glob_band:
+        for t in range(d.T):
+            if band_tok[t]:
+                continue
+            ref = {int(e): w for e, w in zip(info["idx"][t], info["w"][t])}
+            got = {int(e): float(w) for e, w in zip(gi[t], gw[t]) if e >= 0}
+            assert set(got) == set(ref), (t, sorted(got), sorted(ref))
+            assert_close([got[e] for e in ref], [ref[e] for e in ref], f"topk_w[{t}]")
+            assert all(w == 0.0 for e, w in zip(gi[t], gw[t]) if e < 0)
+        if not band_tok.any():
+            assert int(out["n_distinct"].item()) == len(info["union"])
+            members = info["coreset"] if info["coreset"] is not None else np.array(info["union"])
+            bits = out["coreset_bits"].cpu().numpy().view(np.uint32)
+            got = [e for e in range(d.E) if bits[e // 32] >> (e % 32) & 1]
+            assert got == sorted(int(e) for e in members)
+            assert int(out["coreset_size"].item()) == len(members)
+        keep = ~band_tok
+        assert_close(f64(out["y"])[keep], y_ref[keep], "y")
+    return int(band_tok.sum()), glob_band
+
+
+def _phase1_idx(l, K):
+    return np.argsort(-l, axis=1, kind="stable")[:, :K]
+
+
+@pytest.mark.parametrize("bias,top_p", [("flat", 1.0), ("zipf", 1.0), ("zipf", 0.7), ("zipf", 0.9)])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_moe_forward_small_bf16(seed, bias, top_p):
+    d = SMALL_BF16
+    out, y_ref, info, xh = _moe_case(d, seed, bias, top_p)
+    nb, gb = _check_moe(d, out, y_ref, info, xh, top_p)
+    print(f"seed {seed} {bias} top_p {top_p}: |U|={len(info['union'])} band positions {nb} coreset band {gb}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_moe_forward_tiny_fp32(seed):
+    d = SMALL_F32
+    out, y_ref, info, xh = _moe_case(d, seed, "flat", 1.0)
+    _check_moe(d, out, y_ref, info, xh, 1.0)
+
+
+def test_moe_forward_deterministic():
+    d = SMALL_BF16
+    layer = W.layer_weights(5, 0, d, device=DEV, bias="zipf")
+    h = W.block_hidden(5, d, device=DEV)
+    a = bdd.moe_block_forward(dims_of(d), layer, h, 0.9)
+    b = bdd.moe_block_forward(dims_of(d), layer, h, 0.9)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_moe_single_position_block():
+    # block_size 1: the block's routing is the position's own top-K
+    d = W.Dims("one", T=1, H=256, E=40, K=6, I=96, I_s=64, V=16, wdtype="bf16", w_std=0.05, lm_std=0.06)
+    out, y_ref, info, xh = _moe_case(d, 4, "flat", 1.0)
+    _check_moe(d, out, y_ref, info, xh, 1.0)
+    assert int(out["n_distinct"].item()) == d.K
+
+
+@pytest.mark.parametrize("top_p", [0.5, 0.7, 0.9, 1.0])
+def test_coreset_select_api(top_p):
+    rng = np.random.default_rng(int(top_p * 100))
+    T, E, K = 32, 256, 8
+    l = rng.normal(size=(T, E)) * 0.9 - 1.1 * np.log(rng.permutation(E) + 1.0)
+    p32 = torch.softmax(torch.tensor(l, dtype=torch.float64), dim=1).float()
+    idx = np.argsort(-l, axis=1, kind="stable")[:, :K]
+    p = p32.double().numpy()
+    bits, size, mass = bdd.coreset_select(p32.to(DEV), torch.tensor(idx, dtype=torch.int32, device=DEV), top_p)
+    torch.cuda.synchronize()
+    members, mref, _ = O.coreset_select(p, idx, top_p)
+    assert_close(mass.cpu().numpy(), mref, "mass", abs_=1e-6, rel=1e-6)
+    if coreset_in_band(p, idx, top_p):
+        pytest.skip("coreset cut inside the margin band for this draw")
+    b = bits.cpu().numpy().view(np.uint32)
+    got = [e for e in range(E) if b[e // 32] >> (e % 32) & 1]
+    assert got == sorted(int(e) for e in members) and int(size.item()) == len(members)
+
+
+def _lm_dims(dt, T=7, H=256, V=5003):
+    return W.Dims("lm_small", T=T, H=H, E=1, K=1, I=32, I_s=0, V=V, wdtype=dt, w_std=0.02,
+                  lm_std=H ** -0.5)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_lmhead_commit_multiround_small(dt, seed):
+    d = _lm_dims(dt)
+    R = 8
+    # conf = 0.95 sits near logit 12 at V=5003: passing peaks 14.5-16.5, failing 6-10
+    h, _ = W.lmhead_stub_inputs(seed, d, R, p=0.3, pass_logit=(14.5, 16.5), fail_logit=(6.0, 10.0))
+    w_lm = W.lm_head_weight(seed, d, device=DEV)
+    wl = f64(w_lm)
+    h = h.to(torch.float32) if dt == "f32" else h
+    tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=DEV)
+    tok_ref = np.full(d.T, O.MASK)
+    for r in range(R):
+        hr = h[r].contiguous().to(DEV)
+        prev = tok.cpu().numpy().copy()
+        conf, choice, ri = bdd.lmhead_confidence_commit(hr, w_lm, tok)
+        torch.cuda.synchronize()
+        c_ref, ch_ref, z = O.lm_head_confidence(f64(hr), wl)
+        assert_close(conf.cpu().numpy(), c_ref, f"conf round {r}")
+        ok = top2_gap(z) >= BAND
+        assert np.array_equal(choice.cpu().numpy()[ok], ch_ref[ok])
+        if commit_in_band(tok_ref, c_ref):
+            pytest.skip(f"round {r}: commit inside the margin band")
+        tok_ref, acc, fb, left, done = O.commit(tok_ref, c_ref, ch_ref, TAU)
+        got = tok.cpu().numpy()
+        assert np.array_equal(got, tok_ref), (r, got, tok_ref)
+        assert ri.cpu().tolist() == [len(acc), int(fb), left, int(done)]
+        assert np.all(got[prev != O.MASK] == prev[prev != O.MASK])
+        if done:
+            break
+    assert done
+
+
+def test_lmhead_all_equal_logits_and_single_position():
+    # identical rows: conf = 1/V and choice = 0 for every position
+    d = _lm_dims("bf16", T=3, V=777)
+    row = W.counter_normal(W.key_of(9, "row"), d.H, 0.05).to(torch.bfloat16)
+    w_lm = row.repeat(d.V, 1).contiguous().to(DEV)
+    h = W.counter_normal(W.key_of(9, "h"), d.T * d.H, 1.0).to(torch.bfloat16).reshape(d.T, d.H).to(DEV)
+    tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=DEV)
+    conf, choice, ri = bdd.lmhead_confidence_commit(h, w_lm, tok)
+    torch.cuda.synchronize()
+    assert_close(conf.cpu().numpy(), np.full(d.T, 1.0 / d.V), "conf", abs_=1e-7, rel=1e-4)
+    assert choice.cpu().tolist() == [0, 0, 0]
+    assert ri.cpu().tolist()[:2] == [1, 1] and tok.cpu().tolist() == [0, -1, -1]
+    # one position: one round writes its argmax whatever its confidence (autoregressive)
+    d1 = _lm_dims("bf16", T=1, V=5003)
+    w = W.lm_head_weight(2, d1, device=DEV)
+    h1 = W.counter_normal(W.key_of(2, "h1"), d1.H, 1.0).to(torch.bfloat16).reshape(1, d1.H).to(DEV)
+    t1 = torch.full((1,), bdd.MASK, dtype=torch.int32, device=DEV)
+    conf, choice, ri = bdd.lmhead_confidence_commit(h1, w, t1)
+    torch.cuda.synchronize()
+    c_ref, ch_ref, z = O.lm_head_confidence(f64(h1), f64(w))
+    assert ri.cpu().tolist() == [1, int(c_ref[0] < TAU), 0, 1]
+    if top2_gap(z)[0] >= BAND:
+        assert t1.item() == ch_ref[0]
+
+
+def test_lmhead_already_resolved_block_is_left_alone():
+    d = _lm_dims("bf16", T=5, V=300)
+    w = W.lm_head_weight(1, d, device=DEV)
+    h = W.counter_normal(W.key_of(1, "h"), d.T * d.H, 1.0).to(torch.bfloat16).reshape(d.T, d.H).to(DEV)
+    tok = torch.tensor([3, 1, 4, 1, 5], dtype=torch.int32, device=DEV)
+    conf, choice, ri = bdd.lmhead_confidence_commit(h, w, tok)
+    torch.cuda.synchronize()
+    assert tok.cpu().tolist() == [3, 1, 4, 1, 5] and ri.cpu().tolist() == [0, 0, 0, 1]
+
+
+def _round_case(d, seed, n_layers, bias, top_p, R, amp_pass, amp_fail, p=0.4):
+    x, info = W.planted_round_inputs(seed, d, rounds=R, p=p, amp_pass=amp_pass, amp_fail=amp_fail)
+    layers = [W.layer_weights(seed, l, d, device=DEV, bias=bias) for l in range(n_layers)]
+    w_lm = W.lm_head_weight(seed, d, device=DEV, unit_rows=info["unit_rows"])
+    return x, layers, w_lm
+
+
+@pytest.mark.parametrize("case", ["c0_fp32_1layer", "bf16_2layers_coreset"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_block_denoise_round_small(case, seed):
+    if case == "c0_fp32_1layer":
+        d, L, bias, top_p, amp = W.C0, 1, "flat", 1.0, (32.0, (3.0, 7.0))
+    else:
+        d, L, bias, top_p, amp = SMALL_BF16, 2, "zipf", 0.7, (40.0, (4.0, 9.0))
+    R = 8
+    x, layers, w_lm = _round_case(d, seed, L, bias, top_p, R, amp[0], amp[1])
+    plan = bdd.RoundPlan(dims_of(d), layers, w_lm, top_p)
+    tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=DEV)
+    conf = torch.empty(d.T, dtype=torch.float32, device=DEV)
+    choice = torch.empty(d.T, dtype=torch.int32, device=DEV)
+    ri = torch.empty(4, dtype=torch.int32, device=DEV)
+    ltk = torch.empty((L, d.T, d.K), dtype=torch.int32, device=DEV)
+    lnd = torch.empty(L, dtype=torch.int32, device=DEV)
+    hh_gpu = torch.empty((d.T, d.H), dtype=d.torch_wdtype, device=DEV)
+    ol = [oracle_layer(w) for w in layers]
+    wl = f64(w_lm)
+    tok_ref = np.full(d.T, O.MASK)
+    rb = d.wdtype == "bf16"
+    for r in range(R):
+        plan(x[r].to(DEV), tok, conf, choice, ri, ltk, lnd, hh_gpu)
+        torch.cuda.synchronize()
+        hh, infos = O.moe_stack(x[r].double().numpy(), ol, d.K, top_p, round_bf16=rb)
+        # routing of every layer, outside the margin band; a flip upstream
+        # excludes that position downstream
+        flipped = np.zeros(d.T, dtype=bool)
+        g_idx = ltk.cpu().numpy()
+        for li, inf in enumerate(infos):
+            band = topk_gap(inf["logits"], d.K) < BAND
+            if inf["coreset"] is not None:
+                band |= topk_gap(inf["logits"][:, inf["coreset"]], min(d.K, len(inf["coreset"]))) < BAND
+                if band.any() or coreset_in_band(inf["p"], _phase1_idx(inf["logits"], d.K), top_p):
+                    flipped[:] = True
+            flipped |= band
+            for t in np.nonzero(~flipped)[0]:
+                assert set(int(e) for e in g_idx[li, t] if e >= 0) == set(int(e) for e in inf["idx"][t]), (r, li, t)
+        keep = ~flipped
+        if rb:
+            diff = np.abs(f64(hh_gpu)[keep] - hh[keep])
+            assert np.all(diff <= 2 * bf16_ulp(hh[keep]) + 1e-6)
+        c_ref, ch_ref, z = O.lm_head_confidence(hh, wl)
+        assert_close(conf.cpu().numpy()[keep], c_ref[keep], f"conf round {r}")
+        ok = keep & (top2_gap(z) >= BAND)
+        assert np.array_equal(choice.cpu().numpy()[ok], ch_ref[ok])
+        if flipped.any() or commit_in_band(tok_ref, c_ref):
+            pytest.skip(f"round {r}: a decision inside the margin band")
+        tok_ref, acc, fb, left, done = O.commit(tok_ref, c_ref, ch_ref, TAU)
+        assert np.array_equal(tok.cpu().numpy(), tok_ref), (r, tok.cpu().numpy(), tok_ref)
+        assert ri.cpu().tolist() == [len(acc), int(fb), left, int(done)]
+        if done:
+            break
+    assert done
+
+
+def test_generator_gpu_matches_cpu():
+    for key, n in ((W.key_of(1, "a"), 100003), (W.key_of(2, "b"), 3 * (1 << 23) + 5)):
+        a = W.counter_normal(key, n, 0.02, device="cpu")
+        b = W.counter_normal(key, n, 0.02, device=DEV).cpu()
+        assert torch.equal(a, b)
+        assert torch.equal(a.to(torch.bfloat16), b.to(torch.bfloat16))
+    u1 = W.counter_uniform(W.key_of(3), 5000)
+    u2 = W.counter_uniform(W.key_of(3), 5000, device=DEV).cpu()
+    assert torch.equal(u1, u2)
