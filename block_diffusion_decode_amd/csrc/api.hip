@@ -70,7 +70,7 @@ bool timing_wants(const char *name) {
   } while (0)
 
 constexpr int kMaxLmGrid = 1024;
-constexpr int kExpertWgPerCu = 4;
+constexpr int kExpertWgPerCu = 3;
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int wdtype) { return wdtype == BDD_BF16 ? 2 : 4; }
@@ -99,9 +99,9 @@ bdd_status check_dims(const bdd_moe_dims *d) {
   if (d->T > kMaxT) return fail(BDD_ERR_UNSUPPORTED, "T=%d exceeds %d", d->T, kMaxT);
   if (d->E > kMaxE) return fail(BDD_ERR_UNSUPPORTED, "E=%d exceeds %d", d->E, kMaxE);
   if (d->K > 32) return fail(BDD_ERR_UNSUPPORTED, "K=%d exceeds 32", d->K);
-  if (d->H % 32 || d->I % 32 || d->I_shared % 32)
-    return fail(BDD_ERR_UNSUPPORTED, "H=%d, I=%d, I_shared=%d must be multiples of 32", d->H, d->I,
-                d->I_shared);
+  if (d->H % 128 || d->I % 32 || d->I_shared % 32)
+    return fail(BDD_ERR_UNSUPPORTED, "H=%d must be a multiple of 128, I=%d and I_shared=%d of 32", d->H,
+                d->I, d->I_shared);
   if (d->H > 8192 || d->I > 8192 || d->I_shared > 8192)
     return fail(BDD_ERR_UNSUPPORTED, "H, I, I_shared must be <= 8192");
   return BDD_OK;
@@ -214,7 +214,7 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
   LAUNCH("route_select", s, launch_route_select(r, T, E, K, top_p, s));
   if (Is > 0) LAUNCH("shared_gateup", s, launch_shared_gateup(d.wdtype, xhat, w.ws_gate_up, A_s, T, H, Is, s));
   const int union_max = E < T * K ? E : T * K;
-  int g1 = union_max * (I / 16), g2 = union_max * (H / 32);
+  int g1 = union_max * (I / 16), g2 = union_max * (H / 128);
   const int cap = cus * kExpertWgPerCu;
   g1 = g1 < cap ? g1 : cap;
   g2 = g2 < cap ? g2 : cap;

@@ -8,6 +8,8 @@
 // many positions) and section 四 (one shared expert per layer).  The expert
 // activation (SwiGLU) is not on the pages; it is the reading this library
 // documents in its header.
+#include <type_traits>
+
 #include "dense.hpp"
 #include "kernels.hpp"
 
@@ -33,60 +35,133 @@ __device__ __forceinline__ void chunk_to_f32<WF32>(const uint4 &v, float (&f)[4]
   f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
-// Gate/up rows of one wave: gate rows i0..i0+3 and up rows I+i0..I+i0+3 of
-// expert weights wgu_e [2I][H].  xs holds the group's activations as
-// [chunk][kTokGroup positions] 16-byte entries.  Writes A[asg][i] = silu(g) * u.
-template <class W, int NT>
-__device__ __forceinline__ void gateup_rows(const typename W::T *__restrict__ wgu_e,
-                                            const uint4 *__restrict__ xs, int H, int I, int i0,
-                                            int lane, const int32_t *__restrict__ asg, int ng,
-                                            float *__restrict__ A) {
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// a.lo * b.lo + a.hi * b.hi + c for two bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+// Streams the rows of one wave in batches of 8.  Step s covers batch
+// b = s / nq and chunk q = s % nq: the 16-byte chunk c = lane + 64 q of each
+// of the batch's 8 rows (lanes past the row end read the last chunk, and the
+// activation chunk they see is zero).  The next step's 8 loads are issued
+// before the current step's arithmetic (two buffers), and the first step's
+// loads before `ready()` (the caller's LDS staging and barrier), so weight
+// latency overlaps staging, arithmetic and the per-batch epilogue.
+//   rowptr(b, r): wave-uniform pointer to row r of batch b
+//   fma(c, w[8], acc): accumulates chunk c of the 8 rows into acc[8][NT]
+//   batch_end(b, acc): consumes a finished batch (acc is then cleared)
+template <class W, int NT, class RowPtr, class Ready, class Fma, class BatchEnd>
+__device__ __forceinline__ void stream_rows(int nb, int nq, int NC, int lane, RowPtr rowptr,
+                                            Ready ready, Fma fma, BatchEnd batch_end) {
   constexpr int CH = W::kChunk;
-  const int NC = H / CH;
   float acc[8][NT];
 #pragma unroll
   for (int r = 0; r < 8; ++r)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
-
-  const typename W::T *rowp[8];
+  const int steps = nb * nq;
+  uint4 w0[8], w1[8];
+  auto load = [&](int s, uint4(&w)[8]) {
+    const int b = s / nq;
+    const int c = min(lane + 64 * (s - b * nq), NC - 1);
 #pragma unroll
-  for (int r = 0; r < 8; ++r) rowp[r] = wgu_e + (size_t)(r < 4 ? i0 + r : I + i0 + r - 4) * H;
-
-  for (int c = lane; c < NC; c += 64) {
-    uint4 wv[8];
+    for (int r = 0; r < 8; ++r) w[r] = ld16_stream(rowptr(b, r) + (size_t)c * CH);
+  };
+  auto step = [&](int s, const uint4(&w)[8]) {
+    const int b = s / nq, q = s - b * nq;
+    fma(lane + 64 * q, w, acc);
+    if (q == nq - 1) {
+      batch_end(b, acc);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) wv[r] = ld16_stream(rowp[r] + (size_t)c * CH);
-    float xf[NT][CH];
+      for (int r = 0; r < 8; ++r)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) chunk_to_f32<W>(xs[c * kTokGroup + t], xf[t]);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float wf[CH];
-      chunk_to_f32<W>(wv[r], wf);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int j = 0; j < CH; ++j) acc[r][t] = fmaf(wf[j], xf[t][j], acc[r][t]);
+        for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
     }
+  };
+  if (steps > 0) load(0, w0);
+  ready();
+  for (int s = 0; s < steps; s += 2) {
+    if (s + 1 < steps) load(s + 1, w1);
+    step(s, w0);
+    if (s + 1 >= steps) break;
+    if (s + 2 < steps) load(s + 2, w0);
+    step(s + 1, w1);
   }
+}
 
+// Sums acc[8][NT] over the wave; returns the lane's total and its value index
+// q = r * NT + t (see reduce_scatter).
+template <int NT>
+__device__ __forceinline__ float wave_reduce_rows(float (&acc)[8][NT], int lane) {
   constexpr int N = 8 * NT;
   float v[N];
 #pragma unroll
   for (int r = 0; r < 8; ++r)
 #pragma unroll
     for (int t = 0; t < NT; ++t) v[r * NT + t] = acc[r][t];
-  const float tot = reduce_scatter<N>(v, lane);
-  // value index q = lane >> shift; q < N/2 are gate rows, q + N/2 the matching
-  // up rows, held by lane ^ 32.
-  const float up = __shfl_xor(tot, 32);
-  constexpr int shift = 6 - log2i<N>();
-  if ((lane & 32) == 0 && (lane & ((1 << shift) - 1)) == 0) {
-    const int q = lane >> shift;
-    const int r = q / NT, t = q % NT;
-    if (t < ng) A[(size_t)asg[t] * I + i0 + r] = silu(tot) * up;
-  }
+  return reduce_scatter<N>(v, lane);
+}
+
+// Gate/up of one work item (expert e, tile j): wave w owns gate rows
+// j*16 + 4w + r and the matching up rows I + j*16 + 4w + r (r = 0..3), read in
+// full; xs holds the token group's activations as [chunk][kTokGroup] 16-byte
+// entries.  A[asg][i] = silu(gate) * up.
+template <class W, int NT, class Ready>
+__device__ __forceinline__ void gateup_item(const typename W::T *__restrict__ wgu_e, const uint4 *xs,
+                                            int H, int I, int i0, int lane,
+                                            const int32_t *__restrict__ asg, int ng,
+                                            float *__restrict__ A, Ready ready) {
+  constexpr int CH = W::kChunk;
+  const int NC = H / CH;
+  const int nq = (NC + 63) / 64;
+  auto rowptr = [&](int, int r) {
+    return wgu_e + (size_t)(r < 4 ? i0 + r : I + i0 + r - 4) * H;
+  };
+  auto fma = [&](int c, const uint4(&w)[8], float(&acc)[8][NT]) {
+    uint4 xv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xv[t] = c < NC ? xs[c * kTokGroup + t] : make_uint4(0, 0, 0, 0);
+    if constexpr (std::is_same<W, WBf16>::value) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float a = acc[r][t];
+          a = dot2bf(w[r].x, xv[t].x, a);
+          a = dot2bf(w[r].y, xv[t].y, a);
+          a = dot2bf(w[r].z, xv[t].z, a);
+          a = dot2bf(w[r].w, xv[t].w, a);
+          acc[r][t] = a;
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float wf[4];
+        chunk_to_f32<W>(w[r], wf);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float xf[4];
+          chunk_to_f32<W>(xv[t], xf);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r][t] = fmaf(wf[j], xf[j], acc[r][t]);
+        }
+      }
+    }
+  };
+  auto batch_end = [&](int, float(&acc)[8][NT]) {
+    const float tot = wave_reduce_rows<NT>(acc, lane);
+    // q < 4*NT: gate rows; lane ^ 32 holds the matching up row (q + 4*NT)
+    const float up = __shfl_xor(tot, 32);
+    constexpr int shift = 6 - log2i<8 * NT>();
+    if ((lane & 32) == 0 && (lane & ((1 << shift) - 1)) == 0) {
+      const int q = lane >> shift;
+      const int r = q / NT, t = q % NT;
+      if (t < ng) A[(size_t)asg[t] * I + i0 + r] = silu(tot) * up;
+    }
+  };
+  stream_rows<W, NT>(1, nq, NC, lane, rowptr, ready, fma, batch_end);
 }
 
 template <class W>
@@ -106,81 +181,73 @@ __global__ __launch_bounds__(256) void routed_gateup_kernel(const typename W::T 
     const int n = r.slot_n[u];
     const typename W::T *wgu_e = wgu + (size_t)e * 2 * I * H;
     const int32_t *asg_all = r.slot_asg + u * kMaxT;
+    const int i0 = tile * 16 + wave * 4;
     for (int g0 = 0; g0 < n; g0 += kTokGroup) {
       const int ng = min(kTokGroup, n - g0);
-      __syncthreads();
-      for (int idx = tid; idx < kTokGroup * NC; idx += 256) {
-        const int t = idx / NC, c = idx - t * NC;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (t < ng) {
-          const int tok = asg_all[g0 + t] / K;
-          val = ld16(xhat + (size_t)tok * H + (size_t)c * CH);
+      auto ready = [&]() {
+        __syncthreads();  // previous group's readers are done with xs
+        for (int idx = tid; idx < kTokGroup * NC; idx += 256) {
+          const int t = idx / NC, c = idx - t * NC;
+          uint4 val = make_uint4(0, 0, 0, 0);
+          if (t < ng) val = ld16(xhat + (size_t)(asg_all[g0 + t] / K) * H + (size_t)c * CH);
+          xs[c * kTokGroup + t] = val;
         }
-        xs[c * kTokGroup + t] = val;
-      }
-      __syncthreads();
-      const int i0 = tile * 16 + wave * 4;
+        __syncthreads();
+      };
       const int32_t *asg = asg_all + g0;
-      if (ng <= 1)      gateup_rows<W, 1>(wgu_e, xs, H, I, i0, lane, asg, ng, A);
-      else if (ng <= 2) gateup_rows<W, 2>(wgu_e, xs, H, I, i0, lane, asg, ng, A);
-      else              gateup_rows<W, 4>(wgu_e, xs, H, I, i0, lane, asg, ng, A);
+      if (ng <= 1)      gateup_item<W, 1>(wgu_e, xs, H, I, i0, lane, asg, ng, A, ready);
+      else if (ng <= 2) gateup_item<W, 2>(wgu_e, xs, H, I, i0, lane, asg, ng, A, ready);
+      else              gateup_item<W, 4>(wgu_e, xs, H, I, i0, lane, asg, ng, A, ready);
     }
   }
 }
 
-// Down rows of one wave: rows h0..h0+7 of expert weights wd_e [H][I], against
-// the group's fp32 activations xs [chunk][kTokGroup positions][kChunk].  Writes
+constexpr int kDownRowsPerWave = 32;  // four batches of 8 rows
+
+// Down projection of one work item (expert e, 128 output rows): wave w owns
+// rows h0 + 8b + r (b = 0..3, r = 0..7) of W_d[e] [H][I]; xs holds the token
+// group's fp32 activations as [chunk][kTokGroup][kChunk].
 // P[asg][h] = w_asg * (A_asg . W_d[h]).
-template <class W, int NT>
-__device__ __forceinline__ void down_rows(const typename W::T *__restrict__ wd_e,
-                                          const float *__restrict__ xs, int H, int I, int h0,
-                                          int lane, const int32_t *__restrict__ asg,
+template <class W, int NT, class Ready>
+__device__ __forceinline__ void down_item(const typename W::T *__restrict__ wd_e, const float *xs,
+                                          int H, int I, int h0, int lane,
+                                          const int32_t *__restrict__ asg,
                                           const float *__restrict__ wgt, int ng,
-                                          float *__restrict__ P) {
+                                          float *__restrict__ P, Ready ready) {
   constexpr int CH = W::kChunk;
   const int NC = I / CH;
-  float acc[8][NT];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
-
-  for (int c = lane; c < NC; c += 64) {
-    uint4 wv[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) wv[r] = ld16_stream(wd_e + (size_t)(h0 + r) * I + (size_t)c * CH);
+  const int nq = (NC + 63) / 64;
+  const int nb = kDownRowsPerWave / 8;
+  auto rowptr = [&](int b, int r) { return wd_e + (size_t)(h0 + 8 * b + r) * I; };
+  auto fma = [&](int c, const uint4(&w)[8], float(&acc)[8][NT]) {
     float xf[NT][CH];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int j = 0; j < CH; ++j) xf[t][j] = xs[(c * kTokGroup + t) * CH + j];
+      for (int j = 0; j < CH; ++j) xf[t][j] = c < NC ? xs[(c * kTokGroup + t) * CH + j] : 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       float wf[CH];
-      chunk_to_f32<W>(wv[r], wf);
+      chunk_to_f32<W>(w[r], wf);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int j = 0; j < CH; ++j) acc[r][t] = fmaf(wf[j], xf[t][j], acc[r][t]);
     }
-  }
-
-  constexpr int N = 8 * NT;
-  float v[N];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[r * NT + t] = acc[r][t];
-  const float tot = reduce_scatter<N>(v, lane);
-  constexpr int shift = 6 - log2i<N>();
-  if ((lane & ((1 << shift) - 1)) == 0) {
-    const int q = lane >> shift;
-    const int r = q / NT, t = q % NT;
-    if (t < ng) {
-      const int a = asg[t];
-      P[(size_t)a * H + h0 + r] = wgt[a] * tot;
+  };
+  auto batch_end = [&](int b, float(&acc)[8][NT]) {
+    const float tot = wave_reduce_rows<NT>(acc, lane);
+    constexpr int shift = 6 - log2i<8 * NT>();
+    if ((lane & ((1 << shift) - 1)) == 0) {
+      const int q = lane >> shift;
+      const int r = q / NT, t = q % NT;
+      if (t < ng) {
+        const int a = asg[t];
+        P[(size_t)a * H + h0 + 8 * b + r] = wgt[a] * tot;
+      }
     }
-  }
+  };
+  stream_rows<W, NT>(nb, nq, NC, lane, rowptr, ready, fma, batch_end);
 }
 
 template <class W>
@@ -191,7 +258,8 @@ __global__ __launch_bounds__(256) void routed_down_kernel(const float *__restric
   extern __shared__ float xsf[];  // [I / kChunk][kTokGroup][kChunk]
   constexpr int CH = W::kChunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tiles = H / 32;
+  const int rows_per_item = 4 * kDownRowsPerWave;
+  const int tiles = H / rows_per_item;
   const int items = r.meta[0] * tiles;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int u = item / tiles, tile = item - u * tiles;
@@ -199,20 +267,22 @@ __global__ __launch_bounds__(256) void routed_down_kernel(const float *__restric
     const int n = r.slot_n[u];
     const typename W::T *wd_e = wd + (size_t)e * H * I;
     const int32_t *asg_all = r.slot_asg + u * kMaxT;
+    const int h0 = tile * rows_per_item + wave * kDownRowsPerWave;
     for (int g0 = 0; g0 < n; g0 += kTokGroup) {
       const int ng = min(kTokGroup, n - g0);
-      __syncthreads();
-      for (int idx = tid; idx < kTokGroup * I; idx += 256) {
-        const int t = idx / I, k = idx - t * I;
-        const int c = k / CH, j = k - c * CH;
-        xsf[(c * kTokGroup + t) * CH + j] = t < ng ? A[(size_t)asg_all[g0 + t] * I + k] : 0.f;
-      }
-      __syncthreads();
-      const int h0 = tile * 32 + wave * 8;
+      auto ready = [&]() {
+        __syncthreads();
+        for (int idx = tid; idx < kTokGroup * I; idx += 256) {
+          const int t = idx / I, k = idx - t * I;
+          const int c = k / CH, j = k - c * CH;
+          xsf[(c * kTokGroup + t) * CH + j] = t < ng ? A[(size_t)asg_all[g0 + t] * I + k] : 0.f;
+        }
+        __syncthreads();
+      };
       const int32_t *asg = asg_all + g0;
-      if (ng <= 1)      down_rows<W, 1>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P);
-      else if (ng <= 2) down_rows<W, 2>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P);
-      else              down_rows<W, 4>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P);
+      if (ng <= 1)      down_item<W, 1>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P, ready);
+      else if (ng <= 2) down_item<W, 2>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P, ready);
+      else              down_item<W, 4>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P, ready);
     }
   }
 }

@@ -65,7 +65,8 @@ hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const in
                           float *h, float *y_out, void *xhat_out, int T, int H, int K,
                           hipStream_t s);
 
-// LM head online softmax: per (workgroup, position) partial (max, sum, argmax).
+// LM head online softmax: per (position, workgroup) partial (max, sum, argmax),
+// stored [T][grid].
 int lmhead_grid(int cus);
 size_t lmhead_lds_bytes(int wdtype, int T, int H);
 hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,

@@ -16,6 +16,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,6 +39,82 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
   } else {
     s += s2;
     i = min(i, i2);
+  }
+}
+
+// Batch of kLmBatch k-steps: each lane loads one 16-byte chunk per step
+// (chunk 4*step + g of its row), then runs the MFMAs of the batch against the
+// staged block.  Two batches are kept in flight (double buffering), so a wave
+// has up to 2 * kLmBatch loads outstanding.
+constexpr int kLmBatch = 8;
+
+template <class W, int NT>
+__device__ __forceinline__ void lm_load(const typename W::T *__restrict__ wrow, int b, int g,
+                                        uint4 (&a)[kLmBatch]) {
+  constexpr int CH = W::kChunk;
+#pragma unroll
+  for (int j = 0; j < kLmBatch; ++j)
+    a[j] = ld16_stream(wrow + (size_t)((b * kLmBatch + j) * 4 + g) * CH);
+}
+
+template <class W, int NT>
+__device__ __forceinline__ void lm_mma(const uint4 (&a)[kLmBatch], const uint4 *__restrict__ xs,
+                                       int b, int g, int li, f32x4 (&acc)[NT]) {
+  constexpr int TP = 16 * NT;
+#pragma unroll
+  for (int j = 0; j < kLmBatch; ++j) {
+    const int c = (b * kLmBatch + j) * 4 + g;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint4 bv = xs[c * TP + n * 16 + li];
+      if constexpr (std::is_same<W, WBf16>::value) {
+        acc[n] = mfma_bf16(a[j], bv, acc[n]);
+      } else {
+        acc[n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[n]);
+      }
+    }
+  }
+}
+
+// acc[n] += W[row] . xhat[col]^T over the full hidden size: NC chunks of 16
+// bytes per row, 4 chunks per MFMA k-step (lane group g takes chunk 4s + g).
+template <class W, int NT>
+__device__ __forceinline__ void lm_tile_dot(const typename W::T *__restrict__ wrow,
+                                            const uint4 *__restrict__ xs, int NC, int g, int li,
+                                            f32x4 (&acc)[NT]) {
+  const int nb = NC / (4 * kLmBatch);
+  uint4 a0[kLmBatch], a1[kLmBatch];
+  int b = 0;
+  if (nb > 0) lm_load<W, NT>(wrow, 0, g, a0);
+  while (b < nb) {
+    if (b + 1 < nb) lm_load<W, NT>(wrow, b + 1, g, a1);
+    lm_mma<W, NT>(a0, xs, b, g, li, acc);
+    if (++b >= nb) break;
+    if (b + 1 < nb) lm_load<W, NT>(wrow, b + 1, g, a0);
+    lm_mma<W, NT>(a1, xs, b, g, li, acc);
+    ++b;
+  }
+  // remaining k-steps when NC is not a multiple of 4 * kLmBatch
+  constexpr int TP = 16 * NT;
+  constexpr int CH = W::kChunk;
+  for (int c0 = nb * 4 * kLmBatch; c0 < NC; c0 += 4) {
+    const int c = c0 + g;
+    const uint4 a = ld16_stream(wrow + (size_t)c * CH);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint4 bv = xs[c * TP + n * 16 + li];
+      if constexpr (std::is_same<W, WBf16>::value) {
+        acc[n] = mfma_bf16(a, bv, acc[n]);
+      } else {
+        acc[n] = mfma_f32(__uint_as_float(a.x), __uint_as_float(bv.x), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a.y), __uint_as_float(bv.y), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a.z), __uint_as_float(bv.z), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a.w), __uint_as_float(bv.w), acc[n]);
+      }
+    }
   }
 }
 
@@ -73,35 +151,12 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   const int ntiles = (V + 15) / 16;
   for (int tile = blockIdx.x * kLmWaves + wave; tile < ntiles; tile += gridDim.x * kLmWaves) {
     const int row0 = tile * 16;
-    const bool ok = row0 + li < V;
-    const typename W::T *wrow = wlm + (size_t)(ok ? row0 + li : 0) * H;
+    // rows past V read the last row; their logits are dropped in the epilogue
+    const typename W::T *wrow = wlm + (size_t)min(row0 + li, V - 1) * H;
     f32x4 acc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (std::is_same<W, WBf16>::value) {
-#pragma unroll 8
-      for (int c0 = 0; c0 < NC; c0 += 4) {
-        const int c = c0 + g;
-        const uint4 a = ok ? ld16_stream(wrow + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] = mfma_bf16(a, xs[c * TP + n * 16 + li], acc[n]);
-      }
-    } else {
-#pragma unroll 8
-      for (int c0 = 0; c0 < NC; c0 += 4) {
-        const int c = c0 + g;
-        const float4 a = ok ? *reinterpret_cast<const float4 *>(wrow + (size_t)c * 4)
-                            : make_float4(0, 0, 0, 0);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const uint4 bv = xs[c * TP + n * 16 + li];
-          acc[n] = mfma_f32(a.x, __uint_as_float(bv.x), acc[n]);
-          acc[n] = mfma_f32(a.y, __uint_as_float(bv.y), acc[n]);
-          acc[n] = mfma_f32(a.z, __uint_as_float(bv.z), acc[n]);
-          acc[n] = mfma_f32(a.w, __uint_as_float(bv.w), acc[n]);
-        }
-      }
-    }
+    lm_tile_dot<W, NT>(wrow, xs, NC, g, li, acc);
     // epilogue: lane holds rows row0 + 4g + r (r = 0..3) of column li + 16n
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -146,9 +201,9 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
     float mm = -FLT_MAX, ss = 0.f;
     int ii = INT_MAX;
     for (int w = 0; w < kLmWaves; ++w) sm_merge(mm, ss, ii, sm[w][tid], ssum[w][tid], si[w][tid]);
-    part_m[(size_t)blockIdx.x * T + tid] = mm;
-    part_s[(size_t)blockIdx.x * T + tid] = ss;
-    part_i[(size_t)blockIdx.x * T + tid] = ii;
+    part_m[(size_t)tid * gridDim.x + blockIdx.x] = mm;
+    part_s[(size_t)tid * gridDim.x + blockIdx.x] = ss;
+    part_i[(size_t)tid * gridDim.x + blockIdx.x] = ii;
   }
 }
 
@@ -169,7 +224,8 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ 
     float m = -FLT_MAX, s = 0.f;
     int i = INT_MAX;
     for (int p = lane; p < nparts; p += 64)
-      sm_merge(m, s, i, part_m[(size_t)p * T + t], part_s[(size_t)p * T + t], part_i[(size_t)p * T + t]);
+      sm_merge(m, s, i, part_m[(size_t)t * nparts + p], part_s[(size_t)t * nparts + p],
+               part_i[(size_t)t * nparts + p]);
 #pragma unroll
     for (int sft = 1; sft <= 32; sft <<= 1) {
       const float m2 = __shfl_xor(m, sft), s2 = __shfl_xor(s, sft);

@@ -16,35 +16,59 @@ namespace bdd {
 
 constexpr int kMaxK = 32;
 
-__device__ __forceinline__ float block_sum_256(float v, float *red4) {
+// ------------------------------------------------------------------ RMSNorm
+constexpr int kRowThreads = 512;
+constexpr int kRowVec = 4;  // float4 per thread: H <= 4 * 4 * 512 = 8192
+
+__device__ __forceinline__ float block_sum_512(float v, float *red8) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   v = wave_sum(v);
-  if (lane == 0) red4[wave] = v;
+  if (lane == 0) red8[wave] = v;
   __syncthreads();
-  v = red4[0] + red4[1] + red4[2] + red4[3];
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / 64; ++w) t += red8[w];
   __syncthreads();
-  return v;
+  return t;
 }
 
-// ------------------------------------------------------------------ RMSNorm
+template <typename OT>
+__device__ __forceinline__ void store4(OT *out, size_t i, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float *out, size_t i, float4 v) {
+  *reinterpret_cast<float4 *>(out + i) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *out, size_t i, float4 v) {
+  *reinterpret_cast<uint2 *>(out + i) = make_uint2(pack2(f2bf(v.x), f2bf(v.y)), pack2(f2bf(v.z), f2bf(v.w)));
+}
+
 // x_hat = h / sqrt(mean(h^2) + eps), unit gain, one workgroup per position.
 template <typename OT>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *__restrict__ in,
-                                                      float *__restrict__ copy_out,
-                                                      OT *__restrict__ out, int H, float eps) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__restrict__ in,
+                                                              float *__restrict__ copy_out,
+                                                              OT *__restrict__ out, int H, float eps) {
+  __shared__ float red[kRowThreads / 64];
   const size_t base = (size_t)blockIdx.x * H;
+  const int H4 = H / 4;
+  float4 v[kRowVec];
   float ss = 0.f;
-  for (int k = threadIdx.x; k < H; k += 256) {
-    const float v = in[base + k];
-    ss += v * v;
+#pragma unroll
+  for (int q = 0; q < kRowVec; ++q) {
+    const int j = threadIdx.x + q * kRowThreads;
+    v[q] = j < H4 ? reinterpret_cast<const float4 *>(in + base)[j] : make_float4(0, 0, 0, 0);
+    ss += v[q].x * v[q].x + v[q].y * v[q].y + v[q].z * v[q].z + v[q].w * v[q].w;
   }
-  ss = block_sum_256(ss, red);
+  ss = block_sum_512(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int k = threadIdx.x; k < H; k += 256) {
-    const float v = in[base + k];
-    if (copy_out) copy_out[base + k] = v;
-    out[base + k] = from_f32<OT>(v * inv);
+#pragma unroll
+  for (int q = 0; q < kRowVec; ++q) {
+    const int j = threadIdx.x + q * kRowThreads;
+    if (j < H4) {
+      if (copy_out) reinterpret_cast<float4 *>(copy_out + base)[j] = v[q];
+      store4<OT>(out, base + 4 * (size_t)j,
+                 make_float4(v[q].x * inv, v[q].y * inv, v[q].z * inv, v[q].w * inv));
+    }
   }
 }
 
@@ -131,65 +155,125 @@ __device__ void wave_topk(const float (&lv)[4], const float (&pv)[4], int E, int
 }
 
 struct SelShared {
-  int32_t idx[kMaxT][kMaxK];
-  float psel[kMaxT][kMaxK];
-  double mass[kMaxE];
-  int32_t sorted[kMaxE];
-  int32_t member[kMaxE];
-  int32_t cnt[kMaxE];
+  int32_t idx[kMaxT][kMaxK];    // picks of each position (-1: unused slot)
+  float psel[kMaxT][kMaxK];     // their softmax scores
+  uint32_t tokmask[kMaxE];      // positions that picked each expert
+  uint8_t kslot[kMaxT][kMaxE];  // slot k of expert e among position t's picks
+  double mass[kMaxE];           // block expert mass
+  int32_t ulist[kMaxE];         // experts with a pick, ascending id
+  double umass[kMaxE];          // their mass, in ulist order
+  int32_t sorted[kMaxE];        // ulist ranked by (mass desc, id asc)
+  double cum[kMaxE];            // prefix sums of ranked mass
+  int32_t member[kMaxE];        // coreset membership
   int32_t wtot[16];
-  int32_t csize;
+  double wtotd[16];
+  int32_t nu, csize, below;
 };
 
-// Block expert mass, ranking and coreset cut ([P2] coreset section).  Needs
-// sh.idx / sh.psel filled for T positions.  Fills sh.mass, sh.sorted,
-// sh.member and sh.csize.  Called by every thread of a workgroup of >= E
-// threads.
-__device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
+// Rebuilds tokmask / kslot from sh.idx (all threads; ends with a barrier).
+__device__ void build_masks(SelShared &sh, int T, int E, int K) {
   const int tid = threadIdx.x;
+  if (tid < E) sh.tokmask[tid] = 0u;
+  __syncthreads();
+  for (int i = tid; i < T * K; i += blockDim.x) {
+    const int t = i / K, k = i - t * K;
+    const int e = sh.idx[t][k];
+    if (e >= 0) {
+      atomicOr(&sh.tokmask[e], 1u << t);
+      sh.kslot[t][e] = (uint8_t)k;
+    }
+  }
+  __syncthreads();
+}
+
+// Union of experts, ascending id, into sh.ulist / sh.nu (all threads, >= E
+// threads; ends with a barrier).  Returns the caller's slot (or -1).
+__device__ int union_scan(SelShared &sh, int E) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int flag = (tid < E && sh.tokmask[tid] != 0u) ? 1 : 0;
+  int incl = flag;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int o = __shfl_up(incl, s);
+    if (lane >= s) incl += o;
+  }
+  if (lane == 63) sh.wtot[wave] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int w = 0; w < wave; ++w) off += sh.wtot[w];
+  const int slot = flag ? off + incl - 1 : -1;
+  if (flag) sh.ulist[slot] = tid;
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += sh.wtot[w];
+    sh.nu = tot;
+  }
+  __syncthreads();
+  return slot;
+}
+
+// Block expert mass, ranking and coreset cut ([P2] coreset section): mass_e
+// sums the softmax scores of the positions that picked e (ascending position
+// order); experts are ranked by (mass desc, id asc); the coreset is the
+// shortest ranked prefix whose cumulative mass reaches top_p of the total
+// (top_p >= 1: every expert with positive mass).  Needs sh.idx / sh.psel.
+// Fills sh.mass, sh.member, sh.csize (all threads, >= E threads).
+__device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  build_masks(sh, T, E, K);
   if (tid < E) {
     double m = 0.0;
-    for (int t = 0; t < T; ++t)
-      for (int k = 0; k < K; ++k)
-        if (sh.idx[t][k] == tid) m += (double)sh.psel[t][k];
+    uint32_t bits = sh.tokmask[tid];
+    while (bits) {
+      const int t = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      m += (double)sh.psel[t][sh.kslot[t][tid]];
+    }
     sh.mass[tid] = m;
+    sh.member[tid] = 0;
   }
+  union_scan(sh, E);
+  const int nu = sh.nu;
+  if (tid < nu) sh.umass[tid] = sh.mass[sh.ulist[tid]];
   __syncthreads();
-  if (tid < E) {
-    const double m = sh.mass[tid];
+  if (tid < nu) {
+    const double m = sh.umass[tid];
+    const int e = sh.ulist[tid];
     int r = 0;
-    for (int e = 0; e < E; ++e) {
-      const double o = sh.mass[e];
-      r += (o > m) || (o == m && e < tid);
+    for (int j = 0; j < nu; ++j) {
+      const double o = sh.umass[j];
+      r += (o > m) || (o == m && sh.ulist[j] < e);
     }
-    sh.sorted[r] = tid;
+    sh.sorted[r] = e;
+    sh.cum[r] = m;
   }
+  if (tid == 0) sh.below = 0;
   __syncthreads();
-  if (tid == 0) {
-    double total = 0.0;
-    int npos = 0;
-    for (int r = 0; r < E; ++r) {
-      const double m = sh.mass[sh.sorted[r]];
-      total += m;
-      npos += m > 0.0;
+  int k = nu;
+  if (top_p < 1.0f && nu > 0) {
+    // inclusive prefix sum of the ranked masses (fp64), one wave per 64 ranks
+    double v = tid < nu ? sh.cum[tid] : 0.0;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const double o = __shfl_up(v, s);
+      if (lane >= s) v += o;
     }
-    int k = npos;
-    if (top_p < 1.0f) {
-      const double target = (double)top_p * total;
-      double cum = 0.0;
-      k = E;
-      for (int r = 0; r < E; ++r) {
-        cum += sh.mass[sh.sorted[r]];
-        if (cum >= target) { k = r + 1; break; }
-      }
-      k = max(1, min(k, npos));
-    }
-    sh.csize = k;
+    if (lane == 63) sh.wtotd[wave] = v;
+    __syncthreads();
+    double off = 0.0;
+    for (int w = 0; w < wave; ++w) off += sh.wtotd[w];
+    v += off;
+    if (tid < nu) sh.cum[tid] = v;
+    __syncthreads();
+    const double target = (double)top_p * sh.cum[nu - 1];
+    // the prefix with cumulative mass below the target, plus one
+    const unsigned long long b = __ballot(tid < nu && v < target);
+    if (lane == 0 && b) atomicAdd(&sh.below, (int)__popcll(b));
+    __syncthreads();
+    k = max(1, min(sh.below + 1, nu));
   }
-  __syncthreads();
-  if (tid < E) sh.member[tid] = 0;
-  __syncthreads();
-  if (tid < sh.csize) sh.member[sh.sorted[tid]] = 1;
+  if (tid < k) sh.member[sh.sorted[tid]] = 1;
+  if (tid == 0) sh.csize = k;
   __syncthreads();
 }
 
@@ -248,6 +332,8 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
 
   // block mass and coreset (also run without coreset: it reports the union)
   coreset_core(sh, T, E, K, top_p);
+  if (tid < E) r.mass[tid] = (float)sh.mass[tid];
+  write_bits(sh, E, r.cs_bits);
   if (top_p < 1.0f) {
     const int kk = min(K, sh.csize);
     for (int q = 0; q < kTokPerWave; ++q) {
@@ -258,6 +344,7 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
         for (int k = kk; k < K; ++k) { sh.idx[t][k] = -1; sh.psel[t][k] = 0.f; }
     }
     __syncthreads();
+    build_masks(sh, T, E, K);
   }
 
   // renormalised weights, outputs
@@ -269,42 +356,24 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
     r.idx[tid] = e;
     r.wgt[tid] = e >= 0 ? sh.psel[t][k] / s : 0.f;
   }
-  if (tid < E) r.mass[tid] = (float)sh.mass[tid];
-  write_bits(sh, E, r.cs_bits);
 
-  // union of experts and assignment lists
-  int n = 0;
-  if (tid < E) {
-    for (int t = 0; t < T; ++t)
-      for (int k = 0; k < K; ++k) n += sh.idx[t][k] == tid;
-  }
-  // exclusive prefix over experts of (n > 0)
-  const int flag = (tid < E && n > 0) ? 1 : 0;
-  int incl = flag;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int o = __shfl_up(incl, s);
-    if (lane >= s) incl += o;
-  }
-  if (lane == 63) sh.wtot[wave] = incl;
-  __syncthreads();
-  int off = 0;
-  for (int w = 0; w < wave; ++w) off += sh.wtot[w];
-  const int slot = off + incl - flag;
-  if (flag) {
+  // union of experts read and each one's assignment list (t*K + k, ascending t)
+  const int slot = union_scan(sh, E);
+  if (slot >= 0) {
+    uint32_t bits = sh.tokmask[tid];
     r.union_list[slot] = tid;
-    r.slot_n[slot] = n;
+    r.slot_n[slot] = __popc(bits);
     int j = 0;
-    for (int t = 0; t < T; ++t)
-      for (int k = 0; k < K; ++k)
-        if (sh.idx[t][k] == tid) r.slot_asg[slot * kMaxT + j++] = t * K + k;
+    while (bits) {
+      const int t = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      r.slot_asg[slot * kMaxT + j++] = t * K + sh.kslot[t][tid];
+    }
   }
   if (tid == 0) {
-    int tot = 0;
-    for (int w = 0; w < nw; ++w) tot += sh.wtot[w];
-    r.meta[0] = tot;
+    r.meta[0] = sh.nu;
     r.meta[1] = sh.csize;
-    if (r.n_distinct_out) *r.n_distinct_out = tot;
+    if (r.n_distinct_out) *r.n_distinct_out = sh.nu;
     if (r.coreset_size_out) *r.coreset_size_out = sh.csize;
   }
 }
@@ -333,37 +402,59 @@ __global__ __launch_bounds__(256) void coreset_kernel(const float *__restrict__ 
 }
 
 // ------------------------------------------------------------------ combine
-// y_t = sum_k P[t*K+k] (live slots) + P_s[t]; h += y; xhat = RMSNorm(h).
+// y_t = sum_k P[t*K+k] (live slots, in slot order) + P_s[t]; then h += y and
+// xhat = RMSNorm(h), one workgroup per position.
 template <typename OT>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ P,
-                                                      const float *__restrict__ P_s,
-                                                      const int32_t *__restrict__ idx,
-                                                      float *__restrict__ h,
-                                                      float *__restrict__ y_out,
-                                                      OT *__restrict__ xhat_out, int H, int K,
-                                                      float eps) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__restrict__ P,
+                                                              const float *__restrict__ P_s,
+                                                              const int32_t *__restrict__ idx,
+                                                              float *__restrict__ h,
+                                                              float *__restrict__ y_out,
+                                                              OT *__restrict__ xhat_out, int H, int K,
+                                                              float eps) {
+  __shared__ float red[kRowThreads / 64];
   const int t = blockIdx.x;
   uint32_t live = 0;
   for (int k = 0; k < K; ++k) live |= (idx[t * K + k] >= 0 ? 1u : 0u) << k;
   const size_t base = (size_t)t * H;
+  const int H4 = H / 4;
+  float4 hv[kRowVec];
   float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += 256) {
-    float y = 0.f;
-    for (int k = 0; k < K; ++k)
-      if (live >> k & 1u) y += P[((size_t)t * K + k) * H + c];
-    if (P_s) y += P_s[base + c];
-    if (y_out) y_out[base + c] = y;
+#pragma unroll
+  for (int q = 0; q < kRowVec; ++q) {
+    const int j = threadIdx.x + q * kRowThreads;
+    if (j >= H4) continue;
+    float4 y = make_float4(0, 0, 0, 0);
+#pragma unroll 8
+    for (int k = 0; k < K; ++k) {
+      if (live >> k & 1u) {
+        const float4 p = reinterpret_cast<const float4 *>(P + ((size_t)t * K + k) * H)[j];
+        y.x += p.x; y.y += p.y; y.z += p.z; y.w += p.w;
+      }
+    }
+    if (P_s) {
+      const float4 p = reinterpret_cast<const float4 *>(P_s + base)[j];
+      y.x += p.x; y.y += p.y; y.z += p.z; y.w += p.w;
+    }
+    if (y_out) reinterpret_cast<float4 *>(y_out + base)[j] = y;
     if (h) {
-      const float v = h[base + c] + y;
-      h[base + c] = v;
-      ss += v * v;
+      float4 v = reinterpret_cast<float4 *>(h + base)[j];
+      v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
+      reinterpret_cast<float4 *>(h + base)[j] = v;
+      hv[q] = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
   }
   if (h && xhat_out) {
-    ss = block_sum_256(ss, red);
+    ss = block_sum_512(ss, red);
     const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int c = threadIdx.x; c < H; c += 256) xhat_out[base + c] = from_f32<OT>(h[base + c] * inv);
+#pragma unroll
+    for (int q = 0; q < kRowVec; ++q) {
+      const int j = threadIdx.x + q * kRowThreads;
+      if (j < H4)
+        store4<OT>(xhat_out, base + 4 * (size_t)j,
+                   make_float4(hv[q].x * inv, hv[q].y * inv, hv[q].z * inv, hv[q].w * inv));
+    }
   }
 }
 
@@ -372,9 +463,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, int T, int H,
                           hipStream_t s) {
   if (wdtype == 1)
-    rmsnorm_kernel<bf16_t><<<T, 256, 0, s>>>(in, copy_out, (bf16_t *)out, H, 1e-6f);
+    rmsnorm_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(in, copy_out, (bf16_t *)out, H, 1e-6f);
   else
-    rmsnorm_kernel<float><<<T, 256, 0, s>>>(in, copy_out, (float *)out, H, 1e-6f);
+    rmsnorm_kernel<float><<<T, kRowThreads, 0, s>>>(in, copy_out, (float *)out, H, 1e-6f);
   return hipGetLastError();
 }
 
@@ -420,10 +511,10 @@ hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const in
                           float *h, float *y_out, void *xhat_out, int T, int H, int K,
                           hipStream_t s) {
   if (wdtype == 1)
-    combine_kernel<bf16_t><<<T, 256, 0, s>>>(P, P_s, idx, h, y_out, (bf16_t *)xhat_out, H, K,
+    combine_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(P, P_s, idx, h, y_out, (bf16_t *)xhat_out, H, K,
                                              1e-6f);
   else
-    combine_kernel<float><<<T, 256, 0, s>>>(P, P_s, idx, h, y_out, (float *)xhat_out, H, K,
+    combine_kernel<float><<<T, kRowThreads, 0, s>>>(P, P_s, idx, h, y_out, (float *)xhat_out, H, K,
                                             1e-6f);
   return hipGetLastError();
 }

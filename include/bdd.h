@@ -26,9 +26,10 @@
  *     launch failure returns BDD_ERR_HIP.  bdd_last_error() describes the
  *     last failure of the calling thread.  No exception crosses the ABI.
  *   - MASK is -1 and is never a vocabulary candidate.
- *   - Supported shapes: 1 <= T <= 32; H, I, I_shared multiples of 32;
- *     1 <= K <= E <= 256; H <= 2048 for the LM head when T > 16 (the block's
- *     normalised hidden states are kept in the 160 KiB LDS of one CU).
+ *   - Supported shapes: 1 <= T <= 32; 1 <= K <= min(E, 32); E <= 256; H a
+ *     multiple of 128 for the MoE layer (of 32 for the LM head alone); I,
+ *     I_shared multiples of 32; H <= 2048 for the LM head when T > 16 (the
+ *     block's normalised hidden states are kept in the 160 KiB LDS of one CU).
  */
 #ifndef BDD_H
 #define BDD_H

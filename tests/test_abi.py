@@ -68,7 +68,8 @@ def _call_moe(d):
     ((0, 256, 16, 4, 128, 128, 0), -1),       # T < 1
     ((33, 256, 16, 4, 128, 128, 0), -2),      # T > 32
     ((8, 256, 16, 17, 128, 128, 0), -1),      # K > E
-    ((8, 250, 16, 4, 128, 128, 0), -2),       # H not a multiple of 32
+    ((8, 250, 16, 4, 128, 128, 0), -2),       # H not a multiple of 128
+    ((8, 288, 16, 4, 128, 128, 0), -2),       # H multiple of 32, not of 128
     ((8, 256, 300, 4, 128, 128, 0), -2),      # E > 256
     ((8, 256, 16, 4, 128, 128, 7), -1),       # bad dtype
     ((8, 256, 16, 4, 128, 128, 0), -3),       # valid dims, missing workspace
