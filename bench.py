@@ -66,7 +66,8 @@ def main():
     layer = W.layer_weights(args.seed, 0, d, device=dev)
     w_lm = W.lm_head_weight(args.seed, d, device=dev, unit_rows=info["unit_rows"])
     dims = bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16)
-    plan = bdd.RoundPlan(dims, [layer], w_lm, 1.0, 0.95)
+    lm = bdd.pack_lm_head(w_lm)
+    plan = bdd.RoundPlan(dims, [layer], lm, 1.0, 0.95)
     T = d.T
     tok = torch.full((T,), bdd.MASK, dtype=torch.int32, device=dev)
     conf = torch.empty(T, dtype=torch.float32, device=dev)

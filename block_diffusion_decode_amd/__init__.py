@@ -8,7 +8,8 @@ fallback path.
 
 Entry points (same names as the C ABI, without the bdd_ prefix):
   moe_block_forward, coreset_select, lmhead_confidence_commit,
-  block_denoise_round, and the *_workspace_bytes queries.
+  block_denoise_round, pack_lm_head (bdd_lmhead_pack), and the
+  *_workspace_bytes queries.
 """
 
 from __future__ import annotations
@@ -51,7 +52,7 @@ EXPORTS = [
     "bdd_lmhead_workspace_bytes", "bdd_lmhead_confidence_commit",
     "bdd_round_workspace_bytes", "bdd_block_denoise_round",
     "bdd_status_string", "bdd_last_error", "bdd_device_cus",
-    "bdd_timing_enable", "bdd_timing_read",
+    "bdd_timing_enable", "bdd_timing_read", "bdd_lmhead_packed_bytes", "bdd_lmhead_pack",
 ]
 
 _lib = None
@@ -89,6 +90,10 @@ def lib() -> ctypes.CDLL:
     L.bdd_last_error.restype = ctypes.c_char_p
     L.bdd_device_cus.argtypes = []
     L.bdd_device_cus.restype = i32
+    L.bdd_lmhead_packed_bytes.argtypes = [i32, i32, i32]
+    L.bdd_lmhead_packed_bytes.restype = sz
+    L.bdd_lmhead_pack.argtypes = [vp, i32, i32, i32, vp, vp]
+    L.bdd_lmhead_pack.restype = i32
     L.bdd_timing_enable.argtypes = [i32, ctypes.c_char_p]
     L.bdd_timing_enable.restype = i32
     L.bdd_timing_read.argtypes = [i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -253,20 +258,50 @@ def coreset_select(router_prob: torch.Tensor, topk_idx: torch.Tensor, top_p: flo
     return bits, size, mass
 
 
-def lmhead_confidence_commit(hhat: torch.Tensor, w_lm: torch.Tensor, tokens: torch.Tensor,
+@dataclass
+class LMHead:
+    """LM-head weight [V][H] in the packed tile layout (see bdd_lmhead_pack)."""
+    packed: torch.Tensor  # uint8, bdd_lmhead_packed_bytes(V, H, dtype) bytes
+    V: int
+    H: int
+    dtype: torch.dtype
+
+    @property
+    def cdtype(self) -> int:
+        return BDD_BF16 if self.dtype == torch.bfloat16 else BDD_F32
+
+
+def pack_lm_head(w_lm: torch.Tensor, stream=None) -> LMHead:
+    """Pack w_lm [V][H] (bf16 or fp32, on the GPU) for the LM head."""
+    V, H = w_lm.shape
+    dt = w_lm.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise ValueError("w_lm must be float32 or bfloat16")
+    _need(w_lm, "w_lm", dt, (V, H))
+    cdt = BDD_BF16 if dt == torch.bfloat16 else BDD_F32
+    nb = int(lib().bdd_lmhead_packed_bytes(V, H, cdt))
+    if nb == 0:
+        raise BddError(-1, f"cannot pack an LM head of shape {(V, H)}")
+    packed = torch.empty(nb, dtype=torch.uint8, device=w_lm.device)
+    _check(lib().bdd_lmhead_pack(_ptr(w_lm), V, H, cdt, _ptr(packed), _stream(stream)))
+    return LMHead(packed, V, H, dt)
+
+
+def lmhead_confidence_commit(hhat: torch.Tensor, lm: LMHead, tokens: torch.Tensor,
                              threshold: float = 0.95, ws: torch.Tensor | None = None,
                              conf=None, choice=None, round_info=None, stream=None):
     """LM head + confidence + LowConfidence commit (see
     bdd_lmhead_confidence_commit).  ``tokens`` (int32 [T], MASK = -1) is
     updated in place.  Returns (conf, choice, round_info)."""
     T, H = hhat.shape
-    V = w_lm.shape[0]
+    V = lm.V
     dev = hhat.device
     dt = hhat.dtype
-    if dt not in (torch.float32, torch.bfloat16):
-        raise ValueError("hhat must be float32 or bfloat16")
+    if dt != lm.dtype or H != lm.H:
+        raise ValueError(f"hhat {tuple(hhat.shape)} {dt} does not match the LM head (H={lm.H}, {lm.dtype})")
     _need(hhat, "hhat", dt, (T, H))
-    _need(w_lm, "w_lm", dt, (V, H), dev)
+    if lm.packed.device != dev:
+        raise ValueError("LM head and hhat are on different devices")
     _need(tokens, "tokens", torch.int32, (T,), dev)
     conf = torch.empty(T, dtype=torch.float32, device=dev) if conf is None else conf
     choice = torch.empty(T, dtype=torch.int32, device=dev) if choice is None else choice
@@ -274,7 +309,7 @@ def lmhead_confidence_commit(hhat: torch.Tensor, w_lm: torch.Tensor, tokens: tor
     nb = lmhead_workspace_bytes(T, H, V)
     ws = _workspace(nb, dev, ws)
     _check(lib().bdd_lmhead_confidence_commit(
-        _ptr(hhat), _ptr(w_lm), T, H, V, BDD_BF16 if dt == torch.bfloat16 else BDD_F32,
+        _ptr(hhat), _ptr(lm.packed), T, H, V, lm.cdtype,
         float(threshold), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info), _ptr(ws),
         ws.numel(), _stream(stream)))
     return conf, choice, round_info
@@ -284,13 +319,14 @@ class RoundPlan:
     """Marshalled arguments of bdd_block_denoise_round for a fixed set of
     layers and LM head, so repeated rounds only pass pointers."""
 
-    def __init__(self, d: MoEDims, layers: list, w_lm: torch.Tensor, coreset_top_p: float = 1.0,
+    def __init__(self, d: MoEDims, layers: list, lm: LMHead, coreset_top_p: float = 1.0,
                  threshold: float = 0.95):
-        dev = w_lm.device
+        dev = lm.packed.device
         self.d, self.dev = d, dev
-        self.V = int(w_lm.shape[0])
-        _need(w_lm, "w_lm", d.torch_dtype, (self.V, d.H))
-        self.w_lm = w_lm
+        self.V = lm.V
+        if lm.H != d.H or lm.dtype != d.torch_dtype:
+            raise ValueError("LM head does not match the layer dims")
+        self.lm = lm
         self.layers = layers  # keep the tensors alive
         arr = (_Weights * max(1, len(layers)))()
         for i, w in enumerate(layers):
@@ -317,19 +353,19 @@ class RoundPlan:
         if hhat_out is not None:
             _need(hhat_out, "hhat_out", d.torch_dtype, (d.T, d.H), self.dev)
         _check(lib().bdd_block_denoise_round(
-            ctypes.byref(self.c_dims), L, self.c_layers, self.top_p, _ptr(self.w_lm), self.V,
+            ctypes.byref(self.c_dims), L, self.c_layers, self.top_p, _ptr(self.lm.packed), self.V,
             self.threshold, _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info),
             _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(hhat_out), _ptr(self.ws),
             self.ws.numel(), _stream(stream)))
 
 
-def block_denoise_round(d: MoEDims, layers: list, w_lm: torch.Tensor, x_in: torch.Tensor,
+def block_denoise_round(d: MoEDims, layers: list, lm: LMHead, x_in: torch.Tensor,
                         tokens: torch.Tensor, threshold: float = 0.95, coreset_top_p: float = 1.0,
                         layer_topk_idx=None, layer_n_distinct=None, hhat_out=None, stream=None):
     """One full denoising round (see bdd_block_denoise_round).  ``tokens`` is
     updated in place.  Returns (conf, choice, round_info)."""
-    plan = RoundPlan(d, layers, w_lm, coreset_top_p, threshold)
-    dev = w_lm.device
+    plan = RoundPlan(d, layers, lm, coreset_top_p, threshold)
+    dev = lm.packed.device
     conf = torch.empty(d.T, dtype=torch.float32, device=dev)
     choice = torch.empty(d.T, dtype=torch.int32, device=dev)
     ri = torch.empty(4, dtype=torch.int32, device=dev)

@@ -324,6 +324,23 @@ bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx,
   return BDD_OK;
 }
 
+size_t bdd_lmhead_packed_bytes(int32_t V, int32_t H, int32_t dtype) {
+  if (V < 1 || H < 1 || H % 32 || (dtype != BDD_F32 && dtype != BDD_BF16)) return 0;
+  return lmhead_packed_bytes(dtype, H, V);
+}
+
+bdd_status bdd_lmhead_pack(const void *w_lm, int32_t V, int32_t H, int32_t dtype, void *w_packed,
+                           void *stream) {
+  if (!w_lm || !w_packed) return fail(BDD_ERR_INVALID_ARG, "w_lm and w_packed are required");
+  if (dtype != BDD_F32 && dtype != BDD_BF16) return fail(BDD_ERR_INVALID_ARG, "dtype %d", dtype);
+  if (V < 1 || H < 1) return fail(BDD_ERR_INVALID_ARG, "V=%d H=%d", V, H);
+  if (H % 32) return fail(BDD_ERR_UNSUPPORTED, "H=%d must be a multiple of 32", H);
+  if ((long long)V * H >= (1ll << 40)) return fail(BDD_ERR_UNSUPPORTED, "V*H too large");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  LAUNCH("pack_lm", s, launch_pack_lm(dtype, w_lm, V, H, w_packed, s));
+  return BDD_OK;
+}
+
 size_t bdd_lmhead_workspace_bytes(int32_t T, int32_t H, int32_t V) {
   if (T < 1 || T > kMaxT || H < 1 || V < 1) return 0;
   return plan_lm(T, 0).end;

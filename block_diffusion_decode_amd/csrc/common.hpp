@@ -63,6 +63,22 @@ __device__ __forceinline__ uint4 ld16_stream(const void *p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Wave-uniform copy of a value (lets the compiler keep it in an SGPR).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Raw buffer descriptor over [base, base + bytes): loads address it with a
+// per-lane byte offset (VGPR) plus a wave-uniform byte offset (SGPR), and
+// loads outside the range return zeros.  Word 3 = 32-bit data format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 16-byte streaming (non-temporal) load of weights read once per call.
+__device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

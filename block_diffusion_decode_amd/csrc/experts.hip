@@ -42,20 +42,21 @@ __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-// Streams the rows of one wave in batches of 8.  Step s covers batch
-// b = s / nq and chunk q = s % nq: the 16-byte chunk c = lane + 64 q of each
-// of the batch's 8 rows (lanes past the row end read the last chunk, and the
-// activation chunk they see is zero).  The next step's 8 loads are issued
-// before the current step's arithmetic (two buffers), and the first step's
-// loads before `ready()` (the caller's LDS staging and barrier), so weight
-// latency overlaps staging, arithmetic and the per-batch epilogue.
-//   rowptr(b, r): wave-uniform pointer to row r of batch b
+// Streams the rows of one wave in batches of 8 through a buffer descriptor.
+// Step s covers batch b = s / nq and chunk q = s % nq: the 16-byte chunk
+// c = lane + 64 q of each of the batch's 8 rows (lanes past the row end read
+// the last chunk, and the activation chunk they see is zero).  The next
+// step's 8 loads are issued before the current step's arithmetic (two
+// buffers), and the first step's loads before `ready()` (the caller's LDS
+// staging and barrier), so weight latency overlaps staging, arithmetic and
+// the per-batch epilogue.
+//   rowoff(b, r): wave-uniform byte offset of row r of batch b in `rs`
 //   fma(c, w[8], acc): accumulates chunk c of the 8 rows into acc[8][NT]
 //   batch_end(b, acc): consumes a finished batch (acc is then cleared)
-template <class W, int NT, class RowPtr, class Ready, class Fma, class BatchEnd>
-__device__ __forceinline__ void stream_rows(int nb, int nq, int NC, int lane, RowPtr rowptr,
-                                            Ready ready, Fma fma, BatchEnd batch_end) {
-  constexpr int CH = W::kChunk;
+template <class W, int NT, class RowOff, class Ready, class Fma, class BatchEnd>
+__device__ __forceinline__ void stream_rows(rsrc_t rs, int nb, int nq, int NC, int lane,
+                                            RowOff rowoff, Ready ready, Fma fma,
+                                            BatchEnd batch_end) {
   float acc[8][NT];
 #pragma unroll
   for (int r = 0; r < 8; ++r)
@@ -65,9 +66,9 @@ __device__ __forceinline__ void stream_rows(int nb, int nq, int NC, int lane, Ro
   uint4 w0[8], w1[8];
   auto load = [&](int s, uint4(&w)[8]) {
     const int b = s / nq;
-    const int c = min(lane + 64 * (s - b * nq), NC - 1);
+    const uint32_t voff = (uint32_t)min(lane + 64 * (s - b * nq), NC - 1) * 16u;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) w[r] = ld16_stream(rowptr(b, r) + (size_t)c * CH);
+    for (int r = 0; r < 8; ++r) w[r] = buf_ld16(rs, voff, rowoff(b, r));
   };
   auto step = [&](int s, const uint4(&w)[8]) {
     const int b = s / nq, q = s - b * nq;
@@ -116,8 +117,9 @@ __device__ __forceinline__ void gateup_item(const typename W::T *__restrict__ wg
   constexpr int CH = W::kChunk;
   const int NC = H / CH;
   const int nq = (NC + 63) / 64;
-  auto rowptr = [&](int, int r) {
-    return wgu_e + (size_t)(r < 4 ? i0 + r : I + i0 + r - 4) * H;
+  const rsrc_t rs = make_rsrc(wgu_e, (uint32_t)(2 * I * H * sizeof(typename W::T)));
+  auto rowoff = [&](int, int r) {
+    return (uint32_t)((r < 4 ? i0 + r : I + i0 + r - 4) * H * (int)sizeof(typename W::T));
   };
   auto fma = [&](int c, const uint4(&w)[8], float(&acc)[8][NT]) {
     uint4 xv[NT];
@@ -161,7 +163,7 @@ __device__ __forceinline__ void gateup_item(const typename W::T *__restrict__ wg
       if (t < ng) A[(size_t)asg[t] * I + i0 + r] = silu(tot) * up;
     }
   };
-  stream_rows<W, NT>(1, nq, NC, lane, rowptr, ready, fma, batch_end);
+  stream_rows<W, NT>(rs, 1, nq, NC, lane, rowoff, ready, fma, batch_end);
 }
 
 template <class W>
@@ -174,23 +176,31 @@ __global__ __launch_bounds__(256) void routed_gateup_kernel(const typename W::T 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NC = H / CH;
   const int tiles = I / 16;
-  const int items = r.meta[0] * tiles;
+  const int items = uniform(r.meta[0]) * tiles;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int u = item / tiles, tile = item - u * tiles;
-    const int e = r.union_list[u];
-    const int n = r.slot_n[u];
+    const int e = uniform(r.union_list[u]);
+    const int n = uniform(r.slot_n[u]);
     const typename W::T *wgu_e = wgu + (size_t)e * 2 * I * H;
     const int32_t *asg_all = r.slot_asg + u * kMaxT;
-    const int i0 = tile * 16 + wave * 4;
+    const int i0 = uniform(tile * 16 + wave * 4);
     for (int g0 = 0; g0 < n; g0 += kTokGroup) {
       const int ng = min(kTokGroup, n - g0);
       auto ready = [&]() {
+        // position rows of the group (wave-uniform scalar loads), then the
+        // group's chunk loads, independent of each other
+        const typename W::T *xrow[kTokGroup];
+#pragma unroll
+        for (int t = 0; t < kTokGroup; ++t)
+          xrow[t] = t < ng ? xhat + (size_t)(asg_all[g0 + t] / K) * H : nullptr;
         __syncthreads();  // previous group's readers are done with xs
-        for (int idx = tid; idx < kTokGroup * NC; idx += 256) {
-          const int t = idx / NC, c = idx - t * NC;
-          uint4 val = make_uint4(0, 0, 0, 0);
-          if (t < ng) val = ld16(xhat + (size_t)(asg_all[g0 + t] / K) * H + (size_t)c * CH);
-          xs[c * kTokGroup + t] = val;
+        for (int c = tid; c < NC; c += 256) {
+          uint4 val[kTokGroup];
+#pragma unroll
+          for (int t = 0; t < kTokGroup; ++t)
+            val[t] = xrow[t] ? ld16(xrow[t] + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < kTokGroup; ++t) xs[c * kTokGroup + t] = val[t];
         }
         __syncthreads();
       };
@@ -209,7 +219,7 @@ constexpr int kDownRowsPerWave = 32;  // four batches of 8 rows
 // group's fp32 activations as [chunk][kTokGroup][kChunk].
 // P[asg][h] = w_asg * (A_asg . W_d[h]).
 template <class W, int NT, class Ready>
-__device__ __forceinline__ void down_item(const typename W::T *__restrict__ wd_e, const float *xs,
+__device__ __forceinline__ void down_item(const typename W::T *__restrict__ wd_e, const void *xs,
                                           int H, int I, int h0, int lane,
                                           const int32_t *__restrict__ asg,
                                           const float *__restrict__ wgt, int ng,
@@ -218,21 +228,49 @@ __device__ __forceinline__ void down_item(const typename W::T *__restrict__ wd_e
   const int NC = I / CH;
   const int nq = (NC + 63) / 64;
   const int nb = kDownRowsPerWave / 8;
-  auto rowptr = [&](int b, int r) { return wd_e + (size_t)(h0 + 8 * b + r) * I; };
+  const rsrc_t rs = make_rsrc(wd_e, (uint32_t)(H * I * sizeof(typename W::T)));
+  auto rowoff = [&](int b, int r) { return (uint32_t)((h0 + 8 * b + r) * I * (int)sizeof(typename W::T)); };
   auto fma = [&](int c, const uint4(&w)[8], float(&acc)[8][NT]) {
-    float xf[NT][CH];
+    if constexpr (std::is_same<W, WBf16>::value) {
+      // activations as bf16 (high, residual) pairs: two dot2 passes
+      const uint4 *xp = static_cast<const uint4 *>(xs);
+      uint4 xh[NT], xl[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t) {
+        xh[t] = c < NC ? xp[(c * kTokGroup + t) * 2] : make_uint4(0, 0, 0, 0);
+        xl[t] = c < NC ? xp[(c * kTokGroup + t) * 2 + 1] : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-      for (int j = 0; j < CH; ++j) xf[t][j] = c < NC ? xs[(c * kTokGroup + t) * CH + j] : 0.f;
+      for (int r = 0; r < 8; ++r)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float wf[CH];
-      chunk_to_f32<W>(w[r], wf);
+        for (int t = 0; t < NT; ++t) {
+          float a = acc[r][t];
+          a = dot2bf(w[r].x, xh[t].x, a);
+          a = dot2bf(w[r].y, xh[t].y, a);
+          a = dot2bf(w[r].z, xh[t].z, a);
+          a = dot2bf(w[r].w, xh[t].w, a);
+          a = dot2bf(w[r].x, xl[t].x, a);
+          a = dot2bf(w[r].y, xl[t].y, a);
+          a = dot2bf(w[r].z, xl[t].z, a);
+          a = dot2bf(w[r].w, xl[t].w, a);
+          acc[r][t] = a;
+        }
+    } else {
+      const float *xp = static_cast<const float *>(xs);
+      float xf[NT][CH];
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int j = 0; j < CH; ++j) acc[r][t] = fmaf(wf[j], xf[t][j], acc[r][t]);
+        for (int j = 0; j < CH; ++j) xf[t][j] = c < NC ? xp[(c * kTokGroup + t) * CH + j] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float wf[CH];
+        chunk_to_f32<W>(w[r], wf);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int j = 0; j < CH; ++j) acc[r][t] = fmaf(wf[j], xf[t][j], acc[r][t]);
+      }
     }
   };
   auto batch_end = [&](int b, float(&acc)[8][NT]) {
@@ -247,7 +285,7 @@ __device__ __forceinline__ void down_item(const typename W::T *__restrict__ wd_e
       }
     }
   };
-  stream_rows<W, NT>(nb, nq, NC, lane, rowptr, ready, fma, batch_end);
+  stream_rows<W, NT>(rs, nb, nq, NC, lane, rowoff, ready, fma, batch_end);
 }
 
 template <class W>
@@ -255,34 +293,69 @@ __global__ __launch_bounds__(256) void routed_down_kernel(const float *__restric
                                                           const typename W::T *__restrict__ wd,
                                                           RouteBufs r, float *__restrict__ P,
                                                           int H, int I) {
-  extern __shared__ float xsf[];  // [I / kChunk][kTokGroup][kChunk]
+  // bf16 weights: [I / 8][kTokGroup][high, residual] bf16x8 pairs;
+  // fp32 weights: [I / 4][kTokGroup][4] floats.  16 * I bytes either way.
+  extern __shared__ uint4 xsm[];
   constexpr int CH = W::kChunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rows_per_item = 4 * kDownRowsPerWave;
   const int tiles = H / rows_per_item;
-  const int items = r.meta[0] * tiles;
+  const int items = uniform(r.meta[0]) * tiles;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int u = item / tiles, tile = item - u * tiles;
-    const int e = r.union_list[u];
-    const int n = r.slot_n[u];
+    const int e = uniform(r.union_list[u]);
+    const int n = uniform(r.slot_n[u]);
     const typename W::T *wd_e = wd + (size_t)e * H * I;
     const int32_t *asg_all = r.slot_asg + u * kMaxT;
-    const int h0 = tile * rows_per_item + wave * kDownRowsPerWave;
+    const int h0 = uniform(tile * rows_per_item + wave * kDownRowsPerWave);
     for (int g0 = 0; g0 < n; g0 += kTokGroup) {
       const int ng = min(kTokGroup, n - g0);
       auto ready = [&]() {
-        __syncthreads();
-        for (int idx = tid; idx < kTokGroup * I; idx += 256) {
-          const int t = idx / I, k = idx - t * I;
-          const int c = k / CH, j = k - c * CH;
-          xsf[(c * kTokGroup + t) * CH + j] = t < ng ? A[(size_t)asg_all[g0 + t] * I + k] : 0.f;
+        // activation rows of the group (wave-uniform scalar loads of the
+        // assignment ids); one 16-byte weight chunk's worth per thread and row
+        const float *arow[kTokGroup];
+#pragma unroll
+        for (int t = 0; t < kTokGroup; ++t) arow[t] = t < ng ? A + (size_t)asg_all[g0 + t] * I : nullptr;
+        __syncthreads();  // previous group's readers are done with xs
+        for (int c = tid; c < I / CH; c += 256) {
+          if constexpr (std::is_same<W, WBf16>::value) {
+            uint4 *xp = reinterpret_cast<uint4 *>(xsm);
+#pragma unroll
+            for (int t = 0; t < kTokGroup; ++t) {
+              float x[8];
+              if (arow[t]) {
+                const float4 u = reinterpret_cast<const float4 *>(arow[t] + c * 8)[0];
+                const float4 v = reinterpret_cast<const float4 *>(arow[t] + c * 8)[1];
+                x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+                x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+              } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = 0.f;
+              }
+              uint4 hi, lo;
+              split_hi_lo(x, hi, lo);
+              xp[(c * kTokGroup + t) * 2] = hi;
+              xp[(c * kTokGroup + t) * 2 + 1] = lo;
+            }
+          } else {
+            float *xf = reinterpret_cast<float *>(xsm);
+#pragma unroll
+            for (int t = 0; t < kTokGroup; ++t) {
+              const float4 u = arow[t] ? *reinterpret_cast<const float4 *>(arow[t] + c * 4)
+                                       : make_float4(0, 0, 0, 0);
+              xf[(c * kTokGroup + t) * 4 + 0] = u.x;
+              xf[(c * kTokGroup + t) * 4 + 1] = u.y;
+              xf[(c * kTokGroup + t) * 4 + 2] = u.z;
+              xf[(c * kTokGroup + t) * 4 + 3] = u.w;
+            }
+          }
         }
         __syncthreads();
       };
       const int32_t *asg = asg_all + g0;
-      if (ng <= 1)      down_item<W, 1>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P, ready);
-      else if (ng <= 2) down_item<W, 2>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P, ready);
-      else              down_item<W, 4>(wd_e, xsf, H, I, h0, lane, asg, r.wgt, ng, P, ready);
+      if (ng <= 1)      down_item<W, 1>(wd_e, xsm, H, I, h0, lane, asg, r.wgt, ng, P, ready);
+      else if (ng <= 2) down_item<W, 2>(wd_e, xsm, H, I, h0, lane, asg, r.wgt, ng, P, ready);
+      else              down_item<W, 4>(wd_e, xsm, H, I, h0, lane, asg, r.wgt, ng, P, ready);
     }
   }
 }
@@ -385,7 +458,7 @@ hipError_t launch_routed_gateup(int wdtype, const void *xhat, const void *w_gate
 hipError_t launch_routed_down(int wdtype, const float *A, const void *w_down, const RouteBufs &r,
                               float *P, int H, int E, int K, int I, int grid, hipStream_t s) {
   (void)E; (void)K;
-  const size_t lds = (size_t)I * kTokGroup * sizeof(float);
+  const size_t lds = (size_t)I * 16;
   hipError_t err;
   if (wdtype == 1) {
     if ((err = allow_lds(routed_down_kernel<WBf16>, lds)) != hipSuccess) return err;

@@ -68,8 +68,10 @@ hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const in
 // LM head online softmax: per (position, workgroup) partial (max, sum, argmax),
 // stored [T][grid].
 int lmhead_grid(int cus);
+size_t lmhead_packed_bytes(int wdtype, int H, int V);
+hipError_t launch_pack_lm(int wdtype, const void *w_lm, int V, int H, void *packed, hipStream_t s);
 size_t lmhead_lds_bytes(int wdtype, int T, int H);
-hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,
+hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm_packed, int T, int H, int V,
                          float *part_m, float *part_s, int32_t *part_i, int grid, hipStream_t s);
 
 hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,

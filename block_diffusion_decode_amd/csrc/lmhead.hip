@@ -48,13 +48,12 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
 // has up to 2 * kLmBatch loads outstanding.
 constexpr int kLmBatch = 8;
 
+// Packed layout: k-step s of a 16-row tile is one contiguous KiB in which lane
+// l = li + 16 g finds its MFMA operand (row li, chunk 4s + g) at byte 16 l.
 template <class W, int NT>
-__device__ __forceinline__ void lm_load(const typename W::T *__restrict__ wrow, int b, int g,
-                                        uint4 (&a)[kLmBatch]) {
-  constexpr int CH = W::kChunk;
+__device__ __forceinline__ void lm_load(rsrc_t rs, uint32_t vbase, int b, uint4 (&a)[kLmBatch]) {
 #pragma unroll
-  for (int j = 0; j < kLmBatch; ++j)
-    a[j] = ld16_stream(wrow + (size_t)((b * kLmBatch + j) * 4 + g) * CH);
+  for (int j = 0; j < kLmBatch; ++j) a[j] = buf_ld16(rs, vbase, (uint32_t)(b * kLmBatch + j) * 1024u);
 }
 
 template <class W, int NT>
@@ -82,27 +81,25 @@ __device__ __forceinline__ void lm_mma(const uint4 (&a)[kLmBatch], const uint4 *
 // acc[n] += W[row] . xhat[col]^T over the full hidden size: NC chunks of 16
 // bytes per row, 4 chunks per MFMA k-step (lane group g takes chunk 4s + g).
 template <class W, int NT>
-__device__ __forceinline__ void lm_tile_dot(const typename W::T *__restrict__ wrow,
-                                            const uint4 *__restrict__ xs, int NC, int g, int li,
-                                            f32x4 (&acc)[NT]) {
+__device__ __forceinline__ void lm_tile_dot(rsrc_t rs, uint32_t vbase, const uint4 *__restrict__ xs,
+                                            int NC, int g, int li, f32x4 (&acc)[NT]) {
   const int nb = NC / (4 * kLmBatch);
   uint4 a0[kLmBatch], a1[kLmBatch];
   int b = 0;
-  if (nb > 0) lm_load<W, NT>(wrow, 0, g, a0);
+  if (nb > 0) lm_load<W, NT>(rs, vbase, 0, a0);
   while (b < nb) {
-    if (b + 1 < nb) lm_load<W, NT>(wrow, b + 1, g, a1);
+    if (b + 1 < nb) lm_load<W, NT>(rs, vbase, b + 1, a1);
     lm_mma<W, NT>(a0, xs, b, g, li, acc);
     if (++b >= nb) break;
-    if (b + 1 < nb) lm_load<W, NT>(wrow, b + 1, g, a0);
+    if (b + 1 < nb) lm_load<W, NT>(rs, vbase, b + 1, a0);
     lm_mma<W, NT>(a1, xs, b, g, li, acc);
     ++b;
   }
   // remaining k-steps when NC is not a multiple of 4 * kLmBatch
   constexpr int TP = 16 * NT;
-  constexpr int CH = W::kChunk;
   for (int c0 = nb * 4 * kLmBatch; c0 < NC; c0 += 4) {
     const int c = c0 + g;
-    const uint4 a = ld16_stream(wrow + (size_t)c * CH);
+    const uint4 a = buf_ld16(rs, vbase, (uint32_t)(c0 / 4) * 1024u);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const uint4 bv = xs[c * TP + n * 16 + li];
@@ -149,14 +146,17 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   for (int n = 0; n < NT; ++n) { m[n] = -FLT_MAX; s[n] = 0.f; am[n] = INT_MAX; }
 
   const int ntiles = (V + 15) / 16;
-  for (int tile = blockIdx.x * kLmWaves + wave; tile < ntiles; tile += gridDim.x * kLmWaves) {
+  const uint32_t vbase = (uint32_t)lane * 16u;
+  const uint32_t tile_bytes = (uint32_t)(16 * H * (int)sizeof(typename W::T));
+  for (int tile = uniform(blockIdx.x * kLmWaves + wave); tile < ntiles; tile += gridDim.x * kLmWaves) {
     const int row0 = tile * 16;
-    // rows past V read the last row; their logits are dropped in the epilogue
-    const typename W::T *wrow = wlm + (size_t)min(row0 + li, V - 1) * H;
+    // descriptor over this tile's packed rows (rows past V were packed as
+    // zeros; their logits are dropped in the epilogue)
+    const rsrc_t rs = make_rsrc(wlm + (size_t)row0 * H, tile_bytes);
     f32x4 acc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    lm_tile_dot<W, NT>(wrow, xs, NC, g, li, acc);
+    lm_tile_dot<W, NT>(rs, vbase, xs, NC, g, li, acc);
     // epilogue: lane holds rows row0 + 4g + r (r = 0..3) of column li + 16n
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -283,6 +283,42 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ 
       round_info[3] = left == 0 ? 1 : 0;
     }
   }
+}
+
+// Packs w_lm [V][H] into the tile layout the LM-head kernel streams: for
+// tile tau (rows 16 tau .. 16 tau + 15) and MFMA k-step s, a contiguous
+// 16-byte-per-lane block where lane l = li + 16 g holds row 16 tau + li,
+// elements [s*KS + g*CH, s*KS + g*CH + CH) (KS = 4 CH: 32 for bf16, 16 for
+// fp32).  Rows past V are zero.  One thread per 16-byte unit.
+template <class W>
+__global__ __launch_bounds__(256) void pack_lm_kernel(const typename W::T *__restrict__ w, int V, int H,
+                                                      uint4 *__restrict__ out, long long units) {
+  constexpr int CH = W::kChunk;
+  const int S = H / (4 * CH);
+  for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+       u += (long long)gridDim.x * blockDim.x) {
+    const int l = (int)(u & 63);
+    const long long blk = u >> 6;
+    const long long tau = blk / S;
+    const int st = (int)(blk - tau * S);
+    const long long row = tau * 16 + (l & 15);
+    const int k0 = st * 4 * CH + (l >> 4) * CH;
+    out[u] = row < V ? ld16(w + row * H + k0) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+size_t lmhead_packed_bytes(int wdtype, int H, int V) {
+  return (size_t)((V + 15) / 16) * 16 * H * (wdtype == 1 ? 2 : 4);
+}
+
+hipError_t launch_pack_lm(int wdtype, const void *w_lm, int V, int H, void *packed, hipStream_t s) {
+  const long long units = (long long)(lmhead_packed_bytes(wdtype, H, V) / 16);
+  const int grid = (int)((units + 255) / 256 < 65536 ? (units + 255) / 256 : 65536);
+  if (wdtype == 1)
+    pack_lm_kernel<WBf16><<<grid, 256, 0, s>>>((const bf16_t *)w_lm, V, H, (uint4 *)packed, units);
+  else
+    pack_lm_kernel<WF32><<<grid, 256, 0, s>>>((const float *)w_lm, V, H, (uint4 *)packed, units);
+  return hipGetLastError();
 }
 
 int lmhead_grid(int cus) { return cus; }

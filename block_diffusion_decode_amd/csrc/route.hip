@@ -118,38 +118,60 @@ __device__ __forceinline__ void wave_argbest(float &v, int &id) {
   }
 }
 
-// One wave picks up to K experts for one position by descending logit (ties to
-// the lower id) among those allowed (allowed == nullptr: all).  lv / pv hold
-// the lane's logits and softmax scores for experts lane + 64j.  Writes the
-// picks and their scores to idx_row / psel_row (-1 / 0 where fewer than K are
-// allowed) and returns nothing; all lanes take part.
-__device__ void wave_topk(const float (&lv)[4], const float (&pv)[4], int E, int K,
-                          const int32_t *allowed, int lane, int32_t *idx_row, float *psel_row) {
-  bool avail[4];
+// One wave picks up to K experts for each of its NQ positions by descending
+// logit (ties to the lower id) among those allowed (allowed == nullptr: all);
+// the positions' selections run interleaved.  lv / pv hold the lane's logits
+// and softmax scores for experts lane + 64j.  Writes the picks and their
+// scores to idx_row[q] / psel_row[q] (-1 / 0 where fewer than K are allowed);
+// rows with live[q] false are skipped.  All lanes take part.
+template <int NQ>
+__device__ void wave_topk(const float (&lv)[NQ][4], const float (&pv)[NQ][4], const bool (&live)[NQ],
+                          int E, int K, const int32_t *allowed, int lane, int32_t *const (&idx_row)[NQ],
+                          float *const (&psel_row)[NQ]) {
+  bool avail[NQ][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    avail[j] = e < E && (allowed == nullptr || allowed[e] != 0);
-  }
-  for (int k = 0; k < K; ++k) {
-    float bv = -FLT_MAX;
-    int be = INT_MAX;
+  for (int q = 0; q < NQ; ++q)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      if (avail[j] && (be == INT_MAX || lv[j] > bv)) { bv = lv[j]; be = e; }
+      avail[q][j] = live[q] && e < E && (allowed == nullptr || allowed[e] != 0);
     }
-    wave_argbest(bv, be);
-    float ps = 0.f;
-    if (be != INT_MAX) {
-      const int j = be >> 6;                      // uniform across the wave
-      const float pj = j == 0 ? pv[0] : j == 1 ? pv[1] : j == 2 ? pv[2] : pv[3];
-      ps = __shfl(pj, be & 63);
-      if ((be & 63) == lane) avail[j] = false;
+  for (int k = 0; k < K; ++k) {
+    float bv[NQ];
+    int be[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      bv[q] = -FLT_MAX;
+      be[q] = INT_MAX;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        if (avail[q][j] && (be[q] == INT_MAX || lv[q][j] > bv[q])) { bv[q] = lv[q][j]; be[q] = e; }
+      }
     }
-    if (lane == 0) {
-      idx_row[k] = be == INT_MAX ? -1 : be;
-      psel_row[k] = ps;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float v2 = __shfl_xor(bv[q], s);
+        const int i2 = __shfl_xor(be[q], s);
+        if (v2 > bv[q] || (v2 == bv[q] && i2 < be[q])) { bv[q] = v2; be[q] = i2; }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (!live[q]) continue;
+      float ps = 0.f;
+      if (be[q] != INT_MAX) {
+        const int j = be[q] >> 6;                      // uniform across the wave
+        const float pj = j == 0 ? pv[q][0] : j == 1 ? pv[q][1] : j == 2 ? pv[q][2] : pv[q][3];
+        ps = __shfl(pj, be[q] & 63);
+        if ((be[q] & 63) == lane) avail[q][j] = false;
+      }
+      if (lane == 0) {
+        idx_row[q][k] = be[q] == INT_MAX ? -1 : be[q];
+        psel_row[q][k] = ps;
+      }
     }
   }
 }
@@ -162,6 +184,7 @@ struct SelShared {
   double mass[kMaxE];           // block expert mass
   int32_t ulist[kMaxE];         // experts with a pick, ascending id
   double umass[kMaxE];          // their mass, in ulist order
+  int32_t rank[kMaxE];          // rank of each ulist entry
   int32_t sorted[kMaxE];        // ulist ranked by (mass desc, id asc)
   double cum[kMaxE];            // prefix sums of ranked mass
   int32_t member[kMaxE];        // coreset membership
@@ -234,20 +257,35 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
   }
   union_scan(sh, E);
   const int nu = sh.nu;
-  if (tid < nu) sh.umass[tid] = sh.mass[sh.ulist[tid]];
-  __syncthreads();
   if (tid < nu) {
-    const double m = sh.umass[tid];
-    const int e = sh.ulist[tid];
-    int r = 0;
-    for (int j = 0; j < nu; ++j) {
-      const double o = sh.umass[j];
-      r += (o > m) || (o == m && sh.ulist[j] < e);
+    sh.umass[tid] = sh.mass[sh.ulist[tid]];
+    sh.rank[tid] = 0;
+  }
+  __syncthreads();
+  {
+    // rank of union entry j = number of entries before it in (mass desc, id
+    // asc) order; the block's threads split each entry's count into parts
+    const int parts = (int)blockDim.x / kMaxE;
+    const int j = tid % kMaxE, part = tid / kMaxE;
+    if (j < nu) {
+      const double m = sh.umass[j];
+      const int e = sh.ulist[j];
+      const int lo = part * nu / parts, hi = (part + 1) * nu / parts;
+      int r = 0;
+#pragma unroll 8
+      for (int i = lo; i < hi; ++i) {
+        const double o = sh.umass[i];
+        r += (o > m) || (o == m && sh.ulist[i] < e);
+      }
+      atomicAdd(&sh.rank[j], r);
     }
-    sh.sorted[r] = e;
-    sh.cum[r] = m;
   }
   if (tid == 0) sh.below = 0;
+  __syncthreads();
+  if (tid < nu) {
+    sh.sorted[sh.rank[tid]] = sh.ulist[tid];
+    sh.cum[sh.rank[tid]] = sh.umass[tid];
+  }
   __syncthreads();
   int k = nu;
   if (top_p < 1.0f && nu > 0) {
@@ -301,14 +339,20 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
   float lv[kTokPerWave][4], pv[kTokPerWave][4];
 
   // softmax over all experts and top-K by logit
+  bool live[kTokPerWave];
+  int32_t *idx_rows[kTokPerWave];
+  float *psel_rows[kTokPerWave];
+#pragma unroll
   for (int q = 0; q < kTokPerWave; ++q) {
     const int t = wave + q * nw;
-    if (t >= T) continue;
+    live[q] = t < T;
+    idx_rows[q] = sh.idx[live[q] ? t : 0];
+    psel_rows[q] = sh.psel[live[q] ? t : 0];
     float m = -FLT_MAX;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      lv[q][j] = e < E ? r.logits[(size_t)t * E + e] : -FLT_MAX;
+      lv[q][j] = (live[q] && e < E) ? r.logits[(size_t)t * E + e] : -FLT_MAX;
       m = fmaxf(m, lv[q][j]);
     }
     m = wave_max(m);
@@ -316,18 +360,18 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      pv[q][j] = e < E ? expf(lv[q][j] - m) : 0.f;
+      pv[q][j] = (live[q] && e < E) ? expf(lv[q][j] - m) : 0.f;
       s += pv[q][j];
     }
     s = wave_sum(s);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      pv[q][j] = pv[q][j] / s;
-      if (e < E) r.prob[(size_t)t * E + e] = pv[q][j];
+      pv[q][j] = live[q] ? pv[q][j] / s : 0.f;
+      if (live[q] && e < E) r.prob[(size_t)t * E + e] = pv[q][j];
     }
-    wave_topk(lv[q], pv[q], E, K, nullptr, lane, sh.idx[t], sh.psel[t]);
   }
+  wave_topk<kTokPerWave>(lv, pv, live, E, K, nullptr, lane, idx_rows, psel_rows);
   __syncthreads();
 
   // block mass and coreset (also run without coreset: it reports the union)
@@ -336,13 +380,11 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
   write_bits(sh, E, r.cs_bits);
   if (top_p < 1.0f) {
     const int kk = min(K, sh.csize);
-    for (int q = 0; q < kTokPerWave; ++q) {
-      const int t = wave + q * nw;
-      if (t >= T) continue;
-      wave_topk(lv[q], pv[q], E, kk, sh.member, lane, sh.idx[t], sh.psel[t]);
-      if (lane == 0)
-        for (int k = kk; k < K; ++k) { sh.idx[t][k] = -1; sh.psel[t][k] = 0.f; }
-    }
+    wave_topk<kTokPerWave>(lv, pv, live, E, kk, sh.member, lane, idx_rows, psel_rows);
+#pragma unroll
+    for (int q = 0; q < kTokPerWave; ++q)
+      if (live[q] && lane == 0)
+        for (int k = kk; k < K; ++k) { idx_rows[q][k] = -1; psel_rows[q][k] = 0.f; }
     __syncthreads();
     build_masks(sh, T, E, K);
   }

@@ -137,13 +137,29 @@ bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx,
                               uint32_t *coreset_bits, int32_t *coreset_size,
                               float *expert_mass, void *stream);
 
+/* Bytes of the packed LM-head weight (0 if the arguments are invalid). */
+size_t bdd_lmhead_packed_bytes(int32_t V, int32_t H, int32_t dtype);
+
+/* Packs the LM-head weight w_lm [V][H] (dtype) into the tile layout the LM
+ * head streams, once, at load time: rows are grouped in tiles of 16, and for
+ * each tile and each MFMA k-step (32 bf16 or 16 fp32 elements of the hidden
+ * dimension) the 16 x k-step block is stored contiguously as 64 16-byte units,
+ * unit l = li + 16 g holding row li, elements [kstep*s + g*c, kstep*s + g*c + c)
+ * with c = 8 (bf16) or 4 (fp32).  Rows past V are zero.  w_packed must hold
+ * bdd_lmhead_packed_bytes(V, H, dtype) bytes.  Same bytes as w_lm (plus the
+ * padding of the last tile); every load of the LM head then reads a
+ * contiguous KiB. */
+bdd_status bdd_lmhead_pack(const void *w_lm, int32_t V, int32_t H, int32_t dtype, void *w_packed,
+                           void *stream);
+
 /* Workspace bytes bdd_lmhead_confidence_commit needs. */
 size_t bdd_lmhead_workspace_bytes(int32_t T, int32_t H, int32_t V);
 
 /* LM head, confidence and LowConfidence commit ([P1] section 三 pseudocode
  * and rules; [P2] decoding-loop steps 2-4).
- *   hhat   [T][H] dtype     normalised final hidden states
- *   w_lm   [V][H] dtype     output embedding rows
+ *   hhat      [T][H] dtype  normalised final hidden states
+ *   w_packed  the LM-head weight [V][H] (row v = token v) as packed by
+ *             bdd_lmhead_pack
  *   For each position: logits z = hhat W_lm^T (never stored), conf = max
  *   softmax probability = 1 / sum_v exp(z_v - max z), choice = argmax (lowest
  *   token id on ties).  Then among positions whose token is MASK: every one
@@ -154,7 +170,7 @@ size_t bdd_lmhead_workspace_bytes(int32_t T, int32_t H, int32_t V);
  *   conf       [T] fp32 out, choice [T] int32 out (all positions)
  *   round_info [4] int32 out      see BDD_RI_*
  *   threshold in (0, 1]. */
-bdd_status bdd_lmhead_confidence_commit(const void *hhat, const void *w_lm, int32_t T,
+bdd_status bdd_lmhead_confidence_commit(const void *hhat, const void *w_packed, int32_t T,
                                         int32_t H, int32_t V, int32_t dtype,
                                         float threshold, int32_t *tokens, float *conf,
                                         int32_t *choice, int32_t *round_info, void *ws,
@@ -170,14 +186,14 @@ size_t bdd_round_workspace_bytes(const bdd_moe_dims *d, int32_t V);
  * the commit (as in bdd_lmhead_confidence_commit).
  *   layers       HOST array [n_layers] of device weight pointers
  *   x_in         [T][H] fp32 hidden states entering layer 0 (read only)
- *   w_lm         [V][H] wdtype
+ *   w_packed     LM-head weight [V][H] wdtype, packed by bdd_lmhead_pack
  *   tokens, conf, choice, round_info as in bdd_lmhead_confidence_commit
  *   layer_topk_idx   [n_layers][T][K] int32 out (may be NULL)
  *   layer_n_distinct [n_layers] int32 out (may be NULL)
  *   hhat_out     [T][H] wdtype out: the LM-head input (may be NULL) */
 bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
                                    const bdd_moe_weights *layers, float coreset_top_p,
-                                   const void *w_lm, int32_t V, float threshold,
+                                   const void *w_packed, int32_t V, float threshold,
                                    const float *x_in, int32_t *tokens, float *conf,
                                    int32_t *choice, int32_t *round_info,
                                    int32_t *layer_topk_idx, int32_t *layer_n_distinct,
@@ -195,7 +211,7 @@ int32_t bdd_device_cus(void);
  * this library whose name contains `filter` (NULL or "": all) is bracketed by
  * a pair of hipEvents recorded on the launching stream.  Kernel names:
  * rmsnorm, router_logits, route_select, coreset, shared_gateup, routed_gateup,
- * shared_down, routed_down, combine, lmhead, commit.  Not thread-safe. */
+ * shared_down, routed_down, combine, lmhead, commit, pack_lm.  Not thread-safe. */
 bdd_status bdd_timing_enable(int32_t on, const char *filter);
 
 /* Waits for the recorded events, then for up to max_kernels distinct kernel

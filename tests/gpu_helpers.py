@@ -110,3 +110,41 @@ def bf16_ulp(x):
     x = np.abs(np.asarray(x, np.float64))
     e = np.floor(np.log2(np.maximum(x, 1e-38)))
     return np.ldexp(1.0, (e - 7).astype(int))
+
+
+def commit_check(tok_before, c_ref, ch_ref, excl, c_gpu, ch_gpu, tok_after_gpu, ri_gpu, tau=TAU):
+    """Compare one GPU commit with the oracle's.  ``excl`` marks positions whose
+    GPU inputs legitimately differ (an upstream decision inside the margin
+    band).  Returns (tok_ref_after, exact): exact means the whole round was
+    compared and both token states agree; otherwise only the uniquely
+    determined part was compared and the caller must stop comparing rounds.
+    Raises AssertionError on a mismatch."""
+    tok_before = np.asarray(tok_before)
+    tok_after_gpu = np.asarray(tok_after_gpu)
+    masked = tok_before == O.MASK
+    # written tokens never change, and a round with masked positions writes one
+    assert np.array_equal(tok_after_gpu[~masked], tok_before[~masked])
+    if masked.any():
+        assert (tok_after_gpu[masked] != O.MASK).sum() >= 1
+    amb = np.asarray(excl) | (np.abs(np.asarray(c_ref) - tau) < BAND)
+    if not (masked & amb).any() and not commit_in_band(tok_before, c_ref, tau):
+        tok_ref, acc, fb, left, done = O.commit(tok_before, c_ref, ch_ref, tau)
+        assert np.array_equal(tok_after_gpu, tok_ref), (tok_after_gpu, tok_ref)
+        assert list(ri_gpu) == [len(acc), int(fb), left, int(done)]
+        return tok_ref, True
+    # some masked position is ambiguous: if a clear position passes there is no
+    # fallback, and every clear position's decision is unique
+    clear_pass = masked & ~amb & (np.asarray(c_ref) >= tau)
+    if clear_pass.any():
+        for t in np.nonzero(masked & ~amb)[0]:
+            wrote = tok_after_gpu[t] != O.MASK
+            assert wrote == (c_ref[t] >= tau), t
+            if wrote:
+                assert tok_after_gpu[t] == ch_ref[t], t
+        for t in np.nonzero(masked & amb)[0]:   # GPU consistent with its own confidence
+            wrote = tok_after_gpu[t] != O.MASK
+            assert wrote == (c_gpu[t] >= tau), t
+            if wrote:
+                assert tok_after_gpu[t] == ch_gpu[t], t
+        assert ri_gpu[1] == 0
+    return None, False
