@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -69,8 +70,37 @@ bool timing_wants(const char *name) {
     }                                                                            \
   } while (0)
 
+// ----------------------------------------------------------------- side stream
+// The shared expert depends only on the normalised block, so it runs on a
+// library-owned stream of the same device (default priority), forked from and
+// joined back into the caller's stream with events: it overlaps routing and
+// the routed experts.  Calls on one device must not overlap (they share it).
+struct Side {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+Side g_side[64];
+std::mutex g_side_mu;
+
+bdd_status side_for_current_device(Side **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) return fail(BDD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side &sd = g_side[dev];
+  if (!sd.s2) {
+    if ((e = hipStreamCreateWithFlags(&sd.s2, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess)
+      return fail(BDD_ERR_HIP, "side stream: %s", hipGetErrorString(e));
+  }
+  *out = &sd;
+  return BDD_OK;
+}
+
 constexpr int kMaxLmGrid = 1024;
 constexpr int kExpertWgPerCu = 3;
+constexpr int kDownRowsPerItem = 128;
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int wdtype) { return wdtype == BDD_BF16 ? 2 : 4; }
@@ -104,11 +134,14 @@ bdd_status check_dims(const bdd_moe_dims *d) {
                 d->I, d->I_shared);
   if (d->H > 8192 || d->I > 8192 || d->I_shared > 8192)
     return fail(BDD_ERR_UNSUPPORTED, "H, I, I_shared must be <= 8192");
+  if (router_lds_bytes(d->wdtype, d->T, d->H) > 144 * 1024)
+    return fail(BDD_ERR_UNSUPPORTED, "T=%d, H=%d: the normalised block exceeds the LDS budget", d->T, d->H);
   return BDD_OK;
 }
 
 struct MoePlan {
   size_t logits, prob, idx, wgt, meta, ulist, slot_n, slot_asg, bits, mass, xhat, A, A_s, P, P_s;
+  size_t sorted, sel_count;
   size_t end;
 };
 
@@ -132,12 +165,14 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   p.A_s = take(T * (Is ? Is : 1) * 4);
   p.P = take(T * K * H * 4);
   p.P_s = take(T * H * 4);
+  p.sorted = take(T * E * 4);
+  p.sel_count = take(64);
   p.end = o;
   return p;
 }
 
 struct LmPlan {
-  size_t m, s, i, end;
+  size_t m, s, i, count, end;
 };
 
 LmPlan plan_lm(int T, size_t base) {
@@ -147,6 +182,7 @@ LmPlan plan_lm(int T, size_t base) {
   p.m = take((size_t)kMaxLmGrid * T * 4);
   p.s = take((size_t)kMaxLmGrid * T * 4);
   p.i = take((size_t)kMaxLmGrid * T * 4);
+  p.count = take(64);
   p.end = o;
   return p;
 }
@@ -201,26 +237,40 @@ RouteBufs route_bufs(void *ws, const MoePlan &p) {
   return r;
 }
 
-// One MoE layer from xhat (already normalised).  combine: h += y and the next
-// normalisation when h != nullptr, else y_out = y.
-bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_p, const void *xhat,
-                     RouteBufs r, const MoePlan &p, void *ws, float *h, float *y_out,
-                     void *xhat_next, hipStream_t s) {
+// One MoE layer.  With h_in given, the layer first normalises it into xhat
+// (copying it to h_copy and clearing lm_count when those are given); else
+// xhat already holds the normalised block.  combine: h += y and the next
+// normalisation into xhat_next when h != nullptr, else y_out = y.
+bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_p, const float *h_in,
+                     float *h_copy, void *xhat, RouteBufs r, const MoePlan &p, void *ws, float *h,
+                     float *y_out, void *xhat_next, int32_t *lm_count, hipStream_t s) {
   const int T = d.T, H = d.H, E = d.E, K = d.K, I = d.I, Is = d.I_shared;
   const int cus = device_cus();
   float *A = at<float>(ws, p.A), *A_s = at<float>(ws, p.A_s);
   float *P = at<float>(ws, p.P), *P_s = at<float>(ws, p.P_s);
-  LAUNCH("router_logits", s, launch_router_logits(d.wdtype, xhat, w.w_router, w.router_bias, r.logits, T, H, E, s));
-  LAUNCH("route_select", s, launch_route_select(r, T, E, K, top_p, s));
-  if (Is > 0) LAUNCH("shared_gateup", s, launch_shared_gateup(d.wdtype, xhat, w.ws_gate_up, A_s, T, H, Is, s));
+  int32_t *sel_count = at<int32_t>(ws, p.sel_count);
+  if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, T, H, lm_count, s));
+  LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, w.router_bias, r.logits,
+                                           T, H, E, s));
+  Side *sd = nullptr;
+  if (Is > 0) {
+    bdd_status st = side_for_current_device(&sd);
+    if (st != BDD_OK) return st;
+    HIP_TRY(hipEventRecord(sd->fork, s));
+    HIP_TRY(hipStreamWaitEvent(sd->s2, sd->fork, 0));
+    LAUNCH("shared_gateup", sd->s2, launch_shared_gateup(d.wdtype, xhat, w.ws_gate_up, A_s, T, H, Is, sd->s2));
+    LAUNCH("shared_down", sd->s2, launch_shared_down(d.wdtype, A_s, w.ws_down, P_s, T, H, Is, sd->s2));
+    HIP_TRY(hipEventRecord(sd->join, sd->s2));
+  }
+  LAUNCH("route_select", s, launch_route_select(r, T, E, K, top_p, at<int32_t>(ws, p.sorted), sel_count, s));
   const int union_max = E < T * K ? E : T * K;
-  int g1 = union_max * (I / 16), g2 = union_max * (H / 128);
+  int g1 = union_max * (I / 16), g2 = union_max * (H / kDownRowsPerItem);
   const int cap = cus * kExpertWgPerCu;
   g1 = g1 < cap ? g1 : cap;
   g2 = g2 < cap ? g2 : cap;
   LAUNCH("routed_gateup", s, launch_routed_gateup(d.wdtype, xhat, w.w_gate_up, r, A, T, H, E, K, I, g1, s));
-  if (Is > 0) LAUNCH("shared_down", s, launch_shared_down(d.wdtype, A_s, w.ws_down, P_s, T, H, Is, s));
   LAUNCH("routed_down", s, launch_routed_down(d.wdtype, A, w.w_down, r, P, H, E, K, I, g2, s));
+  if (Is > 0) HIP_TRY(hipStreamWaitEvent(s, sd->join, 0));
   LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P_s : nullptr, r.idx, h, y_out, xhat_next, T, H, K, s));
   return BDD_OK;
 }
@@ -305,9 +355,8 @@ bdd_status bdd_moe_block_forward(const bdd_moe_dims *d, const bdd_moe_weights *w
   r.n_distinct_out = n_distinct;
   r.coreset_size_out = coreset_size;
   void *xhat = xhat_out ? xhat_out : at<void>(ws, p.xhat);
-  LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, h, nullptr, xhat, d->T, d->H, s));
-  return moe_layer(*d, *w, coreset_top_p >= 1.0f ? 1.0f : coreset_top_p, xhat, r, p, ws, nullptr, y,
-                   nullptr, s);
+  return moe_layer(*d, *w, coreset_top_p >= 1.0f ? 1.0f : coreset_top_p, h, nullptr, xhat, r, p, ws,
+                   nullptr, y, nullptr, nullptr, s);
 }
 
 bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx, int32_t T, int32_t E,
@@ -361,7 +410,7 @@ bdd_status bdd_lmhead_confidence_commit(const void *hhat, const void *w_lm, int3
   const int grid = lmhead_grid(cus) < kMaxLmGrid ? lmhead_grid(cus) : kMaxLmGrid;
   float *pm = at<float>(ws, p.m), *ps = at<float>(ws, p.s);
   int32_t *pi = at<int32_t>(ws, p.i);
-  LAUNCH("lmhead", s, launch_lmhead(dtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, s));
+  LAUNCH("lmhead", s, launch_lmhead(dtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, nullptr, s));
   LAUNCH("commit", s, launch_commit(pm, ps, pi, grid, T, threshold, tokens, conf, choice, round_info, s));
   return BDD_OK;
 }
@@ -400,20 +449,27 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
   void *xhat = at<void>(ws, p.xhat);
   void *hhat = hhat_out ? hhat_out : xhat;
   const float tp = coreset_top_p >= 1.0f ? 1.0f : coreset_top_p;
-  LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, n_layers == 0 ? hhat : xhat, T, H, s));
+  int32_t *count = at<int32_t>(ws, lp.count);
+  if (n_layers == 0) {
+    // the LM head reads RMSNorm(x_in); the norm kernel clears the counter
+    LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, hhat, T, H, count, s));
+  }
   for (int l = 0; l < n_layers; ++l) {
     RouteBufs r = route_bufs(ws, p);
     if (layer_topk_idx) r.idx = layer_topk_idx + (size_t)l * T * K;
     if (layer_n_distinct) r.n_distinct_out = layer_n_distinct + l;
     void *next = l + 1 == n_layers ? hhat : xhat;
-    if ((st = moe_layer(*d, layers[l], tp, xhat, r, p, ws, h, nullptr, next, s)) != BDD_OK) return st;
+    // layer 0 normalises x_in inside its router and keeps x_in as the residual
+    if ((st = moe_layer(*d, layers[l], tp, l == 0 ? x_in : nullptr, l == 0 ? h : nullptr, xhat, r, p, ws, h,
+                        nullptr, next, l == 0 ? count : nullptr, s)) != BDD_OK)
+      return st;
   }
   const int cus = device_cus();
   const int grid = lmhead_grid(cus) < kMaxLmGrid ? lmhead_grid(cus) : kMaxLmGrid;
   float *pm = at<float>(ws, lp.m), *ps = at<float>(ws, lp.s);
   int32_t *pi = at<int32_t>(ws, lp.i);
-  LAUNCH("lmhead", s, launch_lmhead(d->wdtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, s));
-  LAUNCH("commit", s, launch_commit(pm, ps, pi, grid, T, threshold, tokens, conf, choice, round_info, s));
+  const LmCommit fused = {count, threshold, tokens, conf, choice, round_info};
+  LAUNCH("lmhead", s, launch_lmhead(d->wdtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, &fused, s));
   return BDD_OK;
 }
 

@@ -131,6 +131,48 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
 template <int N>
 constexpr int log2i() { return N <= 1 ? 0 : 1 + log2i<N / 2>(); }
 
+// DPP wave reductions (VALU lane exchanges, no LDS): xor 1 and xor 2 within
+// quads, mirror within 8 and 16 lanes, then row broadcasts 15 and 31 fold the
+// four rows into lane 63, whose value is broadcast with readlane.  `old` is
+// the identity element given to lanes a row mask leaves unwritten.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dppf(float old, float v) {
+  return __int_as_float(dpp<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+#define BDD_DPP_STEPS(F) F(0xB1, 0xF) F(0x4E, 0xF) F(0x141, 0xF) F(0x140, 0xF) F(0x142, 0xA) F(0x143, 0xC)
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define BDD_STEP(C, R) v += dppf<C, R>(0.f, v);
+  BDD_DPP_STEPS(BDD_STEP)
+#undef BDD_STEP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+#define BDD_STEP(C, R) v = fmaxf(v, dppf<C, R>(-3.402823466e38f, v));
+  BDD_DPP_STEPS(BDD_STEP)
+#undef BDD_STEP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+// Largest value, lowest index among equal values; result uniform.
+__device__ __forceinline__ void wave_argmax_dpp(float &v, int &i) {
+#define BDD_STEP(C, R)                                              \
+  {                                                                 \
+    const float v2 = dppf<C, R>(-3.402823466e38f, v);               \
+    const int i2 = dpp<C, R>(0x7fffffff, i);                        \
+    const bool take = v2 > v || (v2 == v && i2 < i);                \
+    v = take ? v2 : v;                                              \
+    i = take ? i2 : i;                                              \
+  }
+  BDD_DPP_STEPS(BDD_STEP)
+#undef BDD_STEP
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
 // ---------------------------------------------------------------- math
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void routed_gateup_kernel(const typename W::T 
   }
 }
 
-constexpr int kDownRowsPerWave = 32;  // four batches of 8 rows
+constexpr int kDownRowsPerWave = 32;  // four batches of 8 rows (128 rows per item)
 
 // Down projection of one work item (expert e, 128 output rows): wave w owns
 // rows h0 + 8b + r (b = 0..3, r = 0..7) of W_d[e] [H][I]; xs holds the token

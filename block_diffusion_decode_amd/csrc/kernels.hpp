@@ -32,16 +32,20 @@ struct ExpertBufs {
 };
 
 // RMSNorm rows of `in` [T][H] into `out` (stored as wdtype); optionally copies
-// `in` to `copy_out`.
+// `in` to `copy_out` and clears `zero_word`.
 hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, int T, int H,
-                          hipStream_t s);
+                          int32_t *zero_word, hipStream_t s);
 
-hipError_t launch_router_logits(int wdtype, const void *xhat, const void *w_router,
-                                const float *bias, float *logits, int T, int H, int E,
-                                hipStream_t s);
+// Router logits from the normalised block; clears zero_word.
+size_t router_lds_bytes(int wdtype, int T, int H);
+hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const void *w_router,
+                         const float *bias, float *logits, int T, int H, int E, hipStream_t s);
 
+// Selection: one workgroup per position, then the block-level steps in the
+// last one.  sorted_ids [T][E] scratch; done_count must be zero (the router
+// kernel clears it) and is left zero.
 hipError_t launch_route_select(const RouteBufs &r, int T, int E, int K, float top_p,
-                               hipStream_t s);
+                               int32_t *sorted_ids, int32_t *done_count, hipStream_t s);
 
 hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, int K, float top_p,
                           uint32_t *bits, int32_t *size, float *mass, hipStream_t s);
@@ -71,8 +75,18 @@ int lmhead_grid(int cus);
 size_t lmhead_packed_bytes(int wdtype, int H, int V);
 hipError_t launch_pack_lm(int wdtype, const void *w_lm, int V, int H, void *packed, hipStream_t s);
 size_t lmhead_lds_bytes(int wdtype, int T, int H);
+// Commit fused into the LM head's last workgroup (done_count must be zero).
+struct LmCommit {
+  int32_t *done_count;
+  float threshold;
+  int32_t *tokens;
+  float *conf;
+  int32_t *choice;
+  int32_t *round_info;
+};
 hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm_packed, int T, int H, int V,
-                         float *part_m, float *part_s, int32_t *part_i, int grid, hipStream_t s);
+                         float *part_m, float *part_s, int32_t *part_i, int grid, const LmCommit *fused,
+                         hipStream_t s);
 
 hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,
                          int nparts, int T, float threshold, int32_t *tokens, float *conf,

@@ -115,17 +115,107 @@ __device__ __forceinline__ void lm_tile_dot(rsrc_t rs, uint32_t vbase, const uin
   }
 }
 
+// Merge the per-workgroup partials of every position (fixed order), then the
+// commit rule on the still-masked positions.  Run by one whole workgroup of
+// any multiple of 64 threads.
+__device__ void commit_block(const float *__restrict__ part_m, const float *__restrict__ part_s,
+                             const int32_t *__restrict__ part_i, int nparts, int T, float threshold,
+                             int32_t *__restrict__ tokens, float *__restrict__ conf,
+                             int32_t *__restrict__ choice, int32_t *__restrict__ round_info) {
+  __shared__ float s_conf[kMaxT];
+  __shared__ int s_choice[kMaxT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  for (int t = wave; t < T; t += nw) {
+    float m = -FLT_MAX, s = 0.f;
+    int i = INT_MAX;
+    for (int p = lane; p < nparts; p += 64)
+      sm_merge(m, s, i, part_m[(size_t)t * nparts + p], part_s[(size_t)t * nparts + p],
+               part_i[(size_t)t * nparts + p]);
+#pragma unroll
+    for (int sft = 1; sft <= 32; sft <<= 1) {
+      const float m2 = __shfl_xor(m, sft), s2 = __shfl_xor(s, sft);
+      const int i2 = __shfl_xor(i, sft);
+      // both partners merge the same pair in the same order: lower lane first
+      if (lane & sft) {
+        float mm = m2, ss = s2;
+        int ii = i2;
+        sm_merge(mm, ss, ii, m, s, i);
+        m = mm; s = ss; i = ii;
+      } else {
+        sm_merge(m, s, i, m2, s2, i2);
+      }
+    }
+    if (lane == 0) {
+      const float c = 1.0f / s;
+      s_conf[t] = c;
+      s_choice[t] = i;
+      conf[t] = c;
+      choice[t] = i;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool in = lane < T;
+    const int tok = in ? tokens[lane] : 0;
+    const bool masked = in && tok == -1;
+    const float c = in ? s_conf[lane] : 0.f;
+    const unsigned long long pass = __ballot(masked && c >= threshold);
+    const unsigned long long msk = __ballot(masked);
+    int committed = 0, fallback = 0;
+    bool write = false;
+    if (pass) {
+      write = (pass >> lane) & 1ull;
+      committed = __popcll(pass);
+    } else if (msk) {
+      float bv = masked ? c : -FLT_MAX;
+      int bi = masked ? lane : INT_MAX;
+      wave_argmax_dpp(bv, bi);
+      write = lane == bi;
+      committed = 1;
+      fallback = 1;
+    }
+    if (write) tokens[lane] = s_choice[lane];
+    const int left = __popcll(msk) - committed;
+    if (lane == 0) {
+      round_info[0] = committed;
+      round_info[1] = fallback;
+      round_info[2] = left;
+      round_info[3] = left == 0 ? 1 : 0;
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ part_m,
+                                                      const float *__restrict__ part_s,
+                                                      const int32_t *__restrict__ part_i,
+                                                      int nparts, int T, float threshold,
+                                                      int32_t *__restrict__ tokens,
+                                                      float *__restrict__ conf,
+                                                      int32_t *__restrict__ choice,
+                                                      int32_t *__restrict__ round_info) {
+  commit_block(part_m, part_s, part_i, nparts, T, threshold, tokens, conf, choice, round_info);
+}
+
 // One workgroup (16 waves) per CU.  The block's normalised hidden states are
 // staged once in LDS as [chunk][position] 16-byte entries; each wave takes
 // 16-row vocabulary tiles round-robin, streams the rows with 16-byte loads,
 // multiplies them by the staged positions on MFMA, and folds the 16 x 32
 // logits into its running (max, sum, argmax).
+// With `done_count` given, the workgroup that finishes last (agent-scope
+// counter; fences make every workgroup's partials visible across XCDs) also
+// merges the partials and runs the commit, then clears the counter.  The
+// counter must be zero when the kernel starts.
 template <class W, int NT>
 __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__restrict__ hhat,
                                                       const typename W::T *__restrict__ wlm, int T,
                                                       int H, int V, float *__restrict__ part_m,
                                                       float *__restrict__ part_s,
-                                                      int32_t *__restrict__ part_i) {
+                                                      int32_t *__restrict__ part_i,
+                                                      int32_t *__restrict__ done_count, float threshold,
+                                                      int32_t *__restrict__ tokens,
+                                                      float *__restrict__ conf,
+                                                      int32_t *__restrict__ choice,
+                                                      int32_t *__restrict__ round_info) {
   extern __shared__ uint4 xs[];  // [H / kChunk][16 * NT]
   __shared__ float sm[kLmWaves][kMaxT], ssum[kLmWaves][kMaxT];
   __shared__ int si[kLmWaves][kMaxT];
@@ -133,9 +223,21 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   constexpr int TP = 16 * NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NC = H / CH;
-  for (int idx = tid; idx < TP * NC; idx += blockDim.x) {
-    const int t = idx / NC, c = idx - t * NC;
-    xs[c * TP + t] = t < T ? ld16(hhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
+  // stage the block: batches of 8 independent loads per thread
+  for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const int t = idx / NC, c = idx - t * NC;
+      v[j] = (idx < TP * NC && t < T) ? ld16(hhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const int t = idx / NC, c = idx - t * NC;
+      if (idx < TP * NC) xs[c * TP + t] = v[j];
+    }
   }
   __syncthreads();
 
@@ -205,84 +307,18 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
     part_s[(size_t)tid * gridDim.x + blockIdx.x] = ss;
     part_i[(size_t)tid * gridDim.x + blockIdx.x] = ii;
   }
-}
-
-// Merge the per-workgroup partials of every position (fixed order), then the
-// commit rule on the still-masked positions.
-__global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ part_m,
-                                                      const float *__restrict__ part_s,
-                                                      const int32_t *__restrict__ part_i,
-                                                      int nparts, int T, float threshold,
-                                                      int32_t *__restrict__ tokens,
-                                                      float *__restrict__ conf,
-                                                      int32_t *__restrict__ choice,
-                                                      int32_t *__restrict__ round_info) {
-  __shared__ float s_conf[kMaxT];
-  __shared__ int s_choice[kMaxT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  for (int t = wave; t < T; t += nw) {
-    float m = -FLT_MAX, s = 0.f;
-    int i = INT_MAX;
-    for (int p = lane; p < nparts; p += 64)
-      sm_merge(m, s, i, part_m[(size_t)t * nparts + p], part_s[(size_t)t * nparts + p],
-               part_i[(size_t)t * nparts + p]);
-#pragma unroll
-    for (int sft = 1; sft <= 32; sft <<= 1) {
-      const float m2 = __shfl_xor(m, sft), s2 = __shfl_xor(s, sft);
-      const int i2 = __shfl_xor(i, sft);
-      // both partners merge the same pair in the same order: lower lane first
-      if (lane & sft) {
-        float mm = m2, ss = s2;
-        int ii = i2;
-        sm_merge(mm, ss, ii, m, s, i);
-        m = mm; s = ss; i = ii;
-      } else {
-        sm_merge(m, s, i, m2, s2, i2);
-      }
-    }
-    if (lane == 0) {
-      const float c = 1.0f / s;
-      s_conf[t] = c;
-      s_choice[t] = i;
-      conf[t] = c;
-      choice[t] = i;
-    }
+  if (done_count == nullptr) return;
+  __shared__ int s_last;
+  __syncthreads();  // the partial stores of this workgroup have completed
+  if (tid == 0) {
+    __threadfence();  // release them device-wide (across XCDs) before counting
+    s_last = atomicAdd(done_count, 1) == (int)gridDim.x - 1;
+    if (s_last) __threadfence();  // acquire every workgroup's partials
   }
   __syncthreads();
-  if (wave == 0) {
-    const bool in = lane < T;
-    const int tok = in ? tokens[lane] : 0;
-    const bool masked = in && tok == -1;
-    const float c = in ? s_conf[lane] : 0.f;
-    const unsigned long long pass = __ballot(masked && c >= threshold);
-    const unsigned long long msk = __ballot(masked);
-    int committed = 0, fallback = 0;
-    bool write = false;
-    if (pass) {
-      write = (pass >> lane) & 1ull;
-      committed = __popcll(pass);
-    } else if (msk) {
-      float bv = masked ? c : -FLT_MAX;
-      int bi = masked ? lane : INT_MAX;
-#pragma unroll
-      for (int sft = 32; sft >= 1; sft >>= 1) {
-        const float v2 = __shfl_xor(bv, sft);
-        const int i2 = __shfl_xor(bi, sft);
-        if (v2 > bv || (v2 == bv && i2 < bi)) { bv = v2; bi = i2; }
-      }
-      write = lane == bi;
-      committed = 1;
-      fallback = 1;
-    }
-    if (write) tokens[lane] = s_choice[lane];
-    const int left = __popcll(msk) - committed;
-    if (lane == 0) {
-      round_info[0] = committed;
-      round_info[1] = fallback;
-      round_info[2] = left;
-      round_info[3] = left == 0 ? 1 : 0;
-    }
-  }
+  if (!s_last) return;
+  commit_block(part_m, part_s, part_i, gridDim.x, T, threshold, tokens, conf, choice, round_info);
+  if (tid == 0) *done_count = 0;
 }
 
 // Packs w_lm [V][H] into the tile layout the LM-head kernel streams: for
@@ -336,32 +372,28 @@ static hipError_t allow_lds(F *fn, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,
-                         float *part_m, float *part_s, int32_t *part_i, int grid, hipStream_t s) {
-  const size_t lds = lmhead_lds_bytes(wdtype, T, H);
-  hipError_t err;
-  if (wdtype == 1) {
-    if (T <= 16) {
-      if ((err = allow_lds(lmhead_kernel<WBf16, 1>, lds)) != hipSuccess) return err;
-      lmhead_kernel<WBf16, 1><<<grid, 1024, lds, s>>>((const bf16_t *)hhat, (const bf16_t *)w_lm, T,
-                                                      H, V, part_m, part_s, part_i);
-    } else {
-      if ((err = allow_lds(lmhead_kernel<WBf16, 2>, lds)) != hipSuccess) return err;
-      lmhead_kernel<WBf16, 2><<<grid, 1024, lds, s>>>((const bf16_t *)hhat, (const bf16_t *)w_lm, T,
-                                                      H, V, part_m, part_s, part_i);
-    }
-  } else {
-    if (T <= 16) {
-      if ((err = allow_lds(lmhead_kernel<WF32, 1>, lds)) != hipSuccess) return err;
-      lmhead_kernel<WF32, 1><<<grid, 1024, lds, s>>>((const float *)hhat, (const float *)w_lm, T, H,
-                                                     V, part_m, part_s, part_i);
-    } else {
-      if ((err = allow_lds(lmhead_kernel<WF32, 2>, lds)) != hipSuccess) return err;
-      lmhead_kernel<WF32, 2><<<grid, 1024, lds, s>>>((const float *)hhat, (const float *)w_lm, T, H,
-                                                     V, part_m, part_s, part_i);
-    }
-  }
+template <class W, int NT>
+static hipError_t lmhead_launch(const void *hhat, const void *w_lm, int T, int H, int V, float *pm,
+                                float *ps, int32_t *pi, int grid, const LmCommit *fused, hipStream_t s) {
+  typedef typename W::T WT;
+  const size_t lds = lmhead_lds_bytes(std::is_same<W, WBf16>::value ? 1 : 0, T, H);
+  hipError_t err = allow_lds(lmhead_kernel<W, NT>, lds);
+  if (err != hipSuccess) return err;
+  lmhead_kernel<W, NT><<<grid, 1024, lds, s>>>(
+      (const WT *)hhat, (const WT *)w_lm, T, H, V, pm, ps, pi, fused ? fused->done_count : nullptr,
+      fused ? fused->threshold : 0.f, fused ? fused->tokens : nullptr, fused ? fused->conf : nullptr,
+      fused ? fused->choice : nullptr, fused ? fused->round_info : nullptr);
   return hipGetLastError();
+}
+
+hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,
+                         float *part_m, float *part_s, int32_t *part_i, int grid, const LmCommit *fused,
+                         hipStream_t s) {
+  if (wdtype == 1)
+    return T <= 16 ? lmhead_launch<WBf16, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+                   : lmhead_launch<WBf16, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
+  return T <= 16 ? lmhead_launch<WF32, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+                 : lmhead_launch<WF32, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
 }
 
 hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,

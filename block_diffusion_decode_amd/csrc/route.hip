@@ -9,6 +9,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "dense.hpp"
 #include "kernels.hpp"
 
@@ -47,8 +49,10 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *out, size_t i, float4 v) 
 template <typename OT>
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__restrict__ in,
                                                               float *__restrict__ copy_out,
-                                                              OT *__restrict__ out, int H, float eps) {
+                                                              OT *__restrict__ out, int H, float eps,
+                                                              int32_t *__restrict__ zero_word) {
   __shared__ float red[kRowThreads / 64];
+  if (blockIdx.x == 0 && threadIdx.x == 0 && zero_word) *zero_word = 0;
   const size_t base = (size_t)blockIdx.x * H;
   const int H4 = H / 4;
   float4 v[kRowVec];
@@ -73,27 +77,79 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__res
 }
 
 // ------------------------------------------------------------------ router logits
-// logits[t][e] = xhat_t . W_r[e] + b_e.  One workgroup per 16 experts; its
-// waves split the hidden dimension and sum through LDS.
+// logits[t][e] = xhat_t . W_r[e] + b_e.  One workgroup per 16 experts.  The
+// normalised block is staged in LDS as [chunk][position] 16-byte entries; the
+// 8 waves split the hidden dimension and sum their partial tiles through LDS.
+// Workgroup 0 also clears `zero_word` (the selection kernel's counter).
+constexpr int kRouterWaves = 8;
+
 template <class W, int NT>
-__global__ __launch_bounds__(512) void router_logits_kernel(const typename W::T *__restrict__ xhat,
-                                                            const typename W::T *__restrict__ wr,
-                                                            const float *__restrict__ bias,
-                                                            float *__restrict__ logits, int T, int H,
-                                                            int E) {
-  __shared__ float red[8 * NT * 4 * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+__global__ __launch_bounds__(64 * kRouterWaves) void router_kernel(
+    const typename W::T *__restrict__ xhat, int32_t *__restrict__ zero_word,
+    const typename W::T *__restrict__ wr, const float *__restrict__ bias, float *__restrict__ logits,
+    int T, int H, int E) {
+  extern __shared__ uint4 xs[];  // [H / kChunk][16 * NT]; reused for the split-K sums
+  constexpr int CH = W::kChunk;
+  constexpr int TP = 16 * NT;
+  typedef typename W::T WT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int NC = H / CH;
+  if (blockIdx.x == 0 && tid == 0 && zero_word) *zero_word = 0;
+  for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const int t = idx / NC, c = idx - t * NC;
+      v[j] = (idx < TP * NC && t < T) ? ld16(xhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const int t = idx / NC, c = idx - t * NC;
+      if (idx < TP * NC) xs[c * TP + t] = v[j];
+    }
+  }
+  __syncthreads();
+
+  // MFMA over this wave's share of the k-steps (4 chunks per k-step)
   const int row0 = blockIdx.x * 16;
-  const int row = row0 + (lane & 15);
-  const bool ok = row < E;
-  int k0, k1;
-  k_slice(H, mfma_kstep<W>(), wave, nw, k0, k1);
+  const int li = lane & 15, g = lane >> 4;
+  const int nrows = min(16, E - row0);
+  const rsrc_t rs = make_rsrc(wr + (size_t)row0 * H, (uint32_t)(nrows * H * (int)sizeof(WT)));
+  const uint32_t vbase = (uint32_t)(li * H + g * CH) * (uint32_t)sizeof(WT);
+  const int steps = NC / 4;
+  const int per = (steps + nw - 1) / nw;
+  const int s0 = min(wave * per, steps), s1 = min(s0 + per, steps);
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  dense_acc_global<W, typename W::T, NT>(wr + (size_t)(ok ? row : 0) * H, ok, xhat, H, T, k0, k1,
-                                         lane, acc);
-  splitk_sum<NT>(acc, red, wave, nw, lane);
+  for (int sb = s0; sb < s1; sb += 8) {
+    uint4 a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      a[j] = sb + j < s1 ? buf_ld16(rs, vbase, (uint32_t)((sb + j) * 4 * CH * (int)sizeof(WT)))
+                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (sb + j >= s1) break;
+      const int c = (sb + j) * 4 + g;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const uint4 bv = xs[c * TP + n * 16 + li];
+        if constexpr (std::is_same<W, WBf16>::value) {
+          acc[n] = mfma_bf16(a[j], bv, acc[n]);
+        } else {
+          acc[n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[n]);
+          acc[n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[n]);
+          acc[n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[n]);
+          acc[n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[n]);
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with xs: reuse it for the split-K sums
+  splitk_sum<NT>(acc, reinterpret_cast<float *>(xs), wave, nw, lane);
   if (wave == 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
@@ -115,64 +171,6 @@ __device__ __forceinline__ void wave_argbest(float &v, int &id) {
     const float v2 = __shfl_xor(v, s);
     const int i2 = __shfl_xor(id, s);
     if (v2 > v || (v2 == v && i2 < id)) { v = v2; id = i2; }
-  }
-}
-
-// One wave picks up to K experts for each of its NQ positions by descending
-// logit (ties to the lower id) among those allowed (allowed == nullptr: all);
-// the positions' selections run interleaved.  lv / pv hold the lane's logits
-// and softmax scores for experts lane + 64j.  Writes the picks and their
-// scores to idx_row[q] / psel_row[q] (-1 / 0 where fewer than K are allowed);
-// rows with live[q] false are skipped.  All lanes take part.
-template <int NQ>
-__device__ void wave_topk(const float (&lv)[NQ][4], const float (&pv)[NQ][4], const bool (&live)[NQ],
-                          int E, int K, const int32_t *allowed, int lane, int32_t *const (&idx_row)[NQ],
-                          float *const (&psel_row)[NQ]) {
-  bool avail[NQ][4];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      avail[q][j] = live[q] && e < E && (allowed == nullptr || allowed[e] != 0);
-    }
-  for (int k = 0; k < K; ++k) {
-    float bv[NQ];
-    int be[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      bv[q] = -FLT_MAX;
-      be[q] = INT_MAX;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        if (avail[q][j] && (be[q] == INT_MAX || lv[q][j] > bv[q])) { bv[q] = lv[q][j]; be[q] = e; }
-      }
-    }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const float v2 = __shfl_xor(bv[q], s);
-        const int i2 = __shfl_xor(be[q], s);
-        if (v2 > bv[q] || (v2 == bv[q] && i2 < be[q])) { bv[q] = v2; be[q] = i2; }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if (!live[q]) continue;
-      float ps = 0.f;
-      if (be[q] != INT_MAX) {
-        const int j = be[q] >> 6;                      // uniform across the wave
-        const float pj = j == 0 ? pv[q][0] : j == 1 ? pv[q][1] : j == 2 ? pv[q][2] : pv[q][3];
-        ps = __shfl(pj, be[q] & 63);
-        if ((be[q] & 63) == lane) avail[q][j] = false;
-      }
-      if (lane == 0) {
-        idx_row[q][k] = be[q] == INT_MAX ? -1 : be[q];
-        psel_row[q][k] = ps;
-      }
-    }
   }
 }
 
@@ -257,6 +255,13 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
   }
   union_scan(sh, E);
   const int nu = sh.nu;
+  if (top_p >= 1.0f) {
+    // no coreset: every expert with a pick (positive mass) is kept
+    if (tid < nu) sh.member[sh.ulist[tid]] = 1;
+    if (tid == 0) sh.csize = nu;
+    __syncthreads();
+    return;
+  }
   if (tid < nu) {
     sh.umass[tid] = sh.mass[sh.ulist[tid]];
     sh.rank[tid] = 0;
@@ -288,7 +293,7 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
   }
   __syncthreads();
   int k = nu;
-  if (top_p < 1.0f && nu > 0) {
+  if (nu > 0) {
     // inclusive prefix sum of the ranked masses (fp64), one wave per 64 ranks
     double v = tid < nu ? sh.cum[tid] : 0.0;
 #pragma unroll
@@ -328,78 +333,122 @@ __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
 }
 
 // ------------------------------------------------------------------ route + select
-// One workgroup of 1024 threads: per-position softmax and top-K, optional
-// coreset and re-routing, then the union of experts and each union expert's
-// list of (position, pick) assignments.
-__global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, int E, int K,
-                                                            float top_p) {
-  __shared__ SelShared sh;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  constexpr int kTokPerWave = kMaxT / 16;
-  float lv[kTokPerWave][4], pv[kTokPerWave][4];
+// One workgroup of kSelThreads per position: softmax over the position's E
+// router logits and a bitonic sort of (logit desc, expert id asc), so its top-K
+// is the prefix of its sorted list.  The workgroup that finishes last (agent
+// counter, cleared by the router kernel; fences make every workgroup's rows
+// visible across XCDs) then takes the block-level steps: expert mass, coreset
+// and re-routing (each position's first min(K, |C|) coreset members in its
+// sorted order), weights, the union of experts and each union expert's list
+// of (position, pick) assignments.  It clears the counter when done.
+constexpr int kSelThreads = 256;
 
-  // softmax over all experts and top-K by logit
-  bool live[kTokPerWave];
-  int32_t *idx_rows[kTokPerWave];
-  float *psel_rows[kTokPerWave];
-#pragma unroll
-  for (int q = 0; q < kTokPerWave; ++q) {
-    const int t = wave + q * nw;
-    live[q] = t < T;
-    idx_rows[q] = sh.idx[live[q] ? t : 0];
-    psel_rows[q] = sh.psel[live[q] ? t : 0];
-    float m = -FLT_MAX;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      lv[q][j] = (live[q] && e < E) ? r.logits[(size_t)t * E + e] : -FLT_MAX;
-      m = fmaxf(m, lv[q][j]);
+__device__ __forceinline__ uint32_t order_key(float v) {
+  // larger float -> smaller key (ascending sort = descending logits)
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  return ((unsigned long long)(uint32_t)__shfl_xor((int)hi, m) << 32) | (uint32_t)__shfl_xor((int)lo, m);
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T, int E, int K,
+                                                             float top_p, int32_t *__restrict__ sorted_ids,
+                                                             int32_t *__restrict__ done_count) {
+  __shared__ unsigned long long s_key[kSelThreads];
+  __shared__ float s_red[kSelThreads / 64];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  {
+    // ---- phase 1: this position
+    const float l = tid < E ? r.logits[(size_t)t * E + tid] : -FLT_MAX;
+    float m = wave_max_dpp(l);
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+    const float ex = tid < E ? expf(l - m) : 0.f;
+    float sum = wave_sum_dpp(ex);
+    if (lane == 0) s_red[wave] = sum;
+    __syncthreads();
+    sum = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    if (tid < E) r.prob[(size_t)t * E + tid] = ex / sum;
+    // bitonic sort, ascending on (order_key(logit), id); padding sorts last
+    unsigned long long key = tid < E ? (((unsigned long long)order_key(l) << 32) | (uint32_t)tid) : ~0ull;
+    for (int k = 2; k <= kSelThreads; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        unsigned long long other;
+        if (j >= 64) {
+          __syncthreads();
+          s_key[tid] = key;
+          __syncthreads();
+          other = s_key[tid ^ j];
+        } else {
+          other = shfl_xor64(key, j);
+        }
+        const bool lower = (tid & j) == 0, asc = (tid & k) == 0;
+        key = (lower == asc) ? (key < other ? key : other) : (key < other ? other : key);
+      }
     }
-    m = wave_max(m);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      pv[q][j] = (live[q] && e < E) ? expf(lv[q][j] - m) : 0.f;
-      s += pv[q][j];
-    }
-    s = wave_sum(s);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      pv[q][j] = live[q] ? pv[q][j] / s : 0.f;
-      if (live[q] && e < E) r.prob[(size_t)t * E + e] = pv[q][j];
-    }
+    if (tid < E) sorted_ids[(size_t)t * E + tid] = (int32_t)(uint32_t)key;
   }
-  wave_topk<kTokPerWave>(lv, pv, live, E, K, nullptr, lane, idx_rows, psel_rows);
+  __syncthreads();  // this position's rows are stored (its stores came from all waves)
+  __threadfence();
   __syncthreads();
+  if (tid == 0) {
+    s_last = atomicAdd(done_count, 1) == (int)gridDim.x - 1;
+    if (s_last) __threadfence();
+  }
+  __syncthreads();
+  if (!s_last) return;
 
-  // block mass and coreset (also run without coreset: it reports the union)
+  // ---- phase 2: the block (last workgroup)
+  __shared__ SelShared sh;
+  for (int i = tid; i < T * K; i += kSelThreads) {
+    const int tt = i / K, k = i - tt * K;
+    const int e = sorted_ids[(size_t)tt * E + k];
+    sh.idx[tt][k] = e;
+    sh.psel[tt][k] = r.prob[(size_t)tt * E + e];
+  }
+  __syncthreads();
   coreset_core(sh, T, E, K, top_p);
   if (tid < E) r.mass[tid] = (float)sh.mass[tid];
   write_bits(sh, E, r.cs_bits);
   if (top_p < 1.0f) {
+    // each position re-takes its first min(K, |C|) coreset members in its own
+    // (logit desc, id asc) order
     const int kk = min(K, sh.csize);
-    wave_topk<kTokPerWave>(lv, pv, live, E, kk, sh.member, lane, idx_rows, psel_rows);
-#pragma unroll
-    for (int q = 0; q < kTokPerWave; ++q)
-      if (live[q] && lane == 0)
-        for (int k = kk; k < K; ++k) { idx_rows[q][k] = -1; psel_rows[q][k] = 0.f; }
+    for (int tt = wave; tt < T; tt += kSelThreads / 64) {
+      int taken = 0;
+      for (int base = 0; base < E && taken < kk; base += 64) {
+        const int e = base + lane < E ? sorted_ids[(size_t)tt * E + base + lane] : -1;
+        const bool mem = e >= 0 && sh.member[e] != 0;
+        const unsigned long long b = __ballot(mem);
+        const int before = __popcll(b & ((1ull << lane) - 1ull));
+        if (mem && taken + before < kk) {
+          sh.idx[tt][taken + before] = e;
+          sh.psel[tt][taken + before] = r.prob[(size_t)tt * E + e];
+        }
+        taken += __popcll(b);
+      }
+      if (lane == 0)
+        for (int k = kk; k < K; ++k) { sh.idx[tt][k] = -1; sh.psel[tt][k] = 0.f; }
+    }
     __syncthreads();
     build_masks(sh, T, E, K);
   }
-
-  // renormalised weights, outputs
-  if (tid < T * K) {
-    const int t = tid / K, k = tid % K;
+  for (int i = tid; i < T * K; i += kSelThreads) {
+    const int tt = i / K, k = i - tt * K;
     float s = 0.f;
-    for (int j = 0; j < K; ++j) s += sh.psel[t][j];
-    const int e = sh.idx[t][k];
-    r.idx[tid] = e;
-    r.wgt[tid] = e >= 0 ? sh.psel[t][k] / s : 0.f;
+    for (int j = 0; j < K; ++j) s += sh.psel[tt][j];
+    const int e = sh.idx[tt][k];
+    r.idx[i] = e;
+    r.wgt[i] = e >= 0 ? sh.psel[tt][k] / s : 0.f;
   }
-
-  // union of experts read and each one's assignment list (t*K + k, ascending t)
   const int slot = union_scan(sh, E);
   if (slot >= 0) {
     uint32_t bits = sh.tokmask[tid];
@@ -407,9 +456,9 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
     r.slot_n[slot] = __popc(bits);
     int j = 0;
     while (bits) {
-      const int t = __ffs(bits) - 1;
+      const int tt = __ffs(bits) - 1;
       bits &= bits - 1u;
-      r.slot_asg[slot * kMaxT + j++] = t * K + sh.kslot[t][tid];
+      r.slot_asg[slot * kMaxT + j++] = tt * K + sh.kslot[tt][tid];
     }
   }
   if (tid == 0) {
@@ -417,6 +466,7 @@ __global__ __launch_bounds__(1024) void route_select_kernel(RouteBufs r, int T, 
     r.meta[1] = sh.csize;
     if (r.n_distinct_out) *r.n_distinct_out = sh.nu;
     if (r.coreset_size_out) *r.coreset_size_out = sh.csize;
+    *done_count = 0;
   }
 }
 
@@ -503,43 +553,52 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, int T, int H,
-                          hipStream_t s) {
+                          int32_t *zero_word, hipStream_t s) {
   if (wdtype == 1)
-    rmsnorm_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(in, copy_out, (bf16_t *)out, H, 1e-6f);
+    rmsnorm_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(in, copy_out, (bf16_t *)out, H, 1e-6f, zero_word);
   else
-    rmsnorm_kernel<float><<<T, kRowThreads, 0, s>>>(in, copy_out, (float *)out, H, 1e-6f);
+    rmsnorm_kernel<float><<<T, kRowThreads, 0, s>>>(in, copy_out, (float *)out, H, 1e-6f, zero_word);
   return hipGetLastError();
 }
 
-hipError_t launch_router_logits(int wdtype, const void *xhat, const void *w_router,
-                                const float *bias, float *logits, int T, int H, int E,
-                                hipStream_t s) {
-  const int grid = (E + 15) / 16;
-  if (wdtype == 1) {
-    if (T <= 16)
-      router_logits_kernel<WBf16, 1><<<grid, 512, 0, s>>>((const bf16_t *)xhat,
-                                                           (const bf16_t *)w_router, bias, logits,
-                                                           T, H, E);
-    else
-      router_logits_kernel<WBf16, 2><<<grid, 512, 0, s>>>((const bf16_t *)xhat,
-                                                           (const bf16_t *)w_router, bias, logits,
-                                                           T, H, E);
-  } else {
-    if (T <= 16)
-      router_logits_kernel<WF32, 1><<<grid, 512, 0, s>>>((const float *)xhat,
-                                                          (const float *)w_router, bias, logits, T,
-                                                          H, E);
-    else
-      router_logits_kernel<WF32, 2><<<grid, 512, 0, s>>>((const float *)xhat,
-                                                          (const float *)w_router, bias, logits, T,
-                                                          H, E);
-  }
+size_t router_lds_bytes(int wdtype, int T, int H) {
+  const int tp = T <= 16 ? 16 : 32;
+  const size_t stage = (size_t)(H / (wdtype == 1 ? 8 : 4)) * tp * 16;
+  const size_t red = (size_t)kRouterWaves * (tp / 16) * 4 * 64 * 4;
+  return stage > red ? stage : red;
+}
+
+template <typename F>
+static hipError_t allow_lds(F *fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <class W, int NT>
+static hipError_t router_launch(const void *xhat, int32_t *zero_word, const void *w_router,
+                                const float *bias, float *logits, int T, int H, int E, hipStream_t s) {
+  typedef typename W::T WT;
+  const size_t lds = router_lds_bytes(std::is_same<W, WBf16>::value ? 1 : 0, T, H);
+  hipError_t err = allow_lds(router_kernel<W, NT>, lds);
+  if (err != hipSuccess) return err;
+  router_kernel<W, NT><<<(E + 15) / 16, 64 * kRouterWaves, lds, s>>>(
+      (const WT *)xhat, zero_word, (const WT *)w_router, bias, logits, T, H, E);
   return hipGetLastError();
+}
+
+hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const void *w_router,
+                         const float *bias, float *logits, int T, int H, int E, hipStream_t s) {
+  if (wdtype == 1)
+    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_word, w_router, bias, logits, T, H, E, s)
+                   : router_launch<WBf16, 2>(xhat, zero_word, w_router, bias, logits, T, H, E, s);
+  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_word, w_router, bias, logits, T, H, E, s)
+                 : router_launch<WF32, 2>(xhat, zero_word, w_router, bias, logits, T, H, E, s);
 }
 
 hipError_t launch_route_select(const RouteBufs &r, int T, int E, int K, float top_p,
-                               hipStream_t s) {
-  route_select_kernel<<<1, 1024, 0, s>>>(r, T, E, K, top_p);
+                               int32_t *sorted_ids, int32_t *done_count, hipStream_t s) {
+  select_kernel<<<T, kSelThreads, 0, s>>>(r, T, E, K, top_p, sorted_ids, done_count);
   return hipGetLastError();
 }
 

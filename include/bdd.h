@@ -21,6 +21,10 @@
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
  *     and return without waiting.  Outputs are valid once the stream has
  *     reached that point.  Calls that share a workspace must not overlap.
+ *     The MoE layer runs its shared expert on a library-owned stream of the
+ *     current device (default priority), forked from and joined back into
+ *     `stream` with events, so calls on one device must be issued from one
+ *     host thread at a time.
  *   - Arguments are checked on the host before anything is enqueued; a
  *     failed check returns a negative status and enqueues nothing.  A
  *     launch failure returns BDD_ERR_HIP.  bdd_last_error() describes the
