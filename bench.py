@@ -8,10 +8,11 @@ routing, no coreset), the final RMSNorm, the LM head over a 248320-token
 vocabulary with the fused softmax-confidence/argmax, and the LowConfidence
 commit.  Inputs are seeded synthetic tensors, resident in HBM before timing.
 
-Prints one JSON line: microseconds per round, achieved HBM bandwidth on the
-round's algorithmic bytes, the roofline of the dominant kernel (its duration
-measured with hipEvents on its launch stream during the timed region), and the
-CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: microseconds per round (K replays of the round's HIP
+graph, timed with events at the ends of the region), achieved HBM bandwidth
+on the round's algorithmic bytes, the roofline of the dominant kernel (its
+launches bracketed by hipEvents on their stream over K further rounds), and
+the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -82,7 +83,10 @@ def main():
     torch.cuda.synchronize()
     n_distinct = nd[:, 0].cpu().numpy().astype(np.int64)
 
-    # warmup, with every kernel timed to find the dominant one
+    # one captured round per stub input (HIP graphs): a decode loop replays them
+    graphs = [bdd.RoundGraph(plan, x[r], tok, conf, choice, ri) for r in range(R)]
+
+    # warmup, with every kernel timed (eager) to find the dominant one
     bdd.timing_enable(True, None)
     for i in range(args.warmup):
         plan(x[i % R], tok, conf, choice, ri)
@@ -92,24 +96,35 @@ def main():
     dominant = max(warm, key=lambda k: warm[k][0])
     log("[bench] warmup per-kernel avg us: " +
         ", ".join(f"{k}={1e3 * v[0] / v[1]:.1f}" for k, v in warm.items()))
+    for i in range(args.warmup):
+        graphs[i % R].launch()
+    torch.cuda.synchronize()
 
-    # timed region: events on torch's current stream (the library launches
-    # there); the dominant kernel is bracketed by its own events
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
+
+    # timed region: K graph replays, events only at its two ends
+    ms, wall = timed(lambda i: graphs[i % R].launch())
+    log(f"[bench] {args.steps} rounds (graph): {ms * 1e3:.1f} us/round (wall {wall * 1e3 / args.steps:.1f} us/round)")
+    ms_eager, _ = timed(lambda i: plan(x[i % R], tok, conf, choice, ri))
+    log(f"[bench] {args.steps} rounds (eager): {ms_eager * 1e3:.1f} us/round")
+
+    # dominant kernel: K more rounds with its launches bracketed by hipEvents
+    # on the stream it runs on
     bdd.timing_enable(True, dominant)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        plan(x[i % R], tok, conf, choice, ri)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    timed(lambda i: plan(x[i % R], tok, conf, choice, ri))
     dom = bdd.timing_read()
     bdd.timing_enable(False)
-    ms = start.elapsed_time(stop) / args.steps
-    log(f"[bench] {args.steps} rounds: {ms * 1e3:.1f} us/round (wall {wall * 1e3 / args.steps:.1f} us/round)")
 
     # algorithmic bytes: union experts + shared expert + router + LM head + block activations
     eb = 3 * d.H * d.I * 2
@@ -120,8 +135,8 @@ def main():
 
     dom_ms = dom[dominant][0] / dom[dominant][1]
     dom_bytes = {"lmhead": lm_bytes,
-                 "routed_gateup": mean_u * 2 * d.I * d.H * 2 + T * d.K * d.H * 2,
-                 "routed_down": mean_u * d.H * d.I * 2 + T * d.K * (d.I + d.H) * 4}.get(dominant)
+                 "expert_gateup": (mean_u * d.I + d.I_s) * 2 * d.H * 2,
+                 "expert_down": (mean_u * d.I + d.I_s) * d.H * 2}.get(dominant)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_bytes else None
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS if achieved else None,
@@ -141,7 +156,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded counter-based inputs, random-init weights of the Clover shape",
         "config": {"workload": WORKLOAD, "global_batch": T, "seq_len": T, "parallelism": "single GPU",
-                   "distinct_experts_mean": mean_u},
+                   "launch": "HIP graph per round (bdd_round_graph)", "distinct_experts_mean": mean_u},
+        "us_per_round_eager": round(ms_eager * 1e3, 2),
         "round_bytes": round_bytes,
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,

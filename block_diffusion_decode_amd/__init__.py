@@ -53,6 +53,7 @@ EXPORTS = [
     "bdd_round_workspace_bytes", "bdd_block_denoise_round",
     "bdd_status_string", "bdd_last_error", "bdd_device_cus",
     "bdd_timing_enable", "bdd_timing_read", "bdd_lmhead_packed_bytes", "bdd_lmhead_pack",
+    "bdd_round_graph_create", "bdd_round_graph_launch", "bdd_round_graph_destroy",
 ]
 
 _lib = None
@@ -94,6 +95,13 @@ def lib() -> ctypes.CDLL:
     L.bdd_lmhead_packed_bytes.restype = sz
     L.bdd_lmhead_pack.argtypes = [vp, i32, i32, i32, vp, vp]
     L.bdd_lmhead_pack.restype = i32
+    L.bdd_round_graph_create.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
+    L.bdd_round_graph_create.restype = i32
+    L.bdd_round_graph_launch.argtypes = [vp, vp]
+    L.bdd_round_graph_launch.restype = i32
+    L.bdd_round_graph_destroy.argtypes = [vp]
+    L.bdd_round_graph_destroy.restype = None
     L.bdd_timing_enable.argtypes = [i32, ctypes.c_char_p]
     L.bdd_timing_enable.restype = i32
     L.bdd_timing_read.argtypes = [i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -357,6 +365,37 @@ class RoundPlan:
             self.threshold, _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info),
             _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(hhat_out), _ptr(self.ws),
             self.ws.numel(), _stream(stream)))
+
+
+class RoundGraph:
+    """A round bound to fixed buffers and captured as a HIP graph
+    (bdd_round_graph_create); call launch() to enqueue one round."""
+
+    def __init__(self, plan: RoundPlan, x_in, tokens, conf, choice, round_info, layer_topk_idx=None,
+                 layer_n_distinct=None, hhat_out=None):
+        d = plan.d
+        _need(x_in, "x_in", torch.float32, (d.T, d.H), plan.dev)
+        _need(tokens, "tokens", torch.int32, (d.T,), plan.dev)
+        _need(conf, "conf", torch.float32, (d.T,), plan.dev)
+        _need(choice, "choice", torch.int32, (d.T,), plan.dev)
+        _need(round_info, "round_info", torch.int32, (4,), plan.dev)
+        self.keep = (plan, x_in, tokens, conf, choice, round_info, layer_topk_idx, layer_n_distinct, hhat_out)
+        h = ctypes.c_void_p()
+        _check(lib().bdd_round_graph_create(
+            ctypes.byref(plan.c_dims), len(plan.layers), plan.c_layers, plan.top_p, _ptr(plan.lm.packed),
+            plan.V, plan.threshold, _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info),
+            _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(hhat_out), _ptr(plan.ws), plan.ws.numel(),
+            ctypes.byref(h)))
+        self.handle = h
+
+    def launch(self, stream=None):
+        _check(lib().bdd_round_graph_launch(self.handle, _stream(stream)))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            lib().bdd_round_graph_destroy(h)
+            self.handle = None
 
 
 def block_denoise_round(d: MoEDims, layers: list, lm: LMHead, x_in: torch.Tensor,

@@ -4,7 +4,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
 #include <string>
 #include <vector>
 
@@ -70,37 +69,8 @@ bool timing_wants(const char *name) {
     }                                                                            \
   } while (0)
 
-// ----------------------------------------------------------------- side stream
-// The shared expert depends only on the normalised block, so it runs on a
-// library-owned stream of the same device (default priority), forked from and
-// joined back into the caller's stream with events: it overlaps routing and
-// the routed experts.  Calls on one device must not overlap (they share it).
-struct Side {
-  hipStream_t s2 = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-Side g_side[64];
-std::mutex g_side_mu;
-
-bdd_status side_for_current_device(Side **out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess || dev < 0 || dev >= 64) return fail(BDD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  Side &sd = g_side[dev];
-  if (!sd.s2) {
-    if ((e = hipStreamCreateWithFlags(&sd.s2, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess)
-      return fail(BDD_ERR_HIP, "side stream: %s", hipGetErrorString(e));
-  }
-  *out = &sd;
-  return BDD_OK;
-}
-
 constexpr int kMaxLmGrid = 1024;
 constexpr int kExpertWgPerCu = 3;
-constexpr int kDownRowsPerItem = 128;
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int wdtype) { return wdtype == BDD_BF16 ? 2 : 4; }
@@ -134,13 +104,11 @@ bdd_status check_dims(const bdd_moe_dims *d) {
                 d->I, d->I_shared);
   if (d->H > 8192 || d->I > 8192 || d->I_shared > 8192)
     return fail(BDD_ERR_UNSUPPORTED, "H, I, I_shared must be <= 8192");
-  if (router_lds_bytes(d->wdtype, d->T, d->H) > 144 * 1024)
-    return fail(BDD_ERR_UNSUPPORTED, "T=%d, H=%d: the normalised block exceeds the LDS budget", d->T, d->H);
   return BDD_OK;
 }
 
 struct MoePlan {
-  size_t logits, prob, idx, wgt, meta, ulist, slot_n, slot_asg, bits, mass, xhat, A, A_s, P, P_s;
+  size_t logits, prob, idx, wgt, meta, ulist, slot_n, slot_asg, glist, bits, mass, xhat, A, P;
   size_t sorted, sel_count;
   size_t end;
 };
@@ -150,7 +118,7 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   size_t o = base;
   auto take = [&o](size_t bytes) { size_t at = o; o = a256(o + bytes); return at; };
   const size_t T = d.T, E = d.E, K = d.K, H = d.H, I = d.I, Is = d.I_shared;
-  p.logits = take(T * E * 4);
+  p.logits = take((size_t)router_slices(d.H) * T * E * 4);
   p.prob = take(T * E * 4);
   p.idx = take(T * K * 4);
   p.wgt = take(T * K * 4);
@@ -158,13 +126,13 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   p.ulist = take(E * 4);
   p.slot_n = take(E * 4);
   p.slot_asg = take(E * kMaxT * 4);
+  p.glist = take((size_t)expert_groups_max(d.T, d.E, d.K) * 4);
   p.bits = take(32);
   p.mass = take(E * 4);
   p.xhat = take(T * H * esize(d.wdtype));
-  p.A = take(T * K * I * 4);
-  p.A_s = take(T * (Is ? Is : 1) * 4);
-  p.P = take(T * K * H * 4);
-  p.P_s = take(T * H * 4);
+  // rows t*K + k of the routed picks, then T*K + t of the shared expert
+  p.A = take((T * K + T) * (I > Is ? I : Is) * 4);
+  p.P = take((T * K + T) * H * 4);
   p.sorted = take(T * E * 4);
   p.sel_count = take(64);
   p.end = o;
@@ -230,6 +198,7 @@ RouteBufs route_bufs(void *ws, const MoePlan &p) {
   r.union_list = at<int32_t>(ws, p.ulist);
   r.slot_n = at<int32_t>(ws, p.slot_n);
   r.slot_asg = at<int32_t>(ws, p.slot_asg);
+  r.glist = at<int32_t>(ws, p.glist);
   r.cs_bits = at<uint32_t>(ws, p.bits);
   r.mass = at<float>(ws, p.mass);
   r.n_distinct_out = nullptr;
@@ -245,33 +214,23 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
                      float *h_copy, void *xhat, RouteBufs r, const MoePlan &p, void *ws, float *h,
                      float *y_out, void *xhat_next, int32_t *lm_count, hipStream_t s) {
   const int T = d.T, H = d.H, E = d.E, K = d.K, I = d.I, Is = d.I_shared;
-  const int cus = device_cus();
-  float *A = at<float>(ws, p.A), *A_s = at<float>(ws, p.A_s);
-  float *P = at<float>(ws, p.P), *P_s = at<float>(ws, p.P_s);
+  const int Imax = I > Is ? I : Is;
+  const int cap = device_cus() * kExpertWgPerCu;
+  float *A = at<float>(ws, p.A), *P = at<float>(ws, p.P);
   int32_t *sel_count = at<int32_t>(ws, p.sel_count);
   if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, T, H, lm_count, s));
-  LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, w.router_bias, r.logits,
-                                           T, H, E, s));
-  Side *sd = nullptr;
-  if (Is > 0) {
-    bdd_status st = side_for_current_device(&sd);
-    if (st != BDD_OK) return st;
-    HIP_TRY(hipEventRecord(sd->fork, s));
-    HIP_TRY(hipStreamWaitEvent(sd->s2, sd->fork, 0));
-    LAUNCH("shared_gateup", sd->s2, launch_shared_gateup(d.wdtype, xhat, w.ws_gate_up, A_s, T, H, Is, sd->s2));
-    LAUNCH("shared_down", sd->s2, launch_shared_down(d.wdtype, A_s, w.ws_down, P_s, T, H, Is, sd->s2));
-    HIP_TRY(hipEventRecord(sd->join, sd->s2));
-  }
-  LAUNCH("route_select", s, launch_route_select(r, T, E, K, top_p, at<int32_t>(ws, p.sorted), sel_count, s));
-  const int union_max = E < T * K ? E : T * K;
-  int g1 = union_max * (I / 16), g2 = union_max * (H / kDownRowsPerItem);
-  const int cap = cus * kExpertWgPerCu;
+  LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, r.logits, T, H, E, s));
+  LAUNCH("route_select", s, launch_route_select(r, w.router_bias, T, H, E, K, top_p, at<int32_t>(ws, p.sorted),
+                                                sel_count, s));
+  int g1 = expert_items_max(T, H, E, K, I, Is, true), g2 = expert_items_max(T, H, E, K, I, Is, false);
   g1 = g1 < cap ? g1 : cap;
   g2 = g2 < cap ? g2 : cap;
-  LAUNCH("routed_gateup", s, launch_routed_gateup(d.wdtype, xhat, w.w_gate_up, r, A, T, H, E, K, I, g1, s));
-  LAUNCH("routed_down", s, launch_routed_down(d.wdtype, A, w.w_down, r, P, H, E, K, I, g2, s));
-  if (Is > 0) HIP_TRY(hipStreamWaitEvent(s, sd->join, 0));
-  LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P_s : nullptr, r.idx, h, y_out, xhat_next, T, H, K, s));
+  LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, w.w_gate_up, w.ws_gate_up, r, A, T, H, K, I,
+                                                  Is, Imax, g1, s));
+  LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, w.w_down, w.ws_down, r, P, T, H, K, I, Is, Imax,
+                                              g2, s));
+  LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P + (size_t)T * K * H : nullptr, r.idx, r.wgt, h,
+                                      y_out, xhat_next, T, H, K, s));
   return BDD_OK;
 }
 
@@ -471,6 +430,63 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
   const LmCommit fused = {count, threshold, tokens, conf, choice, round_info};
   LAUNCH("lmhead", s, launch_lmhead(d->wdtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, &fused, s));
   return BDD_OK;
+}
+
+struct bdd_round_graph_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+bdd_status bdd_round_graph_create(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_weights *layers,
+                                  float coreset_top_p, const void *w_packed, int32_t V, float threshold,
+                                  const float *x_in, int32_t *tokens, float *conf, int32_t *choice,
+                                  int32_t *round_info, int32_t *layer_topk_idx, int32_t *layer_n_distinct,
+                                  void *hhat_out, void *ws, size_t ws_bytes, bdd_round_graph *out) {
+  if (!out) return fail(BDD_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  hipStream_t cs = nullptr;
+  HIP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  const bool timing = g_timing;
+  g_timing = false;
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) {
+    g_timing = timing;
+    (void)hipStreamDestroy(cs);
+    return fail(BDD_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+  }
+  const bdd_status st = bdd_block_denoise_round(d, n_layers, layers, coreset_top_p, w_packed, V, threshold,
+                                                x_in, tokens, conf, choice, round_info, layer_topk_idx,
+                                                layer_n_distinct, hhat_out, ws, ws_bytes, cs);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cs, &graph);
+  g_timing = timing;
+  (void)hipStreamDestroy(cs);
+  if (st != BDD_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (e != hipSuccess) return fail(BDD_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(BDD_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  }
+  *out = new bdd_round_graph_s{graph, exec};
+  return BDD_OK;
+}
+
+bdd_status bdd_round_graph_launch(bdd_round_graph g, void *stream) {
+  if (!g || !g->exec) return fail(BDD_ERR_INVALID_ARG, "graph is NULL");
+  HIP_TRY(hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream)));
+  return BDD_OK;
+}
+
+void bdd_round_graph_destroy(bdd_round_graph g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 }  // extern "C"

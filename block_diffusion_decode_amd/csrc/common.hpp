@@ -79,6 +79,23 @@ __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---------------------------------------------------------------- cross-workgroup handoff
+// Values one workgroup publishes for another workgroup of the same kernel are
+// stored and loaded as agent-scope atomics: on this multi-XCD part they bypass
+// the per-XCD L2s (sc1), so no cache writeback/invalidate fence is needed.  A
+// wave completes its publishing stores (wait_stores) before the counter that
+// announces them is incremented.
+template <typename T>
+__device__ __forceinline__ void publish(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ __forceinline__ T fetch_published(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ int count_done(int32_t *counter) {
+  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -42,78 +42,11 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
   }
 }
 
-// Batch of kLmBatch k-steps: each lane loads one 16-byte chunk per step
-// (chunk 4*step + g of its row), then runs the MFMAs of the batch against the
-// staged block.  Two batches are kept in flight (double buffering), so a wave
-// has up to 2 * kLmBatch loads outstanding.
+// Each lane loads one 16-byte unit per MFMA k-step: k-step s of a 16-row tile
+// is one contiguous KiB of the packed weight in which lane l = li + 16 g finds
+// its operand (row li, chunk 4s + g) at byte 16 l.  Loads go in batches of
+// kLmBatch k-steps; two batches are in flight per wave.
 constexpr int kLmBatch = 8;
-
-// Packed layout: k-step s of a 16-row tile is one contiguous KiB in which lane
-// l = li + 16 g finds its MFMA operand (row li, chunk 4s + g) at byte 16 l.
-template <class W, int NT>
-__device__ __forceinline__ void lm_load(rsrc_t rs, uint32_t vbase, int b, uint4 (&a)[kLmBatch]) {
-#pragma unroll
-  for (int j = 0; j < kLmBatch; ++j) a[j] = buf_ld16(rs, vbase, (uint32_t)(b * kLmBatch + j) * 1024u);
-}
-
-template <class W, int NT>
-__device__ __forceinline__ void lm_mma(const uint4 (&a)[kLmBatch], const uint4 *__restrict__ xs,
-                                       int b, int g, int li, f32x4 (&acc)[NT]) {
-  constexpr int TP = 16 * NT;
-#pragma unroll
-  for (int j = 0; j < kLmBatch; ++j) {
-    const int c = (b * kLmBatch + j) * 4 + g;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const uint4 bv = xs[c * TP + n * 16 + li];
-      if constexpr (std::is_same<W, WBf16>::value) {
-        acc[n] = mfma_bf16(a[j], bv, acc[n]);
-      } else {
-        acc[n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[n]);
-        acc[n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[n]);
-        acc[n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[n]);
-        acc[n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[n]);
-      }
-    }
-  }
-}
-
-// acc[n] += W[row] . xhat[col]^T over the full hidden size: NC chunks of 16
-// bytes per row, 4 chunks per MFMA k-step (lane group g takes chunk 4s + g).
-template <class W, int NT>
-__device__ __forceinline__ void lm_tile_dot(rsrc_t rs, uint32_t vbase, const uint4 *__restrict__ xs,
-                                            int NC, int g, int li, f32x4 (&acc)[NT]) {
-  const int nb = NC / (4 * kLmBatch);
-  uint4 a0[kLmBatch], a1[kLmBatch];
-  int b = 0;
-  if (nb > 0) lm_load<W, NT>(rs, vbase, 0, a0);
-  while (b < nb) {
-    if (b + 1 < nb) lm_load<W, NT>(rs, vbase, b + 1, a1);
-    lm_mma<W, NT>(a0, xs, b, g, li, acc);
-    if (++b >= nb) break;
-    if (b + 1 < nb) lm_load<W, NT>(rs, vbase, b + 1, a0);
-    lm_mma<W, NT>(a1, xs, b, g, li, acc);
-    ++b;
-  }
-  // remaining k-steps when NC is not a multiple of 4 * kLmBatch
-  constexpr int TP = 16 * NT;
-  for (int c0 = nb * 4 * kLmBatch; c0 < NC; c0 += 4) {
-    const int c = c0 + g;
-    const uint4 a = buf_ld16(rs, vbase, (uint32_t)(c0 / 4) * 1024u);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const uint4 bv = xs[c * TP + n * 16 + li];
-      if constexpr (std::is_same<W, WBf16>::value) {
-        acc[n] = mfma_bf16(a, bv, acc[n]);
-      } else {
-        acc[n] = mfma_f32(__uint_as_float(a.x), __uint_as_float(bv.x), acc[n]);
-        acc[n] = mfma_f32(__uint_as_float(a.y), __uint_as_float(bv.y), acc[n]);
-        acc[n] = mfma_f32(__uint_as_float(a.z), __uint_as_float(bv.z), acc[n]);
-        acc[n] = mfma_f32(__uint_as_float(a.w), __uint_as_float(bv.w), acc[n]);
-      }
-    }
-  }
-}
 
 // Merge the per-workgroup partials of every position (fixed order), then the
 // commit rule on the still-masked positions.  Run by one whole workgroup of
@@ -128,9 +61,21 @@ __device__ void commit_block(const float *__restrict__ part_m, const float *__re
   for (int t = wave; t < T; t += nw) {
     float m = -FLT_MAX, s = 0.f;
     int i = INT_MAX;
-    for (int p = lane; p < nparts; p += 64)
-      sm_merge(m, s, i, part_m[(size_t)t * nparts + p], part_s[(size_t)t * nparts + p],
-               part_i[(size_t)t * nparts + p]);
+    // all of a lane's loads first (independent), then the merges
+    for (int base = lane; base < nparts; base += 4 * 64) {
+      float pm[4], ps[4];
+      int pi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = base + 64 * j;
+        const bool ok = p < nparts;
+        pm[j] = ok ? fetch_published(part_m + (size_t)t * nparts + p) : 0.f;
+        ps[j] = ok ? fetch_published(part_s + (size_t)t * nparts + p) : 0.f;
+        pi[j] = ok ? fetch_published(part_i + (size_t)t * nparts + p) : INT_MAX;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm_merge(m, s, i, pm[j], ps[j], pi[j]);
+    }
 #pragma unroll
     for (int sft = 1; sft <= 32; sft <<= 1) {
       const float m2 = __shfl_xor(m, sft), s2 = __shfl_xor(s, sft);
@@ -223,43 +168,60 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   constexpr int TP = 16 * NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NC = H / CH;
-  // stage the block: batches of 8 independent loads per thread
-  for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
-    uint4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const int t = idx / NC, c = idx - t * NC;
-      v[j] = (idx < TP * NC && t < T) ? ld16(hhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const int t = idx / NC, c = idx - t * NC;
-      if (idx < TP * NC) xs[c * TP + t] = v[j];
-    }
-  }
-  __syncthreads();
-
   const int li = lane & 15, g = lane >> 4;
   float m[NT], s[NT];
   int am[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) { m[n] = -FLT_MAX; s[n] = 0.f; am[n] = INT_MAX; }
 
+  // The wave's tiles (first, first + stride, ...) and their k-step batches
+  // form one flat sequence of load steps, so the next tile's first batch is in
+  // flight during a tile's epilogue, and the first batch during the staging.
   const int ntiles = (V + 15) / 16;
+  const int ksteps = NC / 4;
+  const int nb = (ksteps + kLmBatch - 1) / kLmBatch;
+  const int first = uniform(blockIdx.x * kLmWaves + wave);
+  const int stride = gridDim.x * kLmWaves;
+  const int my_tiles = first < ntiles ? (ntiles - 1 - first) / stride + 1 : 0;
+  const int steps = my_tiles * nb;
   const uint32_t vbase = (uint32_t)lane * 16u;
   const uint32_t tile_bytes = (uint32_t)(16 * H * (int)sizeof(typename W::T));
-  for (int tile = uniform(blockIdx.x * kLmWaves + wave); tile < ntiles; tile += gridDim.x * kLmWaves) {
-    const int row0 = tile * 16;
-    // descriptor over this tile's packed rows (rows past V were packed as
-    // zeros; their logits are dropped in the epilogue)
-    const rsrc_t rs = make_rsrc(wlm + (size_t)row0 * H, tile_bytes);
-    f32x4 acc[NT];
+  auto load = [&](int st, uint4(&a)[kLmBatch]) {
+    const int k = st / nb, b = st - k * nb;
+    // descriptor over the tile's packed rows (rows past V were packed as zeros)
+    const rsrc_t rs = make_rsrc(wlm + (size_t)(first + k * stride) * 16 * H, tile_bytes);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    lm_tile_dot<W, NT>(rs, vbase, xs, NC, g, li, acc);
-    // epilogue: lane holds rows row0 + 4g + r (r = 0..3) of column li + 16n
+    for (int j = 0; j < kLmBatch; ++j)   // k-steps past the end reload the last one (unused)
+      a[j] = buf_ld16(rs, vbase, (uint32_t)min(b * kLmBatch + j, ksteps - 1) * 1024u);
+  };
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](int st, const uint4(&a)[kLmBatch]) {
+    const int b = st % nb;
+#pragma unroll
+    for (int j = 0; j < kLmBatch; ++j) {
+      const int ks = b * kLmBatch + j;
+      if (ks >= ksteps) break;
+      const int c = ks * 4 + g;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const uint4 bv = xs[c * TP + n * 16 + li];
+        if constexpr (std::is_same<W, WBf16>::value) {
+          acc[n] = mfma_bf16(a[j], bv, acc[n]);
+        } else {
+          acc[n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[n]);
+          acc[n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[n]);
+          acc[n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[n]);
+          acc[n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[n]);
+        }
+      }
+    }
+  };
+  // epilogue of a finished tile: lane holds rows row0 + 4g + r (r = 0..3) of
+  // column li + 16n; fold them into the running (max, sum, argmax)
+  auto epilogue = [&](int st) {
+    const int row0 = (first + (st / nb) * stride) * 16;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       float tmax = -FLT_MAX;
@@ -287,7 +249,39 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
       tsum += __shfl_xor(tsum, 16);
       tsum += __shfl_xor(tsum, 32);
       sm_merge(m[n], s[n], am[n], tmax, tsum, targ);
+      acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+
+  uint4 a0[kLmBatch], a1[kLmBatch];
+  if (steps > 0) load(0, a0);
+  // stage the block: batches of 8 independent loads per thread
+  for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const int t = idx / NC, c = idx - t * NC;
+      v[j] = (idx < TP * NC && t < T) ? ld16(hhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int idx = base + j * (int)blockDim.x;
+      const int t = idx / NC, c = idx - t * NC;
+      if (idx < TP * NC) xs[c * TP + t] = v[j];
+    }
+  }
+  __syncthreads();
+  // prefetches are unconditional (the step index is clamped) so that the
+  // compiler's load counting sees the same two batches in flight on every path
+  for (int st = 0; st < steps; st += 2) {
+    load(min(st + 1, steps - 1), a1);
+    mma(st, a0);
+    if (st % nb == nb - 1) epilogue(st);
+    if (st + 1 >= steps) break;
+    load(min(st + 2, steps - 1), a0);
+    mma(st + 1, a1);
+    if ((st + 1) % nb == nb - 1) epilogue(st + 1);
   }
 
   if (lane < 16) {
@@ -303,22 +297,21 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
     float mm = -FLT_MAX, ss = 0.f;
     int ii = INT_MAX;
     for (int w = 0; w < kLmWaves; ++w) sm_merge(mm, ss, ii, sm[w][tid], ssum[w][tid], si[w][tid]);
-    part_m[(size_t)tid * gridDim.x + blockIdx.x] = mm;
-    part_s[(size_t)tid * gridDim.x + blockIdx.x] = ss;
-    part_i[(size_t)tid * gridDim.x + blockIdx.x] = ii;
+    publish(part_m + (size_t)tid * gridDim.x + blockIdx.x, mm);
+    publish(part_s + (size_t)tid * gridDim.x + blockIdx.x, ss);
+    publish(part_i + (size_t)tid * gridDim.x + blockIdx.x, ii);
   }
   if (done_count == nullptr) return;
   __shared__ int s_last;
-  __syncthreads();  // the partial stores of this workgroup have completed
+  // the partials come from wave 0 (T <= 32): its stores complete, then count
   if (tid == 0) {
-    __threadfence();  // release them device-wide (across XCDs) before counting
-    s_last = atomicAdd(done_count, 1) == (int)gridDim.x - 1;
-    if (s_last) __threadfence();  // acquire every workgroup's partials
+    wait_stores();
+    s_last = count_done(done_count) == (int)gridDim.x - 1;
   }
   __syncthreads();
   if (!s_last) return;
   commit_block(part_m, part_s, part_i, gridDim.x, T, threshold, tokens, conf, choice, round_info);
-  if (tid == 0) *done_count = 0;
+  if (tid == 0) publish(done_count, 0);
 }
 
 // Packs w_lm [V][H] into the tile layout the LM-head kernel streams: for

@@ -11,7 +11,6 @@
 
 #include <type_traits>
 
-#include "dense.hpp"
 #include "kernels.hpp"
 
 namespace bdd {
@@ -77,89 +76,67 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__res
 }
 
 // ------------------------------------------------------------------ router logits
-// logits[t][e] = xhat_t . W_r[e] + b_e.  One workgroup per 16 experts.  The
-// normalised block is staged in LDS as [chunk][position] 16-byte entries; the
-// 8 waves split the hidden dimension and sum their partial tiles through LDS.
-// Workgroup 0 also clears `zero_word` (the selection kernel's counter).
-constexpr int kRouterWaves = 8;
+// Partial router logits over hidden slices of kRouterSlice elements:
+// part[ks][t][e] = xhat_t[slice ks] . W_r[e][slice ks].  One wave per
+// (16 experts, slice): 16x16 MFMA tiles with the experts as rows and the
+// positions as columns, both operands loaded straight from memory (the block
+// is L2-resident), so the 1 MiB of router weights is spread over ~256
+// workgroups.  The selection kernel sums the slices in slice order and adds
+// the bias.  Workgroup (0, 0) also clears `zero_word` (the selection kernel's
+// counter).
+constexpr int kRouterSlice = 128;
+constexpr uint32_t kRouterOut = 0x7ff00000u;  // out-of-range buffer offset: loads return zeros
 
 template <class W, int NT>
-__global__ __launch_bounds__(64 * kRouterWaves) void router_kernel(
-    const typename W::T *__restrict__ xhat, int32_t *__restrict__ zero_word,
-    const typename W::T *__restrict__ wr, const float *__restrict__ bias, float *__restrict__ logits,
-    int T, int H, int E) {
-  extern __shared__ uint4 xs[];  // [H / kChunk][16 * NT]; reused for the split-K sums
-  constexpr int CH = W::kChunk;
-  constexpr int TP = 16 * NT;
+__global__ __launch_bounds__(64) void router_kernel(const typename W::T *__restrict__ xhat,
+                                                    int32_t *__restrict__ zero_word,
+                                                    const typename W::T *__restrict__ wr,
+                                                    float *__restrict__ part, int T, int H, int E) {
   typedef typename W::T WT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int NC = H / CH;
-  if (blockIdx.x == 0 && tid == 0 && zero_word) *zero_word = 0;
-  for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
-    uint4 v[8];
+  constexpr int CH = W::kChunk;
+  constexpr int NCS = kRouterSlice / CH;  // 16-byte chunks per slice
+  constexpr int NS = NCS / 4;             // MFMA k-steps per slice (4 chunks each)
+  const int lane = threadIdx.x, li = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * 16, ks = blockIdx.y;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && lane == 0 && zero_word) *zero_word = 0;
+  const rsrc_t rw = make_rsrc(wr, (uint32_t)(E * H) * sizeof(WT));
+  const rsrc_t rx = make_rsrc(xhat, (uint32_t)(T * H) * sizeof(WT));
+  const int e_row = row0 + li;
+  uint4 a[NS], b[NS][NT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const int t = idx / NC, c = idx - t * NC;
-      v[j] = (idx < TP * NC && t < T) ? ld16(xhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
-    }
+  for (int j = 0; j < NS; ++j) {
+    const int c = ks * NCS + 4 * j + g;
+    a[j] = buf_ld16(rw, e_row < E ? (uint32_t)(e_row * H + c * CH) * sizeof(WT) : kRouterOut, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const int t = idx / NC, c = idx - t * NC;
-      if (idx < TP * NC) xs[c * TP + t] = v[j];
+    for (int n = 0; n < NT; ++n) {
+      const int t = n * 16 + li;
+      b[j][n] = buf_ld16(rx, t < T ? (uint32_t)(t * H + c * CH) * sizeof(WT) : kRouterOut, 0);
     }
   }
-  __syncthreads();
-
-  // MFMA over this wave's share of the k-steps (4 chunks per k-step)
-  const int row0 = blockIdx.x * 16;
-  const int li = lane & 15, g = lane >> 4;
-  const int nrows = min(16, E - row0);
-  const rsrc_t rs = make_rsrc(wr + (size_t)row0 * H, (uint32_t)(nrows * H * (int)sizeof(WT)));
-  const uint32_t vbase = (uint32_t)(li * H + g * CH) * (uint32_t)sizeof(WT);
-  const int steps = NC / 4;
-  const int per = (steps + nw - 1) / nw;
-  const int s0 = min(wave * per, steps), s1 = min(s0 + per, steps);
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sb = s0; sb < s1; sb += 8) {
-    uint4 a[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      a[j] = sb + j < s1 ? buf_ld16(rs, vbase, (uint32_t)((sb + j) * 4 * CH * (int)sizeof(WT)))
-                         : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < NS; ++j)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (sb + j >= s1) break;
-      const int c = (sb + j) * 4 + g;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const uint4 bv = xs[c * TP + n * 16 + li];
-        if constexpr (std::is_same<W, WBf16>::value) {
-          acc[n] = mfma_bf16(a[j], bv, acc[n]);
-        } else {
-          acc[n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[n]);
-          acc[n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[n]);
-          acc[n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[n]);
-          acc[n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[n]);
-        }
+    for (int n = 0; n < NT; ++n) {
+      if constexpr (std::is_same<W, WBf16>::value) {
+        acc[n] = mfma_bf16(a[j], b[j][n], acc[n]);
+      } else {
+        acc[n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(b[j][n].x), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(b[j][n].y), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(b[j][n].z), acc[n]);
+        acc[n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(b[j][n].w), acc[n]);
       }
     }
-  }
-  __syncthreads();  // every wave is done with xs: reuse it for the split-K sums
-  splitk_sum<NT>(acc, reinterpret_cast<float *>(xs), wave, nw, lane);
-  if (wave == 0) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = row0 + 4 * (lane >> 4) + r;
-        const int t = n * 16 + (lane & 15);
-        if (e < E && t < T) logits[(size_t)t * E + e] = acc[n][r] + (bias ? bias[e] : 0.f);
-      }
-  }
+    for (int r = 0; r < 4; ++r) {
+      const int e = row0 + 4 * g + r;
+      const int t = n * 16 + li;
+      if (e < E && t < T) part[((size_t)ks * T + t) * E + e] = acc[n][r];
+    }
 }
 
 // ------------------------------------------------------------------ selection helpers
@@ -355,17 +332,25 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, i
   return ((unsigned long long)(uint32_t)__shfl_xor((int)hi, m) << 32) | (uint32_t)__shfl_xor((int)lo, m);
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T, int E, int K,
-                                                             float top_p, int32_t *__restrict__ sorted_ids,
+__global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const float *__restrict__ bias,
+                                                             int KS, int T, int E, int K, float top_p,
+                                                             int32_t *__restrict__ sorted_ids,
                                                              int32_t *__restrict__ done_count) {
   __shared__ unsigned long long s_key[kSelThreads];
+  __shared__ float s_p[kSelThreads];
   __shared__ float s_red[kSelThreads / 64];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
   {
-    // ---- phase 1: this position
-    const float l = tid < E ? r.logits[(size_t)t * E + tid] : -FLT_MAX;
+    // ---- phase 1: this position.  Logit = router slices in slice order + bias.
+    float l = -FLT_MAX;
+    if (tid < E) {
+      float acc = 0.f;
+#pragma unroll 16
+      for (int ks = 0; ks < KS; ++ks) acc += r.logits[((size_t)ks * T + t) * E + tid];
+      l = acc + (bias ? bias[tid] : 0.f);
+    }
     float m = wave_max_dpp(l);
     if (lane == 0) s_red[wave] = m;
     __syncthreads();
@@ -376,7 +361,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T,
     if (lane == 0) s_red[wave] = sum;
     __syncthreads();
     sum = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    if (tid < E) r.prob[(size_t)t * E + tid] = ex / sum;
+    const float pr = ex / sum;
+    if (tid < E) publish(r.prob + (size_t)t * E + tid, pr);
+    s_p[tid] = pr;
     // bitonic sort, ascending on (order_key(logit), id); padding sorts last
     unsigned long long key = tid < E ? (((unsigned long long)order_key(l) << 32) | (uint32_t)tid) : ~0ull;
     for (int k = 2; k <= kSelThreads; k <<= 1) {
@@ -394,15 +381,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T,
         key = (lower == asc) ? (key < other ? key : other) : (key < other ? other : key);
       }
     }
-    if (tid < E) sorted_ids[(size_t)t * E + tid] = (int32_t)(uint32_t)key;
+    const int e_sorted = (int32_t)(uint32_t)key;
+    if (tid < E) publish(sorted_ids + (size_t)t * E + tid, e_sorted);
+    // the top-K picks and their scores, in sorted order
+    if (tid < K) {
+      publish(r.idx + (size_t)t * K + tid, e_sorted);
+      publish(r.wgt + (size_t)t * K + tid, s_p[e_sorted]);
+    }
   }
-  __syncthreads();  // this position's rows are stored (its stores came from all waves)
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    s_last = atomicAdd(done_count, 1) == (int)gridDim.x - 1;
-    if (s_last) __threadfence();
-  }
+  wait_stores();     // every wave completes its row stores ...
+  __syncthreads();   // ... before the position is counted
+  if (tid == 0) s_last = count_done(done_count) == (int)gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
 
@@ -410,9 +399,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T,
   __shared__ SelShared sh;
   for (int i = tid; i < T * K; i += kSelThreads) {
     const int tt = i / K, k = i - tt * K;
-    const int e = sorted_ids[(size_t)tt * E + k];
-    sh.idx[tt][k] = e;
-    sh.psel[tt][k] = r.prob[(size_t)tt * E + e];
+    sh.idx[tt][k] = fetch_published(r.idx + i);      // scores are staged in wgt
+    sh.psel[tt][k] = fetch_published(r.wgt + i);
   }
   __syncthreads();
   coreset_core(sh, T, E, K, top_p);
@@ -425,13 +413,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T,
     for (int tt = wave; tt < T; tt += kSelThreads / 64) {
       int taken = 0;
       for (int base = 0; base < E && taken < kk; base += 64) {
-        const int e = base + lane < E ? sorted_ids[(size_t)tt * E + base + lane] : -1;
+        const int e = base + lane < E ? fetch_published(sorted_ids + (size_t)tt * E + base + lane) : -1;
         const bool mem = e >= 0 && sh.member[e] != 0;
         const unsigned long long b = __ballot(mem);
         const int before = __popcll(b & ((1ull << lane) - 1ull));
         if (mem && taken + before < kk) {
           sh.idx[tt][taken + before] = e;
-          sh.psel[tt][taken + before] = r.prob[(size_t)tt * E + e];
+          sh.psel[tt][taken + before] = fetch_published(r.prob + (size_t)tt * E + e);
         }
         taken += __popcll(b);
       }
@@ -450,8 +438,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T,
     r.wgt[i] = e >= 0 ? sh.psel[tt][k] / s : 0.f;
   }
   const int slot = union_scan(sh, E);
+  const uint32_t tbits = slot >= 0 ? sh.tokmask[tid] : 0u;
   if (slot >= 0) {
-    uint32_t bits = sh.tokmask[tid];
+    uint32_t bits = tbits;
     r.union_list[slot] = tid;
     r.slot_n[slot] = __popc(bits);
     int j = 0;
@@ -461,12 +450,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, int T,
       r.slot_asg[slot * kMaxT + j++] = tt * K + sh.kslot[tt][tid];
     }
   }
+  // token groups of kTokGroup positions, in union order (exclusive scan of
+  // each union expert's group count)
+  const int ngr = (__popc(tbits) + kTokGroup - 1) / kTokGroup;
+  int incl = ngr;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int o = __shfl_up(incl, s);
+    if (lane >= s) incl += o;
+  }
+  if (lane == 63) sh.wtot[wave] = incl;
+  __syncthreads();
+  int goff = incl - ngr, gtot = 0;
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    if (w < wave) goff += sh.wtot[w];
+    gtot += sh.wtot[w];
+  }
+  for (int j = 0; j < ngr; ++j) r.glist[goff + j] = (slot << 8) | (j * kTokGroup);
   if (tid == 0) {
+    r.meta[2] = gtot;
     r.meta[0] = sh.nu;
     r.meta[1] = sh.csize;
     if (r.n_distinct_out) *r.n_distinct_out = sh.nu;
     if (r.coreset_size_out) *r.coreset_size_out = sh.csize;
-    *done_count = 0;
+    publish(done_count, 0);
   }
 }
 
@@ -494,12 +501,13 @@ __global__ __launch_bounds__(256) void coreset_kernel(const float *__restrict__ 
 }
 
 // ------------------------------------------------------------------ combine
-// y_t = sum_k P[t*K+k] (live slots, in slot order) + P_s[t]; then h += y and
+// y_t = sum_k w[t*K+k] * P[t*K+k] (live slots, in slot order) + P_s[t]; then h += y and
 // xhat = RMSNorm(h), one workgroup per position.
 template <typename OT>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__restrict__ P,
                                                               const float *__restrict__ P_s,
                                                               const int32_t *__restrict__ idx,
+                                                              const float *__restrict__ wgt,
                                                               float *__restrict__ h,
                                                               float *__restrict__ y_out,
                                                               OT *__restrict__ xhat_out, int H, int K,
@@ -521,7 +529,9 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
     for (int k = 0; k < K; ++k) {
       if (live >> k & 1u) {
         const float4 p = reinterpret_cast<const float4 *>(P + ((size_t)t * K + k) * H)[j];
-        y.x += p.x; y.y += p.y; y.z += p.z; y.w += p.w;
+        const float g = wgt[t * K + k];
+        y.x = fmaf(g, p.x, y.x); y.y = fmaf(g, p.y, y.y);
+        y.z = fmaf(g, p.z, y.z); y.w = fmaf(g, p.w, y.w);
       }
     }
     if (P_s) {
@@ -561,44 +571,29 @@ hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *ou
   return hipGetLastError();
 }
 
-size_t router_lds_bytes(int wdtype, int T, int H) {
-  const int tp = T <= 16 ? 16 : 32;
-  const size_t stage = (size_t)(H / (wdtype == 1 ? 8 : 4)) * tp * 16;
-  const size_t red = (size_t)kRouterWaves * (tp / 16) * 4 * 64 * 4;
-  return stage > red ? stage : red;
-}
-
-template <typename F>
-static hipError_t allow_lds(F *fn, size_t bytes) {
-  if (bytes <= 64 * 1024) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
+int router_slices(int H) { return H / kRouterSlice; }
 
 template <class W, int NT>
-static hipError_t router_launch(const void *xhat, int32_t *zero_word, const void *w_router,
-                                const float *bias, float *logits, int T, int H, int E, hipStream_t s) {
+static hipError_t router_launch(const void *xhat, int32_t *zero_word, const void *w_router, float *part,
+                                int T, int H, int E, hipStream_t s) {
   typedef typename W::T WT;
-  const size_t lds = router_lds_bytes(std::is_same<W, WBf16>::value ? 1 : 0, T, H);
-  hipError_t err = allow_lds(router_kernel<W, NT>, lds);
-  if (err != hipSuccess) return err;
-  router_kernel<W, NT><<<(E + 15) / 16, 64 * kRouterWaves, lds, s>>>(
-      (const WT *)xhat, zero_word, (const WT *)w_router, bias, logits, T, H, E);
+  const dim3 grid((E + 15) / 16, router_slices(H));
+  router_kernel<W, NT><<<grid, 64, 0, s>>>((const WT *)xhat, zero_word, (const WT *)w_router, part, T, H, E);
   return hipGetLastError();
 }
 
 hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const void *w_router,
-                         const float *bias, float *logits, int T, int H, int E, hipStream_t s) {
+                         float *part, int T, int H, int E, hipStream_t s) {
   if (wdtype == 1)
-    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_word, w_router, bias, logits, T, H, E, s)
-                   : router_launch<WBf16, 2>(xhat, zero_word, w_router, bias, logits, T, H, E, s);
-  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_word, w_router, bias, logits, T, H, E, s)
-                 : router_launch<WF32, 2>(xhat, zero_word, w_router, bias, logits, T, H, E, s);
+    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_word, w_router, part, T, H, E, s)
+                   : router_launch<WBf16, 2>(xhat, zero_word, w_router, part, T, H, E, s);
+  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_word, w_router, part, T, H, E, s)
+                 : router_launch<WF32, 2>(xhat, zero_word, w_router, part, T, H, E, s);
 }
 
-hipError_t launch_route_select(const RouteBufs &r, int T, int E, int K, float top_p,
+hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
                                int32_t *sorted_ids, int32_t *done_count, hipStream_t s) {
-  select_kernel<<<T, kSelThreads, 0, s>>>(r, T, E, K, top_p, sorted_ids, done_count);
+  select_kernel<<<T, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids, done_count);
   return hipGetLastError();
 }
 
@@ -609,13 +604,13 @@ hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, i
 }
 
 hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const int32_t *idx,
-                          float *h, float *y_out, void *xhat_out, int T, int H, int K,
+                          const float *wgt, float *h, float *y_out, void *xhat_out, int T, int H, int K,
                           hipStream_t s) {
   if (wdtype == 1)
-    combine_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(P, P_s, idx, h, y_out, (bf16_t *)xhat_out, H, K,
+    combine_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (bf16_t *)xhat_out, H, K,
                                              1e-6f);
   else
-    combine_kernel<float><<<T, kRowThreads, 0, s>>>(P, P_s, idx, h, y_out, (float *)xhat_out, H, K,
+    combine_kernel<float><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (float *)xhat_out, H, K,
                                             1e-6f);
   return hipGetLastError();
 }

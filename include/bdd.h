@@ -20,11 +20,8 @@
  *     (BDD_BF16) or fp32 (BDD_F32); arithmetic accumulates in fp32.
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
  *     and return without waiting.  Outputs are valid once the stream has
- *     reached that point.  Calls that share a workspace must not overlap.
- *     The MoE layer runs its shared expert on a library-owned stream of the
- *     current device (default priority), forked from and joined back into
- *     `stream` with events, so calls on one device must be issued from one
- *     host thread at a time.
+ *     reached that point.  Every kernel of a call runs on `stream`.  Calls
+ *     that share a workspace must not overlap.
  *   - Arguments are checked on the host before anything is enqueued; a
  *     failed check returns a negative status and enqueues nothing.  A
  *     launch failure returns BDD_ERR_HIP.  bdd_last_error() describes the
@@ -203,6 +200,25 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
                                    int32_t *layer_topk_idx, int32_t *layer_n_distinct,
                                    void *hhat_out, void *ws, size_t ws_bytes, void *stream);
 
+/* One denoising round captured as a HIP graph, for callers that replay the
+ * same round structure many times (a decode loop): the arguments are those of
+ * bdd_block_denoise_round, bound at creation (device pointers, sizes and
+ * scalars; the contents of the buffers are read at each launch).  The
+ * round's kernels become the graph's nodes, in stream order.
+ * Launching enqueues one whole round on `stream`.  The graph holds no
+ * memset nodes.  Destroy with bdd_round_graph_destroy. */
+typedef struct bdd_round_graph_s *bdd_round_graph;
+bdd_status bdd_round_graph_create(const bdd_moe_dims *d, int32_t n_layers,
+                                  const bdd_moe_weights *layers, float coreset_top_p,
+                                  const void *w_packed, int32_t V, float threshold,
+                                  const float *x_in, int32_t *tokens, float *conf,
+                                  int32_t *choice, int32_t *round_info,
+                                  int32_t *layer_topk_idx, int32_t *layer_n_distinct,
+                                  void *hhat_out, void *ws, size_t ws_bytes,
+                                  bdd_round_graph *out);
+bdd_status bdd_round_graph_launch(bdd_round_graph g, void *stream);
+void bdd_round_graph_destroy(bdd_round_graph g);
+
 /* Human-readable name of a status, and the calling thread's last error. */
 const char *bdd_status_string(int32_t status);
 const char *bdd_last_error(void);
@@ -214,8 +230,8 @@ int32_t bdd_device_cus(void);
 /* Kernel timing for measurement tools.  While enabled, every kernel launch of
  * this library whose name contains `filter` (NULL or "": all) is bracketed by
  * a pair of hipEvents recorded on the launching stream.  Kernel names:
- * rmsnorm, router_logits, route_select, coreset, shared_gateup, routed_gateup,
- * shared_down, routed_down, combine, lmhead, commit, pack_lm.  Not thread-safe. */
+ * rmsnorm, router_logits, route_select, coreset, expert_gateup, expert_down,
+ * combine, lmhead, commit, pack_lm.  Not thread-safe. */
 bdd_status bdd_timing_enable(int32_t on, const char *filter);
 
 /* Waits for the recorded events, then for up to max_kernels distinct kernel

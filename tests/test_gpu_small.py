@@ -302,3 +302,46 @@ def test_generator_gpu_matches_cpu():
     u1 = W.counter_uniform(W.key_of(3), 5000)
     u2 = W.counter_uniform(W.key_of(3), 5000, device=DEV).cpu()
     assert torch.equal(u1, u2)
+
+
+@pytest.mark.parametrize("case", ["c0_fp32_1layer", "bf16_2layers_coreset"])
+def test_round_graph_replays_match_eager(case):
+    """A captured round replayed several times, with eager rounds and
+    synchronisations in between, gives the eager round's results bit for bit
+    (every kernel's reduction order is fixed)."""
+    if case == "c0_fp32_1layer":
+        d, L, bias, top_p, amp = W.C0, 1, "flat", 1.0, (32.0, (3.0, 7.0))
+    else:
+        d, L, bias, top_p, amp = SMALL_BF16, 2, "zipf", 0.7, (40.0, (4.0, 9.0))
+    R = 3
+    x, layers, w_lm = _round_case(d, 7, L, bias, top_p, R, amp[0], amp[1])
+    lm = bdd.pack_lm_head(w_lm)
+    plan = bdd.RoundPlan(dims_of(d), layers, lm, top_p)
+    gplan = bdd.RoundPlan(dims_of(d), layers, lm, top_p)     # its own workspace
+    T = d.T
+    mk = lambda: (torch.full((T,), bdd.MASK, dtype=torch.int32, device=DEV),
+                  torch.empty(T, dtype=torch.float32, device=DEV),
+                  torch.empty(T, dtype=torch.int32, device=DEV),
+                  torch.empty(4, dtype=torch.int32, device=DEV))
+    xin = torch.empty((T, d.H), dtype=torch.float32, device=DEV)
+    g_tok, g_conf, g_choice, g_ri = mk()
+    graph = bdd.RoundGraph(gplan, xin, g_tok, g_conf, g_choice, g_ri)
+    # eager reference: a resolve of R rounds
+    e_tok, e_conf, e_choice, e_ri = mk()
+    ref = []
+    for r in range(R):
+        plan(x[r].to(DEV), e_tok, e_conf, e_choice, e_ri)
+        torch.cuda.synchronize()
+        ref.append((e_tok.clone(), e_conf.clone(), e_choice.clone(), e_ri.clone()))
+    for rep in range(3):
+        g_tok.fill_(bdd.MASK)
+        for r in range(R):
+            xin.copy_(x[r].to(DEV))
+            graph.launch()
+            torch.cuda.synchronize()
+            for got, want in zip((g_tok, g_conf, g_choice, g_ri), ref[r]):
+                assert torch.equal(got, want), (rep, r)
+            # eager work between replays
+            o_tok, o_conf, o_choice, o_ri = mk()
+            plan(x[r].to(DEV), o_tok, o_conf, o_choice, o_ri)
+            torch.cuda.synchronize()
