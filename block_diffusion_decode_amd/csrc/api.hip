@@ -108,7 +108,7 @@ bdd_status check_dims(const bdd_moe_dims *d) {
 }
 
 struct MoePlan {
-  size_t logits, prob, idx, wgt, meta, ulist, slot_n, slot_asg, glist, bits, mass, xhat, A, P;
+  size_t logits, prob, idx, wgt, meta, ulist, glist, bits, mass, xhat, A, P;
   size_t sorted, sel_count;
   size_t end;
 };
@@ -124,9 +124,7 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   p.wgt = take(T * K * 4);
   p.meta = take(64);
   p.ulist = take(E * 4);
-  p.slot_n = take(E * 4);
-  p.slot_asg = take(E * kMaxT * 4);
-  p.glist = take((size_t)expert_groups_max(d.T, d.E, d.K) * 4);
+  p.glist = take((size_t)expert_groups_max(d.T, d.E, d.K) * 8 * 4);
   p.bits = take(32);
   p.mass = take(E * 4);
   p.xhat = take(T * H * esize(d.wdtype));
@@ -196,8 +194,6 @@ RouteBufs route_bufs(void *ws, const MoePlan &p) {
   r.wgt = at<float>(ws, p.wgt);
   r.meta = at<int32_t>(ws, p.meta);
   r.union_list = at<int32_t>(ws, p.ulist);
-  r.slot_n = at<int32_t>(ws, p.slot_n);
-  r.slot_asg = at<int32_t>(ws, p.slot_asg);
   r.glist = at<int32_t>(ws, p.glist);
   r.cs_bits = at<uint32_t>(ws, p.bits);
   r.mass = at<float>(ws, p.mass);

@@ -114,37 +114,6 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
-// Reduce N partial values per lane across the 64 lanes of a wave, leaving
-// lane l with the total of value index (l >> (6 - log2 N)).  N is a power of
-// two <= 64.  Halving exchange: at each step (partner distance S = 32, 16,
-// ...) lanes keep one half of their values and add the partner's copy of that
-// half; once one value is left the remaining steps are a plain butterfly.
-// All register indices are compile-time constants.
-template <int N, int S>
-__device__ __forceinline__ void reduce_scatter_step(float *v, int lane) {
-  if constexpr (S >= 1) {
-    if constexpr (N > 1) {
-      constexpr int half = N / 2;
-      const bool upper = (lane & S) != 0;
-#pragma unroll
-      for (int i = 0; i < half; ++i) {
-        const float send = upper ? v[i] : v[i + half];
-        const float keep = upper ? v[i + half] : v[i];
-        v[i] = keep + __shfl_xor(send, S);
-      }
-      reduce_scatter_step<half, S / 2>(v, lane);
-    } else {
-      v[0] += __shfl_xor(v[0], S);
-      reduce_scatter_step<1, S / 2>(v, lane);
-    }
-  }
-}
-template <int N>
-__device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
-  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
-  reduce_scatter_step<N, 32>(v, lane);
-  return v[0];
-}
 template <int N>
 constexpr int log2i() { return N <= 1 ? 0 : 1 + log2i<N / 2>(); }
 
@@ -188,6 +157,78 @@ __device__ __forceinline__ void wave_argmax_dpp(float &v, int &i) {
 #undef BDD_STEP
   v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
   i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// keep + the partner's `send`, partners paired by a DPP pattern (S <= 8)
+template <int S>
+__device__ __forceinline__ float pair_level(float keep, float send) {
+  static_assert(S >= 1 && S <= 8, "DPP levels");
+  if constexpr (S == 8) {
+    return keep + dppf<0x140, 0xF>(0.f, send);   // row_mirror
+  } else if constexpr (S == 4) {
+    return keep + dppf<0x141, 0xF>(0.f, send);   // row_half_mirror
+  } else if constexpr (S == 2) {
+    return keep + dppf<0x4E, 0xF>(0.f, send);    // quad_perm [2,3,0,1]
+  } else {
+    return keep + dppf<0xB1, 0xF>(0.f, send);    // quad_perm [1,0,3,2]
+  }
+}
+
+// Levels 32 and 16: lo_half is the value lanes with bit S clear keep, hi_half
+// the one lanes with bit S set keep.  The swap hands each lane its own kept
+// value and its partner's copy of it, in some order; their sum is the level's
+// result.
+template <int S>
+__device__ __forceinline__ float swap_sum(float lo_half, float hi_half) {
+  const uint32_t a = __float_as_uint(lo_half), b = __float_as_uint(hi_half);
+  if constexpr (S == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
+template <int N, int S>
+__device__ __forceinline__ void rs_level(float *v, int lane) {
+  if constexpr (S >= 1) {
+    if constexpr (N > 1) {
+      constexpr int half = N / 2;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        if constexpr (S >= 16) {
+          v[i] = swap_sum<S>(v[i], v[i + half]);
+        } else {
+          const bool upper = (lane & S) != 0;
+          const float send = upper ? v[i] : v[i + half];
+          const float keep = upper ? v[i + half] : v[i];
+          v[i] = pair_level<S>(keep, send);
+        }
+      }
+      rs_level<half, S / 2>(v, lane);
+    } else {
+      if constexpr (S >= 16) v[0] = swap_sum<S>(v[0], v[0]);
+      else v[0] = pair_level<S>(v[0], v[0]);
+      rs_level<1, S / 2>(v, lane);
+    }
+  }
+}
+// Reduce N partial values per lane across the 64 lanes of a wave, leaving
+// lane l with the total of value index (l >> (6 - log2 N)).  N is a power of
+// two <= 64.  Halving exchange: at each level (lane bit S = 32, 16, ..., 1)
+// a lane keeps the half of its values selected by its own bit S and adds the
+// partner's copy of that half; once one value is left the remaining levels
+// are a plain butterfly.  Partners differ in bit S and agree on the higher
+// bits: lane ^ 32 and lane ^ 16 through v_permlane32_swap / v_permlane16_swap,
+// then the mirror within 16 and within 8 lanes and the quad exchanges through
+// DPP, so no exchange goes through LDS.  Register indices are compile-time
+// constants.
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
+  rs_level<N, 32>(v, lane);
+  return v[0];
 }
 
 // ---------------------------------------------------------------- math

@@ -55,52 +55,55 @@ __device__ __forceinline__ float dot8bf(const uint4 &w, const uint4 &x, float c)
 
 // Token group of one work item (wave-uniform).  Assignment rows index A and
 // P: routed (position t, pick k) -> t * K + k, shared expert position t ->
-// T * K + t.
+// T * K + t.  A routed group is one record of the selection kernel's list:
+// [expert, positions, (row | position << 16) x kTokGroup, 0, 0].
 struct Group {
   const void *w;           // the expert's weights
   int ie;                  // its intermediate size
   int ng;                  // positions in the group, 1..kTokGroup
-  const int32_t *asg;      // routed: the group's assignment rows; shared: null
-  int base;                // shared: first position of the group
-  int TK;                  // T * K
-  int K;
-  // assignment row and block position of the group's t-th position
-  __device__ __forceinline__ int row(int t) const { return asg ? asg[t] : TK + base + t; }
-  __device__ __forceinline__ int pos(int t) const { return asg ? asg[t] / K : base + t; }
+  int p[kTokGroup];        // row | position << 16 of the group's positions
+  const int32_t *rec;      // routed: the record (for per-lane reads); shared: null
+  int TK;                  // T * K (shared rows start there)
+  __device__ __forceinline__ int row(int t) const { return p[t] & 0xffff; }
+  __device__ __forceinline__ int pos(int t) const { return p[t] >> 16; }
+  // row of position t where t differs between lanes
+  __device__ __forceinline__ int lane_row(int t) const { return rec ? rec[2 + t] & 0xffff : (p[0] & 0xffff) + t; }
 };
 
 // Resolves work item `item` of a list made of `s_items` shared-expert items
 // (ceil(T / kTokGroup) groups x tiles_s) followed by the routed groups of the
 // selection kernel (r.glist) x tiles.  Items of one group and different tiles
 // are `tiles` apart, so on a grid that is a multiple of 8 they run on one XCD
-// and a group's repeated weight reads stay in that XCD's L2.
+// and a group's repeated weight reads stay in that XCD's L2.  Only scalar
+// loads with no dependence between them, so the next item's record can be
+// fetched while the current item streams.
 __device__ __forceinline__ Group resolve(int item, int s_items, int tiles_s, int tiles, const RouteBufs &r,
                                          const void *w_routed, const void *w_shared, size_t expert_bytes,
                                          int I, int Is, int T, int K, int &tile) {
   Group g;
   g.TK = T * K;
-  g.K = K;
   if (item < s_items) {
     const int grp = item / tiles_s;
     tile = item - grp * tiles_s;
+    const int base = grp * kTokGroup;
     g.w = w_shared;
     g.ie = Is;
-    g.base = grp * kTokGroup;
-    g.ng = min(kTokGroup, T - g.base);
-    g.asg = nullptr;
+    g.ng = min(kTokGroup, T - base);
+#pragma unroll
+    for (int t = 0; t < kTokGroup; ++t) g.p[t] = (T * K + base + t) | ((base + t) << 16);
+    g.rec = nullptr;
   } else {
     const int j = item - s_items;
     const int gi = j / tiles;
     tile = j - gi * tiles;
-    const int v = uniform(r.glist[gi]);
-    const int u = v >> 8, g0 = v & 255;
-    const int e = uniform(r.union_list[u]);
-    const int n = uniform(r.slot_n[u]);
+    const int32_t *rec = r.glist + gi * 8;
+    const int e = uniform(rec[0]);
     g.w = static_cast<const char *>(w_routed) + (size_t)e * expert_bytes;
     g.ie = I;
-    g.base = 0;
-    g.ng = min(kTokGroup, n - g0);
-    g.asg = r.slot_asg + u * kMaxT + g0;
+    g.ng = uniform(rec[1]);
+#pragma unroll
+    for (int t = 0; t < kTokGroup; ++t) g.p[t] = uniform(rec[2 + t]);
+    g.rec = rec;
   }
   return g;
 }
@@ -146,7 +149,7 @@ __device__ __forceinline__ void gateup_group(const Group &g, const typename W::T
   // the lane's output: value index q = r * NT + t after the wave reduction
   constexpr int shift = 6 - log2i<8 * NT>();
   const int my_t = (lane >> shift) % NT;
-  const int my_row = my_t < g.ng ? g.row(my_t) : 0;
+  const int my_row = my_t < g.ng ? g.lane_row(my_t) : 0;
   float acc[8][NT];
 #pragma unroll
   for (int r = 0; r < 8; ++r)
@@ -191,8 +194,10 @@ __device__ __forceinline__ void gateup_group(const Group &g, const typename W::T
 #pragma unroll
     for (int t = 0; t < NT; ++t) v[r * NT + t] = acc[r][t];
   const float tot = reduce_scatter<8 * NT>(v, lane);
-  // q < 4 * NT: gate rows; lane ^ 32 holds the matching up row (q + 4 * NT)
-  const float up = __shfl_xor(tot, 32);
+  // q < 4 * NT: gate rows (lanes 0..31); lane + 32 holds the matching up row
+  // (q + 4 * NT), which the swap hands to the lower lanes as its second result
+  const float up = __uint_as_float(
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false)[1]);
   if ((lane & 32) == 0 && (lane & ((1 << shift) - 1)) == 0 && my_t < g.ng) {
     const int r = (lane >> shift) / NT;
     A[(size_t)my_row * Imax + i0 + r] = silu(tot) * up;
@@ -211,10 +216,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
   const int s_items = Is > 0 ? (T + kTokGroup - 1) / kTokGroup * tiles_s : 0;
   const int items = s_items + uniform(r.meta[2]) * tiles;
   const uint32_t x_bytes = (uint32_t)(T * H) * sizeof(WT);
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    int tile;
-    const Group g = resolve(item, s_items, tiles_s, tiles, r, wgu, wsgu, (size_t)2 * I * H * sizeof(WT),
-                            I, Is, T, K, tile);
+  const size_t eb = (size_t)2 * I * H * sizeof(WT);
+  int item = blockIdx.x, tile_next = 0;
+  Group next;
+  if (item < items) next = resolve(item, s_items, tiles_s, tiles, r, wgu, wsgu, eb, I, Is, T, K, tile_next);
+  for (; item < items; item += gridDim.x) {
+    const Group g = next;
+    const int tile = tile_next;
+    if (item + (int)gridDim.x < items)
+      next = resolve(item + gridDim.x, s_items, tiles_s, tiles, r, wgu, wsgu, eb, I, Is, T, K, tile_next);
     const int i0 = uniform(tile * 16 + wave * 4);
     if (g.ng <= 1)      gateup_group<W, 1>(g, xhat, x_bytes, H, Imax, i0, lane, A);
     else if (g.ng <= 2) gateup_group<W, 2>(g, xhat, x_bytes, H, Imax, i0, lane, A);
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
   }
 }
 
-constexpr int kDownRowsPerWave = 32;  // 128 rows per item
+constexpr int kDownRowsPerWave = 32;  // four batches of 8 rows (128 rows per item)
 constexpr int kDownSub = 2;           // positions per pass of the down projection
 
 template <int NX>
@@ -232,21 +242,23 @@ struct DnBufs {
 };
 
 // Down projection of positions [sub0, sub0 + NT) of a group for this wave's
-// rows h0 .. h0 + 31 of W_d [H][ie].  Lane l works on rows h0 + (l >> 4) + 4i
-// (i = 0..7) and, at step s, on chunk (l & 15) + 16 s of those rows: a load
-// instruction reads four 256-byte row segments, and a row's partial sums meet
-// in one 16-lane group, reduced once per item.  The fp32 activations meet
-// bf16 weights as a bf16 high part plus a bf16 residual (two dot passes).
-// P[row][h] = A_row . W_d[h] (the routing weight is applied by the combine).
-template <class W, int NT>
-__device__ __forceinline__ void down_group(const Group &g, int sub0, const float *__restrict__ A,
+// rows h0 + 8b + r (b = 0..3, r = 0..7) of W_d [H][ie]: lane l covers chunks
+// l, l + 64, ... of each row, so a load reads one contiguous 1 KiB row
+// segment.  With a single chunk per lane (ONCE: ie <= 64 chunks) the lane's
+// activation chunks are read and split once per pass, else with every step.
+// The fp32 activations meet bf16 weights as a bf16 high part plus a bf16
+// residual (two dot passes).  P[row][h] = A_row . W_d[h] (the routing weight
+// is applied by the combine).
+template <class W, int NT, int sub0, bool ONCE>
+__device__ __forceinline__ void down_group(const Group &g, const float *__restrict__ A,
                                            uint32_t a_bytes, int H, int Imax, int h0, int lane,
                                            float *__restrict__ P) {
   typedef typename W::T WT;
+  constexpr bool BF = std::is_same<W, WBf16>::value;
   constexpr int CH = W::kChunk;
   constexpr int NXP = CH / 4;  // 16-byte activation loads per position and chunk
-  const int NC = g.ie / CH, steps = (NC + 15) / 16;
-  const int lg = lane >> 4, lc = lane & 15;
+  const int NC = g.ie / CH, nq = ONCE ? 1 : (NC + 63) / 64;
+  const int nb = kDownRowsPerWave / 8;
   const int ngs = min(NT, g.ng - sub0);
   const uint32_t rowb = (uint32_t)g.ie * sizeof(WT);
   const rsrc_t rw = make_rsrc(g.w, (uint32_t)H * rowb);
@@ -255,69 +267,99 @@ __device__ __forceinline__ void down_group(const Group &g, int sub0, const float
 #pragma unroll
   for (int t = 0; t < NT; ++t)
     aoff[t] = t < ngs ? (uint32_t)uniform(g.row(sub0 + t)) * (uint32_t)Imax * 4u : kOutOfRange;
-  // after the 16-lane reduction lane l holds value q = i * NT + t
-  constexpr int shift = 4 - log2i<8 * NT>();
-  const int my_q = lc >> shift;
-  const int my_t = my_q % NT;
-  const int my_row = my_t < ngs ? g.row(sub0 + my_t) : 0;
-  float acc[8][NT];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[i][t] = 0.f;
-  auto load = [&](int s, DnBufs<NT * NXP> &b) {
-    const int c = lc + 16 * s;
-    const bool live = s < steps && c < NC;
-    const uint32_t vo = live ? (uint32_t)lg * rowb + (uint32_t)c * 16u : kOutOfRange;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b.w[i] = buf_ld16(rw, vo, (uint32_t)(h0 + 4 * i) * rowb);
+  constexpr int shift = 6 - log2i<8 * NT>();
+  const int my_t = (lane >> shift) % NT;
+  const int my_row = my_t < ngs ? g.lane_row(sub0 + my_t) : 0;
+  auto load_act = [&](int c, bool live, uint4 *x) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int j = 0; j < NXP; ++j)
-        b.x[t * NXP + j] = buf_ld16(ra, live ? aoff[t] + (uint32_t)(c * CH * 4 + 16 * j) : kOutOfRange, 0);
+        x[t * NXP + j] = buf_ld16(ra, live ? aoff[t] + (uint32_t)(c * CH * 4 + 16 * j) : kOutOfRange, 0);
   };
-  auto step = [&](int, const DnBufs<NT * NXP> &b) {
-    if constexpr (std::is_same<W, WBf16>::value) {
+  // activation operands of one chunk: bf16 weights take (high, residual)
+  // pairs, fp32 weights the fp32 values
+  uint4 xop[NT][2];
+  auto prep = [&](const uint4 *x) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        float x[8];
-        x[0] = __uint_as_float(b.x[2 * t].x); x[1] = __uint_as_float(b.x[2 * t].y);
-        x[2] = __uint_as_float(b.x[2 * t].z); x[3] = __uint_as_float(b.x[2 * t].w);
-        x[4] = __uint_as_float(b.x[2 * t + 1].x); x[5] = __uint_as_float(b.x[2 * t + 1].y);
-        x[6] = __uint_as_float(b.x[2 * t + 1].z); x[7] = __uint_as_float(b.x[2 * t + 1].w);
-        uint4 hi, lo;
-        split_hi_lo(x, hi, lo);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i][t] = dot8bf(b.w[i], lo, dot8bf(b.w[i], hi, acc[i][t]));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float wf[4];
-        chunk_to_f32<W>(b.w[i], wf);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          float xf[4];
-          chunk_to_f32<W>(b.x[t], xf);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][t] = fmaf(wf[j], xf[j], acc[i][t]);
-        }
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (BF) {
+        float f[8];
+        f[0] = __uint_as_float(x[2 * t].x); f[1] = __uint_as_float(x[2 * t].y);
+        f[2] = __uint_as_float(x[2 * t].z); f[3] = __uint_as_float(x[2 * t].w);
+        f[4] = __uint_as_float(x[2 * t + 1].x); f[5] = __uint_as_float(x[2 * t + 1].y);
+        f[6] = __uint_as_float(x[2 * t + 1].z); f[7] = __uint_as_float(x[2 * t + 1].w);
+        split_hi_lo(f, xop[t][0], xop[t][1]);
+      } else {
+        xop[t][0] = x[t];
       }
     }
   };
-  DnBufs<NT * NXP> b0, b1;
-  pipeline(steps, b0, b1, load, step);
-  float v[8 * NT];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[i * NT + t] = acc[i][t];
-  reduce_scatter_step<8 * NT, 8>(v, lane);
-  if ((lc & ((1 << shift) - 1)) == 0 && my_t < ngs) {
-    const int i = my_q / NT;
-    P[(size_t)my_row * H + h0 + lg + 4 * i] = v[0];
+  if constexpr (ONCE) {
+    uint4 x[NT * NXP];
+    load_act(lane, lane < NC, x);
+    prep(x);
   }
+  float acc[8][NT];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
+  constexpr int NX = ONCE ? 1 : NT * NXP;
+  auto load = [&](int s, DnBufs<NX> &b) {
+    const int bb = s / nq, q = s - bb * nq;
+    const int c = lane + 64 * q;
+    const bool live = bb < nb && c < NC;
+    const uint32_t vo = live ? (uint32_t)c * 16u : kOutOfRange;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) b.w[r] = buf_ld16(rw, vo, (uint32_t)(h0 + 8 * min(bb, nb - 1) + r) * rowb);
+    if constexpr (!ONCE) load_act(c, live, b.x);
+  };
+  auto step = [&](int s, const DnBufs<NX> &b) {
+    if constexpr (!ONCE) prep(b.x);
+    if constexpr (BF) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[r][t] = dot8bf(b.w[r], xop[t][1], dot8bf(b.w[r], xop[t][0], acc[r][t]));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float wf[4];
+        chunk_to_f32<W>(b.w[r], wf);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float xf[4];
+          chunk_to_f32<W>(xop[t][0], xf);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r][t] = fmaf(wf[j], xf[j], acc[r][t]);
+        }
+      }
+    }
+    const int bb = s / nq;
+    if (s - bb * nq == nq - 1) {
+      float v[8 * NT];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) { v[r * NT + t] = acc[r][t]; acc[r][t] = 0.f; }
+      const float tot = reduce_scatter<8 * NT>(v, lane);
+      if ((lane & ((1 << shift) - 1)) == 0 && my_t < ngs) {
+        const int r = (lane >> shift) / NT;
+        P[(size_t)my_row * H + h0 + 8 * bb + r] = tot;
+      }
+    }
+  };
+  DnBufs<NX> b0, b1;
+  pipeline(nb * nq, b0, b1, load, step);
+}
+
+template <class W, int sub0, bool ONCE>
+__device__ __forceinline__ void down_pass(const Group &g, const float *__restrict__ A, uint32_t a_bytes, int H,
+                                          int Imax, int h0, int lane, float *__restrict__ P) {
+  if (g.ng - sub0 <= 1) down_group<W, 1, sub0, ONCE>(g, A, a_bytes, H, Imax, h0, lane, P);
+  else                  down_group<W, kDownSub, sub0, ONCE>(g, A, a_bytes, H, Imax, h0, lane, P);
 }
 
 template <class W>
@@ -332,14 +374,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
   const int s_items = Is > 0 ? (T + kTokGroup - 1) / kTokGroup * tiles : 0;
   const int items = s_items + uniform(r.meta[2]) * tiles;
   const uint32_t a_bytes = (uint32_t)(T * K + T) * (uint32_t)Imax * 4u;
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    int tile;
-    const Group g = resolve(item, s_items, tiles, tiles, r, wd, wsd, (size_t)H * I * sizeof(WT), I, Is,
-                            T, K, tile);
+  const size_t eb = (size_t)H * I * sizeof(WT);
+  int item = blockIdx.x, tile_next = 0;
+  Group next;
+  if (item < items) next = resolve(item, s_items, tiles, tiles, r, wd, wsd, eb, I, Is, T, K, tile_next);
+  for (; item < items; item += gridDim.x) {
+    const Group g = next;
+    const int tile = tile_next;
+    if (item + (int)gridDim.x < items)
+      next = resolve(item + gridDim.x, s_items, tiles, tiles, r, wd, wsd, eb, I, Is, T, K, tile_next);
     const int h0 = uniform(tile * 4 * kDownRowsPerWave + wave * kDownRowsPerWave);
-    for (int sub0 = 0; sub0 < g.ng; sub0 += kDownSub) {
-      if (g.ng - sub0 <= 1) down_group<W, 1>(g, sub0, A, a_bytes, H, Imax, h0, lane, P);
-      else                  down_group<W, kDownSub>(g, sub0, A, a_bytes, H, Imax, h0, lane, P);
+    // passes of kDownSub positions (group rows are picked with constant indices)
+    static_assert(kTokGroup == 2 * kDownSub, "two down passes per token group");
+    if (g.ie <= 64 * W::kChunk) {
+      down_pass<W, 0, true>(g, A, a_bytes, H, Imax, h0, lane, P);
+      if (g.ng > kDownSub) down_pass<W, kDownSub, true>(g, A, a_bytes, H, Imax, h0, lane, P);
+    } else {
+      down_pass<W, 0, false>(g, A, a_bytes, H, Imax, h0, lane, P);
+      if (g.ng > kDownSub) down_pass<W, kDownSub, false>(g, A, a_bytes, H, Imax, h0, lane, P);
     }
   }
 }

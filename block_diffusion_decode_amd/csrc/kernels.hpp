@@ -16,9 +16,7 @@ struct RouteBufs {
   float *wgt;          // [T][K]   their renormalised weights
   int32_t *meta;       // [0] union size, [1] coreset size, [2] token groups
   int32_t *union_list; // [E]      union experts, ascending id
-  int32_t *slot_n;     // [E]      positions routed to each union expert
-  int32_t *slot_asg;   // [E][kMaxT] assignment ids t*K+k, ascending t
-  int32_t *glist;      // [expert_groups_max] token groups: union slot << 8 | first assignment
+  int32_t *glist;      // [expert_groups_max][8] token-group records (see the expert kernels)
   uint32_t *cs_bits;   // [8]      coreset membership bitset
   float *mass;         // [E]      block expert mass
   int32_t *n_distinct_out;    // [1] union size copy (may be null)

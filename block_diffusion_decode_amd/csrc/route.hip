@@ -439,20 +439,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   }
   const int slot = union_scan(sh, E);
   const uint32_t tbits = slot >= 0 ? sh.tokmask[tid] : 0u;
-  if (slot >= 0) {
-    uint32_t bits = tbits;
-    r.union_list[slot] = tid;
-    r.slot_n[slot] = __popc(bits);
-    int j = 0;
-    while (bits) {
-      const int tt = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      r.slot_asg[slot * kMaxT + j++] = tt * K + sh.kslot[tt][tid];
-    }
-  }
+  if (slot >= 0) r.union_list[slot] = tid;
   // token groups of kTokGroup positions, in union order (exclusive scan of
-  // each union expert's group count)
-  const int ngr = (__popc(tbits) + kTokGroup - 1) / kTokGroup;
+  // each union expert's group count), one 8-word record each:
+  // [expert, positions, (t*K + k) | t << 16 per position, 0 ...]
+  const int npos = __popc(tbits);
+  const int ngr = (npos + kTokGroup - 1) / kTokGroup;
   int incl = ngr;
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) {
@@ -466,7 +458,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
     if (w < wave) goff += sh.wtot[w];
     gtot += sh.wtot[w];
   }
-  for (int j = 0; j < ngr; ++j) r.glist[goff + j] = (slot << 8) | (j * kTokGroup);
+  {
+    uint32_t bits = tbits;
+    int j = 0;
+    while (bits) {
+      const int tt = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      int32_t *rec = r.glist + (goff + j / kTokGroup) * 8;
+      if (j % kTokGroup == 0) {
+        rec[0] = tid;
+        rec[1] = min(kTokGroup, npos - j);
+        for (int q = 2 + min(kTokGroup, npos - j); q < 8; ++q) rec[q] = 0;
+      }
+      rec[2 + j % kTokGroup] = (tt * K + sh.kslot[tt][tid]) | (tt << 16);
+      ++j;
+    }
+  }
   if (tid == 0) {
     r.meta[2] = gtot;
     r.meta[0] = sh.nu;
