@@ -8,18 +8,24 @@ routing, no coreset), the final RMSNorm, the LM head over a 248320-token
 vocabulary with the fused softmax-confidence/argmax, and the LowConfidence
 commit.  Inputs are seeded synthetic tensors, resident in HBM before timing.
 
-Prints one JSON line: microseconds per round (K replays of the round's HIP
-graph, timed with events at the ends of the region), achieved HBM bandwidth
-on the round's algorithmic bytes, the roofline of the dominant kernel (its
-launches bracketed by hipEvents on their stream over K further rounds), and
+Prints one JSON line: microseconds per round (K calls of
+bdd_block_denoise_round on one stream, timed with events at the ends of the
+region; the same K rounds replayed as HIP graphs are reported beside it),
+achieved HBM bandwidth on the round's algorithmic bytes, the roofline of the
+dominant kernel (its launches bracketed by hipEvents on their stream over K
+further rounds; HBM traffic from the rocprofv3 counter summary under
+profiles/ while the kernel's sources are unchanged since it was taken), and
 the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration MIB   # plain device copy, for counter scaling
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,6 +51,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (counter scaling)")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="only run 3 rounds on inputs drawn with torch.randn (a handful of kernel launches "
+                         "besides the library's), for hardware-counter collection")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -59,7 +70,23 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # a streaming copy kernel of known size (negation: one fp32 read and
+        # one fp32 write per element) whose counter readings scale the
+        # hardware counters to bytes
+        n = args.copy_calibration << 20
+        a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+        return
     d = W.C1
+    if args.counter_run:
+        counter_run(d, dev)
+        return
     R = 8
     log(f"[bench] generating inputs (seed {args.seed})")
     x, info = W.planted_round_inputs(args.seed, d, rounds=R, p=0.3, amp_pass=24.0, amp_fail=(10.0, 14.0))
@@ -113,11 +140,12 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / args.steps, time.perf_counter() - t0
 
-    # timed region: K graph replays, events only at its two ends
-    ms, wall = timed(lambda i: graphs[i % R].launch())
-    log(f"[bench] {args.steps} rounds (graph): {ms * 1e3:.1f} us/round (wall {wall * 1e3 / args.steps:.1f} us/round)")
-    ms_eager, _ = timed(lambda i: plan(x[i % R], tok, conf, choice, ri))
-    log(f"[bench] {args.steps} rounds (eager): {ms_eager * 1e3:.1f} us/round")
+    # timed region: K rounds through the C ABI, events only at its two ends;
+    # then the same K rounds as graph replays
+    ms, wall = timed(lambda i: plan(x[i % R], tok, conf, choice, ri))
+    log(f"[bench] {args.steps} rounds: {ms * 1e3:.1f} us/round (host wall {wall * 1e3 / args.steps:.1f} us/round)")
+    ms_graph, _ = timed(lambda i: graphs[i % R].launch())
+    log(f"[bench] {args.steps} rounds (graph replays): {ms_graph * 1e3:.1f} us/round")
 
     # dominant kernel: K more rounds with its launches bracketed by hipEvents
     # on the stream it runs on
@@ -138,9 +166,11 @@ def main():
                  "expert_gateup": (mean_u * d.I + d.I_s) * 2 * d.H * 2,
                  "expert_down": (mean_u * d.I + d.I_s) * d.H * 2}.get(dominant)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_bytes else None
+    traffic, traffic_src = measured_traffic(dominant)
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS if achieved else None,
-                "traffic": None, "avg_us": dom_ms * 1e3, "algorithmic_bytes": dom_bytes}
+                "traffic": traffic, "avg_us": dom_ms * 1e3, "algorithmic_bytes": dom_bytes,
+                "launches_timed": dom[dominant][1], "traffic_source": traffic_src}
 
     out = {
         "metric": METRIC,
@@ -156,8 +186,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded counter-based inputs, random-init weights of the Clover shape",
         "config": {"workload": WORKLOAD, "global_batch": T, "seq_len": T, "parallelism": "single GPU",
-                   "launch": "HIP graph per round (bdd_round_graph)", "distinct_experts_mean": mean_u},
-        "us_per_round_eager": round(ms_eager * 1e3, 2),
+                   "launch": "bdd_block_denoise_round per round on one stream",
+                   "distinct_experts_mean": mean_u},
+        "us_per_round_graph": round(ms_graph * 1e3, 2),
         "round_bytes": round_bytes,
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
@@ -168,6 +199,71 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, d, x, layer, w_lm, info, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def counter_run(d, dev):
+    """Three rounds of the benchmark's shape on torch.randn inputs.  The bytes
+    each kernel moves do not depend on the values beyond the routing (the LM
+    head streams its whole weight either way), and the seeded counter
+    generator's thousands of small launches stay out of the profiled process."""
+    import torch
+
+    import block_diffusion_decode_amd as bdd
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bf = torch.bfloat16
+
+    def rnd(shape, std):
+        return (torch.randn(shape, generator=g, device=dev) * std).to(bf)
+
+    layer = {"w_router": rnd((d.E, d.H), d.w_std), "router_bias": torch.zeros(d.E, device=dev),
+             "w_gate_up": rnd((d.E, 2 * d.I, d.H), d.w_std), "w_down": rnd((d.E, d.H, d.I), d.w_std),
+             "ws_gate_up": rnd((2 * d.I_s, d.H), d.w_std), "ws_down": rnd((d.H, d.I_s), d.w_std)}
+    lm = bdd.pack_lm_head(rnd((d.V, d.H), d.lm_std))
+    plan = bdd.RoundPlan(bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16), [layer], lm, 1.0, 0.95)
+    x = torch.randn((d.T, d.H), generator=g, device=dev)
+    tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=dev)
+    conf = torch.empty(d.T, dtype=torch.float32, device=dev)
+    choice = torch.empty(d.T, dtype=torch.int32, device=dev)
+    ri = torch.empty(4, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        plan(x, tok, conf, choice, ri)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run_rounds": 3}), flush=True)
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "lmhead_clover_v248320_hbm_counters.md")
+KERNEL_SOURCES = {"lmhead": ["lmhead.hip", "common.hpp", "kernels.hpp"]}
+
+
+def kernel_sha(kernel):
+    """sha256 over the sources that define `kernel` (None if unknown)."""
+    files = KERNEL_SOURCES.get(kernel)
+    if not files:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "block_diffusion_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the kernel's current sources; else (None, reason)."""
+    sha = kernel_sha(kernel)
+    if sha is None or not os.path.exists(COUNTERS):
+        return None, "no counter summary for this kernel"
+    text = open(COUNTERS).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_k = re.search(r"kernel:\s*(\w+)", text)
+    if not (m_sha and m_b and m_k) or m_k.group(1) != kernel:
+        return None, "counter summary unreadable"
+    if m_sha.group(1) != sha:
+        return None, "kernel changed since the counters were taken"
+    return float(m_b.group(1)), os.path.relpath(COUNTERS, ROOT)
 
 
 def cpu_baseline(args, d, x, layer, w_lm, info, budget_s):

@@ -362,7 +362,7 @@ bdd_status bdd_lmhead_confidence_commit(const void *hhat, const void *w_lm, int3
   if ((st = check_ws(ws, ws_bytes, p.end)) != BDD_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int cus = device_cus();
-  const int grid = lmhead_grid(cus) < kMaxLmGrid ? lmhead_grid(cus) : kMaxLmGrid;
+  const int grid = lmhead_grid(cus, V) < kMaxLmGrid ? lmhead_grid(cus, V) : kMaxLmGrid;
   float *pm = at<float>(ws, p.m), *ps = at<float>(ws, p.s);
   int32_t *pi = at<int32_t>(ws, p.i);
   LAUNCH("lmhead", s, launch_lmhead(dtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, nullptr, s));
@@ -420,7 +420,7 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
       return st;
   }
   const int cus = device_cus();
-  const int grid = lmhead_grid(cus) < kMaxLmGrid ? lmhead_grid(cus) : kMaxLmGrid;
+  const int grid = lmhead_grid(cus, V) < kMaxLmGrid ? lmhead_grid(cus, V) : kMaxLmGrid;
   float *pm = at<float>(ws, lp.m), *ps = at<float>(ws, lp.s);
   int32_t *pi = at<int32_t>(ws, lp.i);
   const LmCommit fused = {count, threshold, tokens, conf, choice, round_info};

@@ -53,58 +53,39 @@ __device__ __forceinline__ float dot8bf(const uint4 &w, const uint4 &x, float c)
   return dot2bf(w.w, x.w, c);
 }
 
-// Token group of one work item (wave-uniform).  Assignment rows index A and
-// P: routed (position t, pick k) -> t * K + k, shared expert position t ->
-// T * K + t.  A routed group is one record of the selection kernel's list:
-// [expert, positions, (row | position << 16) x kTokGroup, 0, 0].
+// Routed token group of one work item (wave-uniform): one record of the
+// selection kernel's list, [expert, positions, (row | position << 16) x
+// kTokGroup, 0, 0], where the row of (position t, pick k) in A and P is
+// t * K + k.
 struct Group {
   const void *w;           // the expert's weights
   int ie;                  // its intermediate size
   int ng;                  // positions in the group, 1..kTokGroup
   int p[kTokGroup];        // row | position << 16 of the group's positions
-  const int32_t *rec;      // routed: the record (for per-lane reads); shared: null
-  int TK;                  // T * K (shared rows start there)
+  const int32_t *rec;      // the record (for per-lane reads)
   __device__ __forceinline__ int row(int t) const { return p[t] & 0xffff; }
   __device__ __forceinline__ int pos(int t) const { return p[t] >> 16; }
   // row of position t where t differs between lanes
-  __device__ __forceinline__ int lane_row(int t) const { return rec ? rec[2 + t] & 0xffff : (p[0] & 0xffff) + t; }
+  __device__ __forceinline__ int lane_row(int t) const { return rec[2 + t] & 0xffff; }
 };
 
-// Resolves work item `item` of a list made of `s_items` shared-expert items
-// (ceil(T / kTokGroup) groups x tiles_s) followed by the routed groups of the
-// selection kernel (r.glist) x tiles.  Items of one group and different tiles
-// are `tiles` apart, so on a grid that is a multiple of 8 they run on one XCD
-// and a group's repeated weight reads stay in that XCD's L2.  Only scalar
-// loads with no dependence between them, so the next item's record can be
-// fetched while the current item streams.
-__device__ __forceinline__ Group resolve(int item, int s_items, int tiles_s, int tiles, const RouteBufs &r,
-                                         const void *w_routed, const void *w_shared, size_t expert_bytes,
-                                         int I, int Is, int T, int K, int &tile) {
+// Resolves routed item j = group * tiles + tile.  Items of one group and
+// different tiles are `tiles` apart, so on a grid that is a multiple of 8
+// they run on one XCD.  Only scalar loads with no dependence between them, so
+// the next item's record can be fetched while the current item streams.
+__device__ __forceinline__ Group resolve(int j, int tiles, const RouteBufs &r, const void *w_routed,
+                                         size_t expert_bytes, int I, int &tile) {
   Group g;
-  g.TK = T * K;
-  if (item < s_items) {
-    const int grp = item / tiles_s;
-    tile = item - grp * tiles_s;
-    const int base = grp * kTokGroup;
-    g.w = w_shared;
-    g.ie = Is;
-    g.ng = min(kTokGroup, T - base);
+  const int gi = j / tiles;
+  tile = j - gi * tiles;
+  const int32_t *rec = r.glist + gi * 8;
+  const int e = uniform(rec[0]);
+  g.w = static_cast<const char *>(w_routed) + (size_t)e * expert_bytes;
+  g.ie = I;
+  g.ng = uniform(rec[1]);
 #pragma unroll
-    for (int t = 0; t < kTokGroup; ++t) g.p[t] = (T * K + base + t) | ((base + t) << 16);
-    g.rec = nullptr;
-  } else {
-    const int j = item - s_items;
-    const int gi = j / tiles;
-    tile = j - gi * tiles;
-    const int32_t *rec = r.glist + gi * 8;
-    const int e = uniform(rec[0]);
-    g.w = static_cast<const char *>(w_routed) + (size_t)e * expert_bytes;
-    g.ie = I;
-    g.ng = uniform(rec[1]);
-#pragma unroll
-    for (int t = 0; t < kTokGroup; ++t) g.p[t] = uniform(rec[2 + t]);
-    g.rec = rec;
-  }
+  for (int t = 0; t < kTokGroup; ++t) g.p[t] = uniform(rec[2 + t]);
+  g.rec = rec;
   return g;
 }
 
@@ -204,6 +185,182 @@ __device__ __forceinline__ void gateup_group(const Group &g, const typename W::T
   }
 }
 
+// ---------------------------------------------------------------------------
+// Shared expert, MFMA.  Every position goes through it, so its contraction is
+// dense: 16x16 tiles with 16 weight rows as A and 16 positions as B (two
+// column tiles for 32 positions), in one pass over its weights.  At k-step s
+// lane group g = lane >> 4 holds chunk 4s + g of its row, so a load reads 64
+// contiguous bytes of each of 16 rows.
+// ---------------------------------------------------------------------------
+
+template <class W>
+__device__ __forceinline__ f32x4 mfma_chunk(const uint4 &a, const uint4 &b, f32x4 c) {
+  if constexpr (std::is_same<W, WBf16>::value) {
+    return mfma_bf16(a, b, c);
+  } else {
+    c = mfma_f32(__uint_as_float(a.x), __uint_as_float(b.x), c);
+    c = mfma_f32(__uint_as_float(a.y), __uint_as_float(b.y), c);
+    c = mfma_f32(__uint_as_float(a.z), __uint_as_float(b.z), c);
+    return mfma_f32(__uint_as_float(a.w), __uint_as_float(b.w), c);
+  }
+}
+
+struct SgBufs {
+  uint4 a[2][2];   // [k-step][gate, up]
+  uint4 b[2][2];   // [k-step][column tile]
+};
+
+// Gate/up rows i0 .. i0 + 15 (and Is + i0 ..) of the shared expert for every
+// position; the four waves split the hidden dimension and add their partial
+// tiles through LDS (`red`, 16 KiB).  A[T*K + t][i] = silu(gate) * up.
+template <class W>
+__device__ __forceinline__ void shared_gateup_item(const typename W::T *__restrict__ wsgu,
+                                                   const typename W::T *__restrict__ xhat, int T, int H, int Is,
+                                                   int TK, int Imax, int i0, int wave, int lane,
+                                                   float *__restrict__ A, f32x4 *red) {
+  typedef typename W::T WT;
+  constexpr int CH = W::kChunk;
+  const int li = lane & 15, g = lane >> 4;
+  const int ncw = H / CH / 4;               // chunks of this wave's quarter of H
+  const int cw0 = wave * ncw;
+  const int ksteps = (ncw + 3) / 4;
+  const rsrc_t rw = make_rsrc(wsgu, (uint32_t)(2 * Is * H) * sizeof(WT));
+  const rsrc_t rx = make_rsrc(xhat, (uint32_t)(T * H) * sizeof(WT));
+  const uint32_t rowg = (uint32_t)((i0 + li) * H) * sizeof(WT);
+  const uint32_t rowu = (uint32_t)((Is + i0 + li) * H) * sizeof(WT);
+  uint32_t rowx[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+    rowx[n] = n * 16 + li < T ? (uint32_t)((n * 16 + li) * H) * sizeof(WT) : kOutOfRange;
+  f32x4 acc[2][2];   // [gate, up][column tile]
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int bt, SgBufs &b) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ks = 2 * bt + j;
+      const int c = 4 * ks + g;
+      const bool live = ks < ksteps && c < ncw;
+      const uint32_t co = (uint32_t)((cw0 + c) * CH) * sizeof(WT);
+      b.a[j][0] = buf_ld16(rw, live ? rowg + co : kOutOfRange, 0);
+      b.a[j][1] = buf_ld16(rw, live ? rowu + co : kOutOfRange, 0);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) b.b[j][n] = buf_ld16(rx, live ? rowx[n] + co : kOutOfRange, 0);
+    }
+  };
+  auto step = [&](int, const SgBufs &b) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[q][n] = mfma_chunk<W>(b.a[j][q], b.b[j][n], acc[q][n]);
+  };
+  SgBufs b0, b1;
+  pipeline((ksteps + 1) / 2, b0, b1, load, step);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) red[((wave * 2 + q) * 2 + n) * 64 + lane] = acc[q][n];
+  __syncthreads();
+  if (wave < 2) {
+    // wave n finishes column tile n: rows i0 + 4g + r, position 16n + li
+    const int n = wave;
+    f32x4 gt = red[n * 64 + lane], up = red[(2 + n) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const f32x4 a = red[((w * 2 + 0) * 2 + n) * 64 + lane], b = red[((w * 2 + 1) * 2 + n) * 64 + lane];
+      gt += a;
+      up += b;
+    }
+    const int t = n * 16 + li;
+    if (t < T) {
+      float4 o;
+      o.x = silu(gt[0]) * up[0]; o.y = silu(gt[1]) * up[1];
+      o.z = silu(gt[2]) * up[2]; o.w = silu(gt[3]) * up[3];
+      *reinterpret_cast<float4 *>(A + (size_t)(TK + t) * Imax + i0 + 4 * g) = o;
+    }
+  }
+  __syncthreads();  // `red` is free for the next item
+}
+
+template <int NX>
+struct SdBufs {
+  uint4 a[2];      // [row tile]
+  uint4 x[2][NX];  // [column tile][16-byte part]
+};
+
+// Down projection of the shared expert for this wave's rows h0 .. h0 + 31 (two
+// row tiles) and every position.  fp32 activations meet bf16 weights as a
+// bf16 high part plus a bf16 residual.  P[T*K + t][h].
+template <class W>
+__device__ __forceinline__ void shared_down_item(const typename W::T *__restrict__ wsd,
+                                                 const float *__restrict__ A, int T, int H, int Is, int TK,
+                                                 int Imax, int h0, int lane, float *__restrict__ P) {
+  typedef typename W::T WT;
+  constexpr bool BF = std::is_same<W, WBf16>::value;
+  constexpr int CH = W::kChunk;
+  constexpr int NXP = CH / 4;
+  const int li = lane & 15, g = lane >> 4;
+  const int NC = Is / CH, ksteps = (NC + 3) / 4;
+  const rsrc_t rw = make_rsrc(wsd, (uint32_t)(H * Is) * sizeof(WT));
+  const rsrc_t ra = make_rsrc(A + (size_t)TK * Imax, (uint32_t)(T * Imax) * 4u);
+  uint32_t rowa[2], rowx[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) rowa[m] = (uint32_t)((h0 + 16 * m + li) * Is) * sizeof(WT);
+#pragma unroll
+  for (int n = 0; n < 2; ++n) rowx[n] = n * 16 + li < T ? (uint32_t)((n * 16 + li) * Imax) * 4u : kOutOfRange;
+  f32x4 acc[2][2];   // [row tile][column tile]
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int ks, SdBufs<NXP> &b) {
+    const int c = 4 * ks + g;
+    const bool live = ks < ksteps && c < NC;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      b.a[m] = buf_ld16(rw, live ? rowa[m] + (uint32_t)(c * CH) * sizeof(WT) : kOutOfRange, 0);
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int q = 0; q < NXP; ++q)
+        b.x[n][q] = buf_ld16(ra, live ? rowx[n] + (uint32_t)(c * CH * 4 + 16 * q) : kOutOfRange, 0);
+  };
+  auto step = [&](int, const SdBufs<NXP> &b) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      if constexpr (BF) {
+        float f[8];
+        f[0] = __uint_as_float(b.x[n][0].x); f[1] = __uint_as_float(b.x[n][0].y);
+        f[2] = __uint_as_float(b.x[n][0].z); f[3] = __uint_as_float(b.x[n][0].w);
+        f[4] = __uint_as_float(b.x[n][1].x); f[5] = __uint_as_float(b.x[n][1].y);
+        f[6] = __uint_as_float(b.x[n][1].z); f[7] = __uint_as_float(b.x[n][1].w);
+        uint4 hi, lo;
+        split_hi_lo(f, hi, lo);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[m][n] = mfma_bf16(b.a[m], lo, mfma_bf16(b.a[m], hi, acc[m][n]));
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[m][n] = mfma_chunk<W>(b.a[m], b.x[n][0], acc[m][n]);
+      }
+    }
+  };
+  SdBufs<NXP> b0, b1;
+  pipeline(ksteps, b0, b1, load, step);
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int t = n * 16 + li;
+    if (t < T)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        *reinterpret_cast<float4 *>(P + (size_t)(TK + t) * H + h0 + 16 * m + 4 * g) =
+            make_float4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
+  }
+}
+
 template <class W>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void expert_gateup_kernel(const typename W::T *__restrict__ xhat,
                                                             const typename W::T *__restrict__ wgu,
@@ -212,19 +369,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
                                                             int H, int K, int I, int Is, int Imax) {
   typedef typename W::T WT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tiles_s = Is / 16, tiles = I / 16;
-  const int s_items = Is > 0 ? (T + kTokGroup - 1) / kTokGroup * tiles_s : 0;
+  const int tiles = I / 16;
+  const int s_items = Is / 16;   // shared expert: one item per 16 intermediate units
   const int items = s_items + uniform(r.meta[2]) * tiles;
   const uint32_t x_bytes = (uint32_t)(T * H) * sizeof(WT);
   const size_t eb = (size_t)2 * I * H * sizeof(WT);
+  __shared__ f32x4 red[4 * 2 * 2 * 64];
+  const int stride = gridDim.x;
   int item = blockIdx.x, tile_next = 0;
   Group next;
-  if (item < items) next = resolve(item, s_items, tiles_s, tiles, r, wgu, wsgu, eb, I, Is, T, K, tile_next);
-  for (; item < items; item += gridDim.x) {
+  if (item < items && item >= s_items) next = resolve(item - s_items, tiles, r, wgu, eb, I, tile_next);
+  for (; item < items; item += stride) {
+    const int nitem = item + stride;
+    if (item < s_items) {
+      if (nitem < items && nitem >= s_items) next = resolve(nitem - s_items, tiles, r, wgu, eb, I, tile_next);
+      shared_gateup_item<W>(wsgu, xhat, T, H, Is, T * K, Imax, item * 16, wave, lane, A, red);
+      continue;
+    }
     const Group g = next;
     const int tile = tile_next;
-    if (item + (int)gridDim.x < items)
-      next = resolve(item + gridDim.x, s_items, tiles_s, tiles, r, wgu, wsgu, eb, I, Is, T, K, tile_next);
+    if (nitem < items) next = resolve(nitem - s_items, tiles, r, wgu, eb, I, tile_next);
     const int i0 = uniform(tile * 16 + wave * 4);
     if (g.ng <= 1)      gateup_group<W, 1>(g, xhat, x_bytes, H, Imax, i0, lane, A);
     else if (g.ng <= 2) gateup_group<W, 2>(g, xhat, x_bytes, H, Imax, i0, lane, A);
@@ -233,7 +397,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
 }
 
 constexpr int kDownRowsPerWave = 32;  // four batches of 8 rows (128 rows per item)
-constexpr int kDownSub = 2;           // positions per pass of the down projection
+constexpr int kDownSub = 2;           // positions per pass when activations reload per step
 
 template <int NX>
 struct DnBufs {
@@ -371,25 +535,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
   typedef typename W::T WT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tiles = H / (4 * kDownRowsPerWave);
-  const int s_items = Is > 0 ? (T + kTokGroup - 1) / kTokGroup * tiles : 0;
+  const int s_items = Is > 0 ? tiles : 0;   // shared expert: every position in one pass
   const int items = s_items + uniform(r.meta[2]) * tiles;
   const uint32_t a_bytes = (uint32_t)(T * K + T) * (uint32_t)Imax * 4u;
   const size_t eb = (size_t)H * I * sizeof(WT);
+  const int stride = gridDim.x;
   int item = blockIdx.x, tile_next = 0;
   Group next;
-  if (item < items) next = resolve(item, s_items, tiles, tiles, r, wd, wsd, eb, I, Is, T, K, tile_next);
-  for (; item < items; item += gridDim.x) {
+  if (item < items && item >= s_items) next = resolve(item - s_items, tiles, r, wd, eb, I, tile_next);
+  for (; item < items; item += stride) {
+    const int nitem = item + stride;
+    if (item < s_items) {
+      if (nitem < items && nitem >= s_items) next = resolve(nitem - s_items, tiles, r, wd, eb, I, tile_next);
+      const int h0 = uniform(item * 4 * kDownRowsPerWave + wave * kDownRowsPerWave);
+      shared_down_item<W>(wsd, A, T, H, Is, T * K, Imax, h0, lane, P);
+      continue;
+    }
     const Group g = next;
     const int tile = tile_next;
-    if (item + (int)gridDim.x < items)
-      next = resolve(item + gridDim.x, s_items, tiles, tiles, r, wd, wsd, eb, I, Is, T, K, tile_next);
+    if (nitem < items) next = resolve(nitem - s_items, tiles, r, wd, eb, I, tile_next);
     const int h0 = uniform(tile * 4 * kDownRowsPerWave + wave * kDownRowsPerWave);
-    // passes of kDownSub positions (group rows are picked with constant indices)
-    static_assert(kTokGroup == 2 * kDownSub, "two down passes per token group");
     if (g.ie <= 64 * W::kChunk) {
-      down_pass<W, 0, true>(g, A, a_bytes, H, Imax, h0, lane, P);
-      if (g.ng > kDownSub) down_pass<W, kDownSub, true>(g, A, a_bytes, H, Imax, h0, lane, P);
+      // one pass over the whole group: the activations sit in registers
+      static_assert(kTokGroup == 4, "token groups of at most 4 positions");
+      if (g.ng <= 1)      down_group<W, 1, 0, true>(g, A, a_bytes, H, Imax, h0, lane, P);
+      else if (g.ng <= 2) down_group<W, 2, 0, true>(g, A, a_bytes, H, Imax, h0, lane, P);
+      else                down_group<W, 4, 0, true>(g, A, a_bytes, H, Imax, h0, lane, P);
     } else {
+      // passes of kDownSub positions (group rows are picked with constant indices)
+      static_assert(kTokGroup == 2 * kDownSub, "two down passes per token group");
       down_pass<W, 0, false>(g, A, a_bytes, H, Imax, h0, lane, P);
       if (g.ng > kDownSub) down_pass<W, kDownSub, false>(g, A, a_bytes, H, Imax, h0, lane, P);
     }
@@ -401,10 +575,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
 // ---------------------------------------------------------------------------
 
 int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup) {
+  (void)T;
   const int groups = expert_groups_max(T, E, K);
-  const int s_groups = Is > 0 ? (T + kTokGroup - 1) / kTokGroup : 0;
-  if (gateup) return s_groups * (Is / 16) + groups * (I / 16);
-  return (s_groups + groups) * (H / (4 * kDownRowsPerWave));
+  if (gateup) return Is / 16 + groups * (I / 16);
+  return (groups + (Is > 0 ? 1 : 0)) * (H / (4 * kDownRowsPerWave));
 }
 
 hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *w_gate_up, const void *ws_gate_up,

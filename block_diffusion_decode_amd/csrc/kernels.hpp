@@ -70,7 +70,7 @@ hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const in
 
 // LM head online softmax: per (position, workgroup) partial (max, sum, argmax),
 // stored [T][grid].
-int lmhead_grid(int cus);
+int lmhead_grid(int cus, int V);
 size_t lmhead_packed_bytes(int wdtype, int H, int V);
 hipError_t launch_pack_lm(int wdtype, const void *w_lm, int V, int H, void *packed, hipStream_t s);
 size_t lmhead_lds_bytes(int wdtype, int T, int H);

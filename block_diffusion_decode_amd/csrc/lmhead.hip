@@ -350,7 +350,16 @@ hipError_t launch_pack_lm(int wdtype, const void *w_lm, int V, int H, void *pack
   return hipGetLastError();
 }
 
-int lmhead_grid(int cus) { return cus; }
+// One workgroup per CU at most; with m = ceil(tiles / (waves of the chip))
+// tiles per wave, the grid shrinks to ceil(tiles / (kLmWaves * m)) so that
+// every wave streams m tiles (or m - 1 in the last workgroup) and none idles
+// through the last round.
+int lmhead_grid(int cus, int V) {
+  const int tiles = (V + 15) / 16;
+  const int m = (tiles + cus * kLmWaves - 1) / (cus * kLmWaves);
+  const int g = (tiles + kLmWaves * m - 1) / (kLmWaves * m);
+  return g < cus ? g : cus;
+}
 
 size_t lmhead_lds_bytes(int wdtype, int T, int H) {
   const int tp = T <= 16 ? 16 : 32;
