@@ -89,10 +89,11 @@ __device__ __forceinline__ Group resolve(int j, int tiles, const RouteBufs &r, c
   return g;
 }
 
-// Two-deep streaming loop: step s's loads are issued before step s-1's
-// arithmetic.  The prefetch past the last step is an out-of-range load, so the
-// loop always has the same loads in flight and the compiler's in-order wait
-// counts stay exact (a conditional prefetch makes it drain every load).
+// Two-deep streaming loop: step s + 1's loads are issued before step s's
+// arithmetic.  The prefetch past the last step is an out-of-range load (no
+// memory access), so the loop always has the same loads in flight and the
+// compiler's in-order wait counts stay exact (a conditional prefetch makes it
+// drain every load).
 template <class Bufs, class Load, class Step>
 __device__ __forceinline__ void pipeline(int steps, Bufs &b0, Bufs &b1, Load load, Step step) {
   load(0, b0);
@@ -102,6 +103,24 @@ __device__ __forceinline__ void pipeline(int steps, Bufs &b0, Bufs &b1, Load loa
     if (s + 1 >= steps) break;
     load(s + 2, b0);
     step(s + 1, b1);
+  }
+}
+
+// The same with an epilogue `post` after some steps: a buffer is refilled
+// with step s + 2 as soon as step s's arithmetic has read it, before post(s),
+// so two steps' loads stay in flight through the epilogue.
+template <class Bufs, class Load, class Step, class Post>
+__device__ __forceinline__ void pipeline_post(int steps, Bufs &b0, Bufs &b1, Load load, Step step, Post post) {
+  load(0, b0);
+  load(1, b1);
+  for (int s = 0; s < steps; s += 2) {
+    step(s, b0);
+    load(s + 2, b0);
+    post(s);
+    if (s + 1 >= steps) break;
+    step(s + 1, b1);
+    load(s + 3, b1);
+    post(s + 1);
   }
 }
 
@@ -205,9 +224,10 @@ __device__ __forceinline__ f32x4 mfma_chunk(const uint4 &a, const uint4 &b, f32x
   }
 }
 
+constexpr int kSgSteps = 4;   // k-steps per load batch of the shared gate/up
 struct SgBufs {
-  uint4 a[2][2];   // [k-step][gate, up]
-  uint4 b[2][2];   // [k-step][column tile]
+  uint4 a[kSgSteps][2];   // [k-step][gate, up]
+  uint4 b[kSgSteps][2];   // [k-step][column tile]
 };
 
 // Gate/up rows i0 .. i0 + 15 (and Is + i0 ..) of the shared expert for every
@@ -239,8 +259,8 @@ __device__ __forceinline__ void shared_gateup_item(const typename W::T *__restri
     for (int n = 0; n < 2; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load = [&](int bt, SgBufs &b) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ks = 2 * bt + j;
+    for (int j = 0; j < kSgSteps; ++j) {
+      const int ks = kSgSteps * bt + j;
       const int c = 4 * ks + g;
       const bool live = ks < ksteps && c < ncw;
       const uint32_t co = (uint32_t)((cw0 + c) * CH) * sizeof(WT);
@@ -252,14 +272,14 @@ __device__ __forceinline__ void shared_gateup_item(const typename W::T *__restri
   };
   auto step = [&](int, const SgBufs &b) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kSgSteps; ++j)
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int n = 0; n < 2; ++n) acc[q][n] = mfma_chunk<W>(b.a[j][q], b.b[j][n], acc[q][n]);
   };
   SgBufs b0, b1;
-  pipeline((ksteps + 1) / 2, b0, b1, load, step);
+  pipeline((ksteps + kSgSteps - 1) / kSgSteps, b0, b1, load, step);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -286,25 +306,26 @@ __device__ __forceinline__ void shared_gateup_item(const typename W::T *__restri
   __syncthreads();  // `red` is free for the next item
 }
 
-template <int NX>
-struct SdBufs {
-  uint4 a[2];      // [row tile]
-  uint4 x[2][NX];  // [column tile][16-byte part]
-};
+constexpr int kSdSteps = 4;   // k-steps per load batch of the shared down projection
 
-// Down projection of the shared expert for this wave's rows h0 .. h0 + 31 (two
-// row tiles) and every position.  fp32 activations meet bf16 weights as a
-// bf16 high part plus a bf16 residual.  P[T*K + t][h].
+// Down projection of the shared expert for rows h0 .. h0 + 31 (two row tiles)
+// and every position.  The four waves split the intermediate dimension; each
+// issues all loads of a batch of kSdSteps k-steps at once, and the partial
+// tiles are added in LDS (`red`, 16 KiB).  fp32 activations meet bf16 weights
+// as a bf16 high part plus a bf16 residual.  P[T*K + t][h].
 template <class W>
 __device__ __forceinline__ void shared_down_item(const typename W::T *__restrict__ wsd,
                                                  const float *__restrict__ A, int T, int H, int Is, int TK,
-                                                 int Imax, int h0, int lane, float *__restrict__ P) {
+                                                 int Imax, int h0, int wave, int lane, float *__restrict__ P,
+                                                 f32x4 *red) {
   typedef typename W::T WT;
   constexpr bool BF = std::is_same<W, WBf16>::value;
   constexpr int CH = W::kChunk;
   constexpr int NXP = CH / 4;
   const int li = lane & 15, g = lane >> 4;
-  const int NC = Is / CH, ksteps = (NC + 3) / 4;
+  const int ncw = Is / CH / 4;            // chunks of this wave's quarter of I_s
+  const int cw0 = wave * ncw;
+  const int ksteps = (ncw + 3) / 4;
   const rsrc_t rw = make_rsrc(wsd, (uint32_t)(H * Is) * sizeof(WT));
   const rsrc_t ra = make_rsrc(A + (size_t)TK * Imax, (uint32_t)(T * Imax) * 4u);
   uint32_t rowa[2], rowx[2];
@@ -317,48 +338,59 @@ __device__ __forceinline__ void shared_down_item(const typename W::T *__restrict
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int ks, SdBufs<NXP> &b) {
-    const int c = 4 * ks + g;
-    const bool live = ks < ksteps && c < NC;
+  for (int k0 = 0; k0 < ksteps; k0 += kSdSteps) {
+    uint4 wa[kSdSteps][2], xa[kSdSteps][2][NXP];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-      b.a[m] = buf_ld16(rw, live ? rowa[m] + (uint32_t)(c * CH) * sizeof(WT) : kOutOfRange, 0);
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int q = 0; q < NXP; ++q)
-        b.x[n][q] = buf_ld16(ra, live ? rowx[n] + (uint32_t)(c * CH * 4 + 16 * q) : kOutOfRange, 0);
-  };
-  auto step = [&](int, const SdBufs<NXP> &b) {
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      if constexpr (BF) {
-        float f[8];
-        f[0] = __uint_as_float(b.x[n][0].x); f[1] = __uint_as_float(b.x[n][0].y);
-        f[2] = __uint_as_float(b.x[n][0].z); f[3] = __uint_as_float(b.x[n][0].w);
-        f[4] = __uint_as_float(b.x[n][1].x); f[5] = __uint_as_float(b.x[n][1].y);
-        f[6] = __uint_as_float(b.x[n][1].z); f[7] = __uint_as_float(b.x[n][1].w);
-        uint4 hi, lo;
-        split_hi_lo(f, hi, lo);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m][n] = mfma_bf16(b.a[m], lo, mfma_bf16(b.a[m], hi, acc[m][n]));
-      } else {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m][n] = mfma_chunk<W>(b.a[m], b.x[n][0], acc[m][n]);
-      }
-    }
-  };
-  SdBufs<NXP> b0, b1;
-  pipeline(ksteps, b0, b1, load, step);
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int t = n * 16 + li;
-    if (t < T)
+    for (int j = 0; j < kSdSteps; ++j) {
+      const int c = 4 * (k0 + j) + g;
+      const bool live = k0 + j < ksteps && c < ncw;
+      const uint32_t cb = (uint32_t)(cw0 + c);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        *reinterpret_cast<float4 *>(P + (size_t)(TK + t) * H + h0 + 16 * m + 4 * g) =
-            make_float4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
+        wa[j][m] = buf_ld16(rw, live ? rowa[m] + cb * CH * sizeof(WT) : kOutOfRange, 0);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int q = 0; q < NXP; ++q)
+          xa[j][n][q] = buf_ld16(ra, live ? rowx[n] + cb * CH * 4u + 16u * q : kOutOfRange, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kSdSteps; ++j)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        if constexpr (BF) {
+          float f[8];
+          f[0] = __uint_as_float(xa[j][n][0].x); f[1] = __uint_as_float(xa[j][n][0].y);
+          f[2] = __uint_as_float(xa[j][n][0].z); f[3] = __uint_as_float(xa[j][n][0].w);
+          f[4] = __uint_as_float(xa[j][n][1].x); f[5] = __uint_as_float(xa[j][n][1].y);
+          f[6] = __uint_as_float(xa[j][n][1].z); f[7] = __uint_as_float(xa[j][n][1].w);
+          uint4 hi, lo;
+          split_hi_lo(f, hi, lo);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) acc[m][n] = mfma_bf16(wa[j][m], lo, mfma_bf16(wa[j][m], hi, acc[m][n]));
+        } else {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) acc[m][n] = mfma_chunk<W>(wa[j][m], xa[j][n][0], acc[m][n]);
+        }
+      }
   }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) red[((wave * 2 + m) * 2 + n) * 64 + lane] = acc[m][n];
+  __syncthreads();
+  {
+    // wave w finishes row tile w >> 1, column tile w & 1
+    const int m = wave >> 1, n = wave & 1;
+    f32x4 v = red[(m * 2 + n) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[((w * 2 + m) * 2 + n) * 64 + lane];
+    const int t = n * 16 + li;
+    if (t < T)
+      *reinterpret_cast<float4 *>(P + (size_t)(TK + t) * H + h0 + 16 * m + 4 * g) =
+          make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __syncthreads();  // `red` is free for the next item
 }
 
 template <class W>
@@ -501,6 +533,9 @@ __device__ __forceinline__ void down_group(const Group &g, const float *__restri
         }
       }
     }
+  };
+  // end of a batch of 8 rows: reduce over the wave and store
+  auto post = [&](int s) {
     const int bb = s / nq;
     if (s - bb * nq == nq - 1) {
       float v[8 * NT];
@@ -516,7 +551,14 @@ __device__ __forceinline__ void down_group(const Group &g, const float *__restri
     }
   };
   DnBufs<NX> b0, b1;
-  pipeline(nb * nq, b0, b1, load, step);
+  if constexpr (NT >= 4 || !ONCE) {
+    // with four positions, or activations reloaded per step, the registers
+    // do not hold the epilogue's state beside two full buffers: the epilogue
+    // runs with one batch in flight
+    pipeline(nb * nq, b0, b1, load, [&](int s, const DnBufs<NX> &b) { step(s, b); post(s); });
+  } else {
+    pipeline_post(nb * nq, b0, b1, load, step, post);
+  }
 }
 
 template <class W, int sub0, bool ONCE>
@@ -535,7 +577,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
   typedef typename W::T WT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tiles = H / (4 * kDownRowsPerWave);
-  const int s_items = Is > 0 ? tiles : 0;   // shared expert: every position in one pass
+  const int s_items = Is > 0 ? H / 32 : 0;   // shared expert: 32 rows x every position per item
+  __shared__ f32x4 red[4 * 2 * 2 * 64];
   const int items = s_items + uniform(r.meta[2]) * tiles;
   const uint32_t a_bytes = (uint32_t)(T * K + T) * (uint32_t)Imax * 4u;
   const size_t eb = (size_t)H * I * sizeof(WT);
@@ -547,8 +590,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
     const int nitem = item + stride;
     if (item < s_items) {
       if (nitem < items && nitem >= s_items) next = resolve(nitem - s_items, tiles, r, wd, eb, I, tile_next);
-      const int h0 = uniform(item * 4 * kDownRowsPerWave + wave * kDownRowsPerWave);
-      shared_down_item<W>(wsd, A, T, H, Is, T * K, Imax, h0, lane, P);
+      shared_down_item<W>(wsd, A, T, H, Is, T * K, Imax, item * 32, wave, lane, P, red);
       continue;
     }
     const Group g = next;
@@ -578,7 +620,7 @@ int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup) {
   (void)T;
   const int groups = expert_groups_max(T, E, K);
   if (gateup) return Is / 16 + groups * (I / 16);
-  return (groups + (Is > 0 ? 1 : 0)) * (H / (4 * kDownRowsPerWave));
+  return (Is > 0 ? H / 32 : 0) + groups * (H / (4 * kDownRowsPerWave));
 }
 
 hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *w_gate_up, const void *ws_gate_up,

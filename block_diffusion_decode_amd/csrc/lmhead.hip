@@ -48,9 +48,33 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
 // kLmBatch k-steps; two batches are in flight per wave.
 constexpr int kLmBatch = 8;
 
+// The value of lane ^ S (S = 16 or 32), through v_permlane16/32_swap: the
+// swap leaves a lane's own value in one result and its partner's in the other.
+template <int S>
+__device__ __forceinline__ uint32_t partner_u32(uint32_t v, int lane) {
+  const auto r = S == 32 ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
+                         : __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (lane & S) ? r[0] : r[1];
+}
+template <int S>
+__device__ __forceinline__ float partner_f32(float v, int lane) {
+  return __uint_as_float(partner_u32<S>(__float_as_uint(v), lane));
+}
+template <int S>
+__device__ __forceinline__ int partner_i32(int v, int lane) {
+  return (int)partner_u32<S>((uint32_t)v, lane);
+}
+
+// A buffer offset past every LM-head tile: such a load returns zeros without
+// a memory access (pads the prefetches past a wave's last step).
+constexpr uint32_t kLmOutOfRange = 0x7ff00000u;
+
 // Merge the per-workgroup partials of every position (fixed order), then the
 // commit rule on the still-masked positions.  Run by one whole workgroup of
-// any multiple of 64 threads.
+// any multiple of 64 threads.  Each half-wave merges one position: its 32
+// lanes load every 32nd partial (all loads issued before any merge), then
+// fold their results pairwise, lower lane first.
+constexpr int kCommitBatch = 8;
 __device__ void commit_block(const float *__restrict__ part_m, const float *__restrict__ part_s,
                              const int32_t *__restrict__ part_i, int nparts, int T, float threshold,
                              int32_t *__restrict__ tokens, float *__restrict__ conf,
@@ -58,26 +82,30 @@ __device__ void commit_block(const float *__restrict__ part_m, const float *__re
   __shared__ float s_conf[kMaxT];
   __shared__ int s_choice[kMaxT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  for (int t = wave; t < T; t += nw) {
+  const int hl = lane & 31;
+  // the block's tokens, read ahead of the merge by the wave that commits
+  const int tok = (wave == 0 && lane < T) ? tokens[lane] : 0;
+  for (int tp = 2 * wave; tp < T; tp += 2 * nw) {
+    const int t = tp + (lane >> 5);
+    const bool live = t < T;
     float m = -FLT_MAX, s = 0.f;
     int i = INT_MAX;
-    // all of a lane's loads first (independent), then the merges
-    for (int base = lane; base < nparts; base += 4 * 64) {
-      float pm[4], ps[4];
-      int pi[4];
+    for (int base = hl; base < nparts; base += 32 * kCommitBatch) {
+      float pm[kCommitBatch], ps[kCommitBatch];
+      int pi[kCommitBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = base + 64 * j;
-        const bool ok = p < nparts;
+      for (int j = 0; j < kCommitBatch; ++j) {
+        const int p = base + 32 * j;
+        const bool ok = live && p < nparts;
         pm[j] = ok ? fetch_published(part_m + (size_t)t * nparts + p) : 0.f;
         ps[j] = ok ? fetch_published(part_s + (size_t)t * nparts + p) : 0.f;
         pi[j] = ok ? fetch_published(part_i + (size_t)t * nparts + p) : INT_MAX;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sm_merge(m, s, i, pm[j], ps[j], pi[j]);
+      for (int j = 0; j < kCommitBatch; ++j) sm_merge(m, s, i, pm[j], ps[j], pi[j]);
     }
 #pragma unroll
-    for (int sft = 1; sft <= 32; sft <<= 1) {
+    for (int sft = 1; sft <= 16; sft <<= 1) {
       const float m2 = __shfl_xor(m, sft), s2 = __shfl_xor(s, sft);
       const int i2 = __shfl_xor(i, sft);
       // both partners merge the same pair in the same order: lower lane first
@@ -90,7 +118,7 @@ __device__ void commit_block(const float *__restrict__ part_m, const float *__re
         sm_merge(m, s, i, m2, s2, i2);
       }
     }
-    if (lane == 0) {
+    if (live && hl == 0) {
       const float c = 1.0f / s;
       s_conf[t] = c;
       s_choice[t] = i;
@@ -101,7 +129,6 @@ __device__ void commit_block(const float *__restrict__ part_m, const float *__re
   __syncthreads();
   if (wave == 0) {
     const bool in = lane < T;
-    const int tok = in ? tokens[lane] : 0;
     const bool masked = in && tok == -1;
     const float c = in ? s_conf[lane] : 0.f;
     const unsigned long long pass = __ballot(masked && c >= threshold);
@@ -187,12 +214,14 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   const uint32_t vbase = (uint32_t)lane * 16u;
   const uint32_t tile_bytes = (uint32_t)(16 * H * (int)sizeof(typename W::T));
   auto load = [&](int st, uint4(&a)[kLmBatch]) {
-    const int k = st / nb, b = st - k * nb;
+    const bool live = st < steps;
+    const int k = live ? st / nb : 0, b = st - (st / nb) * nb;
     // descriptor over the tile's packed rows (rows past V were packed as zeros)
     const rsrc_t rs = make_rsrc(wlm + (size_t)(first + k * stride) * 16 * H, tile_bytes);
 #pragma unroll
-    for (int j = 0; j < kLmBatch; ++j)   // k-steps past the end reload the last one (unused)
-      a[j] = buf_ld16(rs, vbase, (uint32_t)min(b * kLmBatch + j, ksteps - 1) * 1024u);
+    for (int j = 0; j < kLmBatch; ++j)   // k-steps past the tile or the stream: no access
+      a[j] = buf_ld16(rs, live && b * kLmBatch + j < ksteps ? vbase : kLmOutOfRange,
+                      (uint32_t)min(b * kLmBatch + j, ksteps - 1) * 1024u);
   };
   f32x4 acc[NT];
 #pragma unroll
@@ -231,10 +260,17 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
         const int v = row0 + 4 * g + r;
         if (v < V && (targ == INT_MAX || acc[n][r] > tmax)) { tmax = acc[n][r]; targ = v; }
       }
-#pragma unroll
-      for (int sft = 16; sft <= 32; sft <<= 1) {
-        const float m2 = __shfl_xor(tmax, sft);
-        const int a2 = __shfl_xor(targ, sft);
+      {
+        const float m2 = partner_f32<16>(tmax, lane);
+        const int a2 = partner_i32<16>(targ, lane);
+        if (a2 != INT_MAX && (targ == INT_MAX || m2 > tmax || (m2 == tmax && a2 < targ))) {
+          tmax = m2;
+          targ = a2;
+        }
+      }
+      {
+        const float m2 = partner_f32<32>(tmax, lane);
+        const int a2 = partner_i32<32>(targ, lane);
         if (a2 != INT_MAX && (targ == INT_MAX || m2 > tmax || (m2 == tmax && a2 < targ))) {
           tmax = m2;
           targ = a2;
@@ -246,15 +282,16 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
         const int v = row0 + 4 * g + r;
         if (v < V) tsum += __expf(acc[n][r] - tmax);
       }
-      tsum += __shfl_xor(tsum, 16);
-      tsum += __shfl_xor(tsum, 32);
+      tsum += partner_f32<16>(tsum, lane);
+      tsum += partner_f32<32>(tsum, lane);
       sm_merge(m[n], s[n], am[n], tmax, tsum, targ);
       acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
 
   uint4 a0[kLmBatch], a1[kLmBatch];
-  if (steps > 0) load(0, a0);
+  load(0, a0);
+  load(1, a1);
   // stage the block: batches of 8 independent loads per thread
   for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
     uint4 v[8];
@@ -272,15 +309,17 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
     }
   }
   __syncthreads();
-  // prefetches are unconditional (the step index is clamped) so that the
-  // compiler's load counting sees the same two batches in flight on every path
+  // A buffer is refilled as soon as its MFMAs have read it, before a tile's
+  // epilogue, so two batches stay in flight through the epilogue.  Loads past
+  // the last step are out of range (no access): the loop always has the same
+  // loads in flight and the compiler's in-order wait counts stay exact.
   for (int st = 0; st < steps; st += 2) {
-    load(min(st + 1, steps - 1), a1);
     mma(st, a0);
+    load(st + 2, a0);
     if (st % nb == nb - 1) epilogue(st);
     if (st + 1 >= steps) break;
-    load(min(st + 2, steps - 1), a0);
     mma(st + 1, a1);
+    load(st + 3, a1);
     if ((st + 1) % nb == nb - 1) epilogue(st + 1);
   }
 
