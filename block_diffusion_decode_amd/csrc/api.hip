@@ -70,7 +70,8 @@ bool timing_wants(const char *name) {
   } while (0)
 
 constexpr int kMaxLmGrid = 1024;
-constexpr int kExpertWgPerCu = 3;
+constexpr int kGateupWgPerCu = 4;   // persistent workgroups per CU (register budget: 4 waves per SIMD)
+constexpr int kDownWgPerCu = 3;     // (3 waves per SIMD)
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int wdtype) { return wdtype == BDD_BF16 ? 2 : 4; }
@@ -211,18 +212,17 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
                      float *y_out, void *xhat_next, int32_t *lm_count, hipStream_t s) {
   const int T = d.T, H = d.H, E = d.E, K = d.K, I = d.I, Is = d.I_shared;
   const int Imax = I > Is ? I : Is;
-  const int cap = device_cus() * kExpertWgPerCu;
+  const int cus = device_cus();
   float *A = at<float>(ws, p.A), *P = at<float>(ws, p.P);
   int32_t *sel_count = at<int32_t>(ws, p.sel_count);
   if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, T, H, lm_count, s));
   LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, r.logits, T, H, E, s));
   LAUNCH("route_select", s, launch_route_select(r, w.router_bias, T, H, E, K, top_p, at<int32_t>(ws, p.sorted),
-                                                sel_count, s));
+                                                sel_count, d.wdtype, xhat, w.ws_gate_up, A, Is, Imax, s));
   int g1 = expert_items_max(T, H, E, K, I, Is, true), g2 = expert_items_max(T, H, E, K, I, Is, false);
-  g1 = g1 < cap ? g1 : cap;
-  g2 = g2 < cap ? g2 : cap;
-  LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, w.w_gate_up, w.ws_gate_up, r, A, T, H, K, I,
-                                                  Is, Imax, g1, s));
+  g1 = g1 < cus * kGateupWgPerCu ? g1 : cus * kGateupWgPerCu;
+  g2 = g2 < cus * kDownWgPerCu ? g2 : cus * kDownWgPerCu;
+  LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, w.w_gate_up, r, A, T, H, I, Imax, g1, s));
   LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, w.w_down, w.ws_down, r, P, T, H, K, I, Is, Imax,
                                               g2, s));
   LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P + (size_t)T * K * H : nullptr, r.idx, r.wgt, h,

@@ -46,7 +46,8 @@ hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const
 // scratch; done_count must be zero (the router kernel clears it) and is left
 // zero.
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
-                               int32_t *sorted_ids, int32_t *done_count, hipStream_t s);
+                               int32_t *sorted_ids, int32_t *done_count, int wdtype, const void *xhat,
+                               const void *ws_gate_up, float *A, int Is, int Imax, hipStream_t s);
 
 hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, int K, float top_p,
                           uint32_t *bits, int32_t *size, float *mass, hipStream_t s);
@@ -55,9 +56,8 @@ hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, i
 // groups of r.glist.  A [T*K + T][Imax] fp32 activations (rows: t*K + k routed,
 // T*K + t shared), P [T*K + T][H] fp32 unweighted outputs.
 int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup);
-hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *w_gate_up, const void *ws_gate_up,
-                                const RouteBufs &r, float *A, int T, int H, int K, int I, int Is, int Imax,
-                                int grid, hipStream_t s);
+hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *w_gate_up, const RouteBufs &r, float *A,
+                                int T, int H, int I, int Imax, int grid, hipStream_t s);
 hipError_t launch_expert_down(int wdtype, const float *A, const void *w_down, const void *ws_down,
                               const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
                               int grid, hipStream_t s);

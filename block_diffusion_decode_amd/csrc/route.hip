@@ -12,6 +12,7 @@
 #include <type_traits>
 
 #include "kernels.hpp"
+#include "stream.hpp"
 
 namespace bdd {
 
@@ -318,7 +319,20 @@ __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
 // and re-routing (each position's first min(K, |C|) coreset members in its
 // sorted order), weights, the union of experts and each union expert's list
 // of (position, pick) assignments.  It clears the counter when done.
+// Workgroups past the T positions compute the shared expert's gate/up (it
+// needs only the normalised block), so its weights stream while selection
+// runs: workgroup T + j takes intermediate units 16 j .. 16 j + 15.
 constexpr int kSelThreads = 256;
+static_assert(kSelThreads == 256, "the shared gate/up item runs on four waves");
+
+// Shared-expert operands for the workgroups past the positions.
+template <class W>
+struct SharedGU {
+  const typename W::T *xhat;
+  const typename W::T *wsgu;   // [2 I_s][H]
+  float *A;                    // rows T*K + t
+  int H, Is, TK, Imax;
+};
 
 __device__ __forceinline__ uint32_t order_key(float v) {
   // larger float -> smaller key (ascending sort = descending logits)
@@ -332,16 +346,23 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, i
   return ((unsigned long long)(uint32_t)__shfl_xor((int)hi, m) << 32) | (uint32_t)__shfl_xor((int)lo, m);
 }
 
+template <class W>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const float *__restrict__ bias,
                                                              int KS, int T, int E, int K, float top_p,
                                                              int32_t *__restrict__ sorted_ids,
-                                                             int32_t *__restrict__ done_count) {
+                                                             int32_t *__restrict__ done_count,
+                                                             SharedGU<W> sg) {
   __shared__ unsigned long long s_key[kSelThreads];
   __shared__ float s_p[kSelThreads];
   __shared__ float s_red[kSelThreads / 64];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
+  if (t >= T) {
+    __shared__ f32x4 red[4 * 2 * 2 * 64];
+    shared_gateup_item<W>(sg.wsgu, sg.xhat, T, sg.H, sg.Is, sg.TK, sg.Imax, (t - T) * 16, wave, lane, sg.A, red);
+    return;
+  }
   {
     // ---- phase 1: this position.  Logit = router slices in slice order + bias.
     float l = -FLT_MAX;
@@ -391,7 +412,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   }
   wait_stores();     // every wave completes its row stores ...
   __syncthreads();   // ... before the position is counted
-  if (tid == 0) s_last = count_done(done_count) == (int)gridDim.x - 1;
+  if (tid == 0) s_last = count_done(done_count) == T - 1;
   __syncthreads();
   if (!s_last) return;
 
@@ -599,8 +620,18 @@ hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const
 }
 
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
-                               int32_t *sorted_ids, int32_t *done_count, hipStream_t s) {
-  select_kernel<<<T, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids, done_count);
+                               int32_t *sorted_ids, int32_t *done_count, int wdtype, const void *xhat,
+                               const void *ws_gate_up, float *A, int Is, int Imax, hipStream_t s) {
+  const int grid = T + Is / 16;
+  if (wdtype == 1) {
+    const SharedGU<WBf16> sg = {(const bf16_t *)xhat, (const bf16_t *)ws_gate_up, A, H, Is, T * K, Imax};
+    select_kernel<WBf16><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids,
+                                                      done_count, sg);
+  } else {
+    const SharedGU<WF32> sg = {(const float *)xhat, (const float *)ws_gate_up, A, H, Is, T * K, Imax};
+    select_kernel<WF32><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids,
+                                                     done_count, sg);
+  }
   return hipGetLastError();
 }
 
