@@ -83,7 +83,7 @@ def lib() -> ctypes.CDLL:
     L.bdd_round_workspace_bytes.argtypes = [dims_p, i32]
     L.bdd_round_workspace_bytes.restype = sz
     L.bdd_block_denoise_round.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, vp, vp, vp, vp, vp,
-                                          vp, vp, vp, vp, sz, vp]
+                                          vp, vp, vp, vp, vp, sz, vp]
     L.bdd_block_denoise_round.restype = i32
     L.bdd_status_string.argtypes = [i32]
     L.bdd_status_string.restype = ctypes.c_char_p
@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
     L.bdd_lmhead_pack.argtypes = [vp, i32, i32, i32, vp, vp]
     L.bdd_lmhead_pack.restype = i32
     L.bdd_round_graph_create.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, vp, vp, vp, vp, vp,
-                                         vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
+                                         vp, vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
     L.bdd_round_graph_create.restype = i32
     L.bdd_round_graph_launch.argtypes = [vp, vp]
     L.bdd_round_graph_launch.restype = i32
@@ -346,7 +346,7 @@ class RoundPlan:
         self.ws = _workspace(round_workspace_bytes(d, self.V), dev, None)
 
     def __call__(self, x_in, tokens, conf, choice, round_info, layer_topk_idx=None,
-                 layer_n_distinct=None, hhat_out=None, stream=None):
+                 layer_n_distinct=None, hhat_out=None, stream=None, layer_xhat=None):
         d = self.d
         _need(x_in, "x_in", torch.float32, (d.T, d.H), self.dev)
         _need(tokens, "tokens", torch.int32, (d.T,), self.dev)
@@ -360,10 +360,12 @@ class RoundPlan:
             _need(layer_n_distinct, "layer_n_distinct", torch.int32, (L,), self.dev)
         if hhat_out is not None:
             _need(hhat_out, "hhat_out", d.torch_dtype, (d.T, d.H), self.dev)
+        if layer_xhat is not None:
+            _need(layer_xhat, "layer_xhat", d.torch_dtype, (L, d.T, d.H), self.dev)
         _check(lib().bdd_block_denoise_round(
             ctypes.byref(self.c_dims), L, self.c_layers, self.top_p, _ptr(self.lm.packed), self.V,
             self.threshold, _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info),
-            _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(hhat_out), _ptr(self.ws),
+            _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(layer_xhat), _ptr(hhat_out), _ptr(self.ws),
             self.ws.numel(), _stream(stream)))
 
 
@@ -384,7 +386,7 @@ class RoundGraph:
         _check(lib().bdd_round_graph_create(
             ctypes.byref(plan.c_dims), len(plan.layers), plan.c_layers, plan.top_p, _ptr(plan.lm.packed),
             plan.V, plan.threshold, _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info),
-            _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(hhat_out), _ptr(plan.ws), plan.ws.numel(),
+            _ptr(layer_topk_idx), _ptr(layer_n_distinct), None, _ptr(hhat_out), _ptr(plan.ws), plan.ws.numel(),
             ctypes.byref(h)))
         self.handle = h
 

@@ -383,7 +383,8 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
                                    const void *w_lm, int32_t V, float threshold, const float *x_in,
                                    int32_t *tokens, float *conf, int32_t *choice, int32_t *round_info,
                                    int32_t *layer_topk_idx, int32_t *layer_n_distinct,
-                                   void *hhat_out, void *ws, size_t ws_bytes, void *stream) {
+                                   void *layer_xhat_out, void *hhat_out, void *ws, size_t ws_bytes,
+                                   void *stream) {
   bdd_status st = check_dims(d);
   if (st != BDD_OK) return st;
   if (n_layers < 0) return fail(BDD_ERR_INVALID_ARG, "n_layers=%d", n_layers);
@@ -409,13 +410,18 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
     // the LM head reads RMSNorm(x_in); the norm kernel clears the counter
     LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, hhat, T, H, count, s));
   }
+  // layer l's normalised input: the caller's buffer slot, else the workspace
+  const size_t xbytes = (size_t)T * H * esize(d->wdtype);
+  auto xin = [&](int l) -> void * {
+    return layer_xhat_out ? static_cast<void *>(static_cast<char *>(layer_xhat_out) + (size_t)l * xbytes) : xhat;
+  };
   for (int l = 0; l < n_layers; ++l) {
     RouteBufs r = route_bufs(ws, p);
     if (layer_topk_idx) r.idx = layer_topk_idx + (size_t)l * T * K;
     if (layer_n_distinct) r.n_distinct_out = layer_n_distinct + l;
-    void *next = l + 1 == n_layers ? hhat : xhat;
-    // layer 0 normalises x_in inside its router and keeps x_in as the residual
-    if ((st = moe_layer(*d, layers[l], tp, l == 0 ? x_in : nullptr, l == 0 ? h : nullptr, xhat, r, p, ws, h,
+    void *next = l + 1 == n_layers ? hhat : xin(l + 1);
+    // layer 0 normalises x_in and keeps x_in as the residual
+    if ((st = moe_layer(*d, layers[l], tp, l == 0 ? x_in : nullptr, l == 0 ? h : nullptr, xin(l), r, p, ws, h,
                         nullptr, next, l == 0 ? count : nullptr, s)) != BDD_OK)
       return st;
   }
@@ -437,7 +443,8 @@ bdd_status bdd_round_graph_create(const bdd_moe_dims *d, int32_t n_layers, const
                                   float coreset_top_p, const void *w_packed, int32_t V, float threshold,
                                   const float *x_in, int32_t *tokens, float *conf, int32_t *choice,
                                   int32_t *round_info, int32_t *layer_topk_idx, int32_t *layer_n_distinct,
-                                  void *hhat_out, void *ws, size_t ws_bytes, bdd_round_graph *out) {
+                                  void *layer_xhat_out, void *hhat_out, void *ws, size_t ws_bytes,
+                                  bdd_round_graph *out) {
   if (!out) return fail(BDD_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   hipStream_t cs = nullptr;
@@ -452,7 +459,7 @@ bdd_status bdd_round_graph_create(const bdd_moe_dims *d, int32_t n_layers, const
   }
   const bdd_status st = bdd_block_denoise_round(d, n_layers, layers, coreset_top_p, w_packed, V, threshold,
                                                 x_in, tokens, conf, choice, round_info, layer_topk_idx,
-                                                layer_n_distinct, hhat_out, ws, ws_bytes, cs);
+                                                layer_n_distinct, layer_xhat_out, hhat_out, ws, ws_bytes, cs);
   hipGraph_t graph = nullptr;
   e = hipStreamEndCapture(cs, &graph);
   g_timing = timing;

@@ -191,6 +191,8 @@ size_t bdd_round_workspace_bytes(const bdd_moe_dims *d, int32_t V);
  *   tokens, conf, choice, round_info as in bdd_lmhead_confidence_commit
  *   layer_topk_idx   [n_layers][T][K] int32 out (may be NULL)
  *   layer_n_distinct [n_layers] int32 out (may be NULL)
+ *   layer_xhat_out   [n_layers][T][H] wdtype out: each layer's normalised
+ *                    input, RMSNorm(h) as the layer consumes it (may be NULL)
  *   hhat_out     [T][H] wdtype out: the LM-head input (may be NULL) */
 bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
                                    const bdd_moe_weights *layers, float coreset_top_p,
@@ -198,7 +200,8 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
                                    const float *x_in, int32_t *tokens, float *conf,
                                    int32_t *choice, int32_t *round_info,
                                    int32_t *layer_topk_idx, int32_t *layer_n_distinct,
-                                   void *hhat_out, void *ws, size_t ws_bytes, void *stream);
+                                   void *layer_xhat_out, void *hhat_out, void *ws,
+                                   size_t ws_bytes, void *stream);
 
 /* One denoising round captured as a HIP graph, for callers that replay the
  * same round structure many times (a decode loop): the arguments are those of
@@ -214,8 +217,8 @@ bdd_status bdd_round_graph_create(const bdd_moe_dims *d, int32_t n_layers,
                                   const float *x_in, int32_t *tokens, float *conf,
                                   int32_t *choice, int32_t *round_info,
                                   int32_t *layer_topk_idx, int32_t *layer_n_distinct,
-                                  void *hhat_out, void *ws, size_t ws_bytes,
-                                  bdd_round_graph *out);
+                                  void *layer_xhat_out, void *hhat_out, void *ws,
+                                  size_t ws_bytes, bdd_round_graph *out);
 bdd_status bdd_round_graph_launch(bdd_round_graph g, void *stream);
 void bdd_round_graph_destroy(bdd_round_graph g);
 

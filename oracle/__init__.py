@@ -49,6 +49,7 @@ from .decode import (  # noqa: F401
     reroute,
     swiglu_expert,
     moe_layer,
+    moe_given_routing,
     moe_stack,
     lm_head_confidence,
     commit,

@@ -137,10 +137,21 @@ def moe_layer(xhat, layer: dict, K: int, top_p: float = 1.0):
     if top_p < 1.0:
         members, _, _ = coreset_select(p, idx, top_p)
         idx, w = reroute(l, p, members, K)
+    y, union = moe_given_routing(xhat, layer, idx, w)
+    info = {"logits": l, "p": p, "idx": idx, "w": w, "coreset": members, "union": union}
+    return y, info
+
+
+def moe_given_routing(xhat, layer: dict, idx, w):
+    """The expert part of moe_layer for a routing already taken: idx [T][K]
+    expert ids (-1 = unused slot) and their weights w [T][K].
+    y_t = sum_k w[t,k] * SwiGLU_{idx[t,k]}(xhat_t) + SwiGLU_shared(xhat_t)
+    ([P1] 四).  Returns (y, sorted union of experts)."""
     x = np.asarray(xhat, dtype=np.float64)
+    idx = np.asarray(idx)
     T = x.shape[0]
     y = swiglu_expert(x, layer["ws_gate_up"], layer["ws_down"])
-    union = sorted(set(int(e) for e in idx.ravel()))
+    union = sorted(set(int(e) for e in idx.ravel() if e >= 0))
     for e in union:
         gu, dn = layer["experts"][e]
         rows = [t for t in range(T) if e in idx[t]]
@@ -148,8 +159,7 @@ def moe_layer(xhat, layer: dict, K: int, top_p: float = 1.0):
         for j, t in enumerate(rows):
             k = int(np.nonzero(idx[t] == e)[0][0])
             y[t] += w[t, k] * out[j]
-    info = {"logits": l, "p": p, "idx": idx, "w": w, "coreset": members, "union": union}
-    return y, info
+    return y, union
 
 
 def moe_stack(x_in, layers, K: int, top_p: float = 1.0, round_bf16: bool = True,

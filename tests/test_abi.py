@@ -103,5 +103,5 @@ def test_round_rejects_null_layers():
     d = bdd.MoEDims(8, 256, 16, 4, 128, 128, 0)
     p = ctypes.c_void_p(1)
     st = L.bdd_block_denoise_round(ctypes.byref(d.c()), 2, None, 1.0, p, 1024, 0.95, p, p, p, p, p,
-                                   None, None, None, None, 0, None)
+                                   None, None, None, None, None, 0, None)
     assert st == -1
