@@ -53,6 +53,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (counter scaling)")
+    ap.add_argument("--stack", type=int, default=0, metavar="L",
+                    help="also measure an L-layer stack round (Zipf routing, coreset 0.9) and a full block "
+                         "resolve on it; reported under 'stack', not as the value")
     ap.add_argument("--counter-run", action="store_true",
                     help="only run 3 rounds on inputs drawn with torch.randn (a handful of kernel launches "
                          "besides the library's), for hardware-counter collection")
@@ -196,9 +199,102 @@ def main():
         "roofline": roofline,
     }
 
+    if args.stack > 0:
+        del graphs, plan, lm, layer
+        torch.cuda.empty_cache()
+        out["stack"] = stack_round(args, d, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, d, x, layer, w_lm, info, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args, d, x, W.layer_weights(args.seed, 0, d, device=dev), w_lm, info,
+                                           args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def stack_round(args, d, dev):
+    """An L-layer stack of independent Clover-shaped layers (Zipf router bias,
+    block coreset top_p 0.9, identity mixer) + LM head + commit: microseconds
+    per round over K rounds of stub inputs, the distinct experts each layer
+    read, and one block resolved round by round from all-MASK."""
+    import numpy as np
+    import torch
+
+    import block_diffusion_decode_amd as bdd
+    import workloads as W
+
+    L, top_p, T = args.stack, 0.9, d.T
+    log(f"[bench] stack: generating {L} layers")
+    layers = [W.layer_weights(args.seed, l, d, device=dev, bias="zipf", gamma=1.0) for l in range(L)]
+    R = 32
+    x, info = W.planted_round_inputs(args.seed, d, rounds=R, p=0.3, amp_pass=40.0, amp_fail=(14.0, 22.0),
+                                     tag="stack")
+    x = x.to(dev)
+    w_lm = W.lm_head_weight(args.seed, d, device=dev, unit_rows=info["unit_rows"])
+    plan = bdd.RoundPlan(bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16), layers,
+                         bdd.pack_lm_head(w_lm), top_p, 0.95)
+    del w_lm
+    tok = torch.full((T,), bdd.MASK, dtype=torch.int32, device=dev)
+    conf = torch.empty(T, dtype=torch.float32, device=dev)
+    choice = torch.empty(T, dtype=torch.int32, device=dev)
+    ri = torch.empty(4, dtype=torch.int32, device=dev)
+    nd = torch.empty((R, L), dtype=torch.int32, device=dev)
+    for r in range(R):
+        plan(x[r], tok, conf, choice, ri, None, nd[r])
+    torch.cuda.synchronize()
+    distinct = nd.cpu().numpy().astype(np.int64)
+    # the same rounds without the coreset: the experts the coreset saves
+    plan1 = bdd.RoundPlan(plan.d, layers, plan.lm, 1.0, 0.95)
+    nd1 = torch.empty((R, L), dtype=torch.int32, device=dev)
+    for r in range(R):
+        plan1(x[r], tok, conf, choice, ri, None, nd1[r])
+    torch.cuda.synchronize()
+    distinct1 = nd1.cpu().numpy().astype(np.int64)
+    del plan1
+    steps = max(1, min(args.steps, 50))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        plan(x[i % R], tok, conf, choice, ri)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    # per-kernel averages over a few more rounds (each launch bracketed by events)
+    bdd.timing_enable(True, None)
+    for i in range(8):
+        plan(x[i % R], tok, conf, choice, ri)
+    torch.cuda.synchronize()
+    per_kernel = {k: round(1e3 * v[0] / v[1], 2) for k, v in bdd.timing_read().items()}
+    bdd.timing_enable(False)
+    mean_u = float(np.mean([distinct[i % R].sum() for i in range(steps)]))
+    eb = 3 * d.H * d.I * 2
+    round_bytes = mean_u * eb + L * (3 * d.H * d.I_s * 2 + d.E * d.H * 2) + d.V * d.H * 2
+    # one block from all-MASK: round r uses stub r until every position is committed
+    tok.fill_(bdd.MASK)
+    rounds = fallbacks = 0
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for r in range(R):
+        plan(x[r], tok, conf, choice, ri)
+        info_r = ri.cpu().tolist()
+        rounds += 1
+        fallbacks += info_r[1]
+        if info_r[3]:
+            break
+    t1.record()
+    torch.cuda.synchronize()
+    resolve_ms = t0.elapsed_time(t1)
+    res = {"layers": L, "coreset_top_p": top_p, "us_per_round": round(ms * 1e3, 2),
+           "distinct_experts_per_layer_mean": mean_u / L, "round_bytes": round_bytes,
+           "hbm_gbps": round_bytes / (ms * 1e-3) / 1e9, "hbm_frac": round_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "per_kernel_launch_us": per_kernel,
+           "distinct_experts_per_layer_without_coreset": float(distinct1.sum(axis=1).mean()) / L,
+           "expert_bytes_saved_per_round": float((distinct1.sum(axis=1) - distinct.sum(axis=1)).mean()) * eb,
+           "resolve": {"rounds": rounds, "fallback_rounds": fallbacks, "ms": resolve_ms,
+                       "committed_tokens_per_s": T / (resolve_ms * 1e-3),
+                       "note": "host reads round_info after every round"}}
+    log(f"[bench] stack {L} layers: {ms * 1e3:.1f} us/round, {mean_u / L:.1f} experts/layer, "
+        f"{res['hbm_gbps']:.0f} GB/s; block resolved in {rounds} rounds ({fallbacks} fallback), "
+        f"{res['resolve']['committed_tokens_per_s']:.0f} tok/s")
+    return res
 
 
 def counter_run(d, dev):

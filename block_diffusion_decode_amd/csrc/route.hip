@@ -429,23 +429,54 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   write_bits(sh, E, r.cs_bits);
   if (top_p < 1.0f) {
     // each position re-takes its first min(K, |C|) coreset members in its own
-    // (logit desc, id asc) order
+    // (logit desc, id asc) order.  Every position's sorted list is staged in
+    // LDS first (ids fit a byte; all loads in flight at once), the scans run
+    // from LDS, then the chosen experts' probabilities arrive in one batch.
+    __shared__ uint8_t s_sorted[kMaxT * kMaxE];
+    constexpr int kStage = kMaxT * kMaxE / kSelThreads;
+    int v[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = tid + j * kSelThreads;
+      v[j] = i < T * E ? fetch_published(sorted_ids + i) : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = tid + j * kSelThreads;
+      if (i < T * E) s_sorted[i] = (uint8_t)v[j];
+    }
+    __syncthreads();
     const int kk = min(K, sh.csize);
+    constexpr int kChunks = kMaxE / 64;
     for (int tt = wave; tt < T; tt += kSelThreads / 64) {
-      int taken = 0;
-      for (int base = 0; base < E && taken < kk; base += 64) {
-        const int e = base + lane < E ? fetch_published(sorted_ids + (size_t)tt * E + base + lane) : -1;
-        const bool mem = e >= 0 && sh.member[e] != 0;
-        const unsigned long long b = __ballot(mem);
-        const int before = __popcll(b & ((1ull << lane) - 1ull));
-        if (mem && taken + before < kk) {
-          sh.idx[tt][taken + before] = e;
-          sh.psel[tt][taken + before] = fetch_published(r.prob + (size_t)tt * E + e);
-        }
-        taken += __popcll(b);
+      // the position's whole sorted list at once: member flags of the 4
+      // chunks, then each member's rank among the members before it
+      int e[kChunks];
+      unsigned long long b[kChunks];
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int i = c * 64 + lane;
+        e[c] = i < E ? (int)s_sorted[tt * E + i] : -1;
       }
-      if (lane == 0)
-        for (int k = kk; k < K; ++k) { sh.idx[tt][k] = -1; sh.psel[tt][k] = 0.f; }
+      int mem[kChunks];
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) mem[c] = sh.member[e[c] & (kMaxE - 1)];   // unconditional
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) b[c] = __ballot(e[c] >= 0 && mem[c] != 0);
+      int taken = 0;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int before = taken + __popcll(b[c] & ((1ull << lane) - 1ull));
+        if (((b[c] >> lane) & 1ull) && before < kk) sh.idx[tt][before] = e[c];
+        taken += __popcll(b[c]);
+      }
+      if (lane < K && lane >= kk) sh.idx[tt][lane] = -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < T * K; i += kSelThreads) {
+      const int tt = i / K, k = i - tt * K;
+      const int e = sh.idx[tt][k];
+      sh.psel[tt][k] = e >= 0 ? fetch_published(r.prob + (size_t)tt * E + e) : 0.f;
     }
     __syncthreads();
     build_masks(sh, T, E, K);
