@@ -109,7 +109,7 @@ bdd_status check_dims(const bdd_moe_dims *d) {
 }
 
 struct MoePlan {
-  size_t logits, prob, idx, wgt, meta, ulist, glist, bits, mass, xhat, A, P;
+  size_t logits, prob, idx, wgt, meta, ulist, glist, dlist, bits, mass, xhat, xpk, A, act, P;
   size_t sorted, sel_count;
   size_t end;
 };
@@ -126,11 +126,16 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   p.meta = take(64);
   p.ulist = take(E * 4);
   p.glist = take((size_t)expert_groups_max(d.T, d.E, d.K) * 8 * 4);
+  p.dlist = take((size_t)(expert_dense_max(d.T, d.E, d.K) + 1) * kDenseRec * 4);
   p.bits = take(32);
   p.mass = take(E * 4);
   p.xhat = take(T * H * esize(d.wdtype));
+  p.xpk = take(T * H * esize(d.wdtype));
+  // token-group activations, rows t*K + k
+  p.A = take(T * K * (I > Is ? I : Is) * 4);
+  // packed activation slots: the shared expert, then the dense experts
+  p.act = take((size_t)(expert_dense_max(d.T, d.E, d.K) + 1) * (I > Is ? I : Is) * kActSlotPerI);
   // rows t*K + k of the routed picks, then T*K + t of the shared expert
-  p.A = take((T * K + T) * (I > Is ? I : Is) * 4);
   p.P = take((T * K + T) * H * 4);
   p.sorted = take(T * E * 4);
   p.sel_count = take(64);
@@ -196,6 +201,7 @@ RouteBufs route_bufs(void *ws, const MoePlan &p) {
   r.meta = at<int32_t>(ws, p.meta);
   r.union_list = at<int32_t>(ws, p.ulist);
   r.glist = at<int32_t>(ws, p.glist);
+  r.dlist = at<int32_t>(ws, p.dlist);
   r.cs_bits = at<uint32_t>(ws, p.bits);
   r.mass = at<float>(ws, p.mass);
   r.n_distinct_out = nullptr;
@@ -205,28 +211,31 @@ RouteBufs route_bufs(void *ws, const MoePlan &p) {
 
 // One MoE layer.  With h_in given, the layer first normalises it into xhat
 // (copying it to h_copy and clearing lm_count when those are given); else
-// xhat already holds the normalised block.  combine: h += y and the next
-// normalisation into xhat_next when h != nullptr, else y_out = y.
+// xhat already holds the normalised block (and the workspace its packed
+// copy).  combine: h += y and the next normalisation into xhat_next (and the
+// packed copy when xpk_next) when h != nullptr, else y_out = y.
 bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_p, const float *h_in,
                      float *h_copy, void *xhat, RouteBufs r, const MoePlan &p, void *ws, float *h,
-                     float *y_out, void *xhat_next, int32_t *lm_count, hipStream_t s) {
+                     float *y_out, void *xhat_next, bool xpk_next, int32_t *lm_count, hipStream_t s) {
   const int T = d.T, H = d.H, E = d.E, K = d.K, I = d.I, Is = d.I_shared;
   const int Imax = I > Is ? I : Is;
   const int cus = device_cus();
   float *A = at<float>(ws, p.A), *P = at<float>(ws, p.P);
+  void *xpk = at<void>(ws, p.xpk), *act = at<void>(ws, p.act);
   int32_t *sel_count = at<int32_t>(ws, p.sel_count);
-  if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, T, H, lm_count, s));
+  if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, xpk, T, H, lm_count, s));
   LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, r.logits, T, H, E, s));
   LAUNCH("route_select", s, launch_route_select(r, w.router_bias, T, H, E, K, top_p, at<int32_t>(ws, p.sorted),
-                                                sel_count, d.wdtype, xhat, w.ws_gate_up, A, Is, Imax, s));
+                                                sel_count, d.wdtype, xpk, w.ws_gate_up, act, Is, s));
   int g1 = expert_items_max(T, H, E, K, I, Is, true), g2 = expert_items_max(T, H, E, K, I, Is, false);
   g1 = g1 < cus * kGateupWgPerCu ? g1 : cus * kGateupWgPerCu;
   g2 = g2 < cus * kDownWgPerCu ? g2 : cus * kDownWgPerCu;
-  LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, w.w_gate_up, r, A, T, H, I, Imax, g1, s));
-  LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, w.w_down, w.ws_down, r, P, T, H, K, I, Is, Imax,
+  LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, xpk, w.w_gate_up, r, A, act, T, H, I, Imax, g1,
+                                                  s));
+  LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, act, w.w_down, w.ws_down, r, P, T, H, K, I, Is, Imax,
                                               g2, s));
   LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P + (size_t)T * K * H : nullptr, r.idx, r.wgt, h,
-                                      y_out, xhat_next, T, H, K, s));
+                                      y_out, xhat_next, xpk_next ? xpk : nullptr, T, H, K, s));
   return BDD_OK;
 }
 
@@ -311,7 +320,7 @@ bdd_status bdd_moe_block_forward(const bdd_moe_dims *d, const bdd_moe_weights *w
   r.coreset_size_out = coreset_size;
   void *xhat = xhat_out ? xhat_out : at<void>(ws, p.xhat);
   return moe_layer(*d, *w, coreset_top_p >= 1.0f ? 1.0f : coreset_top_p, h, nullptr, xhat, r, p, ws,
-                   nullptr, y, nullptr, nullptr, s);
+                   nullptr, y, nullptr, false, nullptr, s);
 }
 
 bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx, int32_t T, int32_t E,
@@ -408,7 +417,7 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
   int32_t *count = at<int32_t>(ws, lp.count);
   if (n_layers == 0) {
     // the LM head reads RMSNorm(x_in); the norm kernel clears the counter
-    LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, hhat, T, H, count, s));
+    LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, hhat, nullptr, T, H, count, s));
   }
   // layer l's normalised input: the caller's buffer slot, else the workspace
   const size_t xbytes = (size_t)T * H * esize(d->wdtype);
@@ -422,7 +431,7 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
     void *next = l + 1 == n_layers ? hhat : xin(l + 1);
     // layer 0 normalises x_in and keeps x_in as the residual
     if ((st = moe_layer(*d, layers[l], tp, l == 0 ? x_in : nullptr, l == 0 ? h : nullptr, xin(l), r, p, ws, h,
-                        nullptr, next, l == 0 ? count : nullptr, s)) != BDD_OK)
+                        nullptr, next, l + 1 < n_layers, l == 0 ? count : nullptr, s)) != BDD_OK)
       return st;
   }
   const int cus = device_cus();

@@ -9,16 +9,20 @@
 // activation (SwiGLU) is not on the pages; it is the reading this library
 // documents in its header.
 //
-// A routed expert sees ~1.6 positions on average at the Clover shape (at most
-// 32), so its contraction is a matrix-vector product: VALU dot products on
-// weights streamed with 16-byte buffer loads.  Work items are (token group,
-// row tile); a token group is up to kTokGroup positions of one expert (the
-// selection kernel lists them), and the shared expert contributes the first
-// ceil(T / kTokGroup) groups, covering every position.  A wave owns 8 weight
-// rows of its item; lane l covers 16-byte chunks l, l + 64, ... of every row,
-// so a load instruction reads one contiguous 1 KiB segment of a row.  The
-// positions' activations are read per chunk straight from L2 next to the
-// weights, so the four waves of a workgroup never synchronise.
+// A routed expert sees ~1.6 positions on average at the Clover shape under
+// flat routing, so its contraction is a matrix-vector product: VALU dot
+// products on weights streamed with 16-byte buffer loads.  Work items are
+// (token group, row tile); a token group is up to kTokGroup positions of one
+// expert (the selection kernel lists them).  A wave owns 8 weight rows of its
+// item; lane l covers 16-byte chunks l, l + 64, ... of every row, so a load
+// instruction reads one contiguous 1 KiB segment of a row.  The positions'
+// activations are read per chunk straight from L2 next to the weights, so the
+// four waves of a workgroup never synchronise.
+//
+// An expert with more positions than a token group holds (skewed routing
+// sends most of a block to a few experts) and the shared expert (every
+// position) run as dense items instead: MFMA tiles over all their positions
+// at once, so their weights stream once per block rather than once per group.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -165,73 +169,63 @@ __device__ __forceinline__ void gateup_group(const Group &g, const typename W::T
   }
 }
 
-constexpr int kSdSteps = 4;   // k-steps per load batch of the shared down projection
+constexpr int kSdSteps = 4;   // k-steps per load batch of a dense down projection
 
-// Down projection of the shared expert for rows h0 .. h0 + 31 (two row tiles)
-// and every position.  The four waves split the intermediate dimension; each
-// issues all loads of a batch of kSdSteps k-steps at once, and the partial
-// tiles are added in LDS (`red`, 16 KiB).  fp32 activations meet bf16 weights
-// as a bf16 high part plus a bf16 residual.  P[T*K + t][h].
+// Down projection of one dense expert, W_d [H][ie], for rows h0 .. h0 + 31
+// (two row tiles) and up to 32 column entries, from the expert's packed
+// activation slot (see act_unit).  Lane (li, g) names entries li and 16 + li
+// by their rows row[n] in P (-1: no entry).  The four waves split the
+// intermediate dimension; each issues all loads of a batch of kSdSteps
+// k-steps at once, and the partial tiles are added in LDS (`red`, 16 KiB).
+// With bf16 weights the activations enter as bf16 high parts and residuals
+// (two MFMA passes).  P[row][h] = A_entry . W_d[h].
 template <class W>
-__device__ __forceinline__ void shared_down_item(const typename W::T *__restrict__ wsd,
-                                                 const float *__restrict__ A, int T, int H, int Is, int TK,
-                                                 int Imax, int h0, int wave, int lane, float *__restrict__ P,
-                                                 f32x4 *red) {
+__device__ __forceinline__ void dense_down_item(const typename W::T *__restrict__ w, int ie,
+                                                const char *__restrict__ act, int H, const int (&row)[2], int h0,
+                                                int wave, int lane, float *__restrict__ P, f32x4 *red) {
   typedef typename W::T WT;
   constexpr bool BF = std::is_same<W, WBf16>::value;
   constexpr int CH = W::kChunk;
-  constexpr int NXP = CH / 4;
+  constexpr int NP = act_planes<W>();
   const int li = lane & 15, g = lane >> 4;
-  const int ncw = Is / CH / 4;            // chunks of this wave's quarter of I_s
+  const int ncw = ie / CH / 4;            // chunks of this wave's quarter of ie
   const int cw0 = wave * ncw;
   const int ksteps = (ncw + 3) / 4;
-  const rsrc_t rw = make_rsrc(wsd, (uint32_t)(H * Is) * sizeof(WT));
-  const rsrc_t ra = make_rsrc(A + (size_t)TK * Imax, (uint32_t)(T * Imax) * 4u);
-  uint32_t rowa[2], rowx[2];
+  const rsrc_t rw = make_rsrc(w, (uint32_t)(H * ie) * sizeof(WT));
+  const rsrc_t ra = make_rsrc(act, (uint32_t)ie * kActSlotPerI);
+  uint32_t rowa[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) rowa[m] = (uint32_t)((h0 + 16 * m + li) * Is) * sizeof(WT);
-#pragma unroll
-  for (int n = 0; n < 2; ++n) rowx[n] = n * 16 + li < T ? (uint32_t)((n * 16 + li) * Imax) * 4u : kOutOfRange;
+  for (int m = 0; m < 2; ++m) rowa[m] = (uint32_t)((h0 + 16 * m + li) * ie) * sizeof(WT);
   f32x4 acc[2][2];   // [row tile][column tile]
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < ksteps; k0 += kSdSteps) {
-    uint4 wa[kSdSteps][2], xa[kSdSteps][2][NXP];
+    uint4 wa[kSdSteps][2], xa[kSdSteps][2][NP];
 #pragma unroll
     for (int j = 0; j < kSdSteps; ++j) {
       const int c = 4 * (k0 + j) + g;
       const bool live = k0 + j < ksteps && c < ncw;
-      const uint32_t cb = (uint32_t)(cw0 + c);
+      const int C = cw0 + c;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        wa[j][m] = buf_ld16(rw, live ? rowa[m] + cb * CH * sizeof(WT) : kOutOfRange, 0);
+        wa[j][m] = buf_ld16(rw, live ? rowa[m] + (uint32_t)(C * CH) * sizeof(WT) : kOutOfRange, 0);
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int q = 0; q < NXP; ++q)
-          xa[j][n][q] = buf_ld16(ra, live ? rowx[n] + cb * CH * 4u + 16u * q : kOutOfRange, 0);
+        for (int q = 0; q < NP; ++q)
+          xa[j][n][q] = buf_ld16(ra, live && row[n] >= 0 ? act_unit(C, q, 16 * n + li, NP) * 16u : kOutOfRange, 0);
     }
 #pragma unroll
     for (int j = 0; j < kSdSteps; ++j)
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        if constexpr (BF) {
-          float f[8];
-          f[0] = __uint_as_float(xa[j][n][0].x); f[1] = __uint_as_float(xa[j][n][0].y);
-          f[2] = __uint_as_float(xa[j][n][0].z); f[3] = __uint_as_float(xa[j][n][0].w);
-          f[4] = __uint_as_float(xa[j][n][1].x); f[5] = __uint_as_float(xa[j][n][1].y);
-          f[6] = __uint_as_float(xa[j][n][1].z); f[7] = __uint_as_float(xa[j][n][1].w);
-          uint4 hi, lo;
-          split_hi_lo(f, hi, lo);
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
-          for (int m = 0; m < 2; ++m) acc[m][n] = mfma_bf16(wa[j][m], lo, mfma_bf16(wa[j][m], hi, acc[m][n]));
-        } else {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) acc[m][n] = mfma_chunk<W>(wa[j][m], xa[j][n][0], acc[m][n]);
+        for (int m = 0; m < 2; ++m) {
+          if constexpr (BF) acc[m][n] = mfma_bf16(wa[j][m], xa[j][n][1], mfma_bf16(wa[j][m], xa[j][n][0], acc[m][n]));
+          else acc[m][n] = mfma_chunk<W>(wa[j][m], xa[j][n][0], acc[m][n]);
         }
-      }
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -239,37 +233,73 @@ __device__ __forceinline__ void shared_down_item(const typename W::T *__restrict
     for (int n = 0; n < 2; ++n) red[((wave * 2 + m) * 2 + n) * 64 + lane] = acc[m][n];
   __syncthreads();
   {
-    // wave w finishes row tile w >> 1, column tile w & 1
+    // wave v finishes row tile v >> 1, column tile v & 1
     const int m = wave >> 1, n = wave & 1;
     f32x4 v = red[(m * 2 + n) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[((w * 2 + m) * 2 + n) * 64 + lane];
-    const int t = n * 16 + li;
-    if (t < T)
-      *reinterpret_cast<float4 *>(P + (size_t)(TK + t) * H + h0 + 16 * m + 4 * g) =
-          make_float4(v[0], v[1], v[2], v[3]);
+    for (int u = 1; u < 4; ++u) v += red[((u * 2 + m) * 2 + n) * 64 + lane];
+    const int rw_ = row[0] + (n & 1) * (row[1] - row[0]);   // value arithmetic: no runtime-indexed array
+    if (rw_ >= 0)
+      *reinterpret_cast<float4 *>(P + (size_t)rw_ * H + h0 + 16 * m + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
   }
   __syncthreads();  // `red` is free for the next item
 }
 
+// Per-lane column entries of a dense record: entries li and 16 + li.  The
+// record is read with wave-uniform loads (scalar loads where the compiler can
+// prove nothing in the kernel wrote it yet: a workgroup's first item), and
+// each lane picks its two entries.
+__device__ __forceinline__ void dense_entries(const int32_t *rec, int lane, int &e, int &n, int (&v)[2]) {
+  e = uniform(rec[0]);
+  n = uniform(rec[1]);
+  int ent[kMaxT];
+#pragma unroll
+  for (int j = 0; j < kMaxT; ++j) ent[j] = uniform(rec[8 + j]);
+  const int li = lane & 15;
+  v[0] = ent[0];
+  v[1] = ent[16];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) {
+    v[0] = li == j ? ent[j] : v[0];
+    v[1] = li == j ? ent[16 + j] : v[1];
+  }
+}
+
+// Work list: the dense experts' items (expert, 16-row tile), then the token
+// groups' items (group, 16-row tile).
 template <class W>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void expert_gateup_kernel(
-    const typename W::T *__restrict__ xhat, const typename W::T *__restrict__ wgu, RouteBufs r,
-    float *__restrict__ A, int T, int H, int I, int Imax) {
+    const typename W::T *__restrict__ xhat, const typename W::T *__restrict__ xpk,
+    const typename W::T *__restrict__ wgu, RouteBufs r, float *__restrict__ A, char *__restrict__ act, int T,
+    int H, int I, int Imax) {
   typedef typename W::T WT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tiles = I / 16;
-  const int items = uniform(r.meta[2]) * tiles;
+  const int d_items = uniform(r.meta[3]) * tiles;
+  const int items = d_items + uniform(r.meta[2]) * tiles;
   const uint32_t x_bytes = (uint32_t)(T * H) * sizeof(WT);
   const size_t eb = (size_t)2 * I * H * sizeof(WT);
-  int item = blockIdx.x, tile_next = 0;
+  __shared__ f32x4 red[4 * 2 * 2 * 64];
+  int item = blockIdx.x;
+  for (; item < d_items; item += gridDim.x) {
+    const int di = item / tiles, tile = item - di * tiles;
+    int e, n, v[2];
+    dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
+    int pos[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
+    // slot 0 holds the shared expert
+    dense_gateup_item<W, 2>(wgu + (size_t)e * 2 * I * H, I, xpk, T, H, pos, item, tile * 16, wave, lane,
+                            act + (size_t)(1 + di) * Imax * kActSlotPerI, red);
+  }
+  int tile_next = 0;
   Group next;
-  if (item < items) next = resolve(item, tiles, r, wgu, eb, I, tile_next);
+  if (item < items) next = resolve(item - d_items, tiles, r, wgu, eb, I, tile_next);
   for (; item < items; item += gridDim.x) {
+    const int nitem = item + (int)gridDim.x;
     const Group g = next;
     const int tile = tile_next;
-    const int nitem = item + (int)gridDim.x;
-    if (nitem < items) next = resolve(nitem, tiles, r, wgu, eb, I, tile_next);
+    if (nitem < items) next = resolve(nitem - d_items, tiles, r, wgu, eb, I, tile_next);
     const int i0 = uniform(tile * 16 + wave * 4);
     if (g.ng <= 1)      gateup_group<W, 1>(g, xhat, x_bytes, H, Imax, i0, lane, A);
     else if (g.ng <= 2) gateup_group<W, 2>(g, xhat, x_bytes, H, Imax, i0, lane, A);
@@ -417,34 +447,62 @@ __device__ __forceinline__ void down_pass(const Group &g, const float *__restric
   else                  down_group<W, kDownSub, sub0, ONCE>(g, A, a_bytes, H, Imax, h0, lane, P);
 }
 
+// Work list: the shared expert's items (32 rows each), the dense experts'
+// items (expert, 32 rows), then the token groups' items (group, 128 rows).
 template <class W>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void expert_down_kernel(const float *__restrict__ A,
+                                                          const char *__restrict__ act,
                                                           const typename W::T *__restrict__ wd,
                                                           const typename W::T *__restrict__ wsd,
                                                           RouteBufs r, float *__restrict__ P, int T,
                                                           int H, int K, int I, int Is, int Imax) {
   typedef typename W::T WT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tiles = H / (4 * kDownRowsPerWave);
-  const int s_items = Is > 0 ? H / 32 : 0;   // shared expert: 32 rows x every position per item
+  const int tiles = H / (4 * kDownRowsPerWave), dtiles = H / 32;
+  const int s_items = Is > 0 ? dtiles : 0;
+  const int d_end = s_items + uniform(r.meta[3]) * dtiles;
   __shared__ f32x4 red[4 * 2 * 2 * 64];
-  const int items = s_items + uniform(r.meta[2]) * tiles;
-  const uint32_t a_bytes = (uint32_t)(T * K + T) * (uint32_t)Imax * 4u;
+  const int items = d_end + uniform(r.meta[2]) * tiles;
+  const uint32_t a_bytes = (uint32_t)(T * K) * (uint32_t)Imax * 4u;
   const size_t eb = (size_t)H * I * sizeof(WT);
   const int stride = gridDim.x;
-  int item = blockIdx.x, tile_next = 0;
+  int item = blockIdx.x;
+  for (; item < d_end; item += stride) {
+    int row[2];
+    const WT *w;
+    int ie, h0, slot;
+    if (item < s_items) {
+      // the shared expert (slot 0): column entry j is position j, row T*K + j
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int j = c * 16 + (lane & 15);
+        row[c] = j < T ? T * K + j : -1;
+      }
+      w = wsd;
+      ie = Is;
+      h0 = item * 32;
+      slot = 0;
+    } else {
+      const int di = (item - s_items) / dtiles;
+      int e, n, v[2];
+      dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) row[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
+      w = wd + (size_t)e * H * I;
+      ie = I;
+      h0 = (item - s_items - di * dtiles) * 32;
+      slot = 1 + di;
+    }
+    dense_down_item<W>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, H, row, h0, wave, lane, P, red);
+  }
+  int tile_next = 0;
   Group next;
-  if (item < items && item >= s_items) next = resolve(item - s_items, tiles, r, wd, eb, I, tile_next);
+  if (item < items) next = resolve(item - d_end, tiles, r, wd, eb, I, tile_next);
   for (; item < items; item += stride) {
     const int nitem = item + stride;
-    if (item < s_items) {
-      if (nitem < items && nitem >= s_items) next = resolve(nitem - s_items, tiles, r, wd, eb, I, tile_next);
-      shared_down_item<W>(wsd, A, T, H, Is, T * K, Imax, item * 32, wave, lane, P, red);
-      continue;
-    }
     const Group g = next;
     const int tile = tile_next;
-    if (nitem < items) next = resolve(nitem - s_items, tiles, r, wd, eb, I, tile_next);
+    if (nitem < items) next = resolve(nitem - d_end, tiles, r, wd, eb, I, tile_next);
     const int h0 = uniform(tile * 4 * kDownRowsPerWave + wave * kDownRowsPerWave);
     if (g.ie <= 64 * W::kChunk) {
       // one pass over the whole group: the activations sit in registers
@@ -467,31 +525,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
 
 int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup) {
   (void)T;
-  const int groups = expert_groups_max(T, E, K);
-  if (gateup) return groups * (I / 16);
-  return (Is > 0 ? H / 32 : 0) + groups * (H / (4 * kDownRowsPerWave));
+  const int groups = expert_groups_max(T, E, K), dense = expert_dense_max(T, E, K);
+  if (gateup) return (groups + dense) * (I / 16);
+  return (Is > 0 ? H / 32 : 0) + dense * (H / 32) + groups * (H / (4 * kDownRowsPerWave));
 }
 
-hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *w_gate_up, const RouteBufs &r, float *A,
-                                int T, int H, int I, int Imax, int grid, hipStream_t s) {
+hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
+                                const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
+                                hipStream_t s) {
   if (wdtype == 1)
-    expert_gateup_kernel<WBf16><<<grid, 256, 0, s>>>((const bf16_t *)xhat, (const bf16_t *)w_gate_up, r, A, T, H, I,
-                                                     Imax);
+    expert_gateup_kernel<WBf16><<<grid, 256, 0, s>>>((const bf16_t *)xhat, (const bf16_t *)xpk,
+                                                     (const bf16_t *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
   else
-    expert_gateup_kernel<WF32><<<grid, 256, 0, s>>>((const float *)xhat, (const float *)w_gate_up, r, A, T, H, I,
-                                                    Imax);
+    expert_gateup_kernel<WF32><<<grid, 256, 0, s>>>((const float *)xhat, (const float *)xpk,
+                                                    (const float *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down(int wdtype, const float *A, const void *w_down, const void *ws_down,
+hipError_t launch_expert_down(int wdtype, const float *A, const void *act, const void *w_down, const void *ws_down,
                               const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
                               int grid, hipStream_t s) {
   if (wdtype == 1)
-    expert_down_kernel<WBf16><<<grid, 256, 0, s>>>(A, (const bf16_t *)w_down, (const bf16_t *)ws_down, r, P,
-                                                   T, H, K, I, Is, Imax);
+    expert_down_kernel<WBf16><<<grid, 256, 0, s>>>(A, (const char *)act, (const bf16_t *)w_down,
+                                                   (const bf16_t *)ws_down, r, P, T, H, K, I, Is, Imax);
   else
-    expert_down_kernel<WF32><<<grid, 256, 0, s>>>(A, (const float *)w_down, (const float *)ws_down, r, P, T,
-                                                  H, K, I, Is, Imax);
+    expert_down_kernel<WF32><<<grid, 256, 0, s>>>(A, (const char *)act, (const float *)w_down,
+                                                  (const float *)ws_down, r, P, T, H, K, I, Is, Imax);
   return hipGetLastError();
 }
 

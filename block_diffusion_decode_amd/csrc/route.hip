@@ -45,12 +45,20 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *out, size_t i, float4 v) 
   *reinterpret_cast<uint2 *>(out + i) = make_uint2(pack2(f2bf(v.x), f2bf(v.y)), pack2(f2bf(v.z), f2bf(v.w)));
 }
 
-// x_hat = h / sqrt(mean(h^2) + eps), unit gain, one workgroup per position.
+// Elements k .. k + 3 of position t into the packed block (see xpack_unit).
+template <typename OT>
+__device__ __forceinline__ void store4_packed(OT *xpk, int t, int T, int k, float4 v) {
+  constexpr int CH = 16 / (int)sizeof(OT);
+  store4<OT>(xpk, (size_t)xpack_unit(k / CH, t, T) * CH + k % CH, v);
+}
+
+// x_hat = h / sqrt(mean(h^2) + eps), unit gain, one workgroup per position;
+// also into the packed block `xpk` when given.
 template <typename OT>
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__restrict__ in,
                                                               float *__restrict__ copy_out,
-                                                              OT *__restrict__ out, int H, float eps,
-                                                              int32_t *__restrict__ zero_word) {
+                                                              OT *__restrict__ out, OT *__restrict__ xpk, int H,
+                                                              float eps, int32_t *__restrict__ zero_word) {
   __shared__ float red[kRowThreads / 64];
   if (blockIdx.x == 0 && threadIdx.x == 0 && zero_word) *zero_word = 0;
   const size_t base = (size_t)blockIdx.x * H;
@@ -70,8 +78,9 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__res
     const int j = threadIdx.x + q * kRowThreads;
     if (j < H4) {
       if (copy_out) reinterpret_cast<float4 *>(copy_out + base)[j] = v[q];
-      store4<OT>(out, base + 4 * (size_t)j,
-                 make_float4(v[q].x * inv, v[q].y * inv, v[q].z * inv, v[q].w * inv));
+      const float4 o = make_float4(v[q].x * inv, v[q].y * inv, v[q].z * inv, v[q].w * inv);
+      store4<OT>(out, base + 4 * (size_t)j, o);
+      if (xpk) store4_packed<OT>(xpk, blockIdx.x, gridDim.x, 4 * j, o);
     }
   }
 }
@@ -328,10 +337,10 @@ static_assert(kSelThreads == 256, "the shared gate/up item runs on four waves");
 // Shared-expert operands for the workgroups past the positions.
 template <class W>
 struct SharedGU {
-  const typename W::T *xhat;
+  const typename W::T *xpk;    // packed normalised block
   const typename W::T *wsgu;   // [2 I_s][H]
-  float *A;                    // rows T*K + t
-  int H, Is, TK, Imax;
+  char *act;                   // its packed activation slot (entry t = position t)
+  int H, Is;
 };
 
 __device__ __forceinline__ uint32_t order_key(float v) {
@@ -360,7 +369,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   const int t = blockIdx.x;
   if (t >= T) {
     __shared__ f32x4 red[4 * 2 * 2 * 64];
-    shared_gateup_item<W>(sg.wsgu, sg.xhat, T, sg.H, sg.Is, sg.TK, sg.Imax, (t - T) * 16, wave, lane, sg.A, red);
+    // column entry j is position j
+    int pos[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int j = n * 16 + (lane & 15);
+      pos[n] = j < T ? j : -1;
+    }
+    dense_gateup_item<W, kSgSteps>(sg.wsgu, sg.Is, sg.xpk, T, sg.H, pos, t - T, (t - T) * 16, wave, lane, sg.act,
+                                   red);
     return;
   }
   {
@@ -492,12 +509,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   const int slot = union_scan(sh, E);
   const uint32_t tbits = slot >= 0 ? sh.tokmask[tid] : 0u;
   if (slot >= 0) r.union_list[slot] = tid;
-  // token groups of kTokGroup positions, in union order (exclusive scan of
-  // each union expert's group count), one 8-word record each:
-  // [expert, positions, (t*K + k) | t << 16 per position, 0 ...]
+  // Work lists, in union order.  An expert with at most kTokGroup positions
+  // gets one token-group record of 8 words:
+  //   [expert, positions, (t*K + k) | t << 16 per position, 0 ...];
+  // one with more gets a dense record of kDenseRec words:
+  //   [expert, positions, 0 x 6, (t*K + k) | t << 16 per position].
+  // Both counts come from one exclusive scan (groups in the low half-word).
   const int npos = __popc(tbits);
-  const int ngr = (npos + kTokGroup - 1) / kTokGroup;
-  int incl = ngr;
+  const bool dense = npos > kTokGroup;
+  const int cnt = dense ? 1 << 16 : (npos + kTokGroup - 1) / kTokGroup;
+  int incl = cnt;
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) {
     const int o = __shfl_up(incl, s);
@@ -505,12 +526,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   }
   if (lane == 63) sh.wtot[wave] = incl;
   __syncthreads();
-  int goff = incl - ngr, gtot = 0;
+  int off = incl - cnt, tot = 0;
   for (int w = 0; w < kSelThreads / 64; ++w) {
-    if (w < wave) goff += sh.wtot[w];
-    gtot += sh.wtot[w];
+    if (w < wave) off += sh.wtot[w];
+    tot += sh.wtot[w];
   }
-  {
+  const int gtot = tot & 0xffff, dtot = tot >> 16;
+  if (dense) {
+    int32_t *rec = r.dlist + (off >> 16) * kDenseRec;
+    rec[0] = tid;
+    rec[1] = npos;
+    uint32_t bits = tbits;
+    for (int j = 0; bits; ++j) {
+      const int tt = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      rec[8 + j] = (tt * K + sh.kslot[tt][tid]) | (tt << 16);
+    }
+  } else {
+    const int goff = off & 0xffff;
     uint32_t bits = tbits;
     int j = 0;
     while (bits) {
@@ -528,6 +561,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   }
   if (tid == 0) {
     r.meta[2] = gtot;
+    r.meta[3] = dtot;
     r.meta[0] = sh.nu;
     r.meta[1] = sh.csize;
     if (r.n_distinct_out) *r.n_distinct_out = sh.nu;
@@ -561,7 +595,7 @@ __global__ __launch_bounds__(256) void coreset_kernel(const float *__restrict__ 
 
 // ------------------------------------------------------------------ combine
 // y_t = sum_k w[t*K+k] * P[t*K+k] (live slots, in slot order) + P_s[t]; then h += y and
-// xhat = RMSNorm(h), one workgroup per position.
+// xhat = RMSNorm(h) (also packed into xpk_out when given), one workgroup per position.
 template <typename OT>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__restrict__ P,
                                                               const float *__restrict__ P_s,
@@ -569,7 +603,8 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
                                                               const float *__restrict__ wgt,
                                                               float *__restrict__ h,
                                                               float *__restrict__ y_out,
-                                                              OT *__restrict__ xhat_out, int H, int K,
+                                                              OT *__restrict__ xhat_out,
+                                                              OT *__restrict__ xpk_out, int H, int K,
                                                               float eps) {
   __shared__ float red[kRowThreads / 64];
   const int t = blockIdx.x;
@@ -612,21 +647,25 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
 #pragma unroll
     for (int q = 0; q < kRowVec; ++q) {
       const int j = threadIdx.x + q * kRowThreads;
-      if (j < H4)
-        store4<OT>(xhat_out, base + 4 * (size_t)j,
-                   make_float4(hv[q].x * inv, hv[q].y * inv, hv[q].z * inv, hv[q].w * inv));
+      if (j < H4) {
+        const float4 o = make_float4(hv[q].x * inv, hv[q].y * inv, hv[q].z * inv, hv[q].w * inv);
+        store4<OT>(xhat_out, base + 4 * (size_t)j, o);
+        if (xpk_out) store4_packed<OT>(xpk_out, t, gridDim.x, 4 * j, o);
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, int T, int H,
+hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, void *xpk, int T, int H,
                           int32_t *zero_word, hipStream_t s) {
   if (wdtype == 1)
-    rmsnorm_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(in, copy_out, (bf16_t *)out, H, 1e-6f, zero_word);
+    rmsnorm_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(in, copy_out, (bf16_t *)out, (bf16_t *)xpk, H, 1e-6f,
+                                                     zero_word);
   else
-    rmsnorm_kernel<float><<<T, kRowThreads, 0, s>>>(in, copy_out, (float *)out, H, 1e-6f, zero_word);
+    rmsnorm_kernel<float><<<T, kRowThreads, 0, s>>>(in, copy_out, (float *)out, (float *)xpk, H, 1e-6f,
+                                                    zero_word);
   return hipGetLastError();
 }
 
@@ -651,15 +690,15 @@ hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const
 }
 
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
-                               int32_t *sorted_ids, int32_t *done_count, int wdtype, const void *xhat,
-                               const void *ws_gate_up, float *A, int Is, int Imax, hipStream_t s) {
+                               int32_t *sorted_ids, int32_t *done_count, int wdtype, const void *xpk,
+                               const void *ws_gate_up, void *act_shared, int Is, hipStream_t s) {
   const int grid = T + Is / 16;
   if (wdtype == 1) {
-    const SharedGU<WBf16> sg = {(const bf16_t *)xhat, (const bf16_t *)ws_gate_up, A, H, Is, T * K, Imax};
+    const SharedGU<WBf16> sg = {(const bf16_t *)xpk, (const bf16_t *)ws_gate_up, (char *)act_shared, H, Is};
     select_kernel<WBf16><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids,
                                                       done_count, sg);
   } else {
-    const SharedGU<WF32> sg = {(const float *)xhat, (const float *)ws_gate_up, A, H, Is, T * K, Imax};
+    const SharedGU<WF32> sg = {(const float *)xpk, (const float *)ws_gate_up, (char *)act_shared, H, Is};
     select_kernel<WF32><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids,
                                                      done_count, sg);
   }
@@ -673,14 +712,14 @@ hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, i
 }
 
 hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const int32_t *idx,
-                          const float *wgt, float *h, float *y_out, void *xhat_out, int T, int H, int K,
-                          hipStream_t s) {
+                          const float *wgt, float *h, float *y_out, void *xhat_out, void *xpk_out, int T, int H,
+                          int K, hipStream_t s) {
   if (wdtype == 1)
-    combine_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (bf16_t *)xhat_out, H, K,
-                                             1e-6f);
+    combine_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (bf16_t *)xhat_out,
+                                                     (bf16_t *)xpk_out, H, K, 1e-6f);
   else
-    combine_kernel<float><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (float *)xhat_out, H, K,
-                                            1e-6f);
+    combine_kernel<float><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (float *)xhat_out,
+                                                    (float *)xpk_out, H, K, 1e-6f);
   return hipGetLastError();
 }
 

@@ -49,11 +49,13 @@ __device__ __forceinline__ void pipeline_post(int steps, Bufs &b0, Bufs &b1, Loa
 }
 
 // ---------------------------------------------------------------------------
-// Shared expert, MFMA.  Every position goes through it, so its contraction is
-// dense: 16x16 tiles with 16 weight rows as A and 16 positions as B (two
-// column tiles for 32 positions), in one pass over its weights.  At k-step s
-// lane group g = lane >> 4 holds chunk 4s + g of its row, so a load reads 64
-// contiguous bytes of each of 16 rows.
+// Dense experts, MFMA.  Every position goes through the shared expert, and a
+// routed expert picked by more than kTokGroup positions (common under skewed
+// routing) sees many of them, so their contraction is dense: 16x16 tiles with
+// 16 weight rows as A and 16 positions as B (two column tiles for 32
+// positions), in one pass over the weights.  At k-step s lane group
+// g = lane >> 4 holds chunk 4s + g of its row, so a load reads 64 contiguous
+// bytes of each of 16 rows.
 // ---------------------------------------------------------------------------
 
 template <class W>
@@ -68,83 +70,124 @@ __device__ __forceinline__ f32x4 mfma_chunk(const uint4 &a, const uint4 &b, f32x
   }
 }
 
-constexpr int kSgSteps = 4;   // k-steps per load batch of the shared gate/up
-struct SgBufs {
-  uint4 a[kSgSteps][2];   // [k-step][gate, up]
-  uint4 b[kSgSteps][2];   // [k-step][column tile]
+// Packed normalised block (the dense items' B operand): chunk C (kChunk
+// elements) of position t sits at 16-byte unit (C / 4 * T + t) * 4 + C % 4,
+// so the 16 positions x 4 chunks of one MFMA k-step are one contiguous KiB.
+__device__ __forceinline__ uint32_t xpack_unit(int C, int t, int T) {
+  return (uint32_t)(((C >> 2) * T + t) * 4 + (C & 3));
+}
+
+// Packed activations of one dense expert (a slot of Imax * 128 bytes): per
+// k-step of 4 chunks, `planes` planes of kMaxT entries x 4 chunks of 16 B.
+// bf16 weights take two planes, the bf16 high parts and the bf16 residuals
+// of the fp32 activations; fp32 weights take one plane of fp32 values.
+template <class W>
+constexpr int act_planes() { return std::is_same<W, WBf16>::value ? 2 : 1; }
+__device__ __forceinline__ uint32_t act_unit(int C, int plane, int e, int planes) {
+  return (uint32_t)((((C >> 2) * planes + plane) * kMaxT + e) * 4 + (C & 3));
+}
+
+constexpr int kSgSteps = 4;   // k-steps per load batch of the shared gate/up beside selection
+template <int STEPS>
+struct DgBufs {
+  uint4 a[STEPS][2];   // [k-step][gate, up]
+  uint4 b[STEPS][2];   // [k-step][column tile]
 };
 
-// Gate/up rows i0 .. i0 + 15 (and Is + i0 ..) of the shared expert for every
-// position; the four waves split the hidden dimension and add their partial
-// tiles through LDS (`red`, 16 KiB).  A[T*K + t][i] = silu(gate) * up.
-template <class W>
-__device__ __forceinline__ void shared_gateup_item(const typename W::T *__restrict__ wsgu,
-                                                   const typename W::T *__restrict__ xhat, int T, int H, int Is,
-                                                   int TK, int Imax, int i0, int wave, int lane,
-                                                   float *__restrict__ A, f32x4 *red) {
+// Gate/up rows i0 .. i0 + 15 (and ie + i0 ..) of one expert, W_gu [2 ie][H],
+// for up to 32 column entries (two tiles of 16).  Lane (li, g) names entries
+// li and 16 + li by their positions pos[n] (-1: no entry).  The four waves
+// split the hidden dimension, each starting its k-steps `rot` steps in (so
+// concurrent items spread their reads of the packed block), and add their
+// partial tiles through LDS (`red`, 16 KiB); waves 0 and 1 finish column
+// tiles 0 and 1 and store silu(gate) * up into the packed activation slot.
+template <class W, int STEPS>
+__device__ __forceinline__ void dense_gateup_item(const typename W::T *__restrict__ w, int ie,
+                                                  const typename W::T *__restrict__ xpk, int T, int H,
+                                                  const int (&pos)[2], int rot, int i0, int wave, int lane,
+                                                  char *__restrict__ act, f32x4 *red) {
   typedef typename W::T WT;
   constexpr int CH = W::kChunk;
   const int li = lane & 15, g = lane >> 4;
   const int ncw = H / CH / 4;               // chunks of this wave's quarter of H
   const int cw0 = wave * ncw;
   const int ksteps = (ncw + 3) / 4;
-  const rsrc_t rw = make_rsrc(wsgu, (uint32_t)(2 * Is * H) * sizeof(WT));
-  const rsrc_t rx = make_rsrc(xhat, (uint32_t)(T * H) * sizeof(WT));
+  rot %= ksteps;
+  const rsrc_t rw = make_rsrc(w, (uint32_t)(2 * ie * H) * sizeof(WT));
+  const rsrc_t rx = make_rsrc(xpk, (uint32_t)(T * H) * sizeof(WT));
   const uint32_t rowg = (uint32_t)((i0 + li) * H) * sizeof(WT);
-  const uint32_t rowu = (uint32_t)((Is + i0 + li) * H) * sizeof(WT);
-  uint32_t rowx[2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
-    rowx[n] = n * 16 + li < T ? (uint32_t)((n * 16 + li) * H) * sizeof(WT) : kOutOfRange;
+  const uint32_t rowu = (uint32_t)((ie + i0 + li) * H) * sizeof(WT);
   f32x4 acc[2][2];   // [gate, up][column tile]
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int bt, SgBufs &b) {
+  auto load = [&](int bt, DgBufs<STEPS> &b) {
 #pragma unroll
-    for (int j = 0; j < kSgSteps; ++j) {
-      const int ks = kSgSteps * bt + j;
-      const int c = 4 * ks + g;
+    for (int j = 0; j < STEPS; ++j) {
+      const int ks = STEPS * bt + j;
+      int kr = ks + rot;
+      kr = kr >= ksteps ? kr - ksteps : kr;
+      const int c = 4 * kr + g;
       const bool live = ks < ksteps && c < ncw;
       const uint32_t co = (uint32_t)((cw0 + c) * CH) * sizeof(WT);
       b.a[j][0] = buf_ld16(rw, live ? rowg + co : kOutOfRange, 0);
       b.a[j][1] = buf_ld16(rw, live ? rowu + co : kOutOfRange, 0);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) b.b[j][n] = buf_ld16(rx, live ? rowx[n] + co : kOutOfRange, 0);
+      for (int n = 0; n < 2; ++n)
+        b.b[j][n] = buf_ld16(rx, live && pos[n] >= 0 ? xpack_unit(cw0 + c, pos[n], T) * 16u : kOutOfRange, 0);
     }
   };
-  auto step = [&](int, const SgBufs &b) {
+  auto step = [&](int, const DgBufs<STEPS> &b) {
 #pragma unroll
-    for (int j = 0; j < kSgSteps; ++j)
+    for (int j = 0; j < STEPS; ++j)
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int n = 0; n < 2; ++n) acc[q][n] = mfma_chunk<W>(b.a[j][q], b.b[j][n], acc[q][n]);
   };
-  SgBufs b0, b1;
-  pipeline((ksteps + kSgSteps - 1) / kSgSteps, b0, b1, load, step);
+  DgBufs<STEPS> b0, b1;
+  pipeline((ksteps + STEPS - 1) / STEPS, b0, b1, load, step);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int n = 0; n < 2; ++n) red[((wave * 2 + q) * 2 + n) * 64 + lane] = acc[q][n];
   __syncthreads();
   if (wave < 2) {
-    // wave n finishes column tile n: rows i0 + 4g + r, position 16n + li
+    // wave n finishes column tile n: rows i0 + 4g + r, entry 16n + li
     const int n = wave;
     f32x4 gt = red[n * 64 + lane], up = red[(2 + n) * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const f32x4 a = red[((w * 2 + 0) * 2 + n) * 64 + lane], b = red[((w * 2 + 1) * 2 + n) * 64 + lane];
+    for (int v = 1; v < 4; ++v) {
+      const f32x4 a = red[((v * 2 + 0) * 2 + n) * 64 + lane], b = red[((v * 2 + 1) * 2 + n) * 64 + lane];
       gt += a;
       up += b;
     }
-    const int t = n * 16 + li;
-    if (t < T) {
-      float4 o;
-      o.x = silu(gt[0]) * up[0]; o.y = silu(gt[1]) * up[1];
-      o.z = silu(gt[2]) * up[2]; o.w = silu(gt[3]) * up[3];
-      *reinterpret_cast<float4 *>(A + (size_t)(TK + t) * Imax + i0 + 4 * g) = o;
+    // (value arithmetic, not pos[n]: a runtime index would leave the array in
+    // memory, which the compiler places in LDS addressed through the dispatch
+    // packet, a slow first load in every workgroup)
+    const int my_pos = pos[0] + (n & 1) * (pos[1] - pos[0]);
+    if (my_pos >= 0) {
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = silu(gt[r]) * up[r];
+      const int e = 16 * n + li, i = i0 + 4 * g;
+      if constexpr (std::is_same<W, WBf16>::value) {
+        // four values: half of chunk i / 8, as high parts and residuals
+        bf16_t hv[4], lv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          hv[r] = f2bf(o[r]);
+          lv[r] = f2bf(o[r] - bf2f(hv[r]));
+        }
+        const uint32_t half = (uint32_t)(i & 7) * 2u;
+        *reinterpret_cast<uint2 *>(act + act_unit(i >> 3, 0, e, 2) * 16u + half) =
+            make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
+        *reinterpret_cast<uint2 *>(act + act_unit(i >> 3, 1, e, 2) * 16u + half) =
+            make_uint2(pack2(lv[0], lv[1]), pack2(lv[2], lv[3]));
+      } else {
+        *reinterpret_cast<float4 *>(act + act_unit(i >> 2, 0, e, 1) * 16u) = make_float4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
   __syncthreads();  // `red` is free for the next item

@@ -92,6 +92,42 @@ def test_moe_forward_tiny_fp32(seed):
     _check_moe(d, out, y_ref, info, xh, 1.0)
 
 
+@pytest.mark.parametrize("T,top_p", [(4, 1.0), (5, 1.0), (16, 1.0), (17, 1.0), (32, 1.0), (32, 0.7), (13, 0.7)])
+def test_moe_forward_dense_experts(T, top_p):
+    # a large bias on experts 0..2 sends every position to them: experts with
+    # exactly T positions (token-group path at T <= 4, one dense column tile at
+    # T <= 16, two above), next to the other picks' mix of groups and dense
+    # experts; at top_p 0.7 the coreset keeps only the forced experts
+    d = W.Dims(f"forced{T}", T=T, H=256, E=40, K=6, I=96, I_s=64, V=16, wdtype="bf16", w_std=0.05,
+               lm_std=0.06)
+    layer = W.layer_weights(10, 0, d, device=DEV, bias="flat")   # seed 10: no decision in a margin band
+    layer["router_bias"][:3] = 10.0
+    h = W.block_hidden(10, d, device=DEV)
+    out = bdd.moe_block_forward(dims_of(d), layer, h, top_p)
+    torch.cuda.synchronize()
+    xh = O.bf16_round(O.rmsnorm(f64(h)))
+    y_ref, info = O.moe_layer(xh, oracle_layer(layer), d.K, top_p)
+    nb, gb = _check_moe(d, out, y_ref, info, xh, top_p)
+    assert not gb and nb == 0
+    n_e = np.bincount(np.asarray(info["idx"]).ravel()[np.asarray(info["idx"]).ravel() >= 0], minlength=d.E)
+    forced = [e for e in range(3) if info["coreset"] is None or e in info["coreset"]]
+    assert len(forced) >= 2 and (n_e[forced] == T).all()
+    print(f"T={T} top_p {top_p}: positions per union expert {sorted(n_e[n_e > 0].tolist(), reverse=True)}")
+
+
+def test_moe_forward_dense_experts_fp32():
+    d = SMALL_F32
+    layer = W.layer_weights(3, 0, d, device=DEV, bias="flat")
+    layer["router_bias"][:2] = 10.0
+    h = W.block_hidden(3, d, device=DEV)
+    out = bdd.moe_block_forward(dims_of(d), layer, h, 1.0)
+    torch.cuda.synchronize()
+    xh = O.rmsnorm(f64(h))
+    y_ref, info = O.moe_layer(xh, oracle_layer(layer), d.K, 1.0)
+    nb, gb = _check_moe(d, out, y_ref, info, xh, 1.0)
+    assert not gb and nb == 0
+
+
 def test_moe_forward_deterministic():
     d = SMALL_BF16
     layer = W.layer_weights(5, 0, d, device=DEV, bias="zipf")
