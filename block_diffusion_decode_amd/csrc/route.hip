@@ -230,12 +230,21 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   build_masks(sh, T, E, K);
   if (tid < E) {
+    // ascending positions, eight at a time (their slot reads are independent)
     double m = 0.0;
     uint32_t bits = sh.tokmask[tid];
     while (bits) {
-      const int t = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      m += (double)sh.psel[t][sh.kslot[t][tid]];
+      int tt[8], kq[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tt[j] = bits ? __ffs(bits) - 1 : -1;
+        bits &= bits - 1u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kq[j] = tt[j] >= 0 ? sh.kslot[tt[j]][tid] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (tt[j] >= 0) m += (double)sh.psel[tt[j]][kq[j]];
     }
     sh.mass[tid] = m;
     sh.member[tid] = 0;
@@ -246,6 +255,47 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
     // no coreset: every expert with a pick (positive mass) is kept
     if (tid < nu) sh.member[sh.ulist[tid]] = 1;
     if (tid == 0) sh.csize = nu;
+    __syncthreads();
+    return;
+  }
+  if (nu <= 64) {
+    // one wave: lane j holds union entry j; its rank comes from wave-uniform
+    // reads of every other lane, the ranked masses' prefix sum from a
+    // shuffle scan, the cut from a ballot (no barriers)
+    if (wave == 0) {
+      const bool live = lane < nu;
+      const int e = live ? sh.ulist[lane] : 0;
+      const double m = live ? sh.mass[e] : 0.0;
+      const long long mb = __double_as_longlong(m);
+      int r = 0;
+      for (int i = 0; i < nu; ++i) {
+        const double mi = __longlong_as_double(
+            ((long long)__builtin_amdgcn_readlane((int)(mb >> 32), i) << 32) |
+            (long long)(uint32_t)__builtin_amdgcn_readlane((int)mb, i));
+        const int ei = __builtin_amdgcn_readlane(e, i);
+        r += (mi > m) || (mi == m && ei < e);
+      }
+      if (live) {
+        sh.sorted[r] = e;
+        sh.cum[r] = m;
+      }
+      double v = live ? sh.cum[lane] : 0.0;
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) {
+        const double o = __shfl_up(v, s);
+        if (lane >= s) v += o;
+      }
+      const long long tb = __double_as_longlong(v);
+      const double total = __longlong_as_double(
+          ((long long)__builtin_amdgcn_readlane((int)(tb >> 32), nu - 1) << 32) |
+          (long long)(uint32_t)__builtin_amdgcn_readlane((int)tb, nu - 1));
+      const double target = (double)top_p * total;
+      const int below = (int)__popcll(__ballot(live && v < target));
+      const int k = max(1, min(below + 1, nu));
+      if (live) sh.cum[lane] = v;
+      if (lane < k) sh.member[sh.sorted[lane]] = 1;
+      if (lane == 0) sh.csize = k;
+    }
     __syncthreads();
     return;
   }
@@ -307,16 +357,12 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
   __syncthreads();
 }
 
+// Coreset membership bitset from a ballot per wave (>= E threads).
 __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
-  const int tid = threadIdx.x;
-  if (tid < (E + 31) / 32) {
-    uint32_t b = 0;
-    for (int j = 0; j < 32; ++j) {
-      const int e = tid * 32 + j;
-      if (e < E && sh.member[e]) b |= 1u << j;
-    }
-    bits[tid] = b;
-  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const unsigned long long b = __ballot(tid < E && sh.member[tid] != 0);
+  if (lane == 0 && 64 * w < E) bits[2 * w] = (uint32_t)b;
+  if (lane == 32 && 64 * w + 32 < E) bits[2 * w + 1] = (uint32_t)(b >> 32);
 }
 
 // ------------------------------------------------------------------ route + select
@@ -388,6 +434,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
 #pragma unroll 16
       for (int ks = 0; ks < KS; ++ks) acc += r.logits[((size_t)ks * T + t) * E + tid];
       l = acc + (bias ? bias[tid] : 0.f);
+      // the position's full logits replace its row of slice 0 (read by no
+      // other workgroup) for the coreset re-routing
+      publish(r.logits + (size_t)t * E + tid, l);
     }
     float m = wave_max_dpp(l);
     if (lane == 0) s_red[wave] = m;
@@ -446,56 +495,97 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   write_bits(sh, E, r.cs_bits);
   if (top_p < 1.0f) {
     // each position re-takes its first min(K, |C|) coreset members in its own
-    // (logit desc, id asc) order.  Every position's sorted list is staged in
-    // LDS first (ids fit a byte; all loads in flight at once), the scans run
-    // from LDS, then the chosen experts' probabilities arrive in one batch.
-    __shared__ uint8_t s_sorted[kMaxT * kMaxE];
-    constexpr int kStage = kMaxT * kMaxE / kSelThreads;
-    int v[kStage];
-#pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const int i = tid + j * kSelThreads;
-      v[j] = i < T * E ? fetch_published(sorted_ids + i) : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const int i = tid + j * kSelThreads;
-      if (i < T * E) s_sorted[i] = (uint8_t)v[j];
-    }
-    __syncthreads();
+    // (logit desc, id asc) order.
     const int kk = min(K, sh.csize);
-    constexpr int kChunks = kMaxE / 64;
-    for (int tt = wave; tt < T; tt += kSelThreads / 64) {
-      // the position's whole sorted list at once: member flags of the 4
-      // chunks, then each member's rank among the members before it
-      int e[kChunks];
-      unsigned long long b[kChunks];
+    if (sh.csize <= 64) {
+      // Lane j of a wave holds member j (mass rank order) and, for each of the
+      // wave's positions, that member's logit and score; a member's slot is
+      // its rank among the members by (logit desc, id asc).  All loads of a
+      // wave are in flight together.
+      const int C = sh.csize;
+      const int c = lane < C ? sh.sorted[lane] : 0;
+      constexpr int kPer = kMaxT / (kSelThreads / 64);
+      float lv[kPer], pv[kPer];
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const int i = c * 64 + lane;
-        e[c] = i < E ? (int)s_sorted[tt * E + i] : -1;
+      for (int i = 0; i < kPer; ++i) {
+        const int tt = wave + i * (kSelThreads / 64);
+        const bool ok = tt < T && lane < C;
+        lv[i] = ok ? fetch_published(r.logits + (size_t)tt * E + c) : 0.f;
+        pv[i] = ok ? fetch_published(r.prob + (size_t)tt * E + c) : 0.f;
       }
-      int mem[kChunks];
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) mem[c] = sh.member[e[c] & (kMaxE - 1)];   // unconditional
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) b[c] = __ballot(e[c] >= 0 && mem[c] != 0);
-      int taken = 0;
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const int before = taken + __popcll(b[c] & ((1ull << lane) - 1ull));
-        if (((b[c] >> lane) & 1ull) && before < kk) sh.idx[tt][before] = e[c];
-        taken += __popcll(b[c]);
+      for (int i = 0; i < kPer; ++i) {
+        const int tt = wave + i * (kSelThreads / 64);
+        if (tt >= T) break;
+        const unsigned long long key = lane < C ? ((unsigned long long)order_key(lv[i]) << 32) | (uint32_t)c : ~0ull;
+        int rk = 0;
+        for (int j = 0; j < C; ++j) {
+          const unsigned long long kj =
+              ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), j) << 32) |
+              (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+          rk += kj < key;
+        }
+        if (lane < C && rk < kk) {
+          sh.idx[tt][rk] = c;
+          sh.psel[tt][rk] = pv[i];
+        }
+        if (lane < K && lane >= kk) {
+          sh.idx[tt][lane] = -1;
+          sh.psel[tt][lane] = 0.f;
+        }
       }
-      if (lane < K && lane >= kk) sh.idx[tt][lane] = -1;
+      __syncthreads();
+    } else {
+      // every position's sorted list is staged in LDS (ids fit a byte; all
+      // loads in flight at once), the scans run from LDS, then the chosen
+      // experts' probabilities arrive in one batch
+      __shared__ uint8_t s_sorted[kMaxT * kMaxE];
+      constexpr int kStage = kMaxT * kMaxE / kSelThreads;
+      int v[kStage];
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) {
+        const int i = tid + j * kSelThreads;
+        v[j] = i < T * E ? fetch_published(sorted_ids + i) : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) {
+        const int i = tid + j * kSelThreads;
+        if (i < T * E) s_sorted[i] = (uint8_t)v[j];
+      }
+      __syncthreads();
+      constexpr int kChunks = kMaxE / 64;
+      for (int tt = wave; tt < T; tt += kSelThreads / 64) {
+        // the position's whole sorted list at once: member flags of the 4
+        // chunks, then each member's rank among the members before it
+        int e[kChunks];
+        unsigned long long b[kChunks];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const int i = c * 64 + lane;
+          e[c] = i < E ? (int)s_sorted[tt * E + i] : -1;
+        }
+        int mem[kChunks];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) mem[c] = sh.member[e[c] & (kMaxE - 1)];   // unconditional
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) b[c] = __ballot(e[c] >= 0 && mem[c] != 0);
+        int taken = 0;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const int before = taken + __popcll(b[c] & ((1ull << lane) - 1ull));
+          if (((b[c] >> lane) & 1ull) && before < kk) sh.idx[tt][before] = e[c];
+          taken += __popcll(b[c]);
+        }
+        if (lane < K && lane >= kk) sh.idx[tt][lane] = -1;
+      }
+      __syncthreads();
+      for (int i = tid; i < T * K; i += kSelThreads) {
+        const int tt = i / K, k = i - tt * K;
+        const int e = sh.idx[tt][k];
+        sh.psel[tt][k] = e >= 0 ? fetch_published(r.prob + (size_t)tt * E + e) : 0.f;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int i = tid; i < T * K; i += kSelThreads) {
-      const int tt = i / K, k = i - tt * K;
-      const int e = sh.idx[tt][k];
-      sh.psel[tt][k] = e >= 0 ? fetch_published(r.prob + (size_t)tt * E + e) : 0.f;
-    }
-    __syncthreads();
     build_masks(sh, T, E, K);
   }
   for (int i = tid; i < T * K; i += kSelThreads) {
