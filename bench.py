@@ -56,6 +56,9 @@ def main():
     ap.add_argument("--stack", type=int, default=0, metavar="L",
                     help="also measure an L-layer stack round (Zipf routing, coreset 0.9) and a full block "
                          "resolve on it; reported under 'stack', not as the value")
+    ap.add_argument("--stack-only", type=int, default=0, metavar="L",
+                    help="only run the L-layer stack measurement (for a kernel trace of that workload alone); "
+                         "prints one JSON line with the 'stack' object")
     ap.add_argument("--counter-run", action="store_true",
                     help="only run 3 rounds on inputs drawn with torch.randn (a handful of kernel launches "
                          "besides the library's), for hardware-counter collection")
@@ -87,6 +90,10 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
         return
     d = W.C1
+    if args.stack_only:
+        args.stack = args.stack_only
+        print(json.dumps({"stack": stack_round(args, W.C1, dev)}), flush=True)
+        return
     if args.counter_run:
         counter_run(d, dev)
         return
