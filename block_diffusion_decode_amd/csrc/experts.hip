@@ -169,17 +169,22 @@ __device__ __forceinline__ void gateup_group(const Group &g, const typename W::T
   }
 }
 
-constexpr int kSdSteps = 4;   // k-steps per load batch of a dense down projection
+constexpr int kDenseRowTiles = 2;   // 16-row tiles per dense down item (32 rows)
+// k-steps per load batch of a dense down projection: all of a wave's quarter
+// of I = 512 in one batch at two row tiles
+template <int MT>
+constexpr int dense_down_batch() { return MT <= 2 ? 4 : 2; }
 
-// Down projection of one dense expert, W_d [H][ie], for rows h0 .. h0 + 31
-// (two row tiles) and up to 32 column entries, from the expert's packed
+// Down projection of one dense expert, W_d [H][ie], for rows h0 .. h0 + 16 MT - 1
+// (MT row tiles) and up to 32 column entries, from the expert's packed
 // activation slot (see act_unit).  Lane (li, g) names entries li and 16 + li
 // by their rows row[n] in P (-1: no entry).  The four waves split the
-// intermediate dimension; each issues all loads of a batch of kSdSteps
-// k-steps at once, and the partial tiles are added in LDS (`red`, 16 KiB).
-// With bf16 weights the activations enter as bf16 high parts and residuals
-// (two MFMA passes).  P[row][h] = A_entry . W_d[h].
-template <class W>
+// intermediate dimension; each issues the loads of a batch of k-steps at
+// once, and the partial tiles are added in LDS (`red`, MT * 8 KiB).  With bf16
+// weights the activations enter as bf16 high parts and residuals (two MFMA
+// passes); every activation load serves MT weight tiles.
+// P[row][h] = A_entry . W_d[h].
+template <class W, int MT>
 __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict__ w, int ie,
                                                 const char *__restrict__ act, int H, const int (&row)[2], int h0,
                                                 int wave, int lane, float *__restrict__ P, f32x4 *red) {
@@ -193,23 +198,24 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
   const int ksteps = (ncw + 3) / 4;
   const rsrc_t rw = make_rsrc(w, (uint32_t)(H * ie) * sizeof(WT));
   const rsrc_t ra = make_rsrc(act, (uint32_t)ie * kActSlotPerI);
-  uint32_t rowa[2];
+  uint32_t rowa[MT];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) rowa[m] = (uint32_t)((h0 + 16 * m + li) * ie) * sizeof(WT);
-  f32x4 acc[2][2];   // [row tile][column tile]
+  for (int m = 0; m < MT; ++m) rowa[m] = (uint32_t)((h0 + 16 * m + li) * ie) * sizeof(WT);
+  f32x4 acc[MT][2];   // [row tile][column tile]
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int kSdSteps = dense_down_batch<MT>();
   for (int k0 = 0; k0 < ksteps; k0 += kSdSteps) {
-    uint4 wa[kSdSteps][2], xa[kSdSteps][2][NP];
+    uint4 wa[kSdSteps][MT], xa[kSdSteps][2][NP];
 #pragma unroll
     for (int j = 0; j < kSdSteps; ++j) {
       const int c = 4 * (k0 + j) + g;
       const bool live = k0 + j < ksteps && c < ncw;
       const int C = cw0 + c;
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < MT; ++m)
         wa[j][m] = buf_ld16(rw, live ? rowa[m] + (uint32_t)(C * CH) * sizeof(WT) : kOutOfRange, 0);
 #pragma unroll
       for (int n = 0; n < 2; ++n)
@@ -222,23 +228,24 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MT; ++m) {
           if constexpr (BF) acc[m][n] = mfma_bf16(wa[j][m], xa[j][n][1], mfma_bf16(wa[j][m], xa[j][n][0], acc[m][n]));
           else acc[m][n] = mfma_chunk<W>(wa[j][m], xa[j][n][0], acc[m][n]);
         }
   }
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) red[((wave * 2 + m) * 2 + n) * 64 + lane] = acc[m][n];
+    for (int n = 0; n < 2; ++n) red[((wave * MT + m) * 2 + n) * 64 + lane] = acc[m][n];
   __syncthreads();
-  {
-    // wave v finishes row tile v >> 1, column tile v & 1
-    const int m = wave >> 1, n = wave & 1;
-    f32x4 v = red[(m * 2 + n) * 64 + lane];
+  // wave v finishes output tiles v, v + 4, ... (tile q: row tile q >> 1, column tile q & 1)
 #pragma unroll
-    for (int u = 1; u < 4; ++u) v += red[((u * 2 + m) * 2 + n) * 64 + lane];
-    const int rw_ = row[0] + (n & 1) * (row[1] - row[0]);   // value arithmetic: no runtime-indexed array
+  for (int q0 = 0; q0 < 2 * MT; q0 += 4) {
+    const int q = q0 + wave, m = q >> 1, n = q & 1;
+    f32x4 v = red[q * 64 + lane];
+#pragma unroll
+    for (int u = 1; u < 4; ++u) v += red[(u * MT * 2 + q) * 64 + lane];
+    const int rw_ = row[0] + n * (row[1] - row[0]);   // value arithmetic: no runtime-indexed array
     if (rw_ >= 0)
       *reinterpret_cast<float4 *>(P + (size_t)rw_ * H + h0 + 16 * m + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
   }
@@ -458,10 +465,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
                                                           int H, int K, int I, int Is, int Imax) {
   typedef typename W::T WT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tiles = H / (4 * kDownRowsPerWave), dtiles = H / 32;
+  constexpr int DR = 16 * kDenseRowTiles;   // rows per dense item
+  const int tiles = H / (4 * kDownRowsPerWave), dtiles = H / DR;
   const int s_items = Is > 0 ? dtiles : 0;
   const int d_end = s_items + uniform(r.meta[3]) * dtiles;
-  __shared__ f32x4 red[4 * 2 * 2 * 64];
+  __shared__ f32x4 red[4 * kDenseRowTiles * 2 * 64];
   const int items = d_end + uniform(r.meta[2]) * tiles;
   const uint32_t a_bytes = (uint32_t)(T * K) * (uint32_t)Imax * 4u;
   const size_t eb = (size_t)H * I * sizeof(WT);
@@ -480,7 +488,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
       }
       w = wsd;
       ie = Is;
-      h0 = item * 32;
+      h0 = item * DR;
       slot = 0;
     } else {
       const int di = (item - s_items) / dtiles;
@@ -490,10 +498,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
       for (int c = 0; c < 2; ++c) row[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
       w = wd + (size_t)e * H * I;
       ie = I;
-      h0 = (item - s_items - di * dtiles) * 32;
+      h0 = (item - s_items - di * dtiles) * DR;
       slot = 1 + di;
     }
-    dense_down_item<W>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, H, row, h0, wave, lane, P, red);
+    dense_down_item<W, kDenseRowTiles>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, H, row, h0, wave, lane, P,
+                                       red);
   }
   int tile_next = 0;
   Group next;
@@ -527,7 +536,8 @@ int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup) {
   (void)T;
   const int groups = expert_groups_max(T, E, K), dense = expert_dense_max(T, E, K);
   if (gateup) return (groups + dense) * (I / 16);
-  return (Is > 0 ? H / 32 : 0) + dense * (H / 32) + groups * (H / (4 * kDownRowsPerWave));
+  const int dtiles = H / (16 * kDenseRowTiles);
+  return (Is > 0 ? dtiles : 0) + dense * dtiles + groups * (H / (4 * kDownRowsPerWave));
 }
 
 hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,

@@ -240,11 +240,15 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
         tt[j] = bits ? __ffs(bits) - 1 : -1;
         bits &= bits - 1u;
       }
+      // unconditional reads (row 0 stands in for a missing position, whose
+      // term is then +0.0), so the sixteen reads are not serialised by branches
 #pragma unroll
-      for (int j = 0; j < 8; ++j) kq[j] = tt[j] >= 0 ? sh.kslot[tt[j]][tid] : 0;
+      for (int j = 0; j < 8; ++j) kq[j] = sh.kslot[tt[j] >= 0 ? tt[j] : 0][tid];
+      float pq[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (tt[j] >= 0) m += (double)sh.psel[tt[j]][kq[j]];
+      for (int j = 0; j < 8; ++j) pq[j] = sh.psel[tt[j] >= 0 ? tt[j] : 0][kq[j] & (kMaxK - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m += tt[j] >= 0 ? (double)pq[j] : 0.0;
     }
     sh.mass[tid] = m;
     sh.member[tid] = 0;
@@ -627,10 +631,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
     rec[0] = tid;
     rec[1] = npos;
     uint32_t bits = tbits;
-    for (int j = 0; bits; ++j) {
-      const int tt = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      rec[8 + j] = (tt * K + sh.kslot[tt][tid]) | (tt << 16);
+    // eight positions at a time: their slot reads are independent
+    for (int j0 = 0; bits; j0 += 8) {
+      int tt[8], kq[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tt[j] = bits ? __ffs(bits) - 1 : -1;
+        bits &= bits - 1u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kq[j] = sh.kslot[tt[j] >= 0 ? tt[j] : 0][tid];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (tt[j] >= 0) rec[8 + j0 + j] = (tt[j] * K + kq[j]) | (tt[j] << 16);
     }
   } else {
     const int goff = off & 0xffff;
