@@ -59,6 +59,9 @@ def main():
     ap.add_argument("--stack-only", type=int, default=0, metavar="L",
                     help="only run the L-layer stack measurement (for a kernel trace of that workload alone); "
                          "prints one JSON line with the 'stack' object")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the block-size / threshold sweep (T in 8, 16, 32; threshold 0.8 .. 0.99) of "
+                         "block resolves on the round stub; prints one JSON line per (T, threshold)")
     ap.add_argument("--counter-run", action="store_true",
                     help="only run 3 rounds on inputs drawn with torch.randn (a handful of kernel launches "
                          "besides the library's), for hardware-counter collection")
@@ -90,6 +93,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
         return
     d = W.C1
+    if args.sweep:
+        sweep(args, W.C1, dev)
+        return
     if args.stack_only:
         args.stack = args.stack_only
         print(json.dumps({"stack": stack_round(args, W.C1, dev)}), flush=True)
@@ -302,6 +308,88 @@ def stack_round(args, d, dev):
         f"{res['hbm_gbps']:.0f} GB/s; block resolved in {rounds} rounds ({fallbacks} fallback), "
         f"{res['resolve']['committed_tokens_per_s']:.0f} tok/s")
     return res
+
+
+def sweep(args, d1, dev, blocks=4):
+    """Block size and threshold sweep on the round stub: for each T the C1
+    layer and LM head shapes with a T-position block, `blocks` blocks resolved
+    from all-MASK round by round (stub round r feeds round r), for each
+    threshold.  Reports rounds per block, fallback rounds, microseconds per
+    round, algorithmic bytes per committed token and committed tokens/s."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import block_diffusion_decode_amd as bdd
+    import workloads as W
+
+    for T in (8, 16, 32):
+        d = dataclasses.replace(d1, name=f"sweep_T{T}", T=T)
+        dims = bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16)
+        layer = W.layer_weights(args.seed, 0, d, device=dev)
+        xs, rows = [], set()
+        for b in range(blocks):
+            # failing peaks spread over amplitudes 12 .. 22, so confidences of
+            # the not-passing positions cover the swept thresholds
+            x, info = W.planted_round_inputs(args.seed, d, rounds=T, p=0.3, amp_pass=24.0,
+                                             amp_fail=(12.0, 22.0), tag=f"sweep{b}")
+            xs.append(x.to(dev))
+            rows.update(int(v) for v in info["unit_rows"])
+        w_lm = W.lm_head_weight(args.seed, d, device=dev, unit_rows=sorted(rows))
+        lm = bdd.pack_lm_head(w_lm)
+        del w_lm
+        for tau in (0.8, 0.9, 0.95, 0.99):
+            plan = bdd.RoundPlan(dims, [layer], lm, 1.0, tau)
+            tok = torch.empty(T, dtype=torch.int32, device=dev)
+            conf = torch.empty(T, dtype=torch.float32, device=dev)
+            choice = torch.empty(T, dtype=torch.int32, device=dev)
+            ri = torch.empty(4, dtype=torch.int32, device=dev)
+            nd = torch.empty(1, dtype=torch.int32, device=dev)
+            rounds, fallbacks, dist, ms_total = [], [], [], 0.0
+            for b in range(blocks):
+                tok.fill_(bdd.MASK)
+                n = fb = 0
+                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0.record()
+                for r in range(T):
+                    plan(xs[b][r], tok, conf, choice, ri, None, nd)
+                    info_r = ri.cpu().tolist()
+                    dist.append(int(nd.item()))
+                    n += 1
+                    fb += info_r[1]
+                    if info_r[3]:
+                        break
+                t1.record()
+                torch.cuda.synchronize()
+                ms_total += t0.elapsed_time(t1)
+                rounds.append(n)
+                fallbacks.append(fb)
+            # device time per round on the same rounds, without the host read between rounds
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            for r in range(T):
+                plan(xs[0][r], tok, conf, choice, ri)
+            stop.record()
+            torch.cuda.synchronize()
+            us_round = 1e3 * start.elapsed_time(stop) / T
+            eb = 3 * d.H * d.I * 2
+            round_bytes = float(np.mean(dist)) * eb + 3 * d.H * d.I_s * 2 + d.E * d.H * 2 + d.V * d.H * 2
+            mean_rounds = float(np.mean(rounds))
+            res = {"sweep": {"T": T, "threshold": tau, "blocks": blocks, "rounds_per_block": mean_rounds,
+                             "fallback_rounds_per_block": float(np.mean(fallbacks)),
+                             "us_per_round": round(us_round, 2),
+                             "bytes_per_committed_token": round_bytes * mean_rounds / T,
+                             "committed_tokens_per_s_device": T / (mean_rounds * us_round * 1e-6),
+                             "committed_tokens_per_s_with_host_reads": blocks * T / (ms_total * 1e-3),
+                             "distinct_experts_mean": float(np.mean(dist))}}
+            log(f"[bench] sweep T={T} threshold={tau}: {mean_rounds:.2f} rounds/block "
+                f"({np.mean(fallbacks):.2f} fallback), {us_round:.1f} us/round, "
+                f"{res['sweep']['bytes_per_committed_token'] / 1e6:.1f} MB per committed token")
+            print(json.dumps(res), flush=True)
+            del plan
+        del lm, layer
+        torch.cuda.empty_cache()
 
 
 def counter_run(d, dev):
