@@ -25,8 +25,9 @@ LIB_PATH = os.path.join(_HERE, "libbdd.so")
 
 MASK = -1
 BDD_F32, BDD_BF16 = 0, 1
-_STATUS = {0: "BDD_OK", -1: "BDD_ERR_INVALID_ARG", -2: "BDD_ERR_UNSUPPORTED",
+_STATUS = {1: "BDD_UNRESOLVED", 0: "BDD_OK", -1: "BDD_ERR_INVALID_ARG", -2: "BDD_ERR_UNSUPPORTED",
            -3: "BDD_ERR_WORKSPACE", -4: "BDD_ERR_HIP"}
+BDD_UNRESOLVED = 1
 
 
 class BddError(RuntimeError):
@@ -54,6 +55,7 @@ EXPORTS = [
     "bdd_status_string", "bdd_last_error", "bdd_device_cus",
     "bdd_timing_enable", "bdd_timing_read", "bdd_lmhead_packed_bytes", "bdd_lmhead_pack",
     "bdd_round_graph_create", "bdd_round_graph_launch", "bdd_round_graph_destroy",
+    "bdd_generate_fits", "bdd_generate_workspace_bytes", "bdd_generate",
 ]
 
 _lib = None
@@ -102,6 +104,13 @@ def lib() -> ctypes.CDLL:
     L.bdd_round_graph_launch.restype = i32
     L.bdd_round_graph_destroy.argtypes = [vp]
     L.bdd_round_graph_destroy.restype = None
+    L.bdd_generate_fits.argtypes = [i32, i32, i32]
+    L.bdd_generate_fits.restype = i32
+    L.bdd_generate_workspace_bytes.argtypes = [dims_p, i32]
+    L.bdd_generate_workspace_bytes.restype = sz
+    L.bdd_generate.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, i32, i32, i32, i32, vp, i32, vp,
+                               ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), vp, sz, vp]
+    L.bdd_generate.restype = i32
     L.bdd_timing_enable.argtypes = [i32, ctypes.c_char_p]
     L.bdd_timing_enable.restype = i32
     L.bdd_timing_read.argtypes = [i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -367,6 +376,40 @@ class RoundPlan:
             self.threshold, _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info),
             _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(layer_xhat), _ptr(hhat_out), _ptr(self.ws),
             self.ws.numel(), _stream(stream)))
+
+
+def generate_fits(prompt_len: int, max_new_tokens: int, block_size: int) -> bool:
+    """Whether a request fits the 131072-token bound (see bdd_generate_fits)."""
+    return bool(lib().bdd_generate_fits(prompt_len, max_new_tokens, block_size))
+
+
+def generate(plan: "RoundPlan", x_rounds: torch.Tensor, max_new_tokens: int, max_steps: int,
+             eos_token: int, prompt_len: int = 0, out_tokens: torch.Tensor | None = None, stream=None):
+    """Multi-block generation (bdd_generate) with the plan's layers, LM head,
+    coreset and threshold.  x_rounds [n_blocks][max_steps][T][H] fp32 on the
+    device.  Returns (tokens int32 [n_blocks][T], block_rounds list,
+    n_returned, stop) where stop is "eos", "length" or "unresolved"."""
+    d = plan.d
+    if x_rounds.dim() != 4 or x_rounds.shape[1] != max_steps or tuple(x_rounds.shape[2:]) != (d.T, d.H):
+        raise ValueError(f"x_rounds must be [n_blocks][{max_steps}][{d.T}][{d.H}]")
+    _need(x_rounds, "x_rounds", torch.float32, tuple(x_rounds.shape), plan.dev)
+    nb = x_rounds.shape[0]
+    if out_tokens is None:
+        out_tokens = torch.empty((nb, d.T), dtype=torch.int32, device=plan.dev)
+    _need(out_tokens, "out_tokens", torch.int32, (nb, d.T), plan.dev)
+    wsb = int(lib().bdd_generate_workspace_bytes(ctypes.byref(plan.c_dims), plan.V))
+    if getattr(plan, "gen_ws", None) is None or plan.gen_ws.numel() < wsb:
+        plan.gen_ws = _workspace(wsb, plan.dev, None)
+    rounds = (ctypes.c_int32 * nb)()
+    result = (ctypes.c_int32 * 3)()
+    st = lib().bdd_generate(ctypes.byref(plan.c_dims), len(plan.layers), plan.c_layers, plan.top_p,
+                            _ptr(plan.lm.packed), plan.V, plan.threshold, max_steps, prompt_len, max_new_tokens,
+                            eos_token, _ptr(x_rounds), nb, _ptr(out_tokens), rounds, result, _ptr(plan.gen_ws),
+                            plan.gen_ws.numel(), _stream(stream))
+    if st not in (0, BDD_UNRESOLVED):
+        _check(st)
+    stop = "unresolved" if st == BDD_UNRESOLVED else ("eos" if result[2] == 1 else "length")
+    return out_tokens, [int(rounds[i]) for i in range(int(result[1]))], int(result[0]), stop
 
 
 class RoundGraph:

@@ -245,6 +245,7 @@ extern "C" {
 
 const char *bdd_status_string(int32_t st) {
   switch (st) {
+    case BDD_UNRESOLVED: return "BDD_UNRESOLVED";
     case BDD_OK: return "BDD_OK";
     case BDD_ERR_INVALID_ARG: return "BDD_ERR_INVALID_ARG";
     case BDD_ERR_UNSUPPORTED: return "BDD_ERR_UNSUPPORTED";
@@ -440,6 +441,86 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
   int32_t *pi = at<int32_t>(ws, lp.i);
   const LmCommit fused = {count, threshold, tokens, conf, choice, round_info};
   LAUNCH("lmhead", s, launch_lmhead(d->wdtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, &fused, s));
+  return BDD_OK;
+}
+
+// ----------------------------------------------------------------- generation
+// The request bound of the generation controls: prompt plus generated tokens,
+// counting the whole final block, at most this many.
+constexpr long long kMaxRequestTokens = 131072;
+
+int32_t bdd_generate_fits(int32_t prompt_len, int32_t max_new_tokens, int32_t block_size) {
+  if (prompt_len < 0 || max_new_tokens < 1 || block_size < 1) return 0;
+  const long long blocks = ((long long)max_new_tokens + block_size - 1) / block_size;
+  return (long long)prompt_len + blocks * block_size <= kMaxRequestTokens ? 1 : 0;
+}
+
+size_t bdd_generate_workspace_bytes(const bdd_moe_dims *d, int32_t V) {
+  const size_t r = bdd_round_workspace_bytes(d, V);
+  if (r == 0) return 0;
+  // conf [T] f32, choice [T] i32, round_info [4] i32 after the round's workspace
+  return a256(r) + a256((size_t)d->T * 8 + 16);
+}
+
+bdd_status bdd_generate(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_weights *layers,
+                        float coreset_top_p, const void *w_lm, int32_t V, float threshold, int32_t max_steps,
+                        int32_t prompt_len, int32_t max_new_tokens, int32_t eos_token, const float *x_rounds,
+                        int32_t n_blocks, int32_t *out_tokens, int32_t *block_rounds, int32_t *result, void *ws,
+                        size_t ws_bytes, void *stream) {
+  bdd_status st = check_dims(d);
+  if (st != BDD_OK) return st;
+  if (!bdd_generate_fits(prompt_len, max_new_tokens, d->T))
+    return fail(BDD_ERR_INVALID_ARG,
+                "request of %d prompt tokens + %d new tokens (whole blocks of %d) exceeds %lld tokens", prompt_len,
+                max_new_tokens, d->T, kMaxRequestTokens);
+  if (max_steps < 1) return fail(BDD_ERR_INVALID_ARG, "max_steps=%d", max_steps);
+  const int T = d->T, H = d->H;
+  const int need_blocks = (max_new_tokens + T - 1) / T;
+  if (n_blocks < need_blocks)
+    return fail(BDD_ERR_INVALID_ARG, "%d blocks of round inputs given, %d needed for %d new tokens", n_blocks,
+                need_blocks, max_new_tokens);
+  if (!x_rounds || !out_tokens || !block_rounds || !result)
+    return fail(BDD_ERR_INVALID_ARG, "x_rounds, out_tokens, block_rounds and result are required");
+  const size_t r_bytes = bdd_round_workspace_bytes(d, V);
+  if (r_bytes == 0) return fail(BDD_ERR_INVALID_ARG, "bad dims or V");
+  if ((st = check_ws(ws, ws_bytes, bdd_generate_workspace_bytes(d, V))) != BDD_OK) return st;
+  char *tail = static_cast<char *>(ws) + a256(r_bytes);
+  float *conf = reinterpret_cast<float *>(tail);
+  int32_t *choice = reinterpret_cast<int32_t *>(tail + (size_t)T * 4);
+  int32_t *info = reinterpret_cast<int32_t *>(tail + (size_t)T * 8);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  result[0] = result[1] = result[2] = 0;
+  int produced = 0;
+  for (int b = 0; b < need_blocks; ++b) {
+    int32_t *tok = out_tokens + (size_t)b * T;
+    HIP_TRY(hipMemsetAsync(tok, 0xff, (size_t)T * 4, s));   // every position MASK (-1)
+    int32_t ri[4] = {0, 0, 0, 0};
+    int rounds = 0;
+    for (int r = 0; r < max_steps; ++r) {
+      const float *x = x_rounds + ((size_t)b * max_steps + r) * T * H;
+      if ((st = bdd_block_denoise_round(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x, tok, conf,
+                                        choice, info, nullptr, nullptr, nullptr, nullptr, ws, r_bytes, stream)) !=
+          BDD_OK)
+        return st;
+      HIP_TRY(hipMemcpyAsync(ri, info, sizeof(ri), hipMemcpyDeviceToHost, s));
+      HIP_TRY(hipStreamSynchronize(s));
+      ++rounds;
+      if (ri[3]) break;
+    }
+    block_rounds[b] = rounds;
+    produced += T;
+    result[1] = b + 1;
+    result[0] = produced < max_new_tokens ? produced : max_new_tokens;
+    if (!ri[3]) return fail(BDD_UNRESOLVED, "block %d still has masked positions after %d rounds", b, max_steps);
+    int32_t last = 0;
+    HIP_TRY(hipMemcpyAsync(&last, tok + T - 1, 4, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    if (last == eos_token) {
+      result[2] = 1;
+      return BDD_OK;
+    }
+  }
+  result[2] = 0;
   return BDD_OK;
 }
 

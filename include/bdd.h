@@ -45,6 +45,7 @@ extern "C" {
 #define BDD_MASK (-1)
 
 typedef enum {
+  BDD_UNRESOLVED = 1,       /* bdd_generate: a block kept masked positions after max_steps rounds */
   BDD_OK = 0,
   BDD_ERR_INVALID_ARG = -1, /* null pointer, out-of-range size or parameter */
   BDD_ERR_UNSUPPORTED = -2, /* valid but outside the supported shapes      */
@@ -221,6 +222,38 @@ bdd_status bdd_round_graph_create(const bdd_moe_dims *d, int32_t n_layers,
                                   size_t ws_bytes, bdd_round_graph *out);
 bdd_status bdd_round_graph_launch(bdd_round_graph g, void *stream);
 void bdd_round_graph_destroy(bdd_round_graph g);
+
+/* Multi-block generation ([P1] section 三, the block_decode pseudocode, and
+ * [P2] "How does confidence-threshold block decoding work?" step 6): blocks
+ * of T positions start all-MASK and run rounds of bdd_block_denoise_round
+ * until every position is committed; a finished block joins the prefix, and
+ * generation stops after a block whose last token is eos_token, or once
+ * max_new_tokens have been produced (the final block is always resolved
+ * whole).  The mixer and its history state are not built: the caller
+ * supplies each round's block input (the re-embedding stub).
+ *   max_steps      rounds allowed per block (>= 1)
+ *   prompt_len, max_new_tokens  the request; it is rejected (BDD_ERR_INVALID_ARG,
+ *                  nothing enqueued) when prompt_len + max_new_tokens rounded
+ *                  up to whole blocks exceeds 131072 tokens ([P2] "What
+ *                  generation controls ship by default?"), see bdd_generate_fits
+ *   x_rounds       device [n_blocks][max_steps][T][H] fp32: input of round r
+ *                  of block b; n_blocks >= ceil(max_new_tokens / T)
+ *   out_tokens     device [n_blocks][T] int32 out: the blocks' tokens
+ *   block_rounds   HOST [n_blocks] int32 out: rounds each block took
+ *   result         HOST [3] int32 out: tokens returned (min(blocks * T,
+ *                  max_new_tokens)), blocks run, stop (0 length, 1 eos_token)
+ *   ws             bdd_generate_workspace_bytes(d, V) bytes
+ * The host reads round_info after every round (one synchronisation of
+ * `stream` per round).  Returns BDD_UNRESOLVED (result filled up to that
+ * block) when a block still has masked positions after max_steps rounds. */
+int32_t bdd_generate_fits(int32_t prompt_len, int32_t max_new_tokens, int32_t block_size);
+size_t bdd_generate_workspace_bytes(const bdd_moe_dims *d, int32_t V);
+bdd_status bdd_generate(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_weights *layers,
+                        float coreset_top_p, const void *w_packed, int32_t V, float threshold,
+                        int32_t max_steps, int32_t prompt_len, int32_t max_new_tokens,
+                        int32_t eos_token, const float *x_rounds, int32_t n_blocks,
+                        int32_t *out_tokens, int32_t *block_rounds, int32_t *result, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status, and the calling thread's last error. */
 const char *bdd_status_string(int32_t status);

@@ -105,3 +105,33 @@ def test_round_rejects_null_layers():
     st = L.bdd_block_denoise_round(ctypes.byref(d.c()), 2, None, 1.0, p, 1024, 0.95, p, p, p, p, p,
                                    None, None, None, None, None, 0, None)
     assert st == -1
+
+
+def test_generate_request_bound():
+    # prompt + new tokens, rounded up to whole blocks, at most 131072
+    # (goremy.ai page, "What generation controls ship by default?")
+    fits = bdd.generate_fits
+    assert fits(0, 1, 32) and fits(131072 - 32, 32, 32) and fits(131072 - 32, 1, 32)
+    assert not fits(131072 - 31, 1, 32)        # the final block needs 32 positions
+    assert not fits(131040, 33, 32)            # two blocks past 131040
+    assert fits(131072 - 64, 33, 32)
+    assert not fits(-1, 1, 32) and not fits(0, 0, 32)
+    d = bdd.MoEDims(32, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    assert bdd.lib().bdd_generate_workspace_bytes(ctypes.byref(d.c()), 248320) > bdd.round_workspace_bytes(d, 248320)
+
+
+def test_generate_rejects_on_the_host():
+    # rejected before any pointer is used or anything is enqueued
+    L = bdd.lib()
+    d = bdd.MoEDims(32, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    rounds = (ctypes.c_int32 * 4)()
+    result = (ctypes.c_int32 * 3)()
+    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, 131072 - 31, 1, 0, None, 4,
+                        None, rounds, result, None, 0, None)
+    assert st == -1 and b"131072" in L.bdd_last_error()
+    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 0, 0, 32, 0, None, 4,
+                        None, rounds, result, None, 0, None)
+    assert st == -1   # max_steps < 1
+    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, 0, 65, 0, None, 2,
+                        None, rounds, result, None, 0, None)
+    assert st == -1   # three blocks needed, two given
