@@ -263,21 +263,29 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
     return;
   }
   if (nu <= 64) {
-    // one wave: lane j holds union entry j; its rank comes from wave-uniform
-    // reads of every other lane, the ranked masses' prefix sum from a
-    // shuffle scan, the cut from a ballot (no barriers)
+    // one wave: lane j holds union entry j; its rank counts the entries
+    // before it in (mass desc, id asc) order, read from LDS eight at a time
+    // (broadcast reads, all in flight together); the ranked masses' prefix
+    // sum comes from a shuffle scan and the cut from a ballot
+    if (tid < nu) sh.umass[tid] = sh.mass[sh.ulist[tid]];
+    __syncthreads();
     if (wave == 0) {
       const bool live = lane < nu;
       const int e = live ? sh.ulist[lane] : 0;
-      const double m = live ? sh.mass[e] : 0.0;
-      const long long mb = __double_as_longlong(m);
+      const double m = live ? sh.umass[lane] : 0.0;
       int r = 0;
-      for (int i = 0; i < nu; ++i) {
-        const double mi = __longlong_as_double(
-            ((long long)__builtin_amdgcn_readlane((int)(mb >> 32), i) << 32) |
-            (long long)(uint32_t)__builtin_amdgcn_readlane((int)mb, i));
-        const int ei = __builtin_amdgcn_readlane(e, i);
-        r += (mi > m) || (mi == m && ei < e);
+      for (int i0 = 0; i0 < nu; i0 += 8) {
+        double mi[8];
+        int ei[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = min(i0 + j, nu - 1);
+          mi[j] = sh.umass[i];
+          ei[j] = sh.ulist[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)   // bitwise, so no branches per comparison
+          r += (int)(i0 + j < nu) & ((int)(mi[j] > m) | ((int)(mi[j] == m) & (int)(ei[j] < e)));
       }
       if (live) {
         sh.sorted[r] = e;
@@ -321,7 +329,8 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
 #pragma unroll 8
       for (int i = lo; i < hi; ++i) {
         const double o = sh.umass[i];
-        r += (o > m) || (o == m && sh.ulist[i] < e);
+        const int oe = sh.ulist[i];
+        r += (int)(o > m) | ((int)(o == m) & (int)(oe < e));
       }
       atomicAdd(&sh.rank[j], r);
     }
@@ -503,12 +512,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
     const int kk = min(K, sh.csize);
     if (sh.csize <= 64) {
       // Lane j of a wave holds member j (mass rank order) and, for each of the
-      // wave's positions, that member's logit and score; a member's slot is
-      // its rank among the members by (logit desc, id asc).  All loads of a
-      // wave are in flight together.
+      // wave's positions, that member's key (logit desc, id asc) and score; a
+      // member's slot is its rank among the members' keys, which the wave
+      // reads back from LDS eight at a time (broadcast reads).
       const int C = sh.csize;
       const int c = lane < C ? sh.sorted[lane] : 0;
       constexpr int kPer = kMaxT / (kSelThreads / 64);
+      __shared__ unsigned long long s_rk[kMaxT][64];
       float lv[kPer], pv[kPer];
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
@@ -517,17 +527,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
         lv[i] = ok ? fetch_published(r.logits + (size_t)tt * E + c) : 0.f;
         pv[i] = ok ? fetch_published(r.prob + (size_t)tt * E + c) : 0.f;
       }
+      unsigned long long key[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int tt = wave + i * (kSelThreads / 64);
+        key[i] = lane < C ? ((unsigned long long)order_key(lv[i]) << 32) | (uint32_t)c : ~0ull;
+        if (tt < T) s_rk[tt][lane] = key[i];
+      }
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int tt = wave + i * (kSelThreads / 64);
         if (tt >= T) break;
-        const unsigned long long key = lane < C ? ((unsigned long long)order_key(lv[i]) << 32) | (uint32_t)c : ~0ull;
         int rk = 0;
-        for (int j = 0; j < C; ++j) {
-          const unsigned long long kj =
-              ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), j) << 32) |
-              (uint32_t)__builtin_amdgcn_readlane((int)key, j);
-          rk += kj < key;
+        for (int j0 = 0; j0 < C; j0 += 8) {
+          unsigned long long kj[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) kj[j] = s_rk[tt][min(j0 + j, C - 1)];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rk += (int)(j0 + j < C) & (int)(kj[j] < key[i]);
         }
         if (lane < C && rk < kk) {
           sh.idx[tt][rk] = c;
@@ -711,8 +729,6 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
                                                               float eps) {
   __shared__ float red[kRowThreads / 64];
   const int t = blockIdx.x;
-  uint32_t live = 0;
-  for (int k = 0; k < K; ++k) live |= (idx[t * K + k] >= 0 ? 1u : 0u) << k;
   const size_t base = (size_t)t * H;
   const int H4 = H / 4;
   float4 hv[kRowVec];
@@ -722,13 +738,25 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
     const int j = threadIdx.x + q * kRowThreads;
     if (j >= H4) continue;
     float4 y = make_float4(0, 0, 0, 0);
-#pragma unroll 8
-    for (int k = 0; k < K; ++k) {
-      if (live >> k & 1u) {
-        const float4 p = reinterpret_cast<const float4 *>(P + ((size_t)t * K + k) * H)[j];
-        const float g = wgt[t * K + k];
-        y.x = fmaf(g, p.x, y.x); y.y = fmaf(g, p.y, y.y);
-        y.z = fmaf(g, p.z, y.z); y.w = fmaf(g, p.w, y.w);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      // eight slots' pick, weight and row loads in flight together (rows of
+      // unused slots are read but never summed: they may hold stale values)
+      int iv[8];
+      float gv[8];
+      float4 pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = min(k0 + u, K - 1);
+        iv[u] = idx[t * K + k];
+        gv[u] = wgt[t * K + k];
+        pv[u] = reinterpret_cast<const float4 *>(P + ((size_t)t * K + k) * H)[j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u < K && iv[u] >= 0) {
+          y.x = fmaf(gv[u], pv[u].x, y.x); y.y = fmaf(gv[u], pv[u].y, y.y);
+          y.z = fmaf(gv[u], pv[u].z, y.z); y.w = fmaf(gv[u], pv[u].w, y.w);
+        }
       }
     }
     if (P_s) {
