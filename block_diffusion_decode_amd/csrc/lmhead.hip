@@ -170,7 +170,10 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ 
 
 // One workgroup (16 waves) per CU.  The block's normalised hidden states are
 // staged once in LDS as [chunk][position] 16-byte entries; each wave takes
-// 16-row vocabulary tiles round-robin, streams the rows with 16-byte loads,
+// 16-row vocabulary tiles round-robin (wave w of workgroup b starts at tile
+// w * grid + b, so a workgroup's tiles are spread over the whole weight
+// rather than one contiguous MiB per round, which evened out the finish times
+// of the workgroups on the different XCDs), streams the rows with 16-byte loads,
 // multiplies them by the staged positions on MFMA, and folds the 16 x 32
 // logits into its running (max, sum, argmax).
 // With `done_count` given, the workgroup that finishes last (agent-scope
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   const int ntiles = (V + 15) / 16;
   const int ksteps = NC / 4;
   const int nb = (ksteps + kLmBatch - 1) / kLmBatch;
-  const int first = uniform(blockIdx.x * kLmWaves + wave);
+  const int first = uniform(wave * (int)gridDim.x + (int)blockIdx.x);
   const int stride = gridDim.x * kLmWaves;
   const int my_tiles = first < ntiles ? (ntiles - 1 - first) / stride + 1 : 0;
   const int steps = my_tiles * nb;
