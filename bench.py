@@ -68,7 +68,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build targets a single MI355X and has no "
+        print(f"bench.py measures one GPU only: the library runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
