@@ -350,6 +350,50 @@ def test_lmhead_tie_lowest_id():
     assert choice[0] == 1
 
 
+def _merge(a, b):
+    """Online-softmax merge of two (max, sum of exp(z - max), argmax) partials:
+    the larger max wins and the other sum is rescaled onto it; equal maxima
+    add their sums and keep the lower index."""
+    (m1, s1, i1), (m2, s2, i2) = a, b
+    if m2 > m1:
+        return m2, s1 * math.exp(m1 - m2) + s2, i2
+    if m2 < m1:
+        return m1, s1 + s2 * math.exp(m2 - m1), i1
+    return m1, s1 + s2, min(i1, i2)
+
+
+def test_online_softmax_merge_matches_direct_confidence():
+    # The LM head reduces each vocabulary tile to (max, sum, argmax) and merges
+    # the tiles' partials in whatever order its waves and workgroups meet them.
+    # In exact arithmetic the merge is associative and commutative; in fp64 any
+    # split and order must give the oracle's confidence and argmax (ties to the
+    # lowest id) to 1e-12.
+    V, H = 1031, 5
+    hh = RNG.normal(size=(3, H)) * 2.0
+    w = RNG.normal(size=(V, H))
+    w[123] = w[700] = 0.0
+    w[123, 0] = w[700, 0] = 10.0                      # an exact tie of two rows ...
+    hh[2] = 0.0
+    hh[2, 0] = 1.0                                    # ... that is position 2's maximum (10 vs N(0,1))
+    conf, choice, z = O.lm_head_confidence(hh, w)
+    for t in range(hh.shape[0]):
+        for trial in range(6):
+            cuts = np.sort(RNG.choice(np.arange(1, V), size=RNG.integers(1, 40), replace=False))
+            tiles = np.split(np.arange(V), cuts)
+            parts = []
+            for tile in tiles:
+                zt = z[t, tile]
+                j = int(np.argmax(zt))                 # first maximum = lowest id in the tile
+                parts.append((float(zt[j]), float(np.sum(np.exp(zt - zt[j]))), int(tile[j])))
+            order = RNG.permutation(len(parts))
+            acc = parts[order[0]]
+            for k in order[1:]:
+                acc = _merge(acc, parts[k]) if trial % 2 else _merge(parts[k], acc)
+            assert abs(1.0 / acc[1] - conf[t]) <= 1e-12, (t, trial)
+            assert acc[2] == choice[t], (t, trial)
+    assert choice[2] == 123
+
+
 # ---------------------------------------------------------------------------
 # commit rule
 # ---------------------------------------------------------------------------
