@@ -180,7 +180,8 @@ constexpr int dense_down_batch() { return MT <= 2 ? 4 : 2; }
 // activation slot (see act_unit).  Lane (li, g) names entries li and 16 + li
 // by their rows row[n] in P (-1: no entry).  The four waves split the
 // intermediate dimension; each issues the loads of a batch of k-steps at
-// once, and the partial tiles are added in LDS (`red`, MT * 8 KiB).  With bf16
+// once, stages its weights through its own quarter of `red` (MT * 8 KiB), and
+// the partial tiles are then added through all of it.  With bf16
 // weights the activations enter as bf16 high parts and residuals (two MFMA
 // passes); every activation load serves MT weight tiles.
 // P[row][h] = A_entry . W_d[h].
@@ -195,43 +196,69 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
   const int li = lane & 15, g = lane >> 4;
   const int ncw = ie / CH / 4;            // chunks of this wave's quarter of ie
   const int cw0 = wave * ncw;
-  const int ksteps = (ncw + 3) / 4;
   const rsrc_t rw = make_rsrc(w, (uint32_t)(H * ie) * sizeof(WT));
   const rsrc_t ra = make_rsrc(act, (uint32_t)ie * kActSlotPerI);
-  uint32_t rowa[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) rowa[m] = (uint32_t)((h0 + 16 * m + li) * ie) * sizeof(WT);
   f32x4 acc[MT][2];   // [row tile][column tile]
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kSdSteps = dense_down_batch<MT>();
-  for (int k0 = 0; k0 < ksteps; k0 += kSdSteps) {
-    uint4 wa[kSdSteps][MT], xa[kSdSteps][2][NP];
+  static_assert(kSdSteps % 2 == 0, "the dense down item streams whole units of 2 k-steps");
+  constexpr int UB = kSdSteps / 2;          // units per load batch
+  const int nunits = (ncw + 7) / 8;
+  // weights staged as in the dense gate/up item: a load reads 128 bytes of
+  // each of 8 rows (rows 8j + sr, the row offsets wave-uniform), and the wave
+  // passes each unit through its own MT * 2 KiB of `red`
+  const int sr = lane >> 3, sc = lane & 7;
+  const uint32_t rowa = (uint32_t)((h0 + sr) * ie) * sizeof(WT), rows8 = (uint32_t)(8 * ie) * sizeof(WT);
+  f32x4 *stage = red + wave * MT * 128;
+  for (int u0 = 0; u0 < nunits; u0 += UB) {
+    uint4 wa[UB][2 * MT], xa[2 * UB][2][NP];
 #pragma unroll
-    for (int j = 0; j < kSdSteps; ++j) {
-      const int c = 4 * (k0 + j) + g;
-      const bool live = k0 + j < ksteps && c < ncw;
-      const int C = cw0 + c;
+    for (int u = 0; u < UB; ++u) {
+      const bool live_u = u0 + u < nunits;
+      const int cs = 8 * (u0 + u) + sc;
+      const uint32_t vo = live_u && cs < ncw ? rowa + (uint32_t)((cw0 + cs) * CH) * sizeof(WT) : kOutOfRange;
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        wa[j][m] = buf_ld16(rw, live ? rowa[m] + (uint32_t)(C * CH) * sizeof(WT) : kOutOfRange, 0);
+      for (int j = 0; j < 2 * MT; ++j) wa[u][j] = buf_ld16(rw, vo, (uint32_t)j * rows8);
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int h = 0; h < 2; ++h) {
+        const int c = 8 * (u0 + u) + 4 * h + g;
+        const bool live = live_u && c < ncw;
+        const int C = cw0 + c;
 #pragma unroll
-        for (int q = 0; q < NP; ++q)
-          xa[j][n][q] = buf_ld16(ra, live && row[n] >= 0 ? act_unit(C, q, 16 * n + li, NP) * 16u : kOutOfRange, 0);
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int q = 0; q < NP; ++q)
+            xa[2 * u + h][n][q] =
+                buf_ld16(ra, live && row[n] >= 0 ? act_unit(C, q, 16 * n + li, NP) * 16u : kOutOfRange, 0);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kSdSteps; ++j)
+    for (int u = 0; u < UB; ++u) {
+      // lanes read rows other lanes wrote: in-order LDS, fenced against the compiler
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int j = 0; j < 2 * MT; ++j)
+        stage[stage_slot(j >> 1, 8 * (j & 1) + sr, sc)] = __builtin_bit_cast(f32x4, wa[u][j]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      uint4 a[2][MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if constexpr (BF) acc[m][n] = mfma_bf16(wa[j][m], xa[j][n][1], mfma_bf16(wa[j][m], xa[j][n][0], acc[m][n]));
-          else acc[m][n] = mfma_chunk<W>(wa[j][m], xa[j][n][0], acc[m][n]);
-        }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a[h][m] = __builtin_bit_cast(uint4, stage[stage_slot(m, li, 4 * h + g)]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const uint4 *x = xa[2 * u + h][n];
+            if constexpr (BF) acc[m][n] = mfma_bf16(a[h][m], x[1], mfma_bf16(a[h][m], x[0], acc[m][n]));
+            else acc[m][n] = mfma_chunk<W>(a[h][m], x[0], acc[m][n]);
+          }
+    }
   }
 #pragma unroll
   for (int m = 0; m < MT; ++m)

@@ -54,8 +54,9 @@ __device__ __forceinline__ void pipeline_post(int steps, Bufs &b0, Bufs &b1, Loa
 // routing) sees many of them, so their contraction is dense: 16x16 tiles with
 // 16 weight rows as A and 16 positions as B (two column tiles for 32
 // positions), in one pass over the weights.  At k-step s lane group
-// g = lane >> 4 holds chunk 4s + g of its row, so a load reads 64 contiguous
-// bytes of each of 16 rows.
+// g = lane >> 4 holds chunk 4s + g of its row (the MFMA operand layout), so a
+// load straight into operand order reads only 64 contiguous bytes of each of
+// 16 rows.
 // ---------------------------------------------------------------------------
 
 template <class W>
@@ -90,17 +91,28 @@ __device__ __forceinline__ uint32_t act_unit(int C, int plane, int e, int planes
 constexpr int kSgSteps = 4;   // k-steps per load batch of the shared gate/up beside selection
 template <int STEPS>
 struct DgBufs {
-  uint4 a[STEPS][2];   // [k-step][gate, up]
-  uint4 b[STEPS][2];   // [k-step][column tile]
+  uint4 a[STEPS / 2][4];   // [unit of 2 k-steps][gate rows 0-7, 8-15, up rows 0-7, 8-15]
+  uint4 b[STEPS][2];       // [k-step][column tile]
 };
+
+// Weight staging of the dense gate/up item.  A unit is 2 k-steps (8 chunks of
+// 16 bytes, 128 bytes of a row): one load instruction reads 8 rows of it
+// (lane l: row 8j + l / 8, chunk l % 8), 8 full 128-byte lines, and the wave
+// writes the unit to its own 4 KiB of LDS and reads it back in operand order.
+// Chunk c of row r sits at slot c ^ stage_swz(r): the 8 lanes of one row in a
+// write, and the 16 rows of one chunk in a read (16 lanes at a time), fall on
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int stage_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int stage_slot(int q, int r, int c) { return (q * 16 + r) * 8 + (c ^ stage_swz(r)); }
 
 // Gate/up rows i0 .. i0 + 15 (and ie + i0 ..) of one expert, W_gu [2 ie][H],
 // for up to 32 column entries (two tiles of 16).  Lane (li, g) names entries
 // li and 16 + li by their positions pos[n] (-1: no entry).  The four waves
-// split the hidden dimension, each starting its k-steps `rot` steps in (so
-// concurrent items spread their reads of the packed block), and add their
-// partial tiles through LDS (`red`, 16 KiB); waves 0 and 1 finish column
-// tiles 0 and 1 and store silu(gate) * up into the packed activation slot.
+// split the hidden dimension, each starting its units `rot` units in (so
+// concurrent items spread their reads of the packed block); each wave stages
+// its weights through its own quarter of `red` (16 KiB) and afterwards adds
+// its partial tiles through all of it; waves 0 and 1 finish column tiles 0
+// and 1 and store silu(gate) * up into the packed activation slot.
 template <class W, int STEPS>
 __device__ __forceinline__ void dense_gateup_item(const typename W::T *__restrict__ w, int ie,
                                                   const typename W::T *__restrict__ xpk, int T, int H,
@@ -111,12 +123,19 @@ __device__ __forceinline__ void dense_gateup_item(const typename W::T *__restric
   const int li = lane & 15, g = lane >> 4;
   const int ncw = H / CH / 4;               // chunks of this wave's quarter of H
   const int cw0 = wave * ncw;
-  const int ksteps = (ncw + 3) / 4;
-  rot %= ksteps;
+  static_assert(STEPS % 2 == 0, "the dense gate/up item streams whole units of 2 k-steps");
+  constexpr int UB = STEPS / 2;             // units per load batch
+  const int nunits = (ncw + 7) / 8;
+  rot %= nunits;
   const rsrc_t rw = make_rsrc(w, (uint32_t)(2 * ie * H) * sizeof(WT));
   const rsrc_t rx = make_rsrc(xpk, (uint32_t)(T * H) * sizeof(WT));
-  const uint32_t rowg = (uint32_t)((i0 + li) * H) * sizeof(WT);
-  const uint32_t rowu = (uint32_t)((ie + i0 + li) * H) * sizeof(WT);
+  // this lane's row in a staging load, and its chunk in the unit
+  const int sr = lane >> 3, sc = lane & 7;
+  const uint32_t rowg = (uint32_t)((i0 + sr) * H) * sizeof(WT);
+  // wave-uniform offsets of gate rows 8-15 and of the up rows (scalar offsets;
+  // an out-of-range vector offset still returns zeros)
+  const uint32_t rows8 = (uint32_t)(8 * H) * sizeof(WT), upo = (uint32_t)(ie * H) * sizeof(WT);
+  f32x4 *stage = red + wave * 256;
   f32x4 acc[2][2];   // [gate, up][column tile]
 #pragma unroll
   for (int q = 0; q < 2; ++q)
@@ -124,30 +143,56 @@ __device__ __forceinline__ void dense_gateup_item(const typename W::T *__restric
     for (int n = 0; n < 2; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto load = [&](int bt, DgBufs<STEPS> &b) {
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) {
-      const int ks = STEPS * bt + j;
-      int kr = ks + rot;
-      kr = kr >= ksteps ? kr - ksteps : kr;
-      const int c = 4 * kr + g;
-      const bool live = ks < ksteps && c < ncw;
-      const uint32_t co = (uint32_t)((cw0 + c) * CH) * sizeof(WT);
-      b.a[j][0] = buf_ld16(rw, live ? rowg + co : kOutOfRange, 0);
-      b.a[j][1] = buf_ld16(rw, live ? rowu + co : kOutOfRange, 0);
+    for (int u = 0; u < UB; ++u) {
+      const int us = UB * bt + u;
+      int ur = us + rot;
+      ur = ur >= nunits ? ur - nunits : ur;
+      const bool live_u = us < nunits;
+      const int cs = 8 * ur + sc;
+      const uint32_t co = (uint32_t)((cw0 + cs) * CH) * sizeof(WT);
+      const bool ls = live_u && cs < ncw;
+      const uint32_t vo = ls ? rowg + co : kOutOfRange;
+      b.a[u][0] = buf_ld16(rw, vo, 0);
+      b.a[u][1] = buf_ld16(rw, vo, rows8);
+      b.a[u][2] = buf_ld16(rw, vo, upo);
+      b.a[u][3] = buf_ld16(rw, vo, upo + rows8);
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-        b.b[j][n] = buf_ld16(rx, live && pos[n] >= 0 ? xpack_unit(cw0 + c, pos[n], T) * 16u : kOutOfRange, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int c = 8 * ur + 4 * h + g;
+        const bool live = live_u && c < ncw;
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          b.b[2 * u + h][n] =
+              buf_ld16(rx, live && pos[n] >= 0 ? xpack_unit(cw0 + c, pos[n], T) * 16u : kOutOfRange, 0);
+      }
     }
   };
   auto step = [&](int, const DgBufs<STEPS> &b) {
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j)
+    for (int u = 0; u < UB; ++u) {
+      // Lanes read what other lanes of the wave wrote: a wave's LDS accesses
+      // execute in issue order, and the wavefront-scope fences keep the
+      // compiler from moving them across one another.
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int v = 0; v < 4; ++v)
+        stage[stage_slot(v >> 1, 8 * (v & 1) + sr, sc)] = __builtin_bit_cast(f32x4, b.a[u][v]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      uint4 a[2][2];   // [k-step of the unit][gate, up]
 #pragma unroll
-        for (int n = 0; n < 2; ++n) acc[q][n] = mfma_chunk<W>(b.a[j][q], b.b[j][n], acc[q][n]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) a[h][q] = __builtin_bit_cast(uint4, stage[stage_slot(q, li, 4 * h + g)]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc[q][n] = mfma_chunk<W>(a[h][q], b.b[2 * u + h][n], acc[q][n]);
+    }
   };
   DgBufs<STEPS> b0, b1;
-  pipeline((ksteps + STEPS - 1) / STEPS, b0, b1, load, step);
+  pipeline((nunits + UB - 1) / UB, b0, b1, load, step);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll

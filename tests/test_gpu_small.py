@@ -128,6 +128,29 @@ def test_moe_forward_dense_experts_fp32():
     assert not gb and nb == 0
 
 
+@pytest.mark.parametrize("wdtype,I", [("bf16", 160), ("f32", 96)])
+def test_moe_forward_dense_experts_ragged_units(wdtype, I):
+    # the dense items stage their weights in units of 8 chunks (16 bytes each)
+    # per wave quarter: hidden size 384 leaves 12 (bf16) or 24 (fp32) chunks
+    # per wave, I = 160 / 96 leaves 5 / 6 and I_s = 32 leaves 1 or 2, so the
+    # last unit of every projection is partly past the end of the rows
+    d = W.Dims(f"ragged_{wdtype}", T=32, H=384, E=40, K=6, I=I, I_s=32, V=16, wdtype=wdtype, w_std=0.05,
+               lm_std=0.06)
+    layer = W.layer_weights(4, 0, d, device=DEV, bias="flat")
+    layer["router_bias"][:3] = 10.0
+    h = W.block_hidden(4, d, device=DEV)
+    out = bdd.moe_block_forward(dims_of(d), layer, h, 1.0)
+    torch.cuda.synchronize()
+    hn = O.rmsnorm(f64(h))
+    xh = O.bf16_round(hn) if wdtype == "bf16" else hn
+    y_ref, info = O.moe_layer(xh, oracle_layer(layer), d.K, 1.0)
+    nb, gb = _check_moe(d, out, y_ref, info, xh, 1.0)
+    assert not gb and nb <= 2
+    idx = np.asarray(info["idx"]).ravel()
+    n_e = np.bincount(idx[idx >= 0], minlength=d.E)
+    assert (n_e[:3] == d.T).all()   # three experts with two full column tiles
+
+
 def test_moe_forward_deterministic():
     d = SMALL_BF16
     layer = W.layer_weights(5, 0, d, device=DEV, bias="zipf")
