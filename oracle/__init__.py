@@ -32,7 +32,10 @@ Readings taken where the pages are silent (each listed in the design notes):
   * coreset score = the raw softmax probability of each token's top-K picks;
     the coreset is the shortest prefix of experts ranked by summed score
     whose mass reaches top_p of the total; each token then re-takes its
-    top-min(K, |C|) inside the coreset and renormalises.
+    top-min(K, |C|) inside the coreset and renormalises;
+  * INT4 weights (the format is not on the pages): two 4-bit codes per byte,
+    low nibble first, code n standing for n - 8, one bf16 scale per row and
+    128-column group.
 
 Parity unpinned: the shared-expert gating, the coreset score choice, the
 re-routing rule after the coreset and the Zipf router bias are readings the
@@ -52,6 +55,8 @@ from .decode import (  # noqa: F401
     moe_given_routing,
     moe_stack,
     lm_head_confidence,
+    INT4_GROUP,
+    int4_dequantize,
     commit,
     resolve_block,
 )

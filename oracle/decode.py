@@ -209,6 +209,28 @@ def lm_head_confidence(hhat, w_lm, chunk: int = 16384):
     return conf, choice, z
 
 
+INT4_GROUP = 128
+
+
+def int4_dequantize(codes, scales, group: int = INT4_GROUP) -> np.ndarray:
+    """Dequantised weight [R][H] of a 4-bit weight-only format ([P3] 10100.com
+    article on Clover-35B-A3B-Preview, part 03, memory and quantisation: the
+    model is deployed in INT4 on a 16 GB card; the pages give no format).
+
+    Reading taken: codes[r][j] is a byte holding columns 2j (low nibble) and
+    2j + 1 (high nibble); a nibble n in 0..15 stands for the integer n - 8;
+    scales[r][c // group] (bf16 values, here as float64) multiplies every
+    column c of its row-group.  w[r][c] = (n - 8) * s."""
+    b = np.asarray(codes, dtype=np.uint8)
+    R, half = b.shape
+    n = np.empty((R, 2 * half), dtype=np.int64)
+    n[:, 0::2] = b & 0x0F
+    n[:, 1::2] = b >> 4
+    s = np.asarray(scales, dtype=np.float64)
+    assert s.shape == (R, (2 * half) // group)
+    return (n - 8).astype(np.float64) * np.repeat(s, group, axis=1)
+
+
 def commit(tokens, conf, choice, threshold: float = 0.95):
     """One LowConfidence commit.  Among still-masked positions, every one with
     conf >= threshold is written; if none qualifies, the single most

@@ -522,3 +522,46 @@ def test_page_constants_fixture():
     assert c["block_size"]["value"] == 32 and c["threshold"]["value"] == 0.95
     assert c["routed_experts"]["value"] == 256 and c["top_k"]["value"] == 8
     assert c["max_steps"]["value"] == 32
+
+
+# ---------------------------------------------------------------------------
+# 4-bit LM-head weights: two codes per byte, low nibble first, n - 8, one
+# scale per row and 128-column group (the reading taken for the INT4 format)
+# ---------------------------------------------------------------------------
+
+def test_int4_dequantize_hand_example():
+    # 0x8F: column 0 = 15 -> +7, column 1 = 8 -> 0; 0x10: column 2 = 0 -> -8, column 3 = 1 -> -7
+    w = O.int4_dequantize(np.array([[0x8F, 0x10]], np.uint8), np.array([[0.5]]), group=4)
+    assert w.tolist() == [[3.5, 0.0, -4.0, -3.5]]
+
+
+def test_int4_dequantize_matches_per_element_loop():
+    rng = np.random.default_rng(5)
+    R, H, G = 3, 256, 128
+    codes = rng.integers(0, 256, size=(R, H // 2), dtype=np.uint8)
+    scales = rng.uniform(0.01, 0.2, size=(R, H // G))
+    w = O.int4_dequantize(codes, scales)
+    for r in range(R):
+        for c in range(H):
+            byte = int(codes[r][c // 2])
+            nib = byte & 15 if c % 2 == 0 else byte >> 4
+            assert w[r][c] == (nib - 8) * scales[r][c // G], (r, c)
+
+
+def test_int4_dequantize_group_boundary_and_extremes():
+    codes = np.full((2, 128), 0x99, np.uint8)      # every nibble 9 -> +1
+    codes[1, :] = 0xF0                               # even columns -8, odd columns +7
+    scales = np.array([[1.0, 2.0], [0.25, 4.0]])
+    w = O.int4_dequantize(codes, scales)
+    assert (w[0, :128] == 1.0).all() and (w[0, 128:] == 2.0).all()
+    assert (w[1, 0:128:2] == -2.0).all() and (w[1, 1:128:2] == 1.75).all()
+    assert (w[1, 128::2] == -32.0).all() and (w[1, 129::2] == 28.0).all()
+
+
+def test_int4_lm_head_zero_codes_give_uniform_confidence():
+    # every code 8 stands for 0: all logits 0, conf = 1/V, choice = token 0
+    V, H = 300, 256
+    w = O.int4_dequantize(np.full((V, H // 2), 0x88, np.uint8), np.full((V, H // 128), 0.37))
+    h = np.random.default_rng(1).standard_normal((3, H))
+    conf, choice, _ = O.lm_head_confidence(h, w)
+    assert np.allclose(conf, 1.0 / V, rtol=0, atol=1e-15) and (choice == 0).all()

@@ -20,6 +20,7 @@ from .gen import (  # noqa: F401
     layer_weights,
     lm_head_weight,
     lm_head_rows,
+    lm_head_int4,
     block_hidden,
     zipf_router_bias,
     lmhead_stub_inputs,

@@ -222,6 +222,26 @@ def lm_head_weight(seed: int, d: Dims, device="cpu", unit_rows=()) -> torch.Tens
     return w.to(d.torch_wdtype)
 
 
+def lm_head_int4(seed: int, d: Dims, device="cpu", group: int = 128):
+    """Synthetic 4-bit LM head of shape [V][H]: (codes uint8 [V][H/2], scales
+    bf16 [V][H/group]).  Byte j of a row holds columns 2j (low nibble) and
+    2j + 1 (high nibble).  Codes are a rounded normal, n = clamp(round(2.5 z),
+    -8, 7) + 8, the histogram of quantised weights; scales are
+    lm_std / 2.5 * U(0.8, 1.2), so the weights the codes stand for have
+    about the bf16 head's spread."""
+    assert d.H % group == 0
+    n = torch.empty(d.V * d.H, dtype=torch.uint8, device=device)
+    key = key_of(seed, "lm_int4_codes")
+    for s, e in _ranges(0, d.V * d.H):
+        z = counter_normal(key, e - s, 1.0, device, start=s)
+        n[s:e] = (torch.round(z * 2.5).clamp_(-8, 7) + 8).to(torch.uint8)
+    n = n.reshape(d.V, d.H // 2, 2)
+    codes = (n[..., 0] | (n[..., 1] << 4)).contiguous()
+    u = counter_uniform(key_of(seed, "lm_int4_scales"), d.V * (d.H // group), device)
+    scales = (d.lm_std / 2.5 * (0.8 + 0.4 * u)).to(torch.bfloat16).reshape(d.V, d.H // group)
+    return codes, scales
+
+
 def block_hidden(seed: int, d: Dims, device="cpu", tag="h") -> torch.Tensor:
     """Block hidden states h [T][H] float32, N(0, 1)."""
     return counter_normal(key_of(seed, "hidden", tag), d.T * d.H, 1.0, device).reshape(d.T, d.H)
