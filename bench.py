@@ -62,6 +62,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="only run the block-size / threshold sweep (T in 8, 16, 32; threshold 0.8 .. 0.99) of "
                          "block resolves on the round stub; prints one JSON line per (T, threshold)")
+    ap.add_argument("--int4-only", action="store_true",
+                    help="only measure the 4-bit LM head + commit (for a kernel trace of it alone); prints one "
+                         "JSON line with the 'lmhead_int4' object")
     ap.add_argument("--counter-run", action="store_true",
                     help="only run 3 rounds on inputs drawn with torch.randn (a handful of kernel launches "
                          "besides the library's), for hardware-counter collection")
@@ -102,6 +105,9 @@ def main():
         return
     if args.counter_run:
         counter_run(d, dev)
+        return
+    if args.int4_only:
+        print(json.dumps({"lmhead_int4": lmhead_int4(args, d, dev)}), flush=True)
         return
     R = 8
     log(f"[bench] generating inputs (seed {args.seed})")
@@ -212,6 +218,8 @@ def main():
         "roofline": roofline,
     }
 
+    out["lmhead_int4"] = lmhead_int4(args, d, dev)
+    out["lmhead_int4"]["bf16_lmhead_us_same_run"] = roofline["avg_us"]
     if args.stack > 0:
         del graphs, plan, lm, layer
         torch.cuda.empty_cache()
@@ -426,6 +434,46 @@ def counter_run(d, dev):
 
 COUNTERS = os.path.join(ROOT, "profiles", "lmhead_clover_v248320_hbm_counters.md")
 KERNEL_SOURCES = {"lmhead": ["lmhead.hip", "common.hpp", "kernels.hpp"]}
+
+
+def lmhead_int4(args, d, dev, launches=200):
+    """The LM head with 4-bit weights (two codes per byte, code n standing for
+    n - 8, one bf16 scale per row and 128 columns) + commit, on the Clover
+    LM-head shape: average per-launch time from HIP events on the launch
+    stream, against its algorithmic bytes (codes + scales + the block)."""
+    import torch
+    import block_diffusion_decode_amd as bdd
+    import workloads as W
+
+    codes, scales = W.lm_head_int4(args.seed, d, device=dev)
+    lm4 = bdd.pack_lm_head_int4(codes, scales)
+    del codes, scales
+    h = W.counter_normal(W.key_of(args.seed, "int4_h"), d.T * d.H, 1.0).to(torch.bfloat16)
+    h = h.reshape(d.T, d.H).to(dev)
+    ws = torch.empty(bdd.lmhead_workspace_bytes(d.T, d.H, d.V), dtype=torch.uint8, device=dev)
+    tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=dev)
+    conf = torch.empty(d.T, dtype=torch.float32, device=dev)
+    choice = torch.empty(d.T, dtype=torch.int32, device=dev)
+    ri = torch.empty(4, dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        tok.fill_(bdd.MASK)
+        bdd.lmhead_confidence_commit(h, lm4, tok, ws=ws, conf=conf, choice=choice, round_info=ri)
+    torch.cuda.synchronize()
+    bdd.timing_enable(True, None)
+    for _ in range(launches):
+        tok.fill_(bdd.MASK)
+        bdd.lmhead_confidence_commit(h, lm4, tok, ws=ws, conf=conf, choice=choice, round_info=ri)
+    torch.cuda.synchronize()
+    t = bdd.timing_read()
+    bdd.timing_enable(False)
+    us = 1e3 * t["lmhead"][0] / t["lmhead"][1]
+    nbytes = d.V * d.H // 2 + d.V * (d.H // 128) * 2 + d.T * d.H * 2
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"LM head {d.V} x {d.H} with 4-bit weights (bf16 scale per 128 columns), block {d.T}, "
+                        "+ LowConfidence commit (threshold 0.95)",
+            "lmhead_us": round(us, 2), "commit_us": round(1e3 * t["commit"][0] / t["commit"][1], 2),
+            "launches_timed": int(t["lmhead"][1]), "algorithmic_bytes": nbytes, "achieved_gbps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def kernel_sha(kernel):

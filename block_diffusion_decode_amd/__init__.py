@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbdd.so")
 
 MASK = -1
-BDD_F32, BDD_BF16 = 0, 1
+BDD_F32, BDD_BF16, BDD_INT4 = 0, 1, 2
 _STATUS = {1: "BDD_UNRESOLVED", 0: "BDD_OK", -1: "BDD_ERR_INVALID_ARG", -2: "BDD_ERR_UNSUPPORTED",
            -3: "BDD_ERR_WORKSPACE", -4: "BDD_ERR_HIP"}
 BDD_UNRESOLVED = 1
@@ -54,6 +54,7 @@ EXPORTS = [
     "bdd_round_workspace_bytes", "bdd_block_denoise_round",
     "bdd_status_string", "bdd_last_error", "bdd_device_cus",
     "bdd_timing_enable", "bdd_timing_read", "bdd_lmhead_packed_bytes", "bdd_lmhead_pack",
+    "bdd_lmhead_pack_int4",
     "bdd_round_graph_create", "bdd_round_graph_launch", "bdd_round_graph_destroy",
     "bdd_generate_fits", "bdd_generate_workspace_bytes", "bdd_generate",
 ]
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.bdd_lmhead_packed_bytes.restype = sz
     L.bdd_lmhead_pack.argtypes = [vp, i32, i32, i32, vp, vp]
     L.bdd_lmhead_pack.restype = i32
+    L.bdd_lmhead_pack_int4.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.bdd_lmhead_pack_int4.restype = i32
     L.bdd_round_graph_create.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, vp, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
     L.bdd_round_graph_create.restype = i32
@@ -277,14 +280,19 @@ def coreset_select(router_prob: torch.Tensor, topk_idx: torch.Tensor, top_p: flo
 
 @dataclass
 class LMHead:
-    """LM-head weight [V][H] in the packed tile layout (see bdd_lmhead_pack)."""
-    packed: torch.Tensor  # uint8, bdd_lmhead_packed_bytes(V, H, dtype) bytes
+    """LM-head weight [V][H] in the packed tile layout (see bdd_lmhead_pack and
+    bdd_lmhead_pack_int4).  ``dtype`` is the type of the hidden states it
+    takes; ``int4`` marks 4-bit weights (hidden states bf16)."""
+    packed: torch.Tensor  # uint8, bdd_lmhead_packed_bytes(V, H, cdtype) bytes
     V: int
     H: int
     dtype: torch.dtype
+    int4: bool = False
 
     @property
     def cdtype(self) -> int:
+        if self.int4:
+            return BDD_INT4
         return BDD_BF16 if self.dtype == torch.bfloat16 else BDD_F32
 
 
@@ -302,6 +310,22 @@ def pack_lm_head(w_lm: torch.Tensor, stream=None) -> LMHead:
     packed = torch.empty(nb, dtype=torch.uint8, device=w_lm.device)
     _check(lib().bdd_lmhead_pack(_ptr(w_lm), V, H, cdt, _ptr(packed), _stream(stream)))
     return LMHead(packed, V, H, dt)
+
+
+def pack_lm_head_int4(codes: torch.Tensor, scales: torch.Tensor, stream=None) -> LMHead:
+    """Pack a 4-bit LM head (see bdd_lmhead_pack_int4): codes uint8 [V][H/2]
+    (column 2j in the low nibble of byte j, nibble n standing for n - 8) and
+    scales bf16 [V][H/128], both on the GPU."""
+    V, half = codes.shape
+    H = 2 * half
+    _need(codes, "codes", torch.uint8, (V, half))
+    _need(scales, "scales", torch.bfloat16, (V, H // 128), codes.device)
+    nb = int(lib().bdd_lmhead_packed_bytes(V, H, BDD_INT4))
+    if nb == 0:
+        raise BddError(-1, f"cannot pack a 4-bit LM head of shape {(V, H)}")
+    packed = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+    _check(lib().bdd_lmhead_pack_int4(_ptr(codes), _ptr(scales), V, H, _ptr(packed), _stream(stream)))
+    return LMHead(packed, V, H, torch.bfloat16, int4=True)
 
 
 def lmhead_confidence_commit(hhat: torch.Tensor, lm: LMHead, tokens: torch.Tensor,
@@ -341,8 +365,8 @@ class RoundPlan:
         dev = lm.packed.device
         self.d, self.dev = d, dev
         self.V = lm.V
-        if lm.H != d.H or lm.dtype != d.torch_dtype:
-            raise ValueError("LM head does not match the layer dims")
+        if lm.H != d.H or lm.dtype != d.torch_dtype or lm.int4:
+            raise ValueError("LM head does not match the layer dims (the full round takes bf16 or fp32 heads)")
         self.lm = lm
         self.layers = layers  # keep the tensors alive
         arr = (_Weights * max(1, len(layers)))()

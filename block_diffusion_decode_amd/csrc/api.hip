@@ -180,10 +180,12 @@ bdd_status check_weights(const bdd_moe_dims &d, const bdd_moe_weights *w, int la
 }
 
 bdd_status check_lm(int T, int H, int V, int dtype, float threshold) {
-  if (dtype != BDD_F32 && dtype != BDD_BF16) return fail(BDD_ERR_INVALID_ARG, "dtype %d", dtype);
+  if (dtype != BDD_F32 && dtype != BDD_BF16 && dtype != BDD_INT4)
+    return fail(BDD_ERR_INVALID_ARG, "dtype %d", dtype);
   if (T < 1 || H < 1 || V < 1) return fail(BDD_ERR_INVALID_ARG, "T=%d H=%d V=%d", T, H, V);
   if (T > kMaxT) return fail(BDD_ERR_UNSUPPORTED, "T=%d exceeds %d", T, kMaxT);
   if (H % 32) return fail(BDD_ERR_UNSUPPORTED, "H=%d must be a multiple of 32", H);
+  if (dtype == BDD_INT4 && H % 128) return fail(BDD_ERR_UNSUPPORTED, "INT4: H=%d must be a multiple of 128", H);
   if (!(threshold > 0.0f && threshold <= 1.0f))
     return fail(BDD_ERR_INVALID_ARG, "threshold %g outside (0, 1]", (double)threshold);
   if (lmhead_lds_bytes(dtype, T, H) > 144 * 1024)
@@ -339,8 +341,20 @@ bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx,
 }
 
 size_t bdd_lmhead_packed_bytes(int32_t V, int32_t H, int32_t dtype) {
-  if (V < 1 || H < 1 || H % 32 || (dtype != BDD_F32 && dtype != BDD_BF16)) return 0;
+  if (V < 1 || H < 1 || H % 32 || (dtype != BDD_F32 && dtype != BDD_BF16 && dtype != BDD_INT4)) return 0;
+  if (dtype == BDD_INT4 && H % 128) return 0;
   return lmhead_packed_bytes(dtype, H, V);
+}
+
+bdd_status bdd_lmhead_pack_int4(const void *codes, const void *scales, int32_t V, int32_t H, void *w_packed,
+                                void *stream) {
+  if (!codes || !scales || !w_packed) return fail(BDD_ERR_INVALID_ARG, "codes, scales and w_packed are required");
+  if (V < 1 || H < 1) return fail(BDD_ERR_INVALID_ARG, "V=%d H=%d", V, H);
+  if (H % 128) return fail(BDD_ERR_UNSUPPORTED, "H=%d must be a multiple of 128", H);
+  if ((long long)V * H >= (1ll << 40)) return fail(BDD_ERR_UNSUPPORTED, "V*H too large");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  LAUNCH("pack_lm", s, launch_pack_lm_int4(codes, scales, V, H, w_packed, s));
+  return BDD_OK;
 }
 
 bdd_status bdd_lmhead_pack(const void *w_lm, int32_t V, int32_t H, int32_t dtype, void *w_packed,

@@ -88,6 +88,9 @@ hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const in
 int lmhead_grid(int cus, int V);
 size_t lmhead_packed_bytes(int wdtype, int H, int V);
 hipError_t launch_pack_lm(int wdtype, const void *w_lm, int V, int H, void *packed, hipStream_t s);
+// 4-bit head (wdtype 2 in the LM-head calls): codes [V][H/2], scales [V][H/128] bf16.
+hipError_t launch_pack_lm_int4(const void *codes, const void *scales, int V, int H, void *packed,
+                               hipStream_t s);
 size_t lmhead_lds_bytes(int wdtype, int T, int H);
 // Commit fused into the LM head's last workgroup (done_count must be zero).
 struct LmCommit {

@@ -45,8 +45,35 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
 // Each lane loads one 16-byte unit per MFMA k-step: k-step s of a 16-row tile
 // is one contiguous KiB of the packed weight in which lane l = li + 16 g finds
 // its operand (row li, chunk 4s + g) at byte 16 l.  Loads go in batches of
-// kLmBatch k-steps; two batches are in flight per wave.
-constexpr int kLmBatch = 8;
+// lm_batch<W>() such units; two batches are in flight per wave.
+//
+// 4-bit weights (WI4): one KiB unit covers a whole 128-column group of the
+// tile, four k-steps: lane l's 16 bytes hold, in dword kk, the 8 codes of row
+// li at columns 32 (4 grp + kk) + 8 g + e, code e at bit 4 (e / 2) + 16 (e % 2).
+// ((x >> 4 d) & 0x000f000f) | 0x43004300 then turns codes 2d and 2d + 1 into
+// the bf16 values 128 + n (exact), which the MFMA takes as it takes bf16
+// weights.  With S = sum over the group of h, a group's tile sum is
+// sum (128 + n) h = sum (n - 8) h + 136 S, so the kernel subtracts 136 S and
+// multiplies by the row's scale once per group.  Scales: 16 bf16 per (tile,
+// group), after all the codes; lane (li, g) reads those of its output rows
+// 4g .. 4g + 3.
+struct WI4 { typedef bf16_t T; static constexpr int kChunk = 8; };   // h is bf16
+constexpr int kI4Group = 128;
+constexpr float kI4Offset = 136.f;
+template <class W>
+constexpr int lm_batch() { return std::is_same<W, WI4>::value ? 4 : 8; }
+template <class W>
+struct LmBufs {
+  uint4 a[lm_batch<W>()];
+  uint2 sc[std::is_same<W, WI4>::value ? lm_batch<W>() : 1];
+};
+__device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 2);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
 // The value of lane ^ S (S = 16 or 32), through v_permlane16/32_swap: the
 // swap leaves a lane's own value in one result and its partner's in the other.
@@ -182,7 +209,8 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ 
 // counter must be zero when the kernel starts.
 template <class W, int NT>
 __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__restrict__ hhat,
-                                                      const typename W::T *__restrict__ wlm, int T,
+                                                      const typename W::T *__restrict__ wlm,
+                                                      const uint16_t *__restrict__ scl, int T,
                                                       int H, int V, float *__restrict__ part_m,
                                                       float *__restrict__ part_s,
                                                       int32_t *__restrict__ part_i,
@@ -207,33 +235,73 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   // The wave's tiles (first, first + stride, ...) and their k-step batches
   // form one flat sequence of load steps, so the next tile's first batch is in
   // flight during a tile's epilogue, and the first batch during the staging.
+  constexpr bool I4 = std::is_same<W, WI4>::value;
+  constexpr int LB = lm_batch<W>();
   const int ntiles = (V + 15) / 16;
-  const int ksteps = NC / 4;
-  const int nb = (ksteps + kLmBatch - 1) / kLmBatch;
+  const int ksteps = NC / 4;                    // MFMA k-steps per tile
+  const int lsteps = I4 ? ksteps / 4 : ksteps;  // KiB load units per tile
+  const int nb = (lsteps + LB - 1) / LB;
+  float *hs = reinterpret_cast<float *>(xs + NC * TP);   // [H / 128][16 NT]: group sums of h (WI4)
   const int first = uniform(wave * (int)gridDim.x + (int)blockIdx.x);
   const int stride = gridDim.x * kLmWaves;
   const int my_tiles = first < ntiles ? (ntiles - 1 - first) / stride + 1 : 0;
   const int steps = my_tiles * nb;
   const uint32_t vbase = (uint32_t)lane * 16u;
-  const uint32_t tile_bytes = (uint32_t)(16 * H * (int)sizeof(typename W::T));
-  auto load = [&](int st, uint4(&a)[kLmBatch]) {
+  const uint32_t tile_bytes = I4 ? (uint32_t)(8 * H) : (uint32_t)(16 * H * (int)sizeof(typename W::T));
+  auto load = [&](int st, LmBufs<W> &bf) {
     const bool live = st < steps;
     const int k = live ? st / nb : 0, b = st - (st / nb) * nb;
+    const size_t tile = (size_t)(first + k * stride);
     // descriptor over the tile's packed rows (rows past V were packed as zeros)
-    const rsrc_t rs = make_rsrc(wlm + (size_t)(first + k * stride) * 16 * H, tile_bytes);
+    const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(wlm) + tile * tile_bytes, tile_bytes);
 #pragma unroll
-    for (int j = 0; j < kLmBatch; ++j)   // k-steps past the tile or the stream: no access
-      a[j] = buf_ld16(rs, live && b * kLmBatch + j < ksteps ? vbase : kLmOutOfRange,
-                      (uint32_t)min(b * kLmBatch + j, ksteps - 1) * 1024u);
+    for (int j = 0; j < LB; ++j)   // units past the tile or the stream: no access
+      bf.a[j] = buf_ld16(rs, live && b * LB + j < lsteps ? vbase : kLmOutOfRange,
+                         (uint32_t)min(b * LB + j, lsteps - 1) * 1024u);
+    if constexpr (I4) {
+      const rsrc_t rq = make_rsrc(scl + tile * (size_t)lsteps * 16, (uint32_t)lsteps * 32u);
+#pragma unroll
+      for (int j = 0; j < LB; ++j)
+        bf.sc[j] = buf_ld8(rq, live && b * LB + j < lsteps ? (uint32_t)g * 8u : kLmOutOfRange,
+                           (uint32_t)min(b * LB + j, lsteps - 1) * 32u);
+    }
   };
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](int st, const uint4(&a)[kLmBatch]) {
+  auto mma = [&](int st, const LmBufs<W> &bf) {
     const int b = st % nb;
+    if constexpr (I4) {
 #pragma unroll
-    for (int j = 0; j < kLmBatch; ++j) {
-      const int ks = b * kLmBatch + j;
+      for (int j = 0; j < LB; ++j) {
+        const int grp = b * LB + j;
+        if (grp >= lsteps) break;
+        f32x4 ag[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) ag[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t x = kk == 0 ? bf.a[j].x : kk == 1 ? bf.a[j].y : kk == 2 ? bf.a[j].z : bf.a[j].w;
+          const uint4 e = make_uint4((x & 0x000f000fu) | 0x43004300u, ((x >> 4) & 0x000f000fu) | 0x43004300u,
+                                     ((x >> 8) & 0x000f000fu) | 0x43004300u, ((x >> 12) & 0x000f000fu) | 0x43004300u);
+          const int c = (grp * 4 + kk) * 4 + g;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) ag[n] = mfma_bf16(e, xs[c * TP + n * 16 + li], ag[n]);
+        }
+        const float sr[4] = {bf_lo(bf.sc[j].x), bf_hi(bf.sc[j].x), bf_lo(bf.sc[j].y), bf_hi(bf.sc[j].y)};
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const float off = kI4Offset * hs[grp * TP + n * 16 + li];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[n][r] = fmaf(sr[r], ag[n][r] - off, acc[n][r]);
+        }
+      }
+      return;
+    }
+    const uint4(&a)[LB] = bf.a;
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+      const int ks = b * LB + j;
       if (ks >= ksteps) break;
       const int c = ks * 4 + g;
 #pragma unroll
@@ -292,7 +360,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
     }
   };
 
-  uint4 a0[kLmBatch], a1[kLmBatch];
+  LmBufs<W> a0, a1;
   load(0, a0);
   load(1, a1);
   // stage the block: batches of 8 independent loads per thread
@@ -312,6 +380,21 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
     }
   }
   __syncthreads();
+  if constexpr (I4) {
+    // per (group, position): the sum of the group's 128 values of h
+    for (int idx = tid; idx < (H / kI4Group) * TP; idx += (int)blockDim.x) {
+      const int grp = idx / TP, t = idx - grp * TP;
+      float sum = 0.f;
+      for (int c = grp * (kI4Group / 8); c < (grp + 1) * (kI4Group / 8); ++c) {
+        float f[8];
+        unpack8(xs[c * TP + t], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += f[e];
+      }
+      hs[idx] = sum;
+    }
+    __syncthreads();
+  }
   // A buffer is refilled as soon as its MFMAs have read it, before a tile's
   // epilogue, so two batches stay in flight through the epilogue.  Loads past
   // the last step are out of range (no access): the loop always has the same
@@ -378,8 +461,54 @@ __global__ __launch_bounds__(256) void pack_lm_kernel(const typename W::T *__res
   }
 }
 
+// 4-bit LM head: codes [V][H / 2] (column 2j in the low nibble of byte j) and
+// scales [V][H / 128] bf16 into the layout described at WI4: one thread per
+// 16-byte unit (tile tau, group grp, lane l); the lanes with g = 0 also place
+// the unit's 16 scales.  Rows past V get zero codes and zero scales.
+__global__ __launch_bounds__(256) void pack_lm_i4_kernel(const uint8_t *__restrict__ codes,
+                                                         const uint16_t *__restrict__ scales, int V, int H,
+                                                         uint4 *__restrict__ out, uint16_t *__restrict__ sout,
+                                                         long long units) {
+  const int G = H / kI4Group;
+  for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+       u += (long long)gridDim.x * blockDim.x) {
+    const int l = (int)(u & 63), li = l & 15, g = l >> 4;
+    const long long blk = u >> 6;
+    const long long tau = blk / G;
+    const int grp = (int)(blk - tau * G);
+    const long long row = tau * 16 + li;
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+    if (row < V) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint8_t *src = codes + row * (H / 2) + ((grp * 4 + kk) * 32 + 8 * g) / 2;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t byte = src[b];
+          d[kk] |= (byte & 15u) << (4 * b) | (byte >> 4) << (16 + 4 * b);
+        }
+      }
+    }
+    out[u] = make_uint4(d[0], d[1], d[2], d[3]);
+    if (g == 0) sout[blk * 16 + li] = row < V ? scales[row * G + grp] : (uint16_t)0;
+  }
+}
+
 size_t lmhead_packed_bytes(int wdtype, int H, int V) {
-  return (size_t)((V + 15) / 16) * 16 * H * (wdtype == 1 ? 2 : 4);
+  const size_t tiles = (size_t)((V + 15) / 16);
+  if (wdtype == 2) return tiles * (size_t)(8 * H) + tiles * (size_t)(H / kI4Group) * 32;
+  return tiles * 16 * H * (wdtype == 1 ? 2 : 4);
+}
+
+hipError_t launch_pack_lm_int4(const void *codes, const void *scales, int V, int H, void *packed,
+                               hipStream_t s) {
+  const size_t tiles = (size_t)((V + 15) / 16);
+  const long long units = (long long)(tiles * (size_t)(8 * H) / 16);
+  const int grid = (int)((units + 255) / 256 < 65536 ? (units + 255) / 256 : 65536);
+  pack_lm_i4_kernel<<<grid, 256, 0, s>>>((const uint8_t *)codes, (const uint16_t *)scales, V, H,
+                                         (uint4 *)packed,
+                                         (uint16_t *)((char *)packed + tiles * (size_t)(8 * H)), units);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack_lm(int wdtype, const void *w_lm, int V, int H, void *packed, hipStream_t s) {
@@ -405,8 +534,8 @@ int lmhead_grid(int cus, int V) {
 
 size_t lmhead_lds_bytes(int wdtype, int T, int H) {
   const int tp = T <= 16 ? 16 : 32;
-  const int ch = wdtype == 1 ? 8 : 4;
-  return (size_t)(H / ch) * tp * 16;
+  const int ch = wdtype == 0 ? 4 : 8;
+  return (size_t)(H / ch) * tp * 16 + (wdtype == 2 ? (size_t)(H / kI4Group) * tp * 4 : 0);
 }
 
 template <typename F>
@@ -420,11 +549,15 @@ template <class W, int NT>
 static hipError_t lmhead_launch(const void *hhat, const void *w_lm, int T, int H, int V, float *pm,
                                 float *ps, int32_t *pi, int grid, const LmCommit *fused, hipStream_t s) {
   typedef typename W::T WT;
-  const size_t lds = lmhead_lds_bytes(std::is_same<W, WBf16>::value ? 1 : 0, T, H);
+  constexpr int dt = std::is_same<W, WI4>::value ? 2 : std::is_same<W, WBf16>::value ? 1 : 0;
+  const size_t lds = lmhead_lds_bytes(dt, T, H);
   hipError_t err = allow_lds(lmhead_kernel<W, NT>, lds);
   if (err != hipSuccess) return err;
+  // 4-bit heads: the scales follow the codes in the packed buffer
+  const uint16_t *scl =
+      dt == 2 ? (const uint16_t *)((const char *)w_lm + (size_t)((V + 15) / 16) * (size_t)(8 * H)) : nullptr;
   lmhead_kernel<W, NT><<<grid, 1024, lds, s>>>(
-      (const WT *)hhat, (const WT *)w_lm, T, H, V, pm, ps, pi, fused ? fused->done_count : nullptr,
+      (const WT *)hhat, (const WT *)w_lm, scl, T, H, V, pm, ps, pi, fused ? fused->done_count : nullptr,
       fused ? fused->threshold : 0.f, fused ? fused->tokens : nullptr, fused ? fused->conf : nullptr,
       fused ? fused->choice : nullptr, fused ? fused->round_info : nullptr);
   return hipGetLastError();
@@ -433,6 +566,9 @@ static hipError_t lmhead_launch(const void *hhat, const void *w_lm, int T, int H
 hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,
                          float *part_m, float *part_s, int32_t *part_i, int grid, const LmCommit *fused,
                          hipStream_t s) {
+  if (wdtype == 2)
+    return T <= 16 ? lmhead_launch<WI4, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+                   : lmhead_launch<WI4, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
   if (wdtype == 1)
     return T <= 16 ? lmhead_launch<WBf16, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
                    : lmhead_launch<WBf16, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);

@@ -53,7 +53,9 @@ typedef enum {
   BDD_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
 } bdd_status;
 
-typedef enum { BDD_F32 = 0, BDD_BF16 = 1 } bdd_dtype;
+/* BDD_INT4: 4-bit weight-only LM head (bdd_lmhead_pack_int4); the MoE
+ * layers and the full round take BDD_F32 or BDD_BF16 only. */
+typedef enum { BDD_F32 = 0, BDD_BF16 = 1, BDD_INT4 = 2 } bdd_dtype;
 
 /* Shapes of one MoE layer and the block.  T block positions, H hidden, E
  * routed experts, K experts per token, I routed-expert intermediate,
@@ -139,7 +141,8 @@ bdd_status bdd_coreset_select(const float *router_prob, const int32_t *topk_idx,
                               uint32_t *coreset_bits, int32_t *coreset_size,
                               float *expert_mass, void *stream);
 
-/* Bytes of the packed LM-head weight (0 if the arguments are invalid). */
+/* Bytes of the packed LM-head weight (0 if the arguments are invalid).
+ * BDD_INT4 needs H to be a multiple of 128. */
 size_t bdd_lmhead_packed_bytes(int32_t V, int32_t H, int32_t dtype);
 
 /* Packs the LM-head weight w_lm [V][H] (dtype) into the tile layout the LM
@@ -154,14 +157,34 @@ size_t bdd_lmhead_packed_bytes(int32_t V, int32_t H, int32_t dtype);
 bdd_status bdd_lmhead_pack(const void *w_lm, int32_t V, int32_t H, int32_t dtype, void *w_packed,
                            void *stream);
 
+/* Packs a 4-bit weight-only LM head ([P3] 10100.com article on
+ * Clover-35B-A3B-Preview, part 03, memory and quantisation: the model is
+ * deployed in INT4; the pages give no format, so this one is assumed):
+ *   codes   [V][H/2] uint8, device: byte j of row v holds columns 2j (low
+ *           nibble) and 2j + 1 (high nibble); a nibble n stands for n - 8
+ *   scales  [V][H/128] bf16, device: one scale per row and 128-column group
+ *   weight w[v][c] = (n - 8) * scales[v][c / 128].
+ * w_packed (device, bdd_lmhead_packed_bytes(V, H, BDD_INT4) bytes) receives,
+ * per tile of 16 rows and group of 128 columns, one KiB of codes in the order
+ * the LM head's lanes consume them (lane li + 16 g: row li, columns
+ * 32 (4 group + kk) + 8 g + e for kk, e in 0..3, 0..7), then after all codes
+ * the scales as [tile][group][16] bf16.  Rows past V get zero scales.
+ * H must be a multiple of 128.  Runs on `stream`; the caller owns every
+ * buffer.  Errors: BDD_ERR_INVALID_ARG (NULL pointer, V or H < 1),
+ * BDD_ERR_UNSUPPORTED (H not a multiple of 128, V*H too large). */
+bdd_status bdd_lmhead_pack_int4(const void *codes, const void *scales, int32_t V, int32_t H,
+                                void *w_packed, void *stream);
+
 /* Workspace bytes bdd_lmhead_confidence_commit needs. */
 size_t bdd_lmhead_workspace_bytes(int32_t T, int32_t H, int32_t V);
 
 /* LM head, confidence and LowConfidence commit ([P1] section 三 pseudocode
  * and rules; [P2] decoding-loop steps 2-4).
- *   hhat      [T][H] dtype  normalised final hidden states
+ *   hhat      [T][H] dtype  normalised final hidden states (bf16 when dtype
+ *             is BDD_INT4)
  *   w_packed  the LM-head weight [V][H] (row v = token v) as packed by
- *             bdd_lmhead_pack
+ *             bdd_lmhead_pack, or by bdd_lmhead_pack_int4 (dtype BDD_INT4:
+ *             logits of the dequantised weight, accumulated in fp32)
  *   For each position: logits z = hhat W_lm^T (never stored), conf = max
  *   softmax probability = 1 / sum_v exp(z_v - max z), choice = argmax (lowest
  *   token id on ties).  Then among positions whose token is MASK: every one

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(bdd.LIB_PATH),
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(bdd_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(bdd_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_four_entry_points():
@@ -88,6 +88,26 @@ def test_lmhead_rejects_bad_threshold_and_shapes():
     assert L.bdd_lmhead_confidence_commit(*args(32, 4096, 1000, 1, 0.95)) == -2   # LDS budget
     assert L.bdd_lmhead_confidence_commit(*args(32, 2048, 1000, 1, 0.95)) == -3   # no workspace
     assert L.bdd_lmhead_confidence_commit(None, p, 32, 2048, 10, 1, 0.95, p, p, p, p, p, 1 << 30, None) == -1
+
+
+def test_int4_lm_head_sizes_and_host_checks():
+    L = bdd.lib()
+    # 16-row tiles: 8 H bytes of codes and H / 128 * 32 bytes of scales each
+    for V, H in [(16, 128), (5003, 256), (248320, 2048)]:
+        tiles = (V + 15) // 16
+        assert L.bdd_lmhead_packed_bytes(V, H, bdd.BDD_INT4) == tiles * 8 * H + tiles * (H // 128) * 32
+    assert L.bdd_lmhead_packed_bytes(100, 192, bdd.BDD_INT4) == 0
+    assert L.bdd_lmhead_packed_bytes(100, 192, bdd.BDD_BF16) == 7 * 16 * 192 * 2
+    p = ctypes.c_void_p(1)
+    assert L.bdd_lmhead_pack_int4(None, p, 10, 256, p, None) == -1
+    assert L.bdd_lmhead_pack_int4(p, p, 0, 256, p, None) == -1
+    assert L.bdd_lmhead_pack_int4(p, p, 10, 192, p, None) == -2
+    # the float pack does not take the 4-bit type, and INT4 heads need H % 128 == 0
+    assert L.bdd_lmhead_pack(p, 10, 256, bdd.BDD_INT4, p, None) == -1
+    args = lambda H, dt: (p, p, 32, H, 1000, dt, 0.95, p, p, p, p, None, 0, None)
+    assert L.bdd_lmhead_confidence_commit(*args(192, bdd.BDD_INT4)) == -2
+    assert L.bdd_lmhead_confidence_commit(*args(2048, bdd.BDD_INT4)) == -3   # no workspace
+    assert L.bdd_lmhead_confidence_commit(*args(2048, 3)) == -1
 
 
 def test_coreset_rejects_on_host():
