@@ -72,6 +72,17 @@ __device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff)
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 2);
   return make_uint2(v.x, v.y);
 }
+// (a & m) | c in one instruction (the compiler splits the pattern in two)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+// codes 2d and 2d + 1 of a dword (see WI4) as the bf16 pair 128 + n
+__device__ __forceinline__ uint4 i4_expand(uint32_t x) {
+  const uint32_t m = 0x000f000fu, c = 0x43004300u;
+  return make_uint4(and_or(x, m, c), and_or(x >> 4, m, c), and_or(x >> 8, m, c), and_or(x >> 12, m, c));
+}
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -279,14 +290,17 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
         f32x4 ag[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) ag[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the group's block operands first, so their LDS latency overlaps the expansion
+        uint4 bv[4][NT];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) bv[kk][n] = xs[((grp * 4 + kk) * 4 + g) * TP + n * 16 + li];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t x = kk == 0 ? bf.a[j].x : kk == 1 ? bf.a[j].y : kk == 2 ? bf.a[j].z : bf.a[j].w;
-          const uint4 e = make_uint4((x & 0x000f000fu) | 0x43004300u, ((x >> 4) & 0x000f000fu) | 0x43004300u,
-                                     ((x >> 8) & 0x000f000fu) | 0x43004300u, ((x >> 12) & 0x000f000fu) | 0x43004300u);
-          const int c = (grp * 4 + kk) * 4 + g;
+          const uint4 e = i4_expand(kk == 0 ? bf.a[j].x : kk == 1 ? bf.a[j].y : kk == 2 ? bf.a[j].z : bf.a[j].w);
 #pragma unroll
-          for (int n = 0; n < NT; ++n) ag[n] = mfma_bf16(e, xs[c * TP + n * 16 + li], ag[n]);
+          for (int n = 0; n < NT; ++n) ag[n] = mfma_bf16(e, bv[kk][n], ag[n]);
         }
         const float sr[4] = {bf_lo(bf.sc[j].x), bf_hi(bf.sc[j].x), bf_lo(bf.sc[j].y), bf_hi(bf.sc[j].y)};
 #pragma unroll
