@@ -60,12 +60,17 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
 struct WI4 { typedef bf16_t T; static constexpr int kChunk = 8; };   // h is bf16
 constexpr int kI4Group = 128;
 constexpr float kI4Offset = 136.f;
+// units per tile per load batch, and tiles a wave streams side by side: a
+// 4-bit wave works on two tiles at once, so every block operand it reads from
+// LDS feeds both tiles' MFMAs (a bf16 tile is HBM-bound on its own)
 template <class W>
-constexpr int lm_batch() { return std::is_same<W, WI4>::value ? 4 : 8; }
+constexpr int lm_batch() { return std::is_same<W, WI4>::value ? 2 : 8; }
+template <class W>
+constexpr int lm_tiles() { return std::is_same<W, WI4>::value ? 2 : 1; }
 template <class W>
 struct LmBufs {
-  uint4 a[lm_batch<W>()];
-  uint2 sc[std::is_same<W, WI4>::value ? lm_batch<W>() : 1];
+  uint4 a[lm_tiles<W>()][lm_batch<W>()];
+  uint2 sc[lm_tiles<W>()][std::is_same<W, WI4>::value ? lm_batch<W>() : 1];
 };
 __device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -248,6 +253,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   // flight during a tile's epilogue, and the first batch during the staging.
   constexpr bool I4 = std::is_same<W, WI4>::value;
   constexpr int LB = lm_batch<W>();
+  constexpr int TW = lm_tiles<W>();
   const int ntiles = (V + 15) / 16;
   const int ksteps = NC / 4;                    // MFMA k-steps per tile
   const int lsteps = I4 ? ksteps / 4 : ksteps;  // KiB load units per tile
@@ -256,30 +262,37 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   const int first = uniform(wave * (int)gridDim.x + (int)blockIdx.x);
   const int stride = gridDim.x * kLmWaves;
   const int my_tiles = first < ntiles ? (ntiles - 1 - first) / stride + 1 : 0;
-  const int steps = my_tiles * nb;
+  const int steps = (my_tiles + TW - 1) / TW * nb;   // TW tiles per step sequence
   const uint32_t vbase = (uint32_t)lane * 16u;
   const uint32_t tile_bytes = I4 ? (uint32_t)(8 * H) : (uint32_t)(16 * H * (int)sizeof(typename W::T));
   auto load = [&](int st, LmBufs<W> &bf) {
     const bool live = st < steps;
     const int k = live ? st / nb : 0, b = st - (st / nb) * nb;
-    const size_t tile = (size_t)(first + k * stride);
-    // descriptor over the tile's packed rows (rows past V were packed as zeros)
-    const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(wlm) + tile * tile_bytes, tile_bytes);
 #pragma unroll
-    for (int j = 0; j < LB; ++j)   // units past the tile or the stream: no access
-      bf.a[j] = buf_ld16(rs, live && b * LB + j < lsteps ? vbase : kLmOutOfRange,
-                         (uint32_t)min(b * LB + j, lsteps - 1) * 1024u);
-    if constexpr (I4) {
-      const rsrc_t rq = make_rsrc(scl + tile * (size_t)lsteps * 16, (uint32_t)lsteps * 32u);
+    for (int q = 0; q < TW; ++q) {
+      const int kt = TW * k + q;   // the wave's tile number (past my_tiles: no access)
+      const bool lq = live && kt < my_tiles;
+      const size_t tile = (size_t)(first + (lq ? kt : 0) * stride);
+      // descriptor over the tile's packed rows (rows past V were packed as zeros)
+      const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(wlm) + tile * tile_bytes, tile_bytes);
 #pragma unroll
-      for (int j = 0; j < LB; ++j)
-        bf.sc[j] = buf_ld8(rq, live && b * LB + j < lsteps ? (uint32_t)g * 8u : kLmOutOfRange,
-                           (uint32_t)min(b * LB + j, lsteps - 1) * 32u);
+      for (int j = 0; j < LB; ++j)   // units past the tile or the stream: no access
+        bf.a[q][j] = buf_ld16(rs, lq && b * LB + j < lsteps ? vbase : kLmOutOfRange,
+                              (uint32_t)min(b * LB + j, lsteps - 1) * 1024u);
+      if constexpr (I4) {
+        const rsrc_t rq = make_rsrc(scl + tile * (size_t)lsteps * 16, (uint32_t)lsteps * 32u);
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+          bf.sc[q][j] = buf_ld8(rq, lq && b * LB + j < lsteps ? (uint32_t)g * 8u : kLmOutOfRange,
+                                (uint32_t)min(b * LB + j, lsteps - 1) * 32u);
+      }
     }
   };
-  f32x4 acc[NT];
+  f32x4 acc[TW][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < TW; ++q)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto mma = [&](int st, const LmBufs<W> &bf) {
     const int b = st % nb;
     if constexpr (I4) {
@@ -287,32 +300,40 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
       for (int j = 0; j < LB; ++j) {
         const int grp = b * LB + j;
         if (grp >= lsteps) break;
-        f32x4 ag[NT];
+        f32x4 ag[TW][NT];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) ag[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // the group's block operands first, so their LDS latency overlaps the expansion
-        uint4 bv[4][NT];
+        for (int q = 0; q < TW; ++q)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) bv[kk][n] = xs[((grp * 4 + kk) * 4 + g) * TP + n * 16 + li];
+          for (int n = 0; n < NT; ++n) ag[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint4 e = i4_expand(kk == 0 ? bf.a[j].x : kk == 1 ? bf.a[j].y : kk == 2 ? bf.a[j].z : bf.a[j].w);
+          uint4 bv[NT];
 #pragma unroll
-          for (int n = 0; n < NT; ++n) ag[n] = mfma_bf16(e, bv[kk][n], ag[n]);
+          for (int n = 0; n < NT; ++n) bv[n] = xs[((grp * 4 + kk) * 4 + g) * TP + n * 16 + li];
+#pragma unroll
+          for (int q = 0; q < TW; ++q) {
+            const uint4 &aq = bf.a[q][j];
+            const uint4 e = i4_expand(kk == 0 ? aq.x : kk == 1 ? aq.y : kk == 2 ? aq.z : aq.w);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) ag[q][n] = mfma_bf16(e, bv[n], ag[q][n]);
+          }
         }
-        const float sr[4] = {bf_lo(bf.sc[j].x), bf_hi(bf.sc[j].x), bf_lo(bf.sc[j].y), bf_hi(bf.sc[j].y)};
+        float off[NT];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const float off = kI4Offset * hs[grp * TP + n * 16 + li];
+        for (int n = 0; n < NT; ++n) off[n] = kI4Offset * hs[grp * TP + n * 16 + li];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[n][r] = fmaf(sr[r], ag[n][r] - off, acc[n][r]);
+        for (int q = 0; q < TW; ++q) {
+          const uint2 sq = bf.sc[q][j];
+          const float sr[4] = {bf_lo(sq.x), bf_hi(sq.x), bf_lo(sq.y), bf_hi(sq.y)};
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[q][n][r] = fmaf(sr[r], ag[q][n][r] - off[n], acc[q][n][r]);
         }
       }
       return;
     }
-    const uint4(&a)[LB] = bf.a;
+    const uint4(&a)[LB] = bf.a[0];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
       const int ks = b * LB + j;
@@ -322,12 +343,12 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
       for (int n = 0; n < NT; ++n) {
         const uint4 bv = xs[c * TP + n * 16 + li];
         if constexpr (std::is_same<W, WBf16>::value) {
-          acc[n] = mfma_bf16(a[j], bv, acc[n]);
+          acc[0][n] = mfma_bf16(a[j], bv, acc[0][n]);
         } else {
-          acc[n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[n]);
-          acc[n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[n]);
-          acc[n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[n]);
-          acc[n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[n]);
+          acc[0][n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[0][n]);
+          acc[0][n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[0][n]);
+          acc[0][n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[0][n]);
+          acc[0][n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[0][n]);
         }
       }
     }
@@ -335,7 +356,10 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   // epilogue of a finished tile: lane holds rows row0 + 4g + r (r = 0..3) of
   // column li + 16n; fold them into the running (max, sum, argmax)
   auto epilogue = [&](int st) {
-    const int row0 = (first + (st / nb) * stride) * 16;
+#pragma unroll
+    for (int q = 0; q < TW; ++q) {
+    // (a tile past the wave's last has row0 >= V: it folds nothing)
+    const int row0 = (first + (TW * (st / nb) + q) * stride) * 16;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       float tmax = -FLT_MAX;
@@ -343,7 +367,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = row0 + 4 * g + r;
-        if (v < V && (targ == INT_MAX || acc[n][r] > tmax)) { tmax = acc[n][r]; targ = v; }
+        if (v < V && (targ == INT_MAX || acc[q][n][r] > tmax)) { tmax = acc[q][n][r]; targ = v; }
       }
       {
         const float m2 = partner_f32<16>(tmax, lane);
@@ -365,12 +389,13 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = row0 + 4 * g + r;
-        if (v < V) tsum += __expf(acc[n][r] - tmax);
+        if (v < V) tsum += __expf(acc[q][n][r] - tmax);
       }
       tsum += partner_f32<16>(tsum, lane);
       tsum += partner_f32<32>(tsum, lane);
       sm_merge(m[n], s[n], am[n], tmax, tsum, targ);
-      acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     }
   };
 
