@@ -72,9 +72,11 @@ struct LmBufs {
   uint4 a[lm_tiles<W>()][lm_batch<W>()];
   uint2 sc[lm_tiles<W>()][std::is_same<W, WI4>::value ? lm_batch<W>() : 1];
 };
+// 8-byte load of scales: cached normally (a tile's 128-byte line of scales
+// serves several load batches; the streaming hint would evict it in between)
 __device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 2);
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
   return make_uint2(v.x, v.y);
 }
 // (a & m) | c in one instruction (the compiler splits the pattern in two)
