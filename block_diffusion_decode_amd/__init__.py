@@ -456,14 +456,17 @@ class RoundGraph:
             _ptr(layer_topk_idx), _ptr(layer_n_distinct), None, _ptr(hhat_out), _ptr(plan.ws), plan.ws.numel(),
             ctypes.byref(h)))
         self.handle = h
+        # bound now: at interpreter exit the module's globals may be gone before __del__ runs
+        self._destroy = lib().bdd_round_graph_destroy
 
     def launch(self, stream=None):
         _check(lib().bdd_round_graph_launch(self.handle, _stream(stream)))
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
-            lib().bdd_round_graph_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self.handle = None
 
 
