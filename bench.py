@@ -14,10 +14,13 @@ region; the same K rounds replayed as HIP graphs are reported beside it),
 achieved HBM bandwidth on the round's algorithmic bytes, the roofline of the
 dominant kernel (its launches bracketed by hipEvents on their stream over K
 further rounds; HBM traffic from the rocprofv3 counter summary under
-profiles/ while the kernel's sources are unchanged since it was taken), and
-the CPU oracle timed on a bounded sample of the same workload.
+profiles/ while the kernel's sources are unchanged since it was taken), the
+same LM head with 4-bit weights timed alone ('lmhead_int4', not the value),
+and the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --stack 40               # also the 40-layer Zipf/coreset stack
+    python bench.py --int4-only              # the 4-bit LM head + commit alone
     python bench.py --copy-calibration MIB   # plain device copy, for counter scaling
 """
 
