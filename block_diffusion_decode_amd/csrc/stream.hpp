@@ -56,7 +56,9 @@ __device__ __forceinline__ void pipeline_post(int steps, Bufs &b0, Bufs &b1, Loa
 // positions), in one pass over the weights.  At k-step s lane group
 // g = lane >> 4 holds chunk 4s + g of its row (the MFMA operand layout), so a
 // load straight into operand order reads only 64 contiguous bytes of each of
-// 16 rows.
+// 16 rows.  The weights are therefore loaded as whole 128-byte lines of 8 rows
+// and passed through LDS into operand order (stage_slot); the block's packed
+// copy (xpack_unit) and the packed activations are already in operand order.
 // ---------------------------------------------------------------------------
 
 template <class W>
