@@ -310,6 +310,153 @@ def test_moe_coreset_restricts_union():
     assert len(i7["union"]) <= len(i1["union"])
 
 
+def test_coreset_equal_masses_at_the_cut_keep_the_lower_id():
+    # 2 positions, 4 experts, top-2; probabilities exact in binary.
+    #   position 0: p = [0.5, 0.0625, 0.125, 0.3125] -> picks {0, 3}
+    #   position 1: p = [0.5, 0.3125, 0.125, 0.0625] -> picks {0, 1}
+    # mass: e0 = 1.0, e1 = 0.3125, e3 = 0.3125, e2 = 0; total 1.625.
+    # Ranked (mass desc, id asc): e0, e1, e3.  top_p 0.7 -> target 1.1375:
+    # cum 1.0 < 1.1375 <= 1.3125, so the cut falls between the two equal
+    # masses and the lower id (e1) is kept.
+    p = np.array([[0.5, 0.0625, 0.125, 0.3125], [0.5, 0.3125, 0.125, 0.0625]])
+    idx = np.array([[0, 3], [0, 1]])
+    members, mass, order = O.coreset_select(p, idx, 0.7)
+    assert list(mass) == [1.0, 0.3125, 0.0, 0.3125]
+    assert list(order[:3]) == [0, 1, 3]
+    assert list(members) == [0, 1]
+    # the same block with the expert ids of the tied pair swapped keeps e1 again
+    p2 = p[:, [0, 3, 2, 1]]
+    idx2 = np.array([[0, 1], [0, 3]])
+    members2, _, _ = O.coreset_select(p2, idx2, 0.7)
+    assert list(members2) == [0, 1]
+    # re-routing inside C = {0, 1}: position 0 now takes e0 and e1, weights
+    # renormalised over them: 0.5 / 0.5625 and 0.0625 / 0.5625
+    l = np.log(p)
+    i2, w2 = O.reroute(l, p, members, 2)
+    assert [sorted(r) for r in i2.tolist()] == [[0, 1], [0, 1]]
+    assert np.allclose(w2[0], [0.5 / 0.5625, 0.0625 / 0.5625], rtol=0, atol=1e-15)
+
+
+def test_reroute_equal_logits_take_the_lower_id():
+    # coreset {1, 2, 5}; one position's logits: e5 = 2, e1 = e2 = 1 (equal),
+    # the rest outside the coreset larger still (they must be ignored).
+    l = np.array([[9.0, 1.0, 1.0, 9.0, 9.0, 2.0]])
+    p = np.exp(l) / np.exp(l).sum()
+    members = np.array([5, 2, 1])
+    i2, w2 = O.reroute(l, p, members, 2)
+    assert i2.tolist() == [[5, 1]]                    # e5 first, then the lower of the tie
+    assert np.allclose(w2[0], [math.e / (math.e + 1), 1 / (math.e + 1)], rtol=0, atol=1e-15)
+    i1, w1 = O.reroute(l, p, members, 1)
+    assert i1.tolist() == [[5]] and w1[0, 0] == 1.0
+    # all three equal: the two lowest ids
+    l3 = np.array([[0.0, 3.0, 3.0, 0.0, 0.0, 3.0]])
+    i3, w3 = O.reroute(l3, np.exp(l3) / np.exp(l3).sum(), members, 2)
+    assert i3.tolist() == [[1, 2]] and np.allclose(w3, 0.5, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# layer stack: residual, inter-layer RMSNorm, final RMSNorm, bf16 points
+# ---------------------------------------------------------------------------
+
+def _zero_layer(E, H, I, Is):
+    return {"w_router": np.zeros((E, H)), "router_bias": np.zeros(E),
+            "ws_gate_up": np.zeros((2 * Is, H)), "ws_down": np.zeros((H, Is)),
+            "experts": {e: (np.zeros((2 * I, H)), np.zeros((H, I))) for e in range(E)}}
+
+
+def _bf16_torch(x):
+    return torch.from_numpy(np.asarray(x, np.float64)).to(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("n_layers", [1, 2, 5])
+def test_stack_of_zero_layers_is_the_final_norm(n_layers):
+    # every routed and shared weight zero: each layer adds y = 0, so the
+    # stack returns bf16(RMSNorm(x_in)) exactly (RMSNorm written out here,
+    # bf16 by torch's conversion)
+    T, H, E, K, I = 5, 48, 6, 2, 8
+    x = RNG.normal(size=(T, H)) * 3.0
+    layers = [_zero_layer(E, H, I, I) for _ in range(n_layers)]
+    hh, infos = O.moe_stack(x, layers, K)
+    want = _bf16_torch(x / np.sqrt((x * x).sum(axis=1, keepdims=True) / H + 1e-6))
+    assert np.array_equal(hh, want)
+    assert len(infos) == n_layers
+    for inf in infos:                 # every layer saw the same normalised input
+        assert np.array_equal(inf["xhat"], want)
+    hh_f, _ = O.moe_stack(x, layers, K, round_bf16=False)
+    assert np.allclose(hh_f, x / np.sqrt((x * x).mean(axis=1, keepdims=True) + 1e-6), rtol=0, atol=1e-15)
+    # scale invariance of the normalised output (eps 0: exact for any c > 0
+    # up to the last bit before bf16 rounding)
+    for c in (0.25, 3.0, 1024.0):
+        hc, _ = O.moe_stack(c * x, layers, K, eps=0.0)
+        h1, _ = O.moe_stack(x, layers, K, eps=0.0)
+        assert np.array_equal(hc, h1), c
+
+
+def _hand_layers():
+    # H = 2, E = 2, K = 1, I = 1, shared expert I_s = 1; weights [out][in]
+    la = {"w_router": np.array([[1.0, 0.0], [0.0, 1.0]]), "router_bias": np.zeros(2),
+          "ws_gate_up": np.array([[0.5, 0.5], [1.0, -1.0]]), "ws_down": np.array([[1.0], [0.5]]),
+          "experts": {0: (np.array([[1.0, 0.0], [0.0, 1.0]]), np.array([[1.0], [1.0]])),
+                      1: (np.array([[0.0, 1.0], [1.0, 0.0]]), np.array([[2.0], [-1.0]]))}}
+    lb = {"w_router": np.array([[0.0, 1.0], [1.0, 0.0]]), "router_bias": np.array([0.25, 0.0]),
+          "ws_gate_up": np.array([[1.0, 0.0], [1.0, 0.0]]), "ws_down": np.array([[0.0], [1.0]]),
+          "experts": {0: (np.array([[1.0, 1.0], [1.0, 0.0]]), np.array([[-1.0], [1.0]])),
+                      1: (np.array([[1.0, -1.0], [0.0, 1.0]]), np.array([[0.5], [0.5]]))}}
+    return [la, lb]
+
+
+def test_stack_hand_worked_two_layers():
+    # Worked by hand (50-digit decimal arithmetic, one scalar step at a time):
+    # x_in rows (3, 4) and (4, -3).
+    # Layer A: RMSNorm (eps 1e-6) gives (0.848528..., 1.131371...) and its
+    #   mirror; stored as bf16: 0.848528 * 256 = 217.22 -> 217/256 =
+    #   0.84765625; 1.131371 * 128 = 144.82 -> 145/128 = 1.1328125.
+    #   Router = identity: position 0 picks expert 1, position 1 expert 0
+    #   (K = 1, weight 1).  Position 0: expert 1 gate x1 = 1.1328125, up x0,
+    #   a = silu(1.1328125) * 0.84765625, down (2, -1) -> (2a, -a); shared:
+    #   gate 0.5 (x0 + x1), up x0 - x1, down (1, 0.5).  y0 = (1.24667617...,
+    #   -0.82922482...); h = x_in + y.
+    # Layer B normalises h (not y) and rounds to bf16: (1.1328125, 0.84765625)
+    #   and (0.96875, -1.03125); router logits with bias (0.25, 0): position 0
+    #   (1.09765625, 1.1328125) -> expert 1; position 1 (-0.78125, 0.96875)
+    #   -> expert 1.
+    # Final: RMSNorm of h after layer B, then bf16.
+    layers = _hand_layers()
+    x = np.array([[3.0, 4.0], [4.0, -3.0]])
+    hh, infos = O.moe_stack(x, layers, 1)
+    assert np.array_equal(infos[0]["xhat"], [[0.84765625, 1.1328125], [1.1328125, -0.84765625]])
+    assert infos[0]["idx"].tolist() == [[1], [0]]
+    assert np.array_equal(infos[1]["xhat"], [[1.1328125, 0.84765625], [0.96875, -1.03125]])
+    assert np.allclose(infos[1]["logits"], [[1.09765625, 1.1328125], [-0.78125, 0.96875]], rtol=0, atol=1e-15)
+    assert infos[1]["idx"].tolist() == [[1], [1]]
+    assert np.array_equal(hh, [[1.015625, 0.98828125], [0.76953125, -1.1875]])
+    # the layer outputs, from the residual stream: h_B - h_A = y_B
+    yA = np.array([[1.2466761722877542, -0.8292248229677873], [-0.5750477095118931, -0.6506645820338626]])
+    yB = np.array([[0.06898650733380712, 1.0395930595051959], [-0.9083219866646912, -0.2280482216198391]])
+    yA_o, _ = O.moe_layer(infos[0]["xhat"], layers[0], 1)
+    yB_o, _ = O.moe_layer(infos[1]["xhat"], layers[1], 1)
+    assert np.allclose(yA_o, yA, rtol=0, atol=1e-14)
+    assert np.allclose(yB_o, yB, rtol=0, atol=1e-14)
+    # without the bf16 storage rounding: every value follows the fp64 chain
+    hf, inf_f = O.moe_stack(x, layers, 1, round_bf16=False)
+    assert np.allclose(inf_f[0]["xhat"], [[0.8485281034827336, 1.1313708046436448],
+                                          [1.1313708046436448, -0.8485281034827336]], rtol=0, atol=1e-15)
+    assert np.allclose(inf_f[1]["xhat"], [[1.1331079282161627, 0.8462069963574267],
+                                          [0.9674357670102223, -1.0315366581216066]], rtol=0, atol=1e-14)
+    assert np.allclose(hf, [[1.0121513503043398, 0.9876991111323001],
+                            [0.7693474354809785, -1.1866357219127317]], rtol=0, atol=1e-14)
+
+
+def test_stack_single_layer_hand_values():
+    # the first layer alone: h = x_in + yA, then the final norm and bf16
+    # (x_in + yA = (4.24667617..., 3.17077518...), (3.42495229..., -3.65066458...);
+    # RMSNorm -> (1.13319..., 0.84610...) and (0.96761..., -1.03138...);
+    # bf16 -> 145.05/128 -> 145/128, 216.6/256 -> 217/256, 123.85/128 -> 124/128,
+    # -132.02/128 -> -132/128: the input layer B consumed in the two-layer stack)
+    hh, _ = O.moe_stack(np.array([[3.0, 4.0], [4.0, -3.0]]), _hand_layers()[:1], 1)
+    assert np.array_equal(hh, [[1.1328125, 0.84765625], [0.96875, -1.03125]])
+
+
 # ---------------------------------------------------------------------------
 # LM head confidence
 # ---------------------------------------------------------------------------
