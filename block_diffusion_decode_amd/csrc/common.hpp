@@ -81,20 +81,25 @@ __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff
 }
 
 // ---------------------------------------------------------------- cross-workgroup handoff
-// Values one workgroup publishes for another workgroup of the same kernel are
-// stored and loaded as agent-scope atomics: on this multi-XCD part they bypass
-// the per-XCD L2s (sc1), so no cache writeback/invalidate fence is needed.  A
-// wave completes its publishing stores (wait_stores) before the counter that
-// announces them is incremented.
+// One workgroup hands values to another workgroup of the same kernel (the
+// last one to finish) as follows.  The values are stored and loaded as
+// agent-scope atomics, so on this multi-XCD part they are not kept in a
+// per-XCD L2.  The publishing workgroup's waves meet at a barrier (whose
+// workgroup-scope release orders every wave's stores before it), then one
+// thread increments the workgroup counter with an agent-scope acquire-release
+// read-modify-write.  The workgroup whose increment returns the last count
+// has acquired every earlier increment, hence every value published before
+// it; a barrier then passes that on to its other waves.
 template <typename T>
 __device__ __forceinline__ void publish(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 template <typename T>
 __device__ __forceinline__ T fetch_published(const T *p) {
   return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+// Counts this workgroup as done (release of what it published, acquire of
+// what the workgroups counted before it) and returns the previous count.
 __device__ __forceinline__ int count_done(int32_t *counter) {
-  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- wave reductions

@@ -222,8 +222,8 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ 
 // multiplies them by the staged positions on MFMA, and folds the 16 x 32
 // logits into its running (max, sum, argmax).
 // With `done_count` given, the workgroup that finishes last (agent-scope
-// counter; fences make every workgroup's partials visible across XCDs) also
-// merges the partials and runs the commit, then clears the counter.  The
+// acquire-release counter over partials published as agent-scope atomics)
+// also merges the partials and runs the commit, then clears the counter.  The
 // counter must be zero when the kernel starts.
 template <class W, int NT>
 __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__restrict__ hhat,
@@ -469,12 +469,9 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   }
   if (done_count == nullptr) return;
   __shared__ int s_last;
-  // the partials come from wave 0 (T <= 32): its stores complete, then count
-  if (tid == 0) {
-    wait_stores();
-    s_last = count_done(done_count) == (int)gridDim.x - 1;
-  }
-  __syncthreads();
+  __syncthreads();   // the published partials are ordered before the count
+  if (tid == 0) s_last = count_done(done_count) == (int)gridDim.x - 1;
+  __syncthreads();   // the last workgroup's waves read after its acquire
   if (!s_last) return;
   commit_block(part_m, part_s, part_i, gridDim.x, T, threshold, tokens, conf, choice, round_info);
   if (tid == 0) publish(done_count, 0);

@@ -381,9 +381,9 @@ __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
 // ------------------------------------------------------------------ route + select
 // One workgroup of kSelThreads per position: softmax over the position's E
 // router logits and a bitonic sort of (logit desc, expert id asc), so its top-K
-// is the prefix of its sorted list.  The workgroup that finishes last (agent
-// counter, cleared by the router kernel; fences make every workgroup's rows
-// visible across XCDs) then takes the block-level steps: expert mass, coreset
+// is the prefix of its sorted list.  The workgroup that finishes last (an
+// agent-scope acquire-release counter, cleared by the router kernel, over rows
+// published as agent-scope atomics) then takes the block-level steps: expert mass, coreset
 // and re-routing (each position's first min(K, |C|) coreset members in its
 // sorted order), weights, the union of experts and each union expert's list
 // of (position, pick) assignments.  It clears the counter when done.
@@ -489,10 +489,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
       publish(r.wgt + (size_t)t * K + tid, s_p[e_sorted]);
     }
   }
-  wait_stores();     // every wave completes its row stores ...
-  __syncthreads();   // ... before the position is counted
+  __syncthreads();   // every wave's published rows are ordered before the count
   if (tid == 0) s_last = count_done(done_count) == T - 1;
-  __syncthreads();
+  __syncthreads();   // the last workgroup's waves read after its acquire
   if (!s_last) return;
 
   // ---- phase 2: the block (last workgroup)

@@ -9,7 +9,7 @@ import torch
 import block_diffusion_decode_amd as bdd
 import oracle as O
 import workloads as W
-from gpu_helpers import (BAND, TAU, assert_close, bf16_ulp, commit_check, commit_in_band, coreset_in_band,
+from gpu_helpers import (BAND, assert_close, bf16_ulp, commit_check, commit_in_band, coreset_in_band,
                          dims_of, f64, oracle_layer, top2_gap, topk_gap)
 
 pytestmark = pytest.mark.gpu
@@ -68,11 +68,22 @@ def lm_full():
     return seed, bdd.pack_lm_head(w_lm), wl
 
 
-@pytest.mark.parametrize("p", [0.5, 0.2, 0.05])
-def test_lmhead_commit_full_resolve(lm_full, p):
+# Planted logit levels (passing, failing) per threshold.  Over the 248320-token
+# vocabulary the other logits are about N(0, 1), so conf = tau at a planted
+# logit of about 12.92 + ln(tau / (1 - tau)): 15.87 for 0.95, 14.31 for 0.8,
+# 17.52 for 0.99.  The failing levels reach up to just below that point and
+# the passing ones start just above it (at 0.8 and 0.99 a level that decides
+# differently at 0.95 is drawn on purpose).
+LEVELS = {0.95: ((18.5, 20.5), (12.0, 14.0)),
+          0.8: ((14.9, 20.5), (11.0, 13.8)),
+          0.99: ((18.3, 20.5), (12.0, 16.9))}
+
+
+@pytest.mark.parametrize("p,tau", [(0.5, 0.95), (0.2, 0.95), (0.05, 0.95), (0.2, 0.8), (0.2, 0.99)])
+def test_lmhead_commit_full_resolve(lm_full, p, tau):
     seed, lm, wl = lm_full
     R = 32
-    h, _ = W.lmhead_stub_inputs(seed, C1, R, p=p)
+    h, _ = W.lmhead_stub_inputs(seed, C1, R, p=p, pass_logit=LEVELS[tau][0], fail_logit=LEVELS[tau][1])
     tok = torch.full((C1.T,), bdd.MASK, dtype=torch.int32, device=DEV)
     tok_ref = np.full(C1.T, O.MASK)
     ws = torch.empty(bdd.lmhead_workspace_bytes(C1.T, C1.H, C1.V), dtype=torch.uint8, device=DEV)
@@ -80,14 +91,14 @@ def test_lmhead_commit_full_resolve(lm_full, p):
     for r in range(R):
         hr = h[r].contiguous().to(DEV)
         prev = tok.cpu().numpy().copy()
-        conf, choice, ri = bdd.lmhead_confidence_commit(hr, lm, tok, ws=ws)
+        conf, choice, ri = bdd.lmhead_confidence_commit(hr, lm, tok, threshold=tau, ws=ws)
         torch.cuda.synchronize()
         c_ref, ch_ref, z = O.lm_head_confidence(f64(hr), wl)
         assert_close(conf.cpu().numpy(), c_ref, f"conf round {r}")
         ok = top2_gap(z) >= BAND
         assert np.array_equal(choice.cpu().numpy()[ok], ch_ref[ok])
-        assert not commit_in_band(tok_ref, c_ref), f"round {r}: stub landed in the margin band"
-        tok_ref, acc, fb, left, done = O.commit(tok_ref, c_ref, ch_ref, TAU)
+        assert not commit_in_band(tok_ref, c_ref, tau), f"round {r}: stub landed in the margin band"
+        tok_ref, acc, fb, left, done = O.commit(tok_ref, c_ref, ch_ref, tau)
         got = tok.cpu().numpy()
         assert np.array_equal(got, tok_ref), (r, got, tok_ref)
         assert ri.cpu().tolist() == [len(acc), int(fb), left, int(done)]
@@ -97,7 +108,7 @@ def test_lmhead_commit_full_resolve(lm_full, p):
         if done:
             break
     assert done
-    print(f"p={p}: resolved in {rounds} rounds with {fallbacks} fallback rounds")
+    print(f"p={p} threshold {tau}: resolved in {rounds} rounds with {fallbacks} fallback rounds")
 
 
 def test_full_round_clover_layer_plus_lm_head(lm_full):
