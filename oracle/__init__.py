@@ -15,6 +15,10 @@ written from these pages:
        MoE": "How does confidence-threshold block decoding work?" and "What
        is the MoE coreset and why does it matter?".
   [P3] 10100.com article on Clover-35B-A3B-Preview, part 01 (structure).
+  The generation loop follows [P1] 三 (block_decode: blocks after blocks,
+  stop after a block ending in EOS) and [P2] "What generation controls ship
+  by default?" (max_new_tokens is the hard limit; requests beyond 131072
+  tokens including room for the final block are rejected).
 
 Readings taken where the pages are silent (each listed in the design notes):
   * threshold test is ``conf >= threshold`` ([P1] 三 pseudocode);
@@ -33,6 +37,10 @@ Readings taken where the pages are silent (each listed in the design notes):
     the coreset is the shortest prefix of experts ranked by summed score
     whose mass reaches top_p of the total; each token then re-takes its
     top-min(K, |C|) inside the coreset and renormalises;
+  * generation stops after a block whose LAST token is EOS (the pseudocode
+    tests block[-1]); max_new_tokens cuts the returned tokens but the final
+    block is resolved whole; the history state is not modelled (the caller's
+    forward receives the prefix and may ignore it);
   * INT4 weights (the format is not on the pages): two 4-bit codes per byte,
     low nibble first, code n standing for n - 8, one bf16 scale per row and
     128-column group.
@@ -59,4 +67,7 @@ from .decode import (  # noqa: F401
     int4_dequantize,
     commit,
     resolve_block,
+    MAX_REQUEST_TOKENS,
+    request_fits,
+    generate,
 )

@@ -268,3 +268,54 @@ def resolve_block(forward, T: int, threshold: float = 0.95, max_steps: int = 32)
         if done:
             break
     return tok, rounds
+
+
+# ---------------------------------------------------------------------------
+# generation: blocks after blocks ([P1] 三 block_decode pseudocode, outer
+# loop; [P2] decoding step 6 and "What generation controls ship by default?")
+# ---------------------------------------------------------------------------
+
+MAX_REQUEST_TOKENS = 131072
+
+
+def request_fits(prompt_len: int, max_new_tokens: int, T: int,
+                 limit: int = MAX_REQUEST_TOKENS) -> bool:
+    """[P2] generation controls: a request longer than 131072 tokens,
+    counting the room needed to resolve the final block, is rejected.  The
+    final block is resolved whole, so the new tokens occupy whole blocks:
+    prompt_len + ceil(max_new_tokens / T) * T must not exceed the limit."""
+    if prompt_len < 0 or max_new_tokens < 1 or T < 1:
+        return False
+    blocks = -(-max_new_tokens // T)
+    return prompt_len + blocks * T <= limit
+
+
+def generate(forward, T: int, max_new_tokens: int, eos_token: int, prompt=(),
+             threshold: float = 0.95, max_steps: int = 32):
+    """Blocks of T positions after the prompt ([P1] 三 block_decode): each
+    block starts all MASK and is resolved by rounds (resolve_block) of
+    ``forward(block, round, tokens, prefix) -> (conf, choice)``; the resolved
+    block is appended to the prefix and to the output; generation stops after
+    a block whose last token is eos_token, or once max_new_tokens tokens have
+    been produced (the final block is still resolved whole; the output is cut
+    to max_new_tokens).  A block still masked after max_steps rounds ends the
+    generation unresolved.  Requests failing request_fits are rejected
+    (ValueError).  Returns (output tokens, per-block records, stop reason in
+    'eos', 'length', 'unresolved')."""
+    if not request_fits(len(prompt), max_new_tokens, T):
+        raise ValueError("request exceeds the token limit")
+    prefix = list(prompt)
+    out, blocks = [], []
+    while True:
+        b = len(blocks)
+        tok, rounds = resolve_block(lambda r, t: forward(b, r, t, tuple(prefix)), T, threshold, max_steps)
+        blocks.append({"tokens": tok.copy(), "rounds": len(rounds),
+                       "fallbacks": sum(int(x["fallback"]) for x in rounds)})
+        if np.any(tok == MASK):
+            return out, blocks, "unresolved"
+        out.extend(int(v) for v in tok)
+        prefix.extend(int(v) for v in tok)
+        if tok[-1] == eos_token:
+            return out[:max_new_tokens], blocks, "eos"
+        if len(out) >= max_new_tokens:
+            return out[:max_new_tokens], blocks, "length"

@@ -712,3 +712,91 @@ def test_int4_lm_head_zero_codes_give_uniform_confidence():
     h = np.random.default_rng(1).standard_normal((3, H))
     conf, choice, _ = O.lm_head_confidence(h, w)
     assert np.allclose(conf, 1.0 / V, rtol=0, atol=1e-15) and (choice == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# generation: blocks after blocks (aitujian.cn 三 block_decode; goremy.ai
+# decoding step 6 and "What generation controls ship by default?")
+# ---------------------------------------------------------------------------
+
+def _scripted(script):
+    """forward(block, round, tokens, prefix) from a table
+    {(block, round): (conf list, choice list)}; records what it was given."""
+    seen = []
+
+    def forward(b, r, tok, prefix):
+        seen.append((b, r, tuple(int(v) for v in tok), prefix))
+        c, ch = script[(b, r)]
+        return np.array(c, np.float64), np.array(ch)
+    return forward, seen
+
+
+def test_generate_stops_after_a_block_ending_in_eos_only():
+    EOS = 7
+    script = {
+        # block 0: EOS at position 1 (not last): generation goes on
+        (0, 0): ([0.99, 0.99, 0.99, 0.99], [5, 7, 9, 11]),
+        # block 1: two rounds (positions 0, 3 pass; then a fallback on 2, then 1)
+        (1, 0): ([0.97, 0.5, 0.6, 0.96], [1, 2, 3, 7]),
+        (1, 1): ([0.1, 0.3, 0.8, 0.2], [0, 2, 3, 0]),
+        (1, 2): ([0.0, 0.2, 0.0, 0.0], [0, 2, 0, 0]),
+        # block 2 must never run
+    }
+    fwd, seen = _scripted(script)
+    out, blocks, stop = O.generate(fwd, 4, 100, EOS, prompt=(40, 41))
+    assert stop == "eos"
+    assert out == [5, 7, 9, 11, 1, 2, 3, 7]
+    assert [b["rounds"] for b in blocks] == [1, 3]
+    assert [b["fallbacks"] for b in blocks] == [0, 2]
+    # the prefix grows by whole resolved blocks; each round of a block sees
+    # that block's own tokens so far
+    assert [s[3] for s in seen] == [(40, 41), (40, 41, 5, 7, 9, 11), (40, 41, 5, 7, 9, 11),
+                                    (40, 41, 5, 7, 9, 11)]
+    assert [s[2] for s in seen[1:]] == [(-1, -1, -1, -1), (1, -1, -1, 7), (1, -1, 3, 7)]
+
+
+def test_generate_max_new_tokens_cuts_but_resolves_the_final_block():
+    script = {(0, 0): ([0.99] * 4, [1, 2, 3, 4]),
+              (1, 0): ([0.99, 0.2, 0.99, 0.3], [5, 6, 7, 8]),
+              (1, 1): ([0.0, 0.99, 0.0, 0.99], [0, 6, 0, 8])}
+    fwd, seen = _scripted(script)
+    out, blocks, stop = O.generate(fwd, 4, 6, eos_token=99)
+    assert stop == "length" and out == [1, 2, 3, 4, 5, 6]
+    assert blocks[1]["tokens"].tolist() == [5, 6, 7, 8] and blocks[1]["rounds"] == 2
+    # exactly a multiple of the block: no extra block
+    fwd, seen = _scripted(script)
+    out, blocks, stop = O.generate(fwd, 4, 4, eos_token=99)
+    assert stop == "length" and out == [1, 2, 3, 4] and len(blocks) == 1
+
+
+def test_generate_unresolved_block_after_max_steps():
+    script = {(0, 0): ([0.99] * 3, [1, 2, 3]),
+              (1, 0): ([0.5, 0.4, 0.3], [4, 5, 6]),
+              (1, 1): ([0.0, 0.4, 0.3], [4, 5, 6])}
+    fwd, _ = _scripted(script)
+    out, blocks, stop = O.generate(fwd, 3, 9, eos_token=99, max_steps=2)
+    assert stop == "unresolved" and out == [1, 2, 3]
+    assert blocks[1]["tokens"].tolist() == [4, 5, -1] and blocks[1]["rounds"] == 2
+
+
+def test_generate_threshold_decides_the_commits():
+    script = {(0, 0): ([0.85, 0.97, 0.5], [1, 2, 3]),
+              (0, 1): ([0.0, 0.0, 0.9], [1, 2, 3]),
+              (0, 2): ([0.0, 0.0, 0.9], [1, 2, 3])}
+    fwd, _ = _scripted(script)
+    _, blocks, _ = O.generate(fwd, 3, 3, eos_token=99, threshold=0.8)
+    assert blocks[0]["rounds"] == 2 and blocks[0]["fallbacks"] == 0
+    fwd, _ = _scripted(script)
+    _, blocks, _ = O.generate(fwd, 3, 3, eos_token=99, threshold=0.95)
+    assert blocks[0]["rounds"] == 3 and blocks[0]["fallbacks"] == 2
+
+
+def test_request_bound_counts_the_whole_final_block():
+    # 131072 tokens including room to resolve the final block
+    assert O.request_fits(131072 - 32, 32, 32) and O.request_fits(131072 - 32, 1, 32)
+    assert not O.request_fits(131072 - 31, 1, 32)      # the final block needs 32 positions
+    assert not O.request_fits(131040, 33, 32)          # 33 new tokens take two blocks
+    assert O.request_fits(0, 131072, 32) and not O.request_fits(1, 131072, 32)
+    assert O.request_fits(131068, 4, 4) and not O.request_fits(131068, 5, 4)
+    with pytest.raises(ValueError):
+        O.generate(lambda *a: None, 4, 5, 0, prompt=range(131068))
