@@ -57,7 +57,11 @@ EXPORTS = [
     "bdd_lmhead_pack_int4",
     "bdd_round_graph_create", "bdd_round_graph_launch", "bdd_round_graph_destroy",
     "bdd_generate_fits", "bdd_generate_workspace_bytes", "bdd_generate",
+    "bdd_block_denoise_round_noalloc",
 ]
+
+# Scratch bytes of bdd_block_denoise_round_noalloc (BDD_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -88,6 +92,9 @@ def lib() -> ctypes.CDLL:
     L.bdd_block_denoise_round.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp, sz, vp]
     L.bdd_block_denoise_round.restype = i32
+    L.bdd_block_denoise_round_noalloc.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, vp, vp, vp, vp, vp,
+                                                  vp, vp, vp, vp, vp]
+    L.bdd_block_denoise_round_noalloc.restype = i32
     L.bdd_status_string.argtypes = [i32]
     L.bdd_status_string.restype = ctypes.c_char_p
     L.bdd_last_error.argtypes = []
@@ -400,6 +407,30 @@ class RoundPlan:
             self.threshold, _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info),
             _ptr(layer_topk_idx), _ptr(layer_n_distinct), _ptr(layer_xhat), _ptr(hhat_out), _ptr(self.ws),
             self.ws.numel(), _stream(stream)))
+
+
+def block_denoise_round_noalloc(plan: "RoundPlan", x_in, tokens, conf, choice, round_info,
+                                layer_topk_idx=None, layer_n_distinct=None, hhat_out=None, stream=None):
+    """The round of ``plan`` through bdd_block_denoise_round_noalloc: the
+    library's static per-GPU scratch instead of the plan's workspace (no
+    device allocation in the call).  Same outputs as plan(...)."""
+    d = plan.d
+    _need(x_in, "x_in", torch.float32, (d.T, d.H), plan.dev)
+    _need(tokens, "tokens", torch.int32, (d.T,), plan.dev)
+    _need(conf, "conf", torch.float32, (d.T,), plan.dev)
+    _need(choice, "choice", torch.int32, (d.T,), plan.dev)
+    _need(round_info, "round_info", torch.int32, (4,), plan.dev)
+    L = len(plan.layers)
+    if layer_topk_idx is not None:
+        _need(layer_topk_idx, "layer_topk_idx", torch.int32, (L, d.T, d.K), plan.dev)
+    if layer_n_distinct is not None:
+        _need(layer_n_distinct, "layer_n_distinct", torch.int32, (L,), plan.dev)
+    if hhat_out is not None:
+        _need(hhat_out, "hhat_out", d.torch_dtype, (d.T, d.H), plan.dev)
+    _check(lib().bdd_block_denoise_round_noalloc(
+        ctypes.byref(plan.c_dims), L, plan.c_layers, plan.top_p, _ptr(plan.lm.packed), plan.V, plan.threshold,
+        _ptr(x_in), _ptr(tokens), _ptr(conf), _ptr(choice), _ptr(round_info), _ptr(layer_topk_idx),
+        _ptr(layer_n_distinct), None, _ptr(hhat_out), _stream(stream)))
 
 
 def generate_fits(prompt_len: int, max_new_tokens: int, block_size: int) -> bool:

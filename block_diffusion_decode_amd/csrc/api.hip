@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -402,13 +403,17 @@ size_t bdd_round_workspace_bytes(const bdd_moe_dims *d, int32_t V) {
   return l.end;
 }
 
-bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
-                                   const bdd_moe_weights *layers, float coreset_top_p,
-                                   const void *w_lm, int32_t V, float threshold, const float *x_in,
-                                   int32_t *tokens, float *conf, int32_t *choice, int32_t *round_info,
-                                   int32_t *layer_topk_idx, int32_t *layer_n_distinct,
-                                   void *layer_xhat_out, void *hhat_out, void *ws, size_t ws_bytes,
-                                   void *stream) {
+}  // extern "C"
+
+namespace {
+
+// One round (the body of bdd_block_denoise_round and of its no-allocation
+// variant): host checks first, then the launches on `stream`.
+bdd_status round_impl(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_weights *layers,
+                      float coreset_top_p, const void *w_lm, int32_t V, float threshold, const float *x_in,
+                      int32_t *tokens, float *conf, int32_t *choice, int32_t *round_info, int32_t *layer_topk_idx,
+                      int32_t *layer_n_distinct, void *layer_xhat_out, void *hhat_out, void *ws, size_t ws_bytes,
+                      void *stream) {
   bdd_status st = check_dims(d);
   if (st != BDD_OK) return st;
   if (n_layers < 0) return fail(BDD_ERR_INVALID_ARG, "n_layers=%d", n_layers);
@@ -456,6 +461,70 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
   const LmCommit fused = {count, threshold, tokens, conf, choice, round_info};
   LAUNCH("lmhead", s, launch_lmhead(d->wdtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, &fused, s));
   return BDD_OK;
+}
+
+// ----------------------------------------------------------------- no-allocation round
+// Scratch of bdd_block_denoise_round_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is kept here.
+static __device__ __align__(256) unsigned char scratch[BDD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+bdd_status scratch_address(void **out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BDD_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return fail(BDD_ERR_HIP, "hipGetSymbolAddress returned no address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BDD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
+                                   const bdd_moe_weights *layers, float coreset_top_p,
+                                   const void *w_lm, int32_t V, float threshold, const float *x_in,
+                                   int32_t *tokens, float *conf, int32_t *choice, int32_t *round_info,
+                                   int32_t *layer_topk_idx, int32_t *layer_n_distinct,
+                                   void *layer_xhat_out, void *hhat_out, void *ws, size_t ws_bytes,
+                                   void *stream) {
+  return round_impl(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x_in, tokens, conf, choice, round_info,
+                    layer_topk_idx, layer_n_distinct, layer_xhat_out, hhat_out, ws, ws_bytes, stream);
+}
+
+bdd_status bdd_block_denoise_round_noalloc(const bdd_moe_dims *d, int32_t n_layers,
+                                           const bdd_moe_weights *layers, float coreset_top_p,
+                                           const void *w_lm, int32_t V, float threshold, const float *x_in,
+                                           int32_t *tokens, float *conf, int32_t *choice,
+                                           int32_t *round_info, int32_t *layer_topk_idx,
+                                           int32_t *layer_n_distinct, void *layer_xhat_out, void *hhat_out,
+                                           void *stream) {
+  const size_t need = bdd_round_workspace_bytes(d, V);
+  if (need == 0)   // invalid dims or V: the round's own checks name the problem
+    return round_impl(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x_in, tokens, conf, choice,
+                      round_info, layer_topk_idx, layer_n_distinct, layer_xhat_out, hhat_out, nullptr, 0, stream);
+  if (need > (size_t)BDD_NOALLOC_SCRATCH_BYTES)
+    return fail(BDD_ERR_UNSUPPORTED, "these dims need %zu bytes of scratch; the static scratch holds %zu", need,
+                (size_t)BDD_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  const bdd_status st = scratch_address(&ws);
+  if (st != BDD_OK) return st;
+  return round_impl(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x_in, tokens, conf, choice, round_info,
+                    layer_topk_idx, layer_n_distinct, layer_xhat_out, hhat_out, ws, BDD_NOALLOC_SCRATCH_BYTES,
+                    stream);
 }
 
 // ----------------------------------------------------------------- generation

@@ -227,6 +227,26 @@ bdd_status bdd_block_denoise_round(const bdd_moe_dims *d, int32_t n_layers,
                                    void *layer_xhat_out, void *hhat_out, void *ws,
                                    size_t ws_bytes, void *stream);
 
+/* The same round for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * arguments and results as bdd_block_denoise_round, without a workspace.
+ * The scratch is a static device array of BDD_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, one per GPU, held until the process ends; the call
+ * allocates nothing (no hipMalloc, no hipFree).  Dims whose
+ * bdd_round_workspace_bytes exceed it are rejected with BDD_ERR_UNSUPPORTED
+ * before anything is enqueued.  Every call on a GPU shares that GPU's
+ * scratch and leaves its contents behind (the round's kernels clear the
+ * counters they need): calls that overlap on one GPU (on different streams
+ * or from different threads) race and must not be issued. */
+#define BDD_NOALLOC_SCRATCH_BYTES (32u << 20)
+bdd_status bdd_block_denoise_round_noalloc(const bdd_moe_dims *d, int32_t n_layers,
+                                           const bdd_moe_weights *layers, float coreset_top_p,
+                                           const void *w_packed, int32_t V, float threshold,
+                                           const float *x_in, int32_t *tokens, float *conf,
+                                           int32_t *choice, int32_t *round_info,
+                                           int32_t *layer_topk_idx, int32_t *layer_n_distinct,
+                                           void *layer_xhat_out, void *hhat_out, void *stream);
+
 /* One denoising round captured as a HIP graph, for callers that replay the
  * same round structure many times (a decode loop): the arguments are those of
  * bdd_block_denoise_round, bound at creation (device pointers, sizes and

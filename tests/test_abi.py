@@ -155,3 +155,21 @@ def test_generate_rejects_on_the_host():
     st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, 0, 65, 0, None, 2,
                         None, rounds, result, None, 0, None)
     assert st == -1   # three blocks needed, two given
+
+
+def test_noalloc_round_rejects_dims_beyond_its_scratch():
+    # checked on the host before any device call: dims whose round workspace
+    # exceeds the static scratch are refused, invalid dims get the round's error
+    L = bdd.lib()
+    p = ctypes.c_void_p(1)
+    w = bdd._Weights(1, None, 1, 1, 1, 1)
+    args = lambda d, V: (ctypes.byref(d.c()), 1, ctypes.byref(w), 1.0, p, V, 0.95, p, p, p, p, p,
+                         None, None, None, None, None)
+    big = bdd.MoEDims(32, 8192, 256, 8, 8192, 8192, bdd.BDD_F32)
+    assert bdd.round_workspace_bytes(big, 1000) > bdd.NOALLOC_SCRATCH_BYTES
+    assert L.bdd_block_denoise_round_noalloc(*args(big, 1000)) == -2
+    assert b"static scratch" in L.bdd_last_error()
+    bad = bdd.MoEDims(33, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    assert L.bdd_block_denoise_round_noalloc(*args(bad, 1000)) == -2
+    clover = bdd.MoEDims(32, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    assert 0 < bdd.round_workspace_bytes(clover, 248320) <= bdd.NOALLOC_SCRATCH_BYTES
