@@ -118,8 +118,9 @@ def lib() -> ctypes.CDLL:
     L.bdd_generate_fits.restype = i32
     L.bdd_generate_workspace_bytes.argtypes = [dims_p, i32]
     L.bdd_generate_workspace_bytes.restype = sz
-    L.bdd_generate.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, i32, i32, i32, i32, vp, i32, vp,
-                               ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), vp, sz, vp]
+    L.bdd_generate.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, i32, i32, i32, i32, i32, vp, i32, vp,
+                               ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                               ctypes.POINTER(ctypes.c_int32), vp, sz, vp]
     L.bdd_generate.restype = i32
     L.bdd_timing_enable.argtypes = [i32, ctypes.c_char_p]
     L.bdd_timing_enable.restype = i32
@@ -439,11 +440,14 @@ def generate_fits(prompt_len: int, max_new_tokens: int, block_size: int) -> bool
 
 
 def generate(plan: "RoundPlan", x_rounds: torch.Tensor, max_new_tokens: int, max_steps: int,
-             eos_token: int, prompt_len: int = 0, out_tokens: torch.Tensor | None = None, stream=None):
+             eos_token: int, prompt_len: int = 0, out_tokens: torch.Tensor | None = None, stream=None,
+             rounds_per_read: int = 0, with_fallbacks: bool = False):
     """Multi-block generation (bdd_generate) with the plan's layers, LM head,
     coreset and threshold.  x_rounds [n_blocks][max_steps][T][H] fp32 on the
-    device.  Returns (tokens int32 [n_blocks][T], block_rounds list,
-    n_returned, stop) where stop is "eos", "length" or "unresolved"."""
+    device.  rounds_per_read 0: one host read per block.  Returns (tokens
+    int32 [n_blocks][T], block_rounds list, n_returned, stop) where stop is
+    "eos", "length" or "unresolved"; with_fallbacks adds the per-block
+    fallback counts as a fifth element."""
     d = plan.d
     if x_rounds.dim() != 4 or x_rounds.shape[1] != max_steps or tuple(x_rounds.shape[2:]) != (d.T, d.H):
         raise ValueError(f"x_rounds must be [n_blocks][{max_steps}][{d.T}][{d.H}]")
@@ -456,15 +460,18 @@ def generate(plan: "RoundPlan", x_rounds: torch.Tensor, max_new_tokens: int, max
     if getattr(plan, "gen_ws", None) is None or plan.gen_ws.numel() < wsb:
         plan.gen_ws = _workspace(wsb, plan.dev, None)
     rounds = (ctypes.c_int32 * nb)()
+    fallbacks = (ctypes.c_int32 * nb)()
     result = (ctypes.c_int32 * 3)()
     st = lib().bdd_generate(ctypes.byref(plan.c_dims), len(plan.layers), plan.c_layers, plan.top_p,
-                            _ptr(plan.lm.packed), plan.V, plan.threshold, max_steps, prompt_len, max_new_tokens,
-                            eos_token, _ptr(x_rounds), nb, _ptr(out_tokens), rounds, result, _ptr(plan.gen_ws),
-                            plan.gen_ws.numel(), _stream(stream))
+                            _ptr(plan.lm.packed), plan.V, plan.threshold, max_steps, rounds_per_read, prompt_len,
+                            max_new_tokens, eos_token, _ptr(x_rounds), nb, _ptr(out_tokens), rounds, fallbacks,
+                            result, _ptr(plan.gen_ws), plan.gen_ws.numel(), _stream(stream))
     if st not in (0, BDD_UNRESOLVED):
         _check(st)
     stop = "unresolved" if st == BDD_UNRESOLVED else ("eos" if result[2] == 1 else "length")
-    return out_tokens, [int(rounds[i]) for i in range(int(result[1]))], int(result[0]), stop
+    n = int(result[1])
+    out = (out_tokens, [int(rounds[i]) for i in range(n)], int(result[0]), stop)
+    return out + ([int(fallbacks[i]) for i in range(n)],) if with_fallbacks else out
 
 
 class RoundGraph:

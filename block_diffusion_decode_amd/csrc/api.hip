@@ -209,6 +209,7 @@ RouteBufs route_bufs(void *ws, const MoePlan &p) {
   r.mass = at<float>(ws, p.mass);
   r.n_distinct_out = nullptr;
   r.coreset_size_out = nullptr;
+  r.gate = nullptr;
   return r;
 }
 
@@ -226,8 +227,8 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
   float *A = at<float>(ws, p.A), *P = at<float>(ws, p.P);
   void *xpk = at<void>(ws, p.xpk), *act = at<void>(ws, p.act);
   int32_t *sel_count = at<int32_t>(ws, p.sel_count);
-  if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, xpk, T, H, lm_count, s));
-  LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, r.logits, T, H, E, s));
+  if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, xpk, T, H, lm_count, r.gate, s));
+  LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, r.logits, T, H, E, r.gate, s));
   LAUNCH("route_select", s, launch_route_select(r, w.router_bias, T, H, E, K, top_p, at<int32_t>(ws, p.sorted),
                                                 sel_count, d.wdtype, xpk, w.ws_gate_up, act, Is, s));
   int g1 = expert_items_max(T, H, E, K, I, Is, true), g2 = expert_items_max(T, H, E, K, I, Is, false);
@@ -238,7 +239,7 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
   LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, act, w.w_down, w.ws_down, r, P, T, H, K, I, Is, Imax,
                                               g2, s));
   LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P + (size_t)T * K * H : nullptr, r.idx, r.wgt, h,
-                                      y_out, xhat_next, xpk_next ? xpk : nullptr, T, H, K, s));
+                                      y_out, xhat_next, xpk_next ? xpk : nullptr, T, H, K, r.gate, s));
   return BDD_OK;
 }
 
@@ -409,11 +410,13 @@ namespace {
 
 // One round (the body of bdd_block_denoise_round and of its no-allocation
 // variant): host checks first, then the launches on `stream`.
+// With `gate` given, every kernel of the round returns at entry while *gate
+// is set, and the commit sets *resolved_flag when it resolves the block.
 bdd_status round_impl(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_weights *layers,
                       float coreset_top_p, const void *w_lm, int32_t V, float threshold, const float *x_in,
                       int32_t *tokens, float *conf, int32_t *choice, int32_t *round_info, int32_t *layer_topk_idx,
                       int32_t *layer_n_distinct, void *layer_xhat_out, void *hhat_out, void *ws, size_t ws_bytes,
-                      void *stream) {
+                      void *stream, const int32_t *gate = nullptr, int32_t *resolved_flag = nullptr) {
   bdd_status st = check_dims(d);
   if (st != BDD_OK) return st;
   if (n_layers < 0) return fail(BDD_ERR_INVALID_ARG, "n_layers=%d", n_layers);
@@ -437,7 +440,7 @@ bdd_status round_impl(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_wei
   int32_t *count = at<int32_t>(ws, lp.count);
   if (n_layers == 0) {
     // the LM head reads RMSNorm(x_in); the norm kernel clears the counter
-    LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, hhat, nullptr, T, H, count, s));
+    LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, hhat, nullptr, T, H, count, gate, s));
   }
   // layer l's normalised input: the caller's buffer slot, else the workspace
   const size_t xbytes = (size_t)T * H * esize(d->wdtype);
@@ -446,6 +449,7 @@ bdd_status round_impl(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_wei
   };
   for (int l = 0; l < n_layers; ++l) {
     RouteBufs r = route_bufs(ws, p);
+    r.gate = gate;
     if (layer_topk_idx) r.idx = layer_topk_idx + (size_t)l * T * K;
     if (layer_n_distinct) r.n_distinct_out = layer_n_distinct + l;
     void *next = l + 1 == n_layers ? hhat : xin(l + 1);
@@ -458,7 +462,7 @@ bdd_status round_impl(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_wei
   const int grid = lmhead_grid(cus, V) < kMaxLmGrid ? lmhead_grid(cus, V) : kMaxLmGrid;
   float *pm = at<float>(ws, lp.m), *ps = at<float>(ws, lp.s);
   int32_t *pi = at<int32_t>(ws, lp.i);
-  const LmCommit fused = {count, threshold, tokens, conf, choice, round_info};
+  const LmCommit fused = {count, threshold, tokens, conf, choice, round_info, gate, resolved_flag};
   LAUNCH("lmhead", s, launch_lmhead(d->wdtype, hhat, w_lm, T, H, V, pm, ps, pi, grid, &fused, s));
   return BDD_OK;
 }
@@ -541,15 +545,17 @@ int32_t bdd_generate_fits(int32_t prompt_len, int32_t max_new_tokens, int32_t bl
 size_t bdd_generate_workspace_bytes(const bdd_moe_dims *d, int32_t V) {
   const size_t r = bdd_round_workspace_bytes(d, V);
   if (r == 0) return 0;
-  // conf [T] f32, choice [T] i32, round_info [4] i32 after the round's workspace
-  return a256(r) + a256((size_t)d->T * 8 + 16);
+  // after the round's workspace: conf [T] f32 and choice [T] i32, one
+  // round_info slot [4] i32 per round of a block (at most kMaxT rounds), the
+  // block's resolved flag
+  return a256(r) + a256((size_t)d->T * 8) + a256((size_t)kMaxT * 16) + 256;
 }
 
 bdd_status bdd_generate(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_weights *layers,
                         float coreset_top_p, const void *w_lm, int32_t V, float threshold, int32_t max_steps,
-                        int32_t prompt_len, int32_t max_new_tokens, int32_t eos_token, const float *x_rounds,
-                        int32_t n_blocks, int32_t *out_tokens, int32_t *block_rounds, int32_t *result, void *ws,
-                        size_t ws_bytes, void *stream) {
+                        int32_t rounds_per_read, int32_t prompt_len, int32_t max_new_tokens, int32_t eos_token,
+                        const float *x_rounds, int32_t n_blocks, int32_t *out_tokens, int32_t *block_rounds,
+                        int32_t *block_fallbacks, int32_t *result, void *ws, size_t ws_bytes, void *stream) {
   bdd_status st = check_dims(d);
   if (st != BDD_OK) return st;
   if (!bdd_generate_fits(prompt_len, max_new_tokens, d->T))
@@ -557,6 +563,7 @@ bdd_status bdd_generate(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_w
                 "request of %d prompt tokens + %d new tokens (whole blocks of %d) exceeds %lld tokens", prompt_len,
                 max_new_tokens, d->T, kMaxRequestTokens);
   if (max_steps < 1) return fail(BDD_ERR_INVALID_ARG, "max_steps=%d", max_steps);
+  if (rounds_per_read < 0) return fail(BDD_ERR_INVALID_ARG, "rounds_per_read=%d", rounds_per_read);
   const int T = d->T, H = d->H;
   const int need_blocks = (max_new_tokens + T - 1) / T;
   if (n_blocks < need_blocks)
@@ -570,34 +577,49 @@ bdd_status bdd_generate(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_w
   char *tail = static_cast<char *>(ws) + a256(r_bytes);
   float *conf = reinterpret_cast<float *>(tail);
   int32_t *choice = reinterpret_cast<int32_t *>(tail + (size_t)T * 4);
-  int32_t *info = reinterpret_cast<int32_t *>(tail + (size_t)T * 8);
+  int32_t *slots = reinterpret_cast<int32_t *>(tail + a256((size_t)T * 8));
+  int32_t *flag = reinterpret_cast<int32_t *>(tail + a256((size_t)T * 8) + a256((size_t)kMaxT * 16));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Every round commits at least one masked position, so a block resolves
+  // within T rounds: at most min(max_steps, T) rounds are enqueued.  They are
+  // enqueued back to back, each gated on the block's resolved flag (rounds
+  // after the resolving one return at once), and the host reads the rounds'
+  // info once per block (or once per rounds_per_read rounds).
+  const int R = max_steps < T ? max_steps : T;
+  const int per_read = rounds_per_read > 0 ? rounds_per_read : R;
   result[0] = result[1] = result[2] = 0;
   int produced = 0;
   for (int b = 0; b < need_blocks; ++b) {
     int32_t *tok = out_tokens + (size_t)b * T;
-    HIP_TRY(hipMemsetAsync(tok, 0xff, (size_t)T * 4, s));   // every position MASK (-1)
-    int32_t ri[4] = {0, 0, 0, 0};
-    int rounds = 0;
-    for (int r = 0; r < max_steps; ++r) {
-      const float *x = x_rounds + ((size_t)b * max_steps + r) * T * H;
-      if ((st = bdd_block_denoise_round(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x, tok, conf,
-                                        choice, info, nullptr, nullptr, nullptr, nullptr, ws, r_bytes, stream)) !=
-          BDD_OK)
-        return st;
-      HIP_TRY(hipMemcpyAsync(ri, info, sizeof(ri), hipMemcpyDeviceToHost, s));
+    LAUNCH("block_start", s, launch_block_start(tok, T, slots, 4 * R, flag, s));
+    int32_t info[kMaxT][4];
+    int32_t last = 0;
+    int rounds = 0, fallbacks = 0;
+    bool resolved = false;
+    for (int r0 = 0; r0 < R && !resolved; r0 += per_read) {
+      const int r1 = r0 + per_read < R ? r0 + per_read : R;
+      for (int r = r0; r < r1; ++r) {
+        const float *x = x_rounds + ((size_t)b * max_steps + r) * T * H;
+        if ((st = round_impl(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x, tok, conf, choice,
+                             slots + 4 * r, nullptr, nullptr, nullptr, nullptr, ws, r_bytes, stream, flag, flag)) !=
+            BDD_OK)
+          return st;
+      }
+      HIP_TRY(hipMemcpyAsync(info[0], slots, (size_t)r1 * 16, hipMemcpyDeviceToHost, s));
+      HIP_TRY(hipMemcpyAsync(&last, tok + T - 1, 4, hipMemcpyDeviceToHost, s));
       HIP_TRY(hipStreamSynchronize(s));
-      ++rounds;
-      if (ri[3]) break;
+      for (int r = r0; r < r1 && !resolved; ++r) {
+        rounds = r + 1;
+        fallbacks += info[r][1];
+        resolved = info[r][3] != 0;
+      }
     }
     block_rounds[b] = rounds;
-    produced += T;
+    if (block_fallbacks) block_fallbacks[b] = fallbacks;
     result[1] = b + 1;
+    if (!resolved) return fail(BDD_UNRESOLVED, "block %d still has masked positions after %d rounds", b, R);
+    produced += T;
     result[0] = produced < max_new_tokens ? produced : max_new_tokens;
-    if (!ri[3]) return fail(BDD_UNRESOLVED, "block %d still has masked positions after %d rounds", b, max_steps);
-    int32_t last = 0;
-    HIP_TRY(hipMemcpyAsync(&last, tok + T - 1, 4, hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
     if (last == eos_token) {
       result[2] = 1;
       return BDD_OK;

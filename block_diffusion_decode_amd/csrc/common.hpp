@@ -102,6 +102,15 @@ __device__ __forceinline__ int count_done(int32_t *counter) {
   return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------- block-resident rounds
+// A block's rounds can all be enqueued at once: each kernel of a round takes
+// the block's resolved flag as its gate (null: always run) and returns at
+// entry once the commit of an earlier round has set it.  The flag was written
+// by an earlier kernel on the same stream, so a plain load sees it.
+__device__ __forceinline__ bool gated_off(const int32_t *gate) {
+  return gate != nullptr && __builtin_amdgcn_readfirstlane(*gate) != 0;
+}
+
 // ---------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -307,6 +307,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
     const typename W::T *__restrict__ wgu, RouteBufs r, float *__restrict__ A, char *__restrict__ act, int T,
     int H, int I, int Imax) {
   typedef typename W::T WT;
+  if (gated_off(r.gate)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tiles = I / 16;
   const int d_items = uniform(r.meta[3]) * tiles;
@@ -491,6 +492,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
                                                           RouteBufs r, float *__restrict__ P, int T,
                                                           int H, int K, int I, int Is, int Imax) {
   typedef typename W::T WT;
+  if (gated_off(r.gate)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int DR = 16 * kDenseRowTiles;   // rows per dense item
   const int tiles = H / (4 * kDownRowsPerWave), dtiles = H / DR;

@@ -22,6 +22,7 @@ struct RouteBufs {
   float *mass;         // [E]      block expert mass
   int32_t *n_distinct_out;    // [1] union size copy (may be null)
   int32_t *coreset_size_out;  // [1] coreset size copy (may be null)
+  const int32_t *gate;        // block resolved flag (may be null): the layer's kernels return when set
 };
 
 // Upper bound of the routed token groups (kTokGroup positions of one expert)
@@ -43,13 +44,13 @@ inline int expert_dense_max(int T, int E, int K) {
 // RMSNorm rows of `in` [T][H] into `out` (stored as wdtype); optionally copies
 // `in` to `copy_out` and clears `zero_word`.
 hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, void *xpk, int T, int H,
-                          int32_t *zero_word, hipStream_t s);
+                          int32_t *zero_word, const int32_t *gate, hipStream_t s);
 
 // Router logits from the normalised block, as partial sums over hidden slices
 // (part [router_slices(H)][T][E]); clears zero_word.
 int router_slices(int H);
 hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const void *w_router,
-                         float *part, int T, int H, int E, hipStream_t s);
+                         float *part, int T, int H, int E, const int32_t *gate, hipStream_t s);
 
 // Selection: one workgroup per position (logits = slices summed in order +
 // bias), then the block-level steps in the last one; workgroups past the
@@ -81,7 +82,7 @@ hipError_t launch_expert_down(int wdtype, const float *A, const void *act, const
 // packed into xpk_out when given).
 hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const int32_t *idx,
                           const float *wgt, float *h, float *y_out, void *xhat_out, void *xpk_out, int T, int H,
-                          int K, hipStream_t s);
+                          int K, const int32_t *gate, hipStream_t s);
 
 // LM head online softmax: per (position, workgroup) partial (max, sum, argmax),
 // stored [T][grid].
@@ -100,10 +101,15 @@ struct LmCommit {
   float *conf;
   int32_t *choice;
   int32_t *round_info;
+  const int32_t *gate;      // block resolved flag (may be null): the head returns at entry when set
+  int32_t *resolved_flag;   // set to 1 when the commit resolves the block (may be null)
 };
 hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm_packed, int T, int H, int V,
                          float *part_m, float *part_s, int32_t *part_i, int grid, const LmCommit *fused,
                          hipStream_t s);
+
+// Start of a block-resident block: tokens [T] = MASK, info [words] = 0, *flag = 0.
+hipError_t launch_block_start(int32_t *tokens, int T, int32_t *info, int words, int32_t *flag, hipStream_t s);
 
 hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,
                          int nparts, int T, float threshold, int32_t *tokens, float *conf,

@@ -123,7 +123,8 @@ constexpr int kCommitBatch = 8;
 __device__ void commit_block(const float *__restrict__ part_m, const float *__restrict__ part_s,
                              const int32_t *__restrict__ part_i, int nparts, int T, float threshold,
                              int32_t *__restrict__ tokens, float *__restrict__ conf,
-                             int32_t *__restrict__ choice, int32_t *__restrict__ round_info) {
+                             int32_t *__restrict__ choice, int32_t *__restrict__ round_info,
+                             int32_t *__restrict__ resolved_flag) {
   __shared__ float s_conf[kMaxT];
   __shared__ int s_choice[kMaxT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
@@ -198,6 +199,7 @@ __device__ void commit_block(const float *__restrict__ part_m, const float *__re
       round_info[1] = fallback;
       round_info[2] = left;
       round_info[3] = left == 0 ? 1 : 0;
+      if (resolved_flag && left == 0) *resolved_flag = 1;
     }
   }
 }
@@ -210,7 +212,18 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ 
                                                       float *__restrict__ conf,
                                                       int32_t *__restrict__ choice,
                                                       int32_t *__restrict__ round_info) {
-  commit_block(part_m, part_s, part_i, nparts, T, threshold, tokens, conf, choice, round_info);
+  commit_block(part_m, part_s, part_i, nparts, T, threshold, tokens, conf, choice, round_info, nullptr);
+}
+
+// Start of a block whose rounds are all enqueued at once: every position
+// MASK, the per-round info slots cleared, the resolved flag (the rounds'
+// gate) cleared.  A kernel rather than memsets, so it can sit in a graph.
+__global__ __launch_bounds__(256) void block_start_kernel(int32_t *__restrict__ tokens, int T,
+                                                          int32_t *__restrict__ info, int words,
+                                                          int32_t *__restrict__ flag) {
+  for (int i = threadIdx.x; i < T; i += blockDim.x) tokens[i] = -1;
+  for (int i = threadIdx.x; i < words; i += blockDim.x) info[i] = 0;
+  if (threadIdx.x == 0) *flag = 0;
 }
 
 // One workgroup (16 waves) per CU.  The block's normalised hidden states are
@@ -236,7 +249,9 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
                                                       int32_t *__restrict__ tokens,
                                                       float *__restrict__ conf,
                                                       int32_t *__restrict__ choice,
-                                                      int32_t *__restrict__ round_info) {
+                                                      int32_t *__restrict__ round_info,
+                                                      const int32_t *__restrict__ gate,
+                                                      int32_t *__restrict__ resolved_flag) {
   extern __shared__ uint4 xs[];  // [H / kChunk][16 * NT]
   __shared__ float sm[kLmWaves][kMaxT], ssum[kLmWaves][kMaxT];
   __shared__ int si[kLmWaves][kMaxT];
@@ -245,6 +260,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NC = H / CH;
   const int li = lane & 15, g = lane >> 4;
+  if (gated_off(gate)) return;
   float m[NT], s[NT];
   int am[NT];
 #pragma unroll
@@ -473,7 +489,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   if (tid == 0) s_last = count_done(done_count) == (int)gridDim.x - 1;
   __syncthreads();   // the last workgroup's waves read after its acquire
   if (!s_last) return;
-  commit_block(part_m, part_s, part_i, gridDim.x, T, threshold, tokens, conf, choice, round_info);
+  commit_block(part_m, part_s, part_i, gridDim.x, T, threshold, tokens, conf, choice, round_info, resolved_flag);
   if (tid == 0) publish(done_count, 0);
 }
 
@@ -597,7 +613,8 @@ static hipError_t lmhead_launch(const void *hhat, const void *w_lm, int T, int H
   lmhead_kernel<W, NT><<<grid, 1024, lds, s>>>(
       (const WT *)hhat, (const WT *)w_lm, scl, T, H, V, pm, ps, pi, fused ? fused->done_count : nullptr,
       fused ? fused->threshold : 0.f, fused ? fused->tokens : nullptr, fused ? fused->conf : nullptr,
-      fused ? fused->choice : nullptr, fused ? fused->round_info : nullptr);
+      fused ? fused->choice : nullptr, fused ? fused->round_info : nullptr, fused ? fused->gate : nullptr,
+      fused ? fused->resolved_flag : nullptr);
   return hipGetLastError();
 }
 
@@ -612,6 +629,11 @@ hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, 
                    : lmhead_launch<WBf16, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
   return T <= 16 ? lmhead_launch<WF32, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
                  : lmhead_launch<WF32, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
+}
+
+hipError_t launch_block_start(int32_t *tokens, int T, int32_t *info, int words, int32_t *flag, hipStream_t s) {
+  block_start_kernel<<<1, 256, 0, s>>>(tokens, T, info, words, flag);
+  return hipGetLastError();
 }
 
 hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,

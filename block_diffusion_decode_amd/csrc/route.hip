@@ -58,8 +58,10 @@ template <typename OT>
 __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__restrict__ in,
                                                               float *__restrict__ copy_out,
                                                               OT *__restrict__ out, OT *__restrict__ xpk, int H,
-                                                              float eps, int32_t *__restrict__ zero_word) {
+                                                              float eps, int32_t *__restrict__ zero_word,
+                                                              const int32_t *__restrict__ gate) {
   __shared__ float red[kRowThreads / 64];
+  if (gated_off(gate)) return;
   if (blockIdx.x == 0 && threadIdx.x == 0 && zero_word) *zero_word = 0;
   const size_t base = (size_t)blockIdx.x * H;
   const int H4 = H / 4;
@@ -101,10 +103,12 @@ template <class W, int NT>
 __global__ __launch_bounds__(64) void router_kernel(const typename W::T *__restrict__ xhat,
                                                     int32_t *__restrict__ zero_word,
                                                     const typename W::T *__restrict__ wr,
-                                                    float *__restrict__ part, int T, int H, int E) {
+                                                    float *__restrict__ part, int T, int H, int E,
+                                                    const int32_t *__restrict__ gate) {
   typedef typename W::T WT;
   constexpr int CH = W::kChunk;
   constexpr int NCS = kRouterSlice / CH;  // 16-byte chunks per slice
+  if (gated_off(gate)) return;
   constexpr int NS = NCS / 4;             // MFMA k-steps per slice (4 chunks each)
   const int lane = threadIdx.x, li = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * 16, ks = blockIdx.y;
@@ -426,6 +430,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
+  if (gated_off(r.gate)) return;
   if (t >= T) {
     __shared__ f32x4 red[4 * 2 * 2 * 64];
     // column entry j is position j
@@ -725,9 +730,10 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
                                                               float *__restrict__ y_out,
                                                               OT *__restrict__ xhat_out,
                                                               OT *__restrict__ xpk_out, int H, int K,
-                                                              float eps) {
+                                                              float eps, const int32_t *__restrict__ gate) {
   __shared__ float red[kRowThreads / 64];
   const int t = blockIdx.x;
+  if (gated_off(gate)) return;
   const size_t base = (size_t)t * H;
   const int H4 = H / 4;
   float4 hv[kRowVec];
@@ -789,13 +795,13 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const float *__res
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *out, void *xpk, int T, int H,
-                          int32_t *zero_word, hipStream_t s) {
+                          int32_t *zero_word, const int32_t *gate, hipStream_t s) {
   if (wdtype == 1)
     rmsnorm_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(in, copy_out, (bf16_t *)out, (bf16_t *)xpk, H, 1e-6f,
-                                                     zero_word);
+                                                     zero_word, gate);
   else
     rmsnorm_kernel<float><<<T, kRowThreads, 0, s>>>(in, copy_out, (float *)out, (float *)xpk, H, 1e-6f,
-                                                    zero_word);
+                                                    zero_word, gate);
   return hipGetLastError();
 }
 
@@ -803,20 +809,21 @@ int router_slices(int H) { return H / kRouterSlice; }
 
 template <class W, int NT>
 static hipError_t router_launch(const void *xhat, int32_t *zero_word, const void *w_router, float *part,
-                                int T, int H, int E, hipStream_t s) {
+                                int T, int H, int E, const int32_t *gate, hipStream_t s) {
   typedef typename W::T WT;
   const dim3 grid((E + 15) / 16, router_slices(H));
-  router_kernel<W, NT><<<grid, 64, 0, s>>>((const WT *)xhat, zero_word, (const WT *)w_router, part, T, H, E);
+  router_kernel<W, NT><<<grid, 64, 0, s>>>((const WT *)xhat, zero_word, (const WT *)w_router, part, T, H, E,
+                                           gate);
   return hipGetLastError();
 }
 
 hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const void *w_router,
-                         float *part, int T, int H, int E, hipStream_t s) {
+                         float *part, int T, int H, int E, const int32_t *gate, hipStream_t s) {
   if (wdtype == 1)
-    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_word, w_router, part, T, H, E, s)
-                   : router_launch<WBf16, 2>(xhat, zero_word, w_router, part, T, H, E, s);
-  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_word, w_router, part, T, H, E, s)
-                 : router_launch<WF32, 2>(xhat, zero_word, w_router, part, T, H, E, s);
+    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_word, w_router, part, T, H, E, gate, s)
+                   : router_launch<WBf16, 2>(xhat, zero_word, w_router, part, T, H, E, gate, s);
+  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_word, w_router, part, T, H, E, gate, s)
+                 : router_launch<WF32, 2>(xhat, zero_word, w_router, part, T, H, E, gate, s);
 }
 
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
@@ -843,13 +850,13 @@ hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, i
 
 hipError_t launch_combine(int wdtype, const float *P, const float *P_s, const int32_t *idx,
                           const float *wgt, float *h, float *y_out, void *xhat_out, void *xpk_out, int T, int H,
-                          int K, hipStream_t s) {
+                          int K, const int32_t *gate, hipStream_t s) {
   if (wdtype == 1)
     combine_kernel<bf16_t><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (bf16_t *)xhat_out,
-                                                     (bf16_t *)xpk_out, H, K, 1e-6f);
+                                                     (bf16_t *)xpk_out, H, K, 1e-6f, gate);
   else
     combine_kernel<float><<<T, kRowThreads, 0, s>>>(P, P_s, idx, wgt, h, y_out, (float *)xhat_out,
-                                                    (float *)xpk_out, H, K, 1e-6f);
+                                                    (float *)xpk_out, H, K, 1e-6f, gate);
   return hipGetLastError();
 }
 

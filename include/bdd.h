@@ -275,6 +275,12 @@ void bdd_round_graph_destroy(bdd_round_graph g);
  * whole).  The mixer and its history state are not built: the caller
  * supplies each round's block input (the re-embedding stub).
  *   max_steps      rounds allowed per block (>= 1)
+ *   rounds_per_read  0: all of a block's rounds are enqueued back to back and
+ *                  the host reads their results once per block; k > 0: the
+ *                  host reads them every k rounds.  Every round commits at
+ *                  least one masked position, so at most min(max_steps, T)
+ *                  rounds are enqueued; each round's kernels return at once
+ *                  when an earlier round of the block has resolved it.
  *   prompt_len, max_new_tokens  the request; it is rejected (BDD_ERR_INVALID_ARG,
  *                  nothing enqueued) when prompt_len + max_new_tokens rounded
  *                  up to whole blocks exceeds 131072 tokens ([P2] "What
@@ -283,20 +289,24 @@ void bdd_round_graph_destroy(bdd_round_graph g);
  *                  of block b; n_blocks >= ceil(max_new_tokens / T)
  *   out_tokens     device [n_blocks][T] int32 out: the blocks' tokens
  *   block_rounds   HOST [n_blocks] int32 out: rounds each block took
- *   result         HOST [3] int32 out: tokens returned (min(blocks * T,
- *                  max_new_tokens)), blocks run, stop (0 length, 1 eos_token)
+ *   block_fallbacks  HOST [n_blocks] int32 out: its forced (fallback) rounds
+ *                  (may be NULL)
+ *   result         HOST [3] int32 out: tokens returned (those of the resolved
+ *                  blocks, at most max_new_tokens), blocks run, stop (0
+ *                  length, 1 eos_token)
  *   ws             bdd_generate_workspace_bytes(d, V) bytes
- * The host reads round_info after every round (one synchronisation of
- * `stream` per round).  Returns BDD_UNRESOLVED (result filled up to that
- * block) when a block still has masked positions after max_steps rounds. */
+ * Returns BDD_UNRESOLVED (result filled up to that block, which is counted
+ * in blocks run but not in tokens returned) when a block still has masked
+ * positions after max_steps rounds. */
 int32_t bdd_generate_fits(int32_t prompt_len, int32_t max_new_tokens, int32_t block_size);
 size_t bdd_generate_workspace_bytes(const bdd_moe_dims *d, int32_t V);
 bdd_status bdd_generate(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_weights *layers,
                         float coreset_top_p, const void *w_packed, int32_t V, float threshold,
-                        int32_t max_steps, int32_t prompt_len, int32_t max_new_tokens,
-                        int32_t eos_token, const float *x_rounds, int32_t n_blocks,
-                        int32_t *out_tokens, int32_t *block_rounds, int32_t *result, void *ws,
-                        size_t ws_bytes, void *stream);
+                        int32_t max_steps, int32_t rounds_per_read, int32_t prompt_len,
+                        int32_t max_new_tokens, int32_t eos_token, const float *x_rounds,
+                        int32_t n_blocks, int32_t *out_tokens, int32_t *block_rounds,
+                        int32_t *block_fallbacks, int32_t *result, void *ws, size_t ws_bytes,
+                        void *stream);
 
 /* Human-readable name of a status, and the calling thread's last error. */
 const char *bdd_status_string(int32_t status);
@@ -310,7 +320,7 @@ int32_t bdd_device_cus(void);
  * this library whose name contains `filter` (NULL or "": all) is bracketed by
  * a pair of hipEvents recorded on the launching stream.  Kernel names:
  * rmsnorm, router_logits, route_select, coreset, expert_gateup, expert_down,
- * combine, lmhead, commit, pack_lm.  Not thread-safe. */
+ * combine, lmhead, commit, pack_lm, block_start.  Not thread-safe. */
 bdd_status bdd_timing_enable(int32_t on, const char *filter);
 
 /* Waits for the recorded events, then for up to max_kernels distinct kernel

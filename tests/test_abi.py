@@ -146,15 +146,27 @@ def test_generate_rejects_on_the_host():
     d = bdd.MoEDims(32, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
     rounds = (ctypes.c_int32 * 4)()
     result = (ctypes.c_int32 * 3)()
-    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, 131072 - 31, 1, 0, None, 4,
-                        None, rounds, result, None, 0, None)
+    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, 0, 131072 - 31, 1, 0, None, 4,
+                        None, rounds, None, result, None, 0, None)
     assert st == -1 and b"131072" in L.bdd_last_error()
-    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 0, 0, 32, 0, None, 4,
-                        None, rounds, result, None, 0, None)
+    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 0, 0, 0, 32, 0, None, 4,
+                        None, rounds, None, result, None, 0, None)
     assert st == -1   # max_steps < 1
-    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, 0, 65, 0, None, 2,
-                        None, rounds, result, None, 0, None)
+    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, -1, 0, 32, 0, None, 4,
+                        None, rounds, None, result, None, 0, None)
+    assert st == -1   # rounds_per_read < 0
+    st = L.bdd_generate(ctypes.byref(d.c()), 1, None, 1.0, None, 248320, 0.95, 32, 0, 0, 65, 0, None, 2,
+                        None, rounds, None, result, None, 0, None)
     assert st == -1   # three blocks needed, two given
+
+
+def test_generate_bound_matches_the_oracle():
+    # the library's host check of the request bound against the oracle's reading
+    import oracle as O
+    for T in (1, 4, 8, 32):
+        for prompt in (0, 1, 1000, 131072 - 64, 131072 - 33, 131072 - 32, 131072 - 31, 131072 - 1, 131072):
+            for new in (1, 2, 31, 32, 33, 64, 65, 131072):
+                assert bool(bdd.generate_fits(prompt, new, T)) == O.request_fits(prompt, new, T), (T, prompt, new)
 
 
 def test_noalloc_round_rejects_dims_beyond_its_scratch():

@@ -41,7 +41,7 @@ def _dims(T, H, V):
     return W.Dims("lm_int4", T=T, H=H, E=1, K=1, I=32, I_s=0, V=V, wdtype="bf16", w_std=0.02, lm_std=H ** -0.5)
 
 
-def _planted(seed, d, codes, scales, R, p):
+def _planted(seed, d, codes, scales, R, p, pass_amp=(14.5, 16.5), fail_amp=(6.0, 10.0)):
     """Hidden states with a peak planted along the code pattern u = n - 8 of a
     random token per position, h = noise + a u with a = amp / (mean scale *
     |u|^2), so that token's logit is near amp: 14.5-16.5 (pass) with
@@ -57,7 +57,7 @@ def _planted(seed, d, codes, scales, R, p):
             u = np.empty(d.H)
             u[0::2] = (c[v] & 15).astype(np.float64) - 8.0
             u[1::2] = (c[v] >> 4).astype(np.float64) - 8.0
-            amp = rng.uniform(14.5, 16.5) if rng.random() < p else rng.uniform(6.0, 10.0)
+            amp = rng.uniform(*pass_amp) if rng.random() < p else rng.uniform(*fail_amp)
             h[r, t] += amp / (sm[v] * max(float(u @ u), 1.0)) * u
     return torch.tensor(h, dtype=torch.float32).to(torch.bfloat16)
 
@@ -175,7 +175,10 @@ def test_int4_lmhead_full_vocabulary():
     d = _dims(32, 2048, 248320)
     codes, scales = W.lm_head_int4(0, d, device=DEV)
     lm = bdd.pack_lm_head_int4(codes, scales)
-    h = _planted(5, d, codes, scales, 1, p=0.5)[0].contiguous().to(DEV)
+    # at this vocabulary conf = 0.95 near a planted logit of 15.4: passing
+    # levels 18-20 and failing ones 10-13.5 keep every commit out of the band
+    h = _planted(5, d, codes, scales, 1, p=0.5, pass_amp=(18.0, 20.0), fail_amp=(10.0, 13.5))[0]
+    h = h.contiguous().to(DEV)
     tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=DEV)
     conf, choice, ri = bdd.lmhead_confidence_commit(h, lm, tok)
     torch.cuda.synchronize()
