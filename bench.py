@@ -16,10 +16,12 @@ dominant kernel (its launches bracketed by hipEvents on their stream over K
 further rounds; HBM traffic from the rocprofv3 counter summary under
 profiles/ while the kernel's sources are unchanged since it was taken), the
 same LM head with 4-bit weights timed alone ('lmhead_int4', not the value),
-and the CPU oracle timed on a bounded sample of the same workload.
+the 40-layer Zipf/coreset stack round with block resolves through the
+generation driver ('stack', not the value), and the CPU oracle timed on a
+bounded sample of the same workload (all host threads, then one).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --stack 40               # also the 40-layer Zipf/coreset stack
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--stack L]
+                                             # (--stack 0 skips the 40-layer Zipf/coreset stack)
     python bench.py --int4-only              # the 4-bit LM head + commit alone
     python bench.py --copy-calibration MIB   # plain device copy, for counter scaling
 """
@@ -56,12 +58,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (counter scaling)")
-    ap.add_argument("--stack", type=int, default=0, metavar="L",
-                    help="also measure an L-layer stack round (Zipf routing, coreset 0.9) and a full block "
-                         "resolve on it; reported under 'stack', not as the value")
+    ap.add_argument("--stack", type=int, default=40, metavar="L",
+                    help="also measure an L-layer stack round (Zipf routing, coreset 0.9) and block resolves "
+                         "on it; reported under 'stack', not as the value (0: skip)")
     ap.add_argument("--stack-only", type=int, default=0, metavar="L",
                     help="only run the L-layer stack measurement (for a kernel trace of that workload alone); "
                          "prints one JSON line with the 'stack' object")
+    ap.add_argument("--int4-stack", type=int, default=40, metavar="L",
+                    help="also measure the L-layer stack with 4-bit experts and LM head; reported under "
+                         "'stack_int4' (0: skip)")
+    ap.add_argument("--int4-stack-only", type=int, default=0, metavar="L",
+                    help="only run the 4-bit L-layer stack measurement; prints one JSON line with 'stack_int4'")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the block-size / threshold sweep (T in 8, 16, 32; threshold 0.8 .. 0.99) of "
                          "block resolves on the round stub; prints one JSON line per (T, threshold)")
@@ -105,6 +112,10 @@ def main():
     if args.stack_only:
         args.stack = args.stack_only
         print(json.dumps({"stack": stack_round(args, W.C1, dev)}), flush=True)
+        return
+    if args.int4_stack_only:
+        args.int4_stack = args.int4_stack_only
+        print(json.dumps({"stack_int4": stack_round(args, W.C1, dev, int4=True)}), flush=True)
         return
     if args.counter_run:
         counter_run(d, dev)
@@ -171,6 +182,8 @@ def main():
     log(f"[bench] {args.steps} rounds: {ms * 1e3:.1f} us/round (host wall {wall * 1e3 / args.steps:.1f} us/round)")
     ms_graph, _ = timed(lambda i: graphs[i % R].launch())
     log(f"[bench] {args.steps} rounds (graph replays): {ms_graph * 1e3:.1f} us/round")
+    spread = round_spread(args, lambda i: plan(x[i % R], tok, conf, choice, ri), stream)
+    log(f"[bench] per-round events: median {spread['median']} us, p10 {spread['p10']}, p90 {spread['p90']}")
 
     # dominant kernel: K more rounds with its launches bracketed by hipEvents
     # on the stream it runs on
@@ -214,6 +227,7 @@ def main():
                    "launch": "bdd_block_denoise_round per round on one stream",
                    "distinct_experts_mean": mean_u},
         "us_per_round_graph": round(ms_graph * 1e3, 2),
+        "us_per_round_spread": spread,
         "round_bytes": round_bytes,
         "hbm_gbps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
@@ -227,34 +241,77 @@ def main():
         del graphs, plan, lm, layer
         torch.cuda.empty_cache()
         out["stack"] = stack_round(args, d, dev)
+        torch.cuda.empty_cache()
+    if args.int4_stack > 0:
+        out["stack_int4"] = stack_round(args, d, dev, int4=True)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, d, x, W.layer_weights(args.seed, 0, d, device=dev), w_lm, info,
                                            args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def stack_round(args, d, dev):
+def round_spread(args, fn, stream, reps=None):
+    """Median, p10 and p90 of single rounds, each bracketed by its own pair of
+    events on the launch stream (a separate pass after the timed region)."""
+    import numpy as np
+    import torch
+
+    reps = max(50, args.steps) if reps is None else reps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([1e3 * a.elapsed_time(b) for a, b in evs])
+    return {"reps": reps, "median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2)}
+
+
+def stack_round(args, d, dev, int4=False):
     """An L-layer stack of independent Clover-shaped layers (Zipf router bias,
     block coreset top_p 0.9, identity mixer) + LM head + commit: microseconds
-    per round over K rounds of stub inputs, the distinct experts each layer
-    read, and one block resolved round by round from all-MASK."""
+    per round over K rounds of stub inputs (and the spread of single rounds),
+    the distinct experts each layer read, and one block resolved from
+    all-MASK by the generation driver (wall clock, host included).  With
+    int4, every expert matrix (routed and shared) and the LM head are 4-bit
+    (router bf16)."""
     import numpy as np
     import torch
 
     import block_diffusion_decode_amd as bdd
     import workloads as W
 
-    L, top_p, T = args.stack, 0.9, d.T
-    log(f"[bench] stack: generating {L} layers")
-    layers = [W.layer_weights(args.seed, l, d, device=dev, bias="zipf", gamma=1.0) for l in range(L)]
+    L, top_p, T = (args.int4_stack if int4 else args.stack), 0.9, d.T
+    log(f"[bench] {'4-bit ' if int4 else ''}stack: generating {L} layers")
     R = 32
     x, info = W.planted_round_inputs(args.seed, d, rounds=R, p=0.3, amp_pass=40.0, amp_fail=(14.0, 22.0),
                                      tag="stack")
     x = x.to(dev)
-    w_lm = W.lm_head_weight(args.seed, d, device=dev, unit_rows=info["unit_rows"])
-    plan = bdd.RoundPlan(bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16), layers,
-                         bdd.pack_lm_head(w_lm), top_p, 0.95)
-    del w_lm
+    if int4:
+        layers = []
+        for l in range(L):
+            w = W.layer_weights_int4(args.seed, l, d, device=dev, bias="zipf", gamma=1.0)
+            layers.append({"w_router": w["w_router"], "router_bias": w["router_bias"],
+                           "w_gate_up": bdd.pack_int4(w["gu_codes"], w["gu_scales"]),
+                           "w_down": bdd.pack_int4(w["dn_codes"], w["dn_scales"]),
+                           "ws_gate_up": bdd.pack_int4(w["sgu_codes"], w["sgu_scales"]),
+                           "ws_down": bdd.pack_int4(w["sdn_codes"], w["sdn_scales"])})
+            del w
+        codes, scales = W.lm_head_int4(args.seed, d, device=dev, unit_rows=info["unit_rows"])
+        lm = bdd.pack_lm_head_int4(codes, scales)
+        del codes, scales
+        wdt = bdd.BDD_INT4
+    else:
+        layers = [W.layer_weights(args.seed, l, d, device=dev, bias="zipf", gamma=1.0) for l in range(L)]
+        w_lm = W.lm_head_weight(args.seed, d, device=dev, unit_rows=info["unit_rows"])
+        lm = bdd.pack_lm_head(w_lm)
+        del w_lm
+        wdt = bdd.BDD_BF16
+    torch.cuda.empty_cache()
+    plan = bdd.RoundPlan(bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, wdt), layers, lm, top_p, 0.95)
     tok = torch.full((T,), bdd.MASK, dtype=torch.int32, device=dev)
     conf = torch.empty(T, dtype=torch.float32, device=dev)
     choice = torch.empty(T, dtype=torch.int32, device=dev)
@@ -289,35 +346,44 @@ def stack_round(args, d, dev):
     per_kernel = {k: round(1e3 * v[0] / v[1], 2) for k, v in bdd.timing_read().items()}
     bdd.timing_enable(False)
     mean_u = float(np.mean([distinct[i % R].sum() for i in range(steps)]))
-    eb = 3 * d.H * d.I * 2
-    round_bytes = mean_u * eb + L * (3 * d.H * d.I_s * 2 + d.E * d.H * 2) + d.V * d.H * 2
-    # one block from all-MASK: round r uses stub r until every position is committed
-    tok.fill_(bdd.MASK)
-    rounds = fallbacks = 0
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for r in range(R):
-        plan(x[r], tok, conf, choice, ri)
-        info_r = ri.cpu().tolist()
-        rounds += 1
-        fallbacks += info_r[1]
-        if info_r[3]:
-            break
-    t1.record()
-    torch.cuda.synchronize()
-    resolve_ms = t0.elapsed_time(t1)
-    res = {"layers": L, "coreset_top_p": top_p, "us_per_round": round(ms * 1e3, 2),
+    # algorithmic bytes: the union experts, the shared experts, the routers and
+    # the LM head; a 4-bit matrix of n weights is n / 2 bytes of codes plus a
+    # bf16 scale per 128 weights
+    mat = (lambda n: n // 2 + n // 128 * 2) if int4 else (lambda n: 2 * n)
+    eb = mat(3 * d.H * d.I)
+    round_bytes = mean_u * eb + L * (mat(3 * d.H * d.I_s) + d.E * d.H * 2) + mat(d.V * d.H)
+    spread = round_spread(args, lambda i: plan(x[i % R], tok, conf, choice, ri), torch.cuda.current_stream(),
+                          reps=max(20, steps))
+    # one block from all-MASK (round r takes stub r) through the generation
+    # driver: the host one round ahead (the default), a host read after every
+    # round, and all rounds enqueued with one read per block
+    resolve = {}
+    for mode, per_read in (("lookahead", 0), ("read_per_round", 1), ("one_read_per_block", R)):
+        xr = x.reshape(1, R, T, d.H)
+        bdd.generate(plan, xr, max_new_tokens=T, max_steps=R, eos_token=-7, rounds_per_read=per_read)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, rounds, _, stop, fbs = bdd.generate(plan, xr, max_new_tokens=T, max_steps=R, eos_token=-7,
+                                                   rounds_per_read=per_read, with_fallbacks=True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        resolve[mode] = {"rounds": rounds[0], "fallback_rounds": fbs[0], "ms": round(1e3 * wall, 3),
+                         "committed_tokens_per_s": round(T / wall, 1)}
+    rounds, fallbacks = resolve["lookahead"]["rounds"], resolve["lookahead"]["fallback_rounds"]
+    res = {"layers": L, "weights": "int4 experts and LM head, bf16 router" if int4 else "bf16",
+           "coreset_top_p": top_p, "us_per_round": round(ms * 1e3, 2),
+           "us_per_round_spread": spread,
            "distinct_experts_per_layer_mean": mean_u / L, "round_bytes": round_bytes,
            "hbm_gbps": round_bytes / (ms * 1e-3) / 1e9, "hbm_frac": round_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
            "per_kernel_launch_us": per_kernel,
            "distinct_experts_per_layer_without_coreset": float(distinct1.sum(axis=1).mean()) / L,
            "expert_bytes_saved_per_round": float((distinct1.sum(axis=1) - distinct.sum(axis=1)).mean()) * eb,
-           "resolve": {"rounds": rounds, "fallback_rounds": fallbacks, "ms": resolve_ms,
-                       "committed_tokens_per_s": T / (resolve_ms * 1e-3),
-                       "note": "host reads round_info after every round"}}
-    log(f"[bench] stack {L} layers: {ms * 1e3:.1f} us/round, {mean_u / L:.1f} experts/layer, "
+           "resolve": resolve}
+    log(f"[bench] {'4-bit ' if int4 else ''}stack {L} layers: {ms * 1e3:.1f} us/round, {mean_u / L:.1f} experts/layer, "
         f"{res['hbm_gbps']:.0f} GB/s; block resolved in {rounds} rounds ({fallbacks} fallback), "
-        f"{res['resolve']['committed_tokens_per_s']:.0f} tok/s")
+        f"{resolve['lookahead']['committed_tokens_per_s']:.0f} tok/s with the host one round ahead, "
+        f"{resolve['read_per_round']['committed_tokens_per_s']:.0f} with a read per round, "
+        f"{resolve['one_read_per_block']['committed_tokens_per_s']:.0f} with one read per block")
     return res
 
 
@@ -510,17 +576,18 @@ def measured_traffic(kernel):
 
 def cpu_baseline(args, d, x, layer, w_lm, info, budget_s):
     """The CPU oracle (float64 NumPy) on the same round, inputs already in host
-    memory as float64; rounds run until the time budget is spent."""
+    memory as float64; rounds run until the time budget is spent, with BLAS on
+    every host thread, then a shorter sample on one thread."""
     import numpy as np
-    import torch
 
     import oracle as O
 
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:
-        cores = os.cpu_count()
+        threadpool_limits = None
+        threads = os.cpu_count()
     log("[bench] preparing float64 host copies for the CPU oracle")
     L = {"w_router": layer["w_router"].double().cpu().numpy(),
          "router_bias": layer["router_bias"].double().cpu().numpy(),
@@ -530,22 +597,33 @@ def cpu_baseline(args, d, x, layer, w_lm, info, budget_s):
     L["experts"] = {e: (gu[e].double().cpu().numpy(), dn[e].double().cpu().numpy()) for e in range(d.E)}
     wl = w_lm.double().cpu().numpy()
     xs = x.double().cpu().numpy()
-    tok = np.full(d.T, O.MASK)
-    times = []
-    t_end = time.perf_counter() + budget_s
-    r = 0
-    while time.perf_counter() < t_end or r == 0:
-        t0 = time.perf_counter()
-        hh, _ = O.moe_stack(xs[r % xs.shape[0]], [L], d.K, 1.0)
-        c, ch, _ = O.lm_head_confidence(hh, wl)
-        tok, *_ = O.commit(tok, c, ch, 0.95)
-        times.append(time.perf_counter() - t0)
-        r += 1
-    us = 1e6 * float(np.median(times))
-    log(f"[bench] cpu oracle: {len(times)} rounds, median {us / 1e3:.1f} ms/round on {cores} threads")
-    return {"value": round(us, 1), "unit": "us/round", "cores": cores, "kind": "oracle",
-            "sample": f"{len(times)} full rounds of the same workload (float64 NumPy oracle, "
-                      f"median), inputs prepared as float64 host arrays before timing"}
+
+    def sample(seconds):
+        tok = np.full(d.T, O.MASK)
+        times = []
+        t_end = time.perf_counter() + seconds
+        r = 0
+        while time.perf_counter() < t_end or r == 0:
+            t0 = time.perf_counter()
+            hh, _ = O.moe_stack(xs[r % xs.shape[0]], [L], d.K, 1.0)
+            c, ch, _ = O.lm_head_confidence(hh, wl)
+            tok, *_ = O.commit(tok, c, ch, 0.95)
+            times.append(time.perf_counter() - t0)
+            r += 1
+        return 1e6 * float(np.median(times)), len(times)
+
+    us, n = sample(budget_s)
+    log(f"[bench] cpu oracle: {n} rounds, median {us / 1e3:.1f} ms/round on {threads} threads")
+    out = {"value": round(us, 1), "unit": "us/round", "cores": threads, "kind": "oracle",
+           "host_cpus": os.cpu_count(),
+           "sample": f"{n} full rounds of the same workload (float64 NumPy oracle, median), BLAS on {threads} "
+                     f"threads, inputs prepared as float64 host arrays before timing"}
+    if threadpool_limits is not None:
+        with threadpool_limits(1):
+            us1, n1 = sample(budget_s / 3)
+        log(f"[bench] cpu oracle, one thread: {n1} rounds, median {us1 / 1e3:.1f} ms/round")
+        out["single_thread"] = {"value": round(us1, 1), "unit": "us/round", "cores": 1, "rounds": n1}
+    return out
 
 
 if __name__ == "__main__":

@@ -57,7 +57,7 @@ EXPORTS = [
     "bdd_lmhead_pack_int4",
     "bdd_round_graph_create", "bdd_round_graph_launch", "bdd_round_graph_destroy",
     "bdd_generate_fits", "bdd_generate_workspace_bytes", "bdd_generate",
-    "bdd_block_denoise_round_noalloc",
+    "bdd_block_denoise_round_noalloc", "bdd_int4_packed_bytes", "bdd_pack_int4",
 ]
 
 # Scratch bytes of bdd_block_denoise_round_noalloc (BDD_NOALLOC_SCRATCH_BYTES).
@@ -107,6 +107,10 @@ def lib() -> ctypes.CDLL:
     L.bdd_lmhead_pack.restype = i32
     L.bdd_lmhead_pack_int4.argtypes = [vp, vp, i32, i32, vp, vp]
     L.bdd_lmhead_pack_int4.restype = i32
+    L.bdd_int4_packed_bytes.argtypes = [i32, i32, i32]
+    L.bdd_int4_packed_bytes.restype = sz
+    L.bdd_pack_int4.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.bdd_pack_int4.restype = i32
     L.bdd_round_graph_create.argtypes = [dims_p, i32, w_p, f32, vp, i32, f32, vp, vp, vp, vp, vp,
                                          vp, vp, vp, vp, vp, sz, ctypes.POINTER(vp)]
     L.bdd_round_graph_create.restype = i32
@@ -146,11 +150,12 @@ class MoEDims:
     K: int
     I: int
     I_shared: int
-    wdtype: int  # BDD_F32 or BDD_BF16
+    wdtype: int  # BDD_F32, BDD_BF16 or BDD_INT4 (4-bit experts, bf16 router and activations)
 
     @property
     def torch_dtype(self):
-        return torch.bfloat16 if self.wdtype == BDD_BF16 else torch.float32
+        """dtype of the router and the normalised activations"""
+        return torch.float32 if self.wdtype == BDD_F32 else torch.bfloat16
 
     def c(self) -> _Dims:
         return _Dims(self.T, self.H, self.E, self.K, self.I, self.I_shared, self.wdtype)
@@ -181,17 +186,30 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def int4_packed_bytes(n_mats: int, rows: int, cols: int) -> int:
+    return int(lib().bdd_int4_packed_bytes(n_mats, rows, cols))
+
+
 def _weights(d: MoEDims, w: dict, dev) -> _Weights:
     dt = d.torch_dtype
     _need(w["w_router"], "w_router", dt, (d.E, d.H), dev)
-    _need(w["w_gate_up"], "w_gate_up", dt, (d.E, 2 * d.I, d.H), dev)
-    _need(w["w_down"], "w_down", dt, (d.E, d.H, d.I), dev)
+    if d.wdtype == BDD_INT4:
+        # packed by pack_int4: E matrices of 2I x H and of H x I, the shared expert's one each
+        _need(w["w_gate_up"], "w_gate_up", torch.uint8, (int4_packed_bytes(d.E, 2 * d.I, d.H),), dev)
+        _need(w["w_down"], "w_down", torch.uint8, (int4_packed_bytes(d.E, d.H, d.I),), dev)
+    else:
+        _need(w["w_gate_up"], "w_gate_up", dt, (d.E, 2 * d.I, d.H), dev)
+        _need(w["w_down"], "w_down", dt, (d.E, d.H, d.I), dev)
     bias = w.get("router_bias")
     if bias is not None:
         _need(bias, "router_bias", torch.float32, (d.E,), dev)
     if d.I_shared > 0:
-        _need(w["ws_gate_up"], "ws_gate_up", dt, (2 * d.I_shared, d.H), dev)
-        _need(w["ws_down"], "ws_down", dt, (d.H, d.I_shared), dev)
+        if d.wdtype == BDD_INT4:
+            _need(w["ws_gate_up"], "ws_gate_up", torch.uint8, (int4_packed_bytes(1, 2 * d.I_shared, d.H),), dev)
+            _need(w["ws_down"], "ws_down", torch.uint8, (int4_packed_bytes(1, d.H, d.I_shared),), dev)
+        else:
+            _need(w["ws_gate_up"], "ws_gate_up", dt, (2 * d.I_shared, d.H), dev)
+            _need(w["ws_down"], "ws_down", dt, (d.H, d.I_shared), dev)
     return _Weights(w["w_router"].data_ptr(), None if bias is None else bias.data_ptr(),
                     w["w_gate_up"].data_ptr(), w["w_down"].data_ptr(),
                     w["ws_gate_up"].data_ptr() if d.I_shared > 0 else None,
@@ -320,6 +338,25 @@ def pack_lm_head(w_lm: torch.Tensor, stream=None) -> LMHead:
     return LMHead(packed, V, H, dt)
 
 
+def pack_int4(codes: torch.Tensor, scales: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pack 4-bit weight matrices for the 4-bit expert kernels (bdd_pack_int4):
+    codes uint8 [n][rows][cols/2] or [rows][cols/2] (column 2j in the low
+    nibble of byte j, nibble n standing for n - 8), scales bf16 [n][rows][cols/128]
+    or [rows][cols/128], on the GPU.  Returns the packed uint8 tensor."""
+    if codes.dim() == 2:
+        codes, scales = codes.unsqueeze(0), scales.unsqueeze(0)
+    n, rows, half = codes.shape
+    cols = 2 * half
+    _need(codes, "codes", torch.uint8, (n, rows, half))
+    _need(scales, "scales", torch.bfloat16, (n, rows, cols // 128), codes.device)
+    nb = int4_packed_bytes(n, rows, cols)
+    if nb == 0:
+        raise BddError(-2, f"cannot pack 4-bit matrices of shape {(n, rows, cols)}")
+    packed = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+    _check(lib().bdd_pack_int4(_ptr(codes), _ptr(scales), n, rows, cols, _ptr(packed), _stream(stream)))
+    return packed
+
+
 def pack_lm_head_int4(codes: torch.Tensor, scales: torch.Tensor, stream=None) -> LMHead:
     """Pack a 4-bit LM head (see bdd_lmhead_pack_int4): codes uint8 [V][H/2]
     (column 2j in the low nibble of byte j, nibble n standing for n - 8) and
@@ -373,8 +410,9 @@ class RoundPlan:
         dev = lm.packed.device
         self.d, self.dev = d, dev
         self.V = lm.V
-        if lm.H != d.H or lm.dtype != d.torch_dtype or lm.int4:
-            raise ValueError("LM head does not match the layer dims (the full round takes bf16 or fp32 heads)")
+        if lm.H != d.H or lm.dtype != d.torch_dtype or lm.int4 != (d.wdtype == BDD_INT4):
+            raise ValueError("LM head does not match the layer dims (a round's head has the layers' weight type: "
+                             "bf16, fp32, or 4-bit with 4-bit experts)")
         self.lm = lm
         self.layers = layers  # keep the tensors alive
         arr = (_Weights * max(1, len(layers)))()

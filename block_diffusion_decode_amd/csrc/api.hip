@@ -75,7 +75,10 @@ constexpr int kGateupWgPerCu = 4;   // persistent workgroups per CU (register bu
 constexpr int kDownWgPerCu = 3;     // (3 waves per SIMD)
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
-int esize(int wdtype) { return wdtype == BDD_BF16 ? 2 : 4; }
+// bytes of a stored normalised activation (bf16 for the bf16 and 4-bit layers)
+int esize(int wdtype) { return wdtype == BDD_F32 ? 4 : 2; }
+// dtype of the activations and the router: the 4-bit layers keep both in bf16
+int act_dtype(int wdtype) { return wdtype == BDD_INT4 ? BDD_BF16 : wdtype; }
 
 int device_cus() {
   static int cache[64] = {0};
@@ -92,8 +95,8 @@ int device_cus() {
 
 bdd_status check_dims(const bdd_moe_dims *d) {
   if (!d) return fail(BDD_ERR_INVALID_ARG, "dims is NULL");
-  if (d->wdtype != BDD_F32 && d->wdtype != BDD_BF16)
-    return fail(BDD_ERR_INVALID_ARG, "wdtype %d is not BDD_F32 or BDD_BF16", d->wdtype);
+  if (d->wdtype != BDD_F32 && d->wdtype != BDD_BF16 && d->wdtype != BDD_INT4)
+    return fail(BDD_ERR_INVALID_ARG, "wdtype %d is not BDD_F32, BDD_BF16 or BDD_INT4", d->wdtype);
   if (d->T < 1 || d->H < 1 || d->E < 1 || d->K < 1 || d->I < 1 || d->I_shared < 0)
     return fail(BDD_ERR_INVALID_ARG, "non-positive size in dims (T=%d H=%d E=%d K=%d I=%d I_shared=%d)",
                 d->T, d->H, d->E, d->K, d->I, d->I_shared);
@@ -106,12 +109,15 @@ bdd_status check_dims(const bdd_moe_dims *d) {
                 d->I, d->I_shared);
   if (d->H > 8192 || d->I > 8192 || d->I_shared > 8192)
     return fail(BDD_ERR_UNSUPPORTED, "H, I, I_shared must be <= 8192");
+  if (d->wdtype == BDD_INT4 && (d->I % 128 || d->I_shared % 128))
+    return fail(BDD_ERR_UNSUPPORTED, "4-bit experts: I=%d and I_shared=%d must be multiples of 128", d->I,
+                d->I_shared);
   return BDD_OK;
 }
 
 struct MoePlan {
-  size_t logits, prob, idx, wgt, meta, ulist, glist, dlist, bits, mass, xhat, xpk, A, act, P;
-  size_t sorted, sel_count;
+  size_t logits, idx, wgt, meta, ulist, glist, dlist, bits, mass, xhat, xpk, A, act, P;
+  size_t sync;
   size_t end;
 };
 
@@ -121,7 +127,6 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   auto take = [&o](size_t bytes) { size_t at = o; o = a256(o + bytes); return at; };
   const size_t T = d.T, E = d.E, K = d.K, H = d.H, I = d.I, Is = d.I_shared;
   p.logits = take((size_t)router_slices(d.H) * T * E * 4);
-  p.prob = take(T * E * 4);
   p.idx = take(T * K * 4);
   p.wgt = take(T * K * 4);
   p.meta = take(64);
@@ -138,8 +143,7 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   p.act = take((size_t)(expert_dense_max(d.T, d.E, d.K) + 1) * (I > Is ? I : Is) * kActSlotPerI);
   // rows t*K + k of the routed picks, then T*K + t of the shared expert
   p.P = take((T * K + T) * H * 4);
-  p.sorted = take(T * E * 4);
-  p.sel_count = take(64);
+  p.sync = take(sel_sync_bytes(d.E));
   p.end = o;
   return p;
 }
@@ -198,7 +202,6 @@ bdd_status check_lm(int T, int H, int V, int dtype, float threshold) {
 RouteBufs route_bufs(void *ws, const MoePlan &p) {
   RouteBufs r;
   r.logits = at<float>(ws, p.logits);
-  r.prob = at<float>(ws, p.prob);
   r.idx = at<int32_t>(ws, p.idx);
   r.wgt = at<float>(ws, p.wgt);
   r.meta = at<int32_t>(ws, p.meta);
@@ -226,19 +229,22 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
   const int cus = device_cus();
   float *A = at<float>(ws, p.A), *P = at<float>(ws, p.P);
   void *xpk = at<void>(ws, p.xpk), *act = at<void>(ws, p.act);
-  int32_t *sel_count = at<int32_t>(ws, p.sel_count);
-  if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(d.wdtype, h_in, h_copy, xhat, xpk, T, H, lm_count, r.gate, s));
-  LAUNCH("router_logits", s, launch_router(d.wdtype, xhat, sel_count, w.w_router, r.logits, T, H, E, r.gate, s));
-  LAUNCH("route_select", s, launch_route_select(r, w.router_bias, T, H, E, K, top_p, at<int32_t>(ws, p.sorted),
-                                                sel_count, d.wdtype, xpk, w.ws_gate_up, act, Is, s));
-  int g1 = expert_items_max(T, H, E, K, I, Is, true), g2 = expert_items_max(T, H, E, K, I, Is, false);
+  r.sync = sel_sync_at(at<void>(ws, p.sync), E);
+  const int adt = act_dtype(d.wdtype);
+  if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(adt, h_in, h_copy, xhat, xpk, T, H, lm_count, r.gate, s));
+  LAUNCH("router_logits", s, launch_router(adt, xhat, reinterpret_cast<uint32_t *>(at<void>(ws, p.sync)),
+                                           (int)(sel_sync_bytes(E) / 4), w.w_router, r.logits, T, H, E, r.gate, s));
+  LAUNCH("route_select", s, launch_route_select(r, w.router_bias, T, H, E, K, top_p, d.wdtype, xpk, w.ws_gate_up,
+                                                act, Is, s));
+  const bool i4 = d.wdtype == BDD_INT4;
+  int g1 = expert_items_max(T, H, E, K, I, Is, true, i4), g2 = expert_items_max(T, H, E, K, I, Is, false, i4);
   g1 = g1 < cus * kGateupWgPerCu ? g1 : cus * kGateupWgPerCu;
   g2 = g2 < cus * kDownWgPerCu ? g2 : cus * kDownWgPerCu;
   LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, xpk, w.w_gate_up, r, A, act, T, H, I, Imax, g1,
                                                   s));
   LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, act, w.w_down, w.ws_down, r, P, T, H, K, I, Is, Imax,
                                               g2, s));
-  LAUNCH("combine", s, launch_combine(d.wdtype, P, Is > 0 ? P + (size_t)T * K * H : nullptr, r.idx, r.wgt, h,
+  LAUNCH("combine", s, launch_combine(adt, P, Is > 0 ? P + (size_t)T * K * H : nullptr, r.idx, r.wgt, h,
                                       y_out, xhat_next, xpk_next ? xpk : nullptr, T, H, K, r.gate, s));
   return BDD_OK;
 }
@@ -359,6 +365,29 @@ bdd_status bdd_lmhead_pack_int4(const void *codes, const void *scales, int32_t V
   return BDD_OK;
 }
 
+size_t bdd_int4_packed_bytes(int32_t n_mats, int32_t rows, int32_t cols) {
+  if (n_mats < 1 || rows < 1 || cols < 1 || rows % 16 || cols % 128) return 0;
+  return (size_t)n_mats * lmhead_packed_bytes(BDD_INT4, cols, rows);
+}
+
+bdd_status bdd_pack_int4(const void *codes, const void *scales, int32_t n_mats, int32_t rows, int32_t cols,
+                         void *packed, void *stream) {
+  if (!codes || !scales || !packed) return fail(BDD_ERR_INVALID_ARG, "codes, scales and packed are required");
+  if (n_mats < 1 || rows < 1 || cols < 1)
+    return fail(BDD_ERR_INVALID_ARG, "n_mats=%d rows=%d cols=%d", n_mats, rows, cols);
+  if (rows % 16 || cols % 128)
+    return fail(BDD_ERR_UNSUPPORTED, "rows=%d must be a multiple of 16 and cols=%d of 128", rows, cols);
+  if ((long long)rows * cols >= (1ll << 31)) return fail(BDD_ERR_UNSUPPORTED, "rows*cols too large");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t mb = lmhead_packed_bytes(BDD_INT4, cols, rows);
+  const size_t cb = (size_t)rows * (cols / 2), sb = (size_t)rows * (cols / 128) * 2;
+  for (int m = 0; m < n_mats; ++m)
+    LAUNCH("pack_lm", s, launch_pack_lm_int4(static_cast<const char *>(codes) + m * cb,
+                                             static_cast<const char *>(scales) + m * sb, rows, cols,
+                                             static_cast<char *>(packed) + m * mb, s));
+  return BDD_OK;
+}
+
 bdd_status bdd_lmhead_pack(const void *w_lm, int32_t V, int32_t H, int32_t dtype, void *w_packed,
                            void *stream) {
   if (!w_lm || !w_packed) return fail(BDD_ERR_INVALID_ARG, "w_lm and w_packed are required");
@@ -440,7 +469,7 @@ bdd_status round_impl(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_wei
   int32_t *count = at<int32_t>(ws, lp.count);
   if (n_layers == 0) {
     // the LM head reads RMSNorm(x_in); the norm kernel clears the counter
-    LAUNCH("rmsnorm", s, launch_rmsnorm(d->wdtype, x_in, h, hhat, nullptr, T, H, count, gate, s));
+    LAUNCH("rmsnorm", s, launch_rmsnorm(act_dtype(d->wdtype), x_in, h, hhat, nullptr, T, H, count, gate, s));
   }
   // layer l's normalised input: the caller's buffer slot, else the workspace
   const size_t xbytes = (size_t)T * H * esize(d->wdtype);
@@ -581,37 +610,65 @@ bdd_status bdd_generate(const bdd_moe_dims *d, int32_t n_layers, const bdd_moe_w
   int32_t *flag = reinterpret_cast<int32_t *>(tail + a256((size_t)T * 8) + a256((size_t)kMaxT * 16));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // Every round commits at least one masked position, so a block resolves
-  // within T rounds: at most min(max_steps, T) rounds are enqueued.  They are
-  // enqueued back to back, each gated on the block's resolved flag (rounds
-  // after the resolving one return at once), and the host reads the rounds'
-  // info once per block (or once per rounds_per_read rounds).
+  // within T rounds: at most min(max_steps, T) rounds run.  Each round is
+  // gated on the block's resolved flag, so a round enqueued after the
+  // resolving one returns at once.
   const int R = max_steps < T ? max_steps : T;
-  const int per_read = rounds_per_read > 0 ? rounds_per_read : R;
   result[0] = result[1] = result[2] = 0;
+  // rounds_per_read == 0: the host keeps one round ahead of the one whose
+  // info it reads (copied to pinned host memory, waited for on an event), so
+  // the GPU runs back to back and at most one gated round per block is spent
+  thread_local int32_t *pinned = nullptr;
+  thread_local hipEvent_t evs[2] = {nullptr, nullptr};
+  if (rounds_per_read == 0) {
+    if (!pinned) HIP_TRY(hipHostMalloc(reinterpret_cast<void **>(&pinned), (size_t)kMaxT * 16));
+    for (hipEvent_t &e : evs)
+      if (!e) HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
   int produced = 0;
   for (int b = 0; b < need_blocks; ++b) {
     int32_t *tok = out_tokens + (size_t)b * T;
     LAUNCH("block_start", s, launch_block_start(tok, T, slots, 4 * R, flag, s));
+    auto enqueue = [&](int r) -> bdd_status {
+      const float *x = x_rounds + ((size_t)b * max_steps + r) * T * H;
+      return round_impl(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x, tok, conf, choice, slots + 4 * r,
+                        nullptr, nullptr, nullptr, nullptr, ws, r_bytes, stream, flag, flag);
+    };
     int32_t info[kMaxT][4];
     int32_t last = 0;
     int rounds = 0, fallbacks = 0;
     bool resolved = false;
-    for (int r0 = 0; r0 < R && !resolved; r0 += per_read) {
-      const int r1 = r0 + per_read < R ? r0 + per_read : R;
-      for (int r = r0; r < r1; ++r) {
-        const float *x = x_rounds + ((size_t)b * max_steps + r) * T * H;
-        if ((st = round_impl(d, n_layers, layers, coreset_top_p, w_lm, V, threshold, x, tok, conf, choice,
-                             slots + 4 * r, nullptr, nullptr, nullptr, nullptr, ws, r_bytes, stream, flag, flag)) !=
-            BDD_OK)
-          return st;
+    if (rounds_per_read == 0) {
+      auto enqueue_and_copy = [&](int r) -> bdd_status {
+        const bdd_status st2 = enqueue(r);
+        if (st2 != BDD_OK) return st2;
+        HIP_TRY(hipMemcpyAsync(pinned + 4 * r, slots + 4 * r, 16, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipEventRecord(evs[r & 1], s));
+        return BDD_OK;
+      };
+      if ((st = enqueue_and_copy(0)) != BDD_OK) return st;
+      for (int r = 0; r < R && !resolved; ++r) {
+        if (r + 1 < R && (st = enqueue_and_copy(r + 1)) != BDD_OK) return st;
+        HIP_TRY(hipEventSynchronize(evs[r & 1]));
+        rounds = r + 1;
+        fallbacks += pinned[4 * r + 1];
+        resolved = pinned[4 * r + 3] != 0;
       }
-      HIP_TRY(hipMemcpyAsync(info[0], slots, (size_t)r1 * 16, hipMemcpyDeviceToHost, s));
       HIP_TRY(hipMemcpyAsync(&last, tok + T - 1, 4, hipMemcpyDeviceToHost, s));
       HIP_TRY(hipStreamSynchronize(s));
-      for (int r = r0; r < r1 && !resolved; ++r) {
-        rounds = r + 1;
-        fallbacks += info[r][1];
-        resolved = info[r][3] != 0;
+    } else {
+      for (int r0 = 0; r0 < R && !resolved; r0 += rounds_per_read) {
+        const int r1 = r0 + rounds_per_read < R ? r0 + rounds_per_read : R;
+        for (int r = r0; r < r1; ++r)
+          if ((st = enqueue(r)) != BDD_OK) return st;
+        HIP_TRY(hipMemcpyAsync(info[0], slots, (size_t)r1 * 16, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipMemcpyAsync(&last, tok + T - 1, 4, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        for (int r = r0; r < r1 && !resolved; ++r) {
+          rounds = r + 1;
+          fallbacks += info[r][1];
+          resolved = info[r][3] != 0;
+        }
       }
     }
     block_rounds[b] = rounds;

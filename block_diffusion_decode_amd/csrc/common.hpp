@@ -246,6 +246,55 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
   return v[0];
 }
 
+// ---------------------------------------------------------------- 4-bit weights
+// 4-bit weight-only matrices (two codes per byte, code n standing for n - 8,
+// one bf16 scale per row and 128-column group) are packed in 16-row tiles:
+// per tile and group one KiB in MFMA lane order (lane li + 16 g: row li; dword
+// kk: the 8 codes of k-step 4 group + kk, columns 32 (4 group + kk) + 8 g + e,
+// code e at bit 4 (e / 2) + 16 (e % 2)), then the scales [tile][group][16].
+// ((x >> 4 d) & 0x000f000f) | 0x43004300 turns codes 2d and 2d + 1 into the
+// bf16 pair 128 + n (exact), which MFMAs take as bf16 weights; a group's sum
+// over (128 + n) h is its sum over (n - 8) h plus 136 sum h.
+struct WI4 { typedef bf16_t T; static constexpr int kChunk = 8; };   // h is bf16
+constexpr int kI4Group = 128;
+constexpr float kI4Offset = 136.f;
+// 8-byte load of scales: cached normally (a tile's 128-byte line of scales
+// serves several load batches; the streaming hint would evict it in between)
+__device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  return make_uint2(v.x, v.y);
+}
+// (a & m) | c for a c with no bit inside m: a bitfield insert of a's m bits
+// into c, which the compiler issues as one v_bfi_b32.  (Plain code, so the
+// compiler's hazard tracking sees every instruction next to the MFMAs.)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | (c & ~m); }
+// codes 2d and 2d + 1 of a dword (see WI4) as the bf16 pair 128 + n
+__device__ __forceinline__ uint4 i4_expand(uint32_t x) {
+  const uint32_t m = 0x000f000fu, c = 0x43004300u;
+  return make_uint4(and_or(x, m, c), and_or(x >> 4, m, c), and_or(x >> 8, m, c), and_or(x >> 12, m, c));
+}
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// The value of lane ^ S (S = 16 or 32), through v_permlane16/32_swap: the
+// swap leaves a lane's own value in one result and its partner's in the other.
+template <int S>
+__device__ __forceinline__ uint32_t partner_u32(uint32_t v, int lane) {
+  const auto r = S == 32 ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
+                         : __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (lane & S) ? r[0] : r[1];
+}
+template <int S>
+__device__ __forceinline__ float partner_f32(float v, int lane) {
+  return __uint_as_float(partner_u32<S>(__float_as_uint(v), lane));
+}
+template <int S>
+__device__ __forceinline__ int partner_i32(int v, int lane) {
+  return (int)partner_u32<S>((uint32_t)v, lane);
+}
+
+
 // ---------------------------------------------------------------- math
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }

@@ -25,6 +25,7 @@
 // at once, so their weights stream once per block rather than once per group.
 #include <type_traits>
 
+#include "int4.hpp"
 #include "kernels.hpp"
 #include "stream.hpp"
 
@@ -558,21 +559,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit expert weights: every item on MFMA (see int4.hpp).  w_gate_up and
+// w_down are stacks of E packed matrices ([2I][H] and [H][I]), the shared
+// expert's one matrix each.
+// ---------------------------------------------------------------------------
+
+constexpr int kI4GroupDownTiles = 4;   // 16-row tiles per token-group down item (64 rows)
+
+// Per-lane entry of a token-group record: entry li (< positions) of the
+// group, as (row t*K + k, position t); -1, -1 past the group.
+__device__ __forceinline__ void group_entry(const int32_t *rec, int lane, int &row, int &pos) {
+  const int li = lane & 15;
+  const int ng = uniform(rec[1]);
+  const int v = rec[2 + min(li, kTokGroup - 1)];
+  row = li < ng ? (v & 0xffff) : -1;
+  pos = li < ng ? (v >> 16) : -1;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void expert_gateup_i4_kernel(
+    const bf16_t *__restrict__ xpk, const char *__restrict__ wgu, RouteBufs r, float *__restrict__ A,
+    char *__restrict__ act, int T, int H, int I, int Imax) {
+  if (gated_off(r.gate)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tiles = I / 16;
+  const int d_items = uniform(r.meta[3]) * tiles;
+  const int items = d_items + uniform(r.meta[2]) * tiles;
+  const size_t mb = i4_mat_bytes(2 * I, H);
+  __shared__ f32x4 red[4 * 2 * 2 * 64];
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    if (item < d_items) {
+      const int di = item / tiles, tile = item - di * tiles;
+      int e, n, v[2];
+      dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
+      int pos[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
+      const I4Mat w = i4_mat(wgu + (size_t)e * mb, 2 * I, H);
+      i4_gateup_item<2>(w, I, xpk, T, pos, tile * 16, wave, lane, act + (size_t)(1 + di) * Imax * kActSlotPerI,
+                        nullptr, nullptr, Imax, red);
+    } else {
+      const int j = item - d_items;
+      const int gi = j / tiles, tile = j - gi * tiles;
+      const int32_t *rec = r.glist + gi * 8;
+      const int e = uniform(rec[0]);
+      int row[1], pos[1];
+      group_entry(rec, lane, row[0], pos[0]);
+      const I4Mat w = i4_mat(wgu + (size_t)e * mb, 2 * I, H);
+      i4_gateup_item<1>(w, I, xpk, T, pos, tile * 16, wave, lane, nullptr, A, row, Imax, red);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void expert_down_i4_kernel(
+    const float *__restrict__ A, const char *__restrict__ act, const char *__restrict__ wd,
+    const char *__restrict__ wsd, RouteBufs r, float *__restrict__ P, int T, int H, int K, int I, int Is,
+    int Imax) {
+  if (gated_off(r.gate)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int DR = 16 * kDenseRowTiles;              // rows per dense item
+  constexpr int GR = 16 * kI4GroupDownTiles;           // rows per token-group item
+  const int dtiles = H / DR, gtiles = H / GR;
+  const int s_items = Is > 0 ? dtiles : 0;
+  const int d_end = s_items + uniform(r.meta[3]) * dtiles;
+  const int items = d_end + uniform(r.meta[2]) * gtiles;
+  const uint32_t a_bytes = (uint32_t)(T * K) * (uint32_t)Imax * 4u;
+  const size_t mb = i4_mat_bytes(H, I);
+  __shared__ f32x4 red[4 * kI4GroupDownTiles * 2 * 64];
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    if (item < d_end) {
+      int prow[2];
+      I4Mat w;
+      int ie, h0, slot;
+      if (item < s_items) {
+        // the shared expert (slot 0): column entry j is position j, row T*K + j
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int j = c * 16 + (lane & 15);
+          prow[c] = j < T ? T * K + j : -1;
+        }
+        w = i4_mat(wsd, H, Is);
+        ie = Is;
+        h0 = item * DR;
+        slot = 0;
+      } else {
+        const int di = (item - s_items) / dtiles;
+        int e, n, v[2];
+        dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) prow[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
+        w = i4_mat(wd + (size_t)e * mb, H, I);
+        ie = I;
+        h0 = (item - s_items - di * dtiles) * DR;
+        slot = 1 + di;
+      }
+      i4_down_item<kDenseRowTiles, 2>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, nullptr, nullptr, 0, Imax, H,
+                                      prow, h0, wave, lane, P, red);
+    } else {
+      const int j = item - d_end;
+      const int gi = j / gtiles, tile = j - gi * gtiles;
+      const int32_t *rec = r.glist + gi * 8;
+      const int e = uniform(rec[0]);
+      int row[1], pos[1];
+      group_entry(rec, lane, row[0], pos[0]);
+      const I4Mat w = i4_mat(wd + (size_t)e * mb, H, I);
+      i4_down_item<kI4GroupDownTiles, 1>(w, I, nullptr, A, row, a_bytes, Imax, H, row, tile * GR, wave, lane, P,
+                                         red);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
-int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup) {
-  (void)T;
+int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup, bool int4) {
   const int groups = expert_groups_max(T, E, K), dense = expert_dense_max(T, E, K);
   if (gateup) return (groups + dense) * (I / 16);
   const int dtiles = H / (16 * kDenseRowTiles);
-  return (Is > 0 ? dtiles : 0) + dense * dtiles + groups * (H / (4 * kDownRowsPerWave));
+  const int gtiles = int4 ? H / (16 * kI4GroupDownTiles) : H / (4 * kDownRowsPerWave);
+  return (Is > 0 ? dtiles : 0) + dense * dtiles + groups * gtiles;
 }
 
 hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
                                 const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
                                 hipStream_t s) {
-  if (wdtype == 1)
+  if (wdtype == 2)
+    expert_gateup_i4_kernel<<<grid, 256, 0, s>>>((const bf16_t *)xpk, (const char *)w_gate_up, r, A, (char *)act, T,
+                                                 H, I, Imax);
+  else if (wdtype == 1)
     expert_gateup_kernel<WBf16><<<grid, 256, 0, s>>>((const bf16_t *)xhat, (const bf16_t *)xpk,
                                                      (const bf16_t *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
   else
@@ -584,7 +698,10 @@ hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, c
 hipError_t launch_expert_down(int wdtype, const float *A, const void *act, const void *w_down, const void *ws_down,
                               const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
                               int grid, hipStream_t s) {
-  if (wdtype == 1)
+  if (wdtype == 2)
+    expert_down_i4_kernel<<<grid, 256, 0, s>>>(A, (const char *)act, (const char *)w_down, (const char *)ws_down, r, P,
+                                               T, H, K, I, Is, Imax);
+  else if (wdtype == 1)
     expert_down_kernel<WBf16><<<grid, 256, 0, s>>>(A, (const char *)act, (const bf16_t *)w_down,
                                                    (const bf16_t *)ws_down, r, P, T, H, K, I, Is, Imax);
   else

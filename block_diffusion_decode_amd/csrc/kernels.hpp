@@ -8,18 +8,42 @@
 
 namespace bdd {
 
+// Cross-workgroup state of the selection kernel (one contiguous block of
+// sel_sync_bytes(E) in the workspace, cleared by the router kernel).
+struct SelSync {
+  unsigned long long *mass_fx;  // [E] block expert mass of the first picks, units of 2^-56
+  uint32_t *mask1;              // [E] positions whose first picks include the expert
+  uint32_t *mask2;              // [E] positions whose final picks include the expert
+  uint32_t *kslot;              // [E][kMaxT / 4] slot of the expert among position t's final picks (byte t % 4)
+  uint32_t *cbits;              // [8] coreset membership, published for the positions
+  int32_t *words;               // [0] coreset published, [1] first count, [2] second count, [3] coreset size
+};
+inline size_t sel_sync_bytes(int E) { return (size_t)E * (8 + 4 + 4 + kMaxT) + 32 + 64; }
+inline SelSync sel_sync_at(void *base, int E) {
+  char *b = static_cast<char *>(base);
+  SelSync s;
+  s.mass_fx = reinterpret_cast<unsigned long long *>(b);
+  s.mask1 = reinterpret_cast<uint32_t *>(b + (size_t)E * 8);
+  s.mask2 = reinterpret_cast<uint32_t *>(b + (size_t)E * 12);
+  s.kslot = reinterpret_cast<uint32_t *>(b + (size_t)E * 16);
+  s.cbits = reinterpret_cast<uint32_t *>(b + (size_t)E * (16 + kMaxT));
+  s.words = reinterpret_cast<int32_t *>(b + (size_t)E * (16 + kMaxT) + 32);
+  return s;
+}
+
 // Per-layer routing results and expert work lists, in the caller's workspace.
 struct RouteBufs {
   float *logits;       // [H/128][T][E] router logit slices (bias not added)
-  float *prob;         // [T][E]   softmax over all experts
   int32_t *idx;        // [T][K]   picked experts (-1 = unused slot)
   float *wgt;          // [T][K]   their renormalised weights
-  int32_t *meta;       // [0] union size, [1] coreset size, [2] token groups, [3] dense experts
+  int32_t *meta;       // [0] union size, [1] coreset size, [2] token groups, [3] dense experts,
+                       // [4] set if a wait for the coreset timed out
   int32_t *union_list; // [E]      union experts, ascending id
   int32_t *glist;      // [expert_groups_max][8] token-group records (see the expert kernels)
   int32_t *dlist;      // [expert_dense_max][kDenseRec] dense-expert records
   uint32_t *cs_bits;   // [8]      coreset membership bitset
-  float *mass;         // [E]      block expert mass
+  float *mass;         // [E]      block expert mass (with the coreset)
+  SelSync sync;        // selection kernel's cross-workgroup state
   int32_t *n_distinct_out;    // [1] union size copy (may be null)
   int32_t *coreset_size_out;  // [1] coreset size copy (may be null)
   const int32_t *gate;        // block resolved flag (may be null): the layer's kernels return when set
@@ -47,19 +71,20 @@ hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *ou
                           int32_t *zero_word, const int32_t *gate, hipStream_t s);
 
 // Router logits from the normalised block, as partial sums over hidden slices
-// (part [router_slices(H)][T][E]); clears zero_word.
+// (part [router_slices(H)][T][E]); clears zero_words words at zero_base (the
+// selection kernel's state).
 int router_slices(int H);
-hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const void *w_router,
+hipError_t launch_router(int wdtype, const void *xhat, uint32_t *zero_base, int zero_words, const void *w_router,
                          float *part, int T, int H, int E, const int32_t *gate, hipStream_t s);
 
 // Selection: one workgroup per position (logits = slices summed in order +
-// bias), then the block-level steps in the last one; workgroups past the
-// positions compute the shared expert's gate/up from the packed block `xpk`
-// into its packed activation slot `act_shared`.  sorted_ids [T][E] scratch;
-// done_count must be zero (the router kernel clears it) and is left zero.
+// bias), the coreset and the work lists (r.sync must have been cleared by the
+// router kernel); workgroups past the positions compute the shared expert's
+// gate/up from the packed block `xpk` into its packed activation slot
+// `act_shared`.
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
-                               int32_t *sorted_ids, int32_t *done_count, int wdtype, const void *xpk,
-                               const void *ws_gate_up, void *act_shared, int Is, hipStream_t s);
+                               int wdtype, const void *xpk, const void *ws_gate_up, void *act_shared, int Is,
+                               hipStream_t s);
 
 hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, int K, float top_p,
                           uint32_t *bits, int32_t *size, float *mass, hipStream_t s);
@@ -69,7 +94,7 @@ hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, i
 // (Imax * 128 bytes each; slot 0 the shared expert, slot 1 + d dense record
 // d).  P [T*K + T][H] fp32 unweighted outputs (rows t*K + k routed, T*K + t
 // shared).
-int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup);
+int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup, bool int4);
 hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
                                 const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
                                 hipStream_t s);

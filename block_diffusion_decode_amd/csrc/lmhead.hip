@@ -57,9 +57,6 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
 // multiplies by the row's scale once per group.  Scales: 16 bf16 per (tile,
 // group), after all the codes; lane (li, g) reads those of its output rows
 // 4g .. 4g + 3.
-struct WI4 { typedef bf16_t T; static constexpr int kChunk = 8; };   // h is bf16
-constexpr int kI4Group = 128;
-constexpr float kI4Offset = 136.f;
 // units per tile per load batch, and tiles a wave streams side by side: a
 // 4-bit wave works on two tiles at once, so every block operand it reads from
 // LDS feeds both tiles' MFMAs (a bf16 tile is HBM-bound on its own)
@@ -72,44 +69,6 @@ struct LmBufs {
   uint4 a[lm_tiles<W>()][lm_batch<W>()];
   uint2 sc[lm_tiles<W>()][std::is_same<W, WI4>::value ? lm_batch<W>() : 1];
 };
-// 8-byte load of scales: cached normally (a tile's 128-byte line of scales
-// serves several load batches; the streaming hint would evict it in between)
-__device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
-  return make_uint2(v.x, v.y);
-}
-// (a & m) | c in one instruction (the compiler splits the pattern in two)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
-  return r;
-}
-// codes 2d and 2d + 1 of a dword (see WI4) as the bf16 pair 128 + n
-__device__ __forceinline__ uint4 i4_expand(uint32_t x) {
-  const uint32_t m = 0x000f000fu, c = 0x43004300u;
-  return make_uint4(and_or(x, m, c), and_or(x >> 4, m, c), and_or(x >> 8, m, c), and_or(x >> 12, m, c));
-}
-__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-
-// The value of lane ^ S (S = 16 or 32), through v_permlane16/32_swap: the
-// swap leaves a lane's own value in one result and its partner's in the other.
-template <int S>
-__device__ __forceinline__ uint32_t partner_u32(uint32_t v, int lane) {
-  const auto r = S == 32 ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
-                         : __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return (lane & S) ? r[0] : r[1];
-}
-template <int S>
-__device__ __forceinline__ float partner_f32(float v, int lane) {
-  return __uint_as_float(partner_u32<S>(__float_as_uint(v), lane));
-}
-template <int S>
-__device__ __forceinline__ int partner_i32(int v, int lane) {
-  return (int)partner_u32<S>((uint32_t)v, lane);
-}
-
 // A buffer offset past every LM-head tile: such a load returns zeros without
 // a memory access (pads the prefetches past a wave's last step).
 constexpr uint32_t kLmOutOfRange = 0x7ff00000u;
@@ -139,13 +98,22 @@ __device__ void commit_block(const float *__restrict__ part_m, const float *__re
     for (int base = hl; base < nparts; base += 32 * kCommitBatch) {
       float pm[kCommitBatch], ps[kCommitBatch];
       int pi[kCommitBatch];
+      // (after the acquire of the workgroup count, or a kernel boundary:
+      // plain loads of clamped indices, all in flight together; entries past
+      // the partials are then neutralised)
 #pragma unroll
       for (int j = 0; j < kCommitBatch; ++j) {
         const int p = base + 32 * j;
-        const bool ok = live && p < nparts;
-        pm[j] = ok ? fetch_published(part_m + (size_t)t * nparts + p) : 0.f;
-        ps[j] = ok ? fetch_published(part_s + (size_t)t * nparts + p) : 0.f;
-        pi[j] = ok ? fetch_published(part_i + (size_t)t * nparts + p) : INT_MAX;
+        const size_t at = (size_t)min(t, T - 1) * nparts + min(p, nparts - 1);
+        pm[j] = part_m[at];
+        ps[j] = part_s[at];
+        pi[j] = part_i[at];
+      }
+#pragma unroll
+      for (int j = 0; j < kCommitBatch; ++j) {
+        const bool ok = live && base + 32 * j < nparts;
+        ps[j] = ok ? ps[j] : 0.f;
+        pi[j] = ok ? pi[j] : INT_MAX;
       }
 #pragma unroll
       for (int j = 0; j < kCommitBatch; ++j) sm_merge(m, s, i, pm[j], ps[j], pi[j]);

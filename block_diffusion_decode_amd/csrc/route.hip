@@ -11,6 +11,7 @@
 
 #include <type_traits>
 
+#include "int4.hpp"
 #include "kernels.hpp"
 #include "stream.hpp"
 
@@ -94,14 +95,13 @@ __global__ __launch_bounds__(kRowThreads) void rmsnorm_kernel(const float *__res
 // positions as columns, both operands loaded straight from memory (the block
 // is L2-resident), so the 1 MiB of router weights is spread over ~256
 // workgroups.  The selection kernel sums the slices in slice order and adds
-// the bias.  Workgroup (0, 0) also clears `zero_word` (the selection kernel's
-// counter).
+// the bias.  The workgroups also clear the selection kernel's state.
 constexpr int kRouterSlice = 128;
 constexpr uint32_t kRouterOut = 0x7ff00000u;  // out-of-range buffer offset: loads return zeros
 
 template <class W, int NT>
 __global__ __launch_bounds__(64) void router_kernel(const typename W::T *__restrict__ xhat,
-                                                    int32_t *__restrict__ zero_word,
+                                                    uint32_t *__restrict__ zero_base, int zero_words,
                                                     const typename W::T *__restrict__ wr,
                                                     float *__restrict__ part, int T, int H, int E,
                                                     const int32_t *__restrict__ gate) {
@@ -112,7 +112,10 @@ __global__ __launch_bounds__(64) void router_kernel(const typename W::T *__restr
   constexpr int NS = NCS / 4;             // MFMA k-steps per slice (4 chunks each)
   const int lane = threadIdx.x, li = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * 16, ks = blockIdx.y;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && lane == 0 && zero_word) *zero_word = 0;
+  {
+    const int nthr = (int)(gridDim.x * gridDim.y) * 64;
+    for (int i = (int)(blockIdx.y * gridDim.x + blockIdx.x) * 64 + lane; i < zero_words; i += nthr) zero_base[i] = 0u;
+  }
   const rsrc_t rw = make_rsrc(wr, (uint32_t)(E * H) * sizeof(WT));
   const rsrc_t rx = make_rsrc(xhat, (uint32_t)(T * H) * sizeof(WT));
   const int e_row = row0 + li;
@@ -384,18 +387,30 @@ __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
 
 // ------------------------------------------------------------------ route + select
 // One workgroup of kSelThreads per position: softmax over the position's E
-// router logits and a bitonic sort of (logit desc, expert id asc), so its top-K
-// is the prefix of its sorted list.  The workgroup that finishes last (an
-// agent-scope acquire-release counter, cleared by the router kernel, over rows
-// published as agent-scope atomics) then takes the block-level steps: expert mass, coreset
-// and re-routing (each position's first min(K, |C|) coreset members in its
-// sorted order), weights, the union of experts and each union expert's list
-// of (position, pick) assignments.  It clears the counter when done.
+// router logits and a bitonic sort of (logit desc, expert id asc), so its
+// top-K is the prefix of its sorted list.  The block-level steps run mostly
+// in these workgroups, in parallel:
+//   - with the coreset, each adds its first picks' softmax scores to the block
+//     mass (64-bit fixed-point atomics: the sums are exact, so their order
+//     does not matter) and its bit to each picked expert's position mask; the
+//     workgroup counted last ranks the experts, cuts the coreset and publishes
+//     it behind a release flag; the others wait for the flag (acquire) and
+//     each re-takes its position's first min(K, |C|) coreset members in its
+//     own sorted order;
+//   - each writes its final picks and weights, and adds its bit and pick slot
+//     to each picked expert's mask and slot word; the workgroup counted last
+//     then builds the union and the experts' work lists from them.
+// The waiting workgroups have all been counted, so the one they wait for is
+// running: the wait needs no co-residency.  It is bounded all the same (every
+// wave leaves it), and a timeout is reported in meta[4].
 // Workgroups past the T positions compute the shared expert's gate/up (it
 // needs only the normalised block), so its weights stream while selection
 // runs: workgroup T + j takes intermediate units 16 j .. 16 j + 15.
 constexpr int kSelThreads = 256;
 static_assert(kSelThreads == 256, "the shared gate/up item runs on four waves");
+static_assert(kSelThreads >= kMaxE, "one thread per expert in the block steps");
+constexpr int kSelSpinMax = 1 << 21;          // bound of the wait for the coreset (~0.1 s)
+constexpr double kMassScale = 72057594037927936.0;   // 2^56: fixed-point unit of the block mass
 
 // Shared-expert operands for the workgroups past the positions.
 template <class W>
@@ -418,16 +433,236 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, i
   return ((unsigned long long)(uint32_t)__shfl_xor((int)hi, m) << 32) | (uint32_t)__shfl_xor((int)lo, m);
 }
 
+__device__ __forceinline__ unsigned long long lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Exclusive prefix over the workgroup of flags (0/1), via ballots; returns
+// this thread's prefix and leaves the total in *total.  Ends with a barrier.
+__device__ __forceinline__ int block_flag_scan(bool flag, int *s_wave, int *total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long b = __ballot(flag);
+  if (lane == 0) s_wave[wave] = __popcll(b);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    off += w < wave ? s_wave[w] : 0;
+    tot += s_wave[w];
+  }
+  *total = tot;
+  __syncthreads();
+  return off + __popcll(b & lanes_below(lane));
+}
+
+// The coreset step ([P2] coreset section), by the workgroup counted last:
+// experts with a first pick, ranked by (mass desc, id asc) from the exact
+// fixed-point masses; the shortest ranked prefix whose cumulative mass reaches
+// top_p of the total; its bitset published for the other positions.
+// It runs after the workgroup's acquire (count and barrier), so the other
+// workgroups' atomics are visible to plain loads, all issued at once.  The
+// coreset is left in s_cb / *s_csize for the caller.
+__device__ void coreset_step(const RouteBufs &r, int E, float top_p, int *s_wave, uint32_t *s_cb, int *s_csize) {
+  __shared__ unsigned long long s_um[kMaxE];
+  __shared__ int s_ue[kMaxE], s_rank[kMaxE], s_sorted[kMaxE];
+  __shared__ unsigned long long s_cum[kMaxE];
+  __shared__ unsigned long long s_wtot[kSelThreads / 64];
+  __shared__ int s_below;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int te = min(tid, E - 1);
+  const unsigned long long m_all = r.sync.mass_fx[te];
+  const uint32_t msk_all = r.sync.mask1[te];
+  const unsigned long long m = tid < E ? m_all : 0ull;
+  const uint32_t msk = tid < E ? msk_all : 0u;
+  if (tid < kMaxE / 32) s_cb[tid] = 0u;
+  if (tid == 0) s_below = 0;
+  int nu = 0;
+  const int slot = block_flag_scan(msk != 0u, s_wave, &nu);
+  if (msk != 0u) {
+    s_um[slot] = m;
+    s_ue[slot] = tid;
+  }
+  if (tid < kMaxE) s_rank[tid] = 0;
+  __syncthreads();
+  {
+    // rank of entry j = entries before it in (mass desc, id asc) order; the
+    // threads split each entry's comparisons into `parts` ranges
+    const int parts = nu <= 64 ? 4 : nu <= 128 ? 2 : 1;
+    const int span = parts == 4 ? 64 : parts == 2 ? 128 : 256;
+    const int j = tid % span, part = tid / span;
+    if (j < nu && part < parts) {
+      const unsigned long long mj = s_um[j];
+      const int ej = s_ue[j];
+      const int lo = part * nu / parts, hi = (part + 1) * nu / parts;
+      int rk = 0;
+      for (int i0 = lo; i0 < hi; i0 += 8) {
+        unsigned long long mi[8];
+        int ei[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = min(i0 + q, hi - 1);
+          mi[q] = s_um[i];
+          ei[q] = s_ue[i];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          rk += (int)(i0 + q < hi) & ((int)(mi[q] > mj) | ((int)(mi[q] == mj) & (int)(ei[q] < ej)));
+      }
+      atomicAdd(&s_rank[j], rk);
+    }
+  }
+  __syncthreads();
+  if (tid < nu) {
+    s_sorted[s_rank[tid]] = s_ue[tid];
+    s_cum[s_rank[tid]] = s_um[tid];
+  }
+  __syncthreads();
+  // inclusive prefix of the ranked masses (exact integer sums)
+  unsigned long long v = tid < nu ? s_cum[tid] : 0ull;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const unsigned long long o = __shfl_up(v, sft);
+    if (lane >= sft) v += o;
+  }
+  if (lane == 63) s_wtot[wave] = v;
+  __syncthreads();
+  unsigned long long off = 0ull, tot = 0ull;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    off += w < wave ? s_wtot[w] : 0ull;
+    tot += s_wtot[w];
+  }
+  v += off;
+  // the prefix whose cumulative mass stays below top_p of the total, plus one
+  const double target = (double)top_p * (double)tot;
+  const unsigned long long b = __ballot(tid < nu && (double)v < target);
+  if (lane == 0 && b) atomicAdd(&s_below, (int)__popcll(b));
+  __syncthreads();
+  const int k = max(1, min(s_below + 1, nu));
+  if (tid < k) atomicOr(&s_cb[s_sorted[tid] >> 5], 1u << (s_sorted[tid] & 31));
+  __syncthreads();
+  if (tid < (E + 31) / 32) {
+    publish(r.sync.cbits + tid, s_cb[tid]);
+    r.cs_bits[tid] = s_cb[tid];
+  }
+  if (tid < E) r.mass[tid] = (float)((double)m / kMassScale);
+  if (tid == 0) {
+    publish(r.sync.words + 3, k);
+    *s_csize = k;
+    r.meta[1] = k;
+    if (r.coreset_size_out) *r.coreset_size_out = k;
+  }
+  __syncthreads();   // every published word is ordered before the flag
+  if (tid == 0) __hip_atomic_store(r.sync.words, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The union of the final picks and the experts' work lists, by the workgroup
+// counted last after every position published its final picks.  An expert
+// with at most kTokGroup positions gets token-group records of 8 words:
+//   [expert, positions, (t*K + k) | t << 16 per position, 0 ...];
+// one with more gets a dense record of kDenseRec words:
+//   [expert, positions, 0 x 6, (t*K + k) | t << 16 per position],
+// positions ascending, records in union (ascending expert) order.
+__device__ void union_records(const RouteBufs &r, int T, int E, int K, bool coreset, int *s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int KW = kMaxT / 4;   // slot words per expert
+  static_assert(KW % 4 == 0, "slot words load as 16-byte vectors");
+  // after the workgroup's acquire: plain loads, all in flight together; the
+  // expert's slot words go to its own LDS row (a register array indexed by
+  // position would be placed in scratch memory)
+  __shared__ uint32_t s_kw[kSelThreads][KW + 1];
+  const int te = min(tid, E - 1);
+  const uint32_t tb_all = r.sync.mask2[te];
+#pragma unroll
+  for (int j = 0; j < KW; j += 4) {
+    const uint4 v = reinterpret_cast<const uint4 *>(r.sync.kslot + (size_t)te * KW)[j / 4];
+    s_kw[tid][j] = v.x;
+    s_kw[tid][j + 1] = v.y;
+    s_kw[tid][j + 2] = v.z;
+    s_kw[tid][j + 3] = v.w;
+  }
+  const uint32_t tbits = tid < E ? tb_all : 0u;
+  int nu = 0;
+  const int slot = block_flag_scan(tbits != 0u, s_wave, &nu);
+  if (tbits != 0u) r.union_list[slot] = tid;
+  if (!coreset) {
+    // without the coreset every expert with a pick is reported as its member
+    const unsigned long long b = __ballot(tid < E && tbits != 0u);
+    if (lane == 0 && 64 * wave < E) r.cs_bits[2 * wave] = (uint32_t)b;
+    if (lane == 32 && 64 * wave + 32 < E) r.cs_bits[2 * wave + 1] = (uint32_t)(b >> 32);
+  }
+  // group and dense-record counts: exclusive prefix by bit-sliced ballots
+  // (an expert has at most kMaxT / kTokGroup groups, bits 0..3 of its count;
+  // the dense flag is bit 16, so the block's group total stays below it)
+  const int npos = __popc(tbits);
+  const bool dense = npos > kTokGroup;
+  const int ng = dense ? 0 : (npos + kTokGroup - 1) / kTokGroup;
+  static_assert(kMaxT / kTokGroup < 16, "group counts fit four bits");
+  const int cnt = ng | (dense ? 1 << 16 : 0);
+  int pre = 0, wtot = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const int sh = bit < 4 ? bit : 16;
+    const unsigned long long bb = __ballot((cnt >> sh) & 1);
+    pre += __popcll(bb & lanes_below(lane)) << sh;
+    wtot += __popcll(bb) << sh;
+  }
+  if (lane == 0) s_wave[wave] = wtot;
+  __syncthreads();
+  int off = pre, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    off += w < wave ? s_wave[w] : 0;
+    tot += s_wave[w];
+  }
+  // the pick slot of position t: byte t % 4 of the expert's word t / 4
+  auto kslot_of = [&](int t) { return (int)((s_kw[tid][t >> 2] >> (8 * (t & 3))) & 0xffu); };
+  if (dense) {
+    int32_t *rec = r.dlist + (off >> 16) * kDenseRec;
+    rec[0] = tid;
+    rec[1] = npos;
+    uint32_t bits = tbits;
+    for (int j = 0; bits; ++j) {
+      const int t = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      rec[8 + j] = (t * K + kslot_of(t)) | (t << 16);
+    }
+  } else if (npos > 0) {
+    const int g0 = off & 0xffff;
+    uint32_t bits = tbits;
+    for (int j = 0; bits; ++j) {
+      const int t = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      int32_t *rec = r.glist + (g0 + j / kTokGroup) * 8;
+      if (j % kTokGroup == 0) {
+        rec[0] = tid;
+        rec[1] = min(kTokGroup, npos - j);
+        for (int q = 2 + min(kTokGroup, npos - j); q < 8; ++q) rec[q] = 0;
+      }
+      rec[2 + j % kTokGroup] = (t * K + kslot_of(t)) | (t << 16);
+    }
+  }
+  if (tid == 0) {
+    r.meta[2] = tot & 0xffff;
+    r.meta[3] = tot >> 16;
+    r.meta[0] = nu;
+    if (!coreset) r.meta[1] = nu;
+    if (r.n_distinct_out) *r.n_distinct_out = nu;
+    if (!coreset && r.coreset_size_out) *r.coreset_size_out = nu;
+  }
+}
+
 template <class W>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const float *__restrict__ bias,
                                                              int KS, int T, int E, int K, float top_p,
-                                                             int32_t *__restrict__ sorted_ids,
-                                                             int32_t *__restrict__ done_count,
                                                              SharedGU<W> sg) {
   __shared__ unsigned long long s_key[kSelThreads];
   __shared__ float s_p[kSelThreads];
   __shared__ float s_red[kSelThreads / 64];
-  __shared__ int s_last;
+  __shared__ int s_wave[kSelThreads / 64];
+  __shared__ int s_pick[kMaxK];
+  __shared__ uint32_t s_cb[kMaxE / 32];
+  __shared__ int s_last, s_csize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
   if (gated_off(r.gate)) return;
@@ -440,259 +675,110 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
       const int j = n * 16 + (lane & 15);
       pos[n] = j < T ? j : -1;
     }
-    dense_gateup_item<W, kSgSteps>(sg.wsgu, sg.Is, sg.xpk, T, sg.H, pos, t - T, (t - T) * 16, wave, lane, sg.act,
-                                   red);
+    if constexpr (std::is_same<W, WI4>::value)
+      i4_gateup_item<2>(i4_mat(sg.wsgu, 2 * sg.Is, sg.H), sg.Is, sg.xpk, T, pos, (t - T) * 16, wave, lane, sg.act,
+                        nullptr, nullptr, 0, red);
+    else
+      dense_gateup_item<W, kSgSteps>(sg.wsgu, sg.Is, sg.xpk, T, sg.H, pos, t - T, (t - T) * 16, wave, lane, sg.act,
+                                     red);
     return;
   }
-  {
-    // ---- phase 1: this position.  Logit = router slices in slice order + bias.
-    float l = -FLT_MAX;
-    if (tid < E) {
-      float acc = 0.f;
+  // ---- this position: logit = router slices in slice order + bias
+  float l = -FLT_MAX;
+  if (tid < E) {
+    float acc = 0.f;
 #pragma unroll 16
-      for (int ks = 0; ks < KS; ++ks) acc += r.logits[((size_t)ks * T + t) * E + tid];
-      l = acc + (bias ? bias[tid] : 0.f);
-      // the position's full logits replace its row of slice 0 (read by no
-      // other workgroup) for the coreset re-routing
-      publish(r.logits + (size_t)t * E + tid, l);
-    }
-    float m = wave_max_dpp(l);
-    if (lane == 0) s_red[wave] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    __syncthreads();
-    const float ex = tid < E ? expf(l - m) : 0.f;
-    float sum = wave_sum_dpp(ex);
-    if (lane == 0) s_red[wave] = sum;
-    __syncthreads();
-    sum = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    const float pr = ex / sum;
-    if (tid < E) publish(r.prob + (size_t)t * E + tid, pr);
-    s_p[tid] = pr;
-    // bitonic sort, ascending on (order_key(logit), id); padding sorts last
-    unsigned long long key = tid < E ? (((unsigned long long)order_key(l) << 32) | (uint32_t)tid) : ~0ull;
-    for (int k = 2; k <= kSelThreads; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        unsigned long long other;
-        if (j >= 64) {
-          __syncthreads();
-          s_key[tid] = key;
-          __syncthreads();
-          other = s_key[tid ^ j];
-        } else {
-          other = shfl_xor64(key, j);
-        }
-        const bool lower = (tid & j) == 0, asc = (tid & k) == 0;
-        key = (lower == asc) ? (key < other ? key : other) : (key < other ? other : key);
+    for (int ks = 0; ks < KS; ++ks) acc += r.logits[((size_t)ks * T + t) * E + tid];
+    l = acc + (bias ? bias[tid] : 0.f);
+  }
+  float m = wave_max_dpp(l);
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  const float ex = tid < E ? expf(l - m) : 0.f;
+  float sum = wave_sum_dpp(ex);
+  if (lane == 0) s_red[wave] = sum;
+  __syncthreads();
+  sum = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  s_p[tid] = ex / sum;
+  // bitonic sort, ascending on (order_key(logit), id); padding sorts last
+  unsigned long long key = tid < E ? (((unsigned long long)order_key(l) << 32) | (uint32_t)tid) : ~0ull;
+  for (int k = 2; k <= kSelThreads; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      unsigned long long other;
+      if (j >= 64) {
+        __syncthreads();
+        s_key[tid] = key;
+        __syncthreads();
+        other = s_key[tid ^ j];
+      } else {
+        other = shfl_xor64(key, j);
       }
+      const bool lower = (tid & j) == 0, asc = (tid & k) == 0;
+      key = (lower == asc) ? (key < other ? key : other) : (key < other ? other : key);
     }
-    const int e_sorted = (int32_t)(uint32_t)key;
-    if (tid < E) publish(sorted_ids + (size_t)t * E + tid, e_sorted);
-    // the top-K picks and their scores, in sorted order
+  }
+  const int e_sorted = (int32_t)(uint32_t)key;   // rank tid of the position's sorted list
+  const bool coreset = top_p < 1.0f;
+  int kk = K;
+  if (coreset) {
+    // contribute the first picks to the block mass and the position masks
     if (tid < K) {
-      publish(r.idx + (size_t)t * K + tid, e_sorted);
-      publish(r.wgt + (size_t)t * K + tid, s_p[e_sorted]);
+      atomicAdd(r.sync.mass_fx + e_sorted, (unsigned long long)((double)s_p[e_sorted] * kMassScale));
+      atomicOr(r.sync.mask1 + e_sorted, 1u << t);
     }
-  }
-  __syncthreads();   // every wave's published rows are ordered before the count
-  if (tid == 0) s_last = count_done(done_count) == T - 1;
-  __syncthreads();   // the last workgroup's waves read after its acquire
-  if (!s_last) return;
-
-  // ---- phase 2: the block (last workgroup)
-  __shared__ SelShared sh;
-  for (int i = tid; i < T * K; i += kSelThreads) {
-    const int tt = i / K, k = i - tt * K;
-    sh.idx[tt][k] = fetch_published(r.idx + i);      // scores are staged in wgt
-    sh.psel[tt][k] = fetch_published(r.wgt + i);
-  }
-  __syncthreads();
-  coreset_core(sh, T, E, K, top_p);
-  if (tid < E) r.mass[tid] = (float)sh.mass[tid];
-  write_bits(sh, E, r.cs_bits);
-  if (top_p < 1.0f) {
-    // each position re-takes its first min(K, |C|) coreset members in its own
-    // (logit desc, id asc) order.
-    const int kk = min(K, sh.csize);
-    if (sh.csize <= 64) {
-      // Lane j of a wave holds member j (mass rank order) and, for each of the
-      // wave's positions, that member's key (logit desc, id asc) and score; a
-      // member's slot is its rank among the members' keys, which the wave
-      // reads back from LDS eight at a time (broadcast reads).
-      const int C = sh.csize;
-      const int c = lane < C ? sh.sorted[lane] : 0;
-      constexpr int kPer = kMaxT / (kSelThreads / 64);
-      __shared__ unsigned long long s_rk[kMaxT][64];
-      float lv[kPer], pv[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int tt = wave + i * (kSelThreads / 64);
-        const bool ok = tt < T && lane < C;
-        lv[i] = ok ? fetch_published(r.logits + (size_t)tt * E + c) : 0.f;
-        pv[i] = ok ? fetch_published(r.prob + (size_t)tt * E + c) : 0.f;
-      }
-      unsigned long long key[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int tt = wave + i * (kSelThreads / 64);
-        key[i] = lane < C ? ((unsigned long long)order_key(lv[i]) << 32) | (uint32_t)c : ~0ull;
-        if (tt < T) s_rk[tt][lane] = key[i];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int tt = wave + i * (kSelThreads / 64);
-        if (tt >= T) break;
-        int rk = 0;
-        for (int j0 = 0; j0 < C; j0 += 8) {
-          unsigned long long kj[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kj[j] = s_rk[tt][min(j0 + j, C - 1)];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) rk += (int)(j0 + j < C) & (int)(kj[j] < key[i]);
+    __syncthreads();
+    if (tid == 0) s_last = count_done(r.sync.words + 1) == T - 1;
+    __syncthreads();
+    if (s_last) {
+      coreset_step(r, E, top_p, s_wave, s_cb, &s_csize);
+    } else if (tid == 0) {
+      int n = 0;
+      while (__hip_atomic_load(r.sync.words, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        if (++n > kSelSpinMax) {
+          r.meta[4] = 1;    // the coreset was never published: reported, and the wait ends
+          break;
         }
-        if (lane < C && rk < kk) {
-          sh.idx[tt][rk] = c;
-          sh.psel[tt][rk] = pv[i];
-        }
-        if (lane < K && lane >= kk) {
-          sh.idx[tt][lane] = -1;
-          sh.psel[tt][lane] = 0.f;
-        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      __syncthreads();
-    } else {
-      // every position's sorted list is staged in LDS (ids fit a byte; all
-      // loads in flight at once), the scans run from LDS, then the chosen
-      // experts' probabilities arrive in one batch
-      __shared__ uint8_t s_sorted[kMaxT * kMaxE];
-      constexpr int kStage = kMaxT * kMaxE / kSelThreads;
-      int v[kStage];
-#pragma unroll
-      for (int j = 0; j < kStage; ++j) {
-        const int i = tid + j * kSelThreads;
-        v[j] = i < T * E ? fetch_published(sorted_ids + i) : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < kStage; ++j) {
-        const int i = tid + j * kSelThreads;
-        if (i < T * E) s_sorted[i] = (uint8_t)v[j];
-      }
-      __syncthreads();
-      constexpr int kChunks = kMaxE / 64;
-      for (int tt = wave; tt < T; tt += kSelThreads / 64) {
-        // the position's whole sorted list at once: member flags of the 4
-        // chunks, then each member's rank among the members before it
-        int e[kChunks];
-        unsigned long long b[kChunks];
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-          const int i = c * 64 + lane;
-          e[c] = i < E ? (int)s_sorted[tt * E + i] : -1;
-        }
-        int mem[kChunks];
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) mem[c] = sh.member[e[c] & (kMaxE - 1)];   // unconditional
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) b[c] = __ballot(e[c] >= 0 && mem[c] != 0);
-        int taken = 0;
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-          const int before = taken + __popcll(b[c] & ((1ull << lane) - 1ull));
-          if (((b[c] >> lane) & 1ull) && before < kk) sh.idx[tt][before] = e[c];
-          taken += __popcll(b[c]);
-        }
-        if (lane < K && lane >= kk) sh.idx[tt][lane] = -1;
-      }
-      __syncthreads();
-      for (int i = tid; i < T * K; i += kSelThreads) {
-        const int tt = i / K, k = i - tt * K;
-        const int e = sh.idx[tt][k];
-        sh.psel[tt][k] = e >= 0 ? fetch_published(r.prob + (size_t)tt * E + e) : 0.f;
-      }
-      __syncthreads();
     }
-    build_masks(sh, T, E, K);
-  }
-  for (int i = tid; i < T * K; i += kSelThreads) {
-    const int tt = i / K, k = i - tt * K;
-    float s = 0.f;
-    for (int j = 0; j < K; ++j) s += sh.psel[tt][j];
-    const int e = sh.idx[tt][k];
-    r.idx[i] = e;
-    r.wgt[i] = e >= 0 ? sh.psel[tt][k] / s : 0.f;
-  }
-  const int slot = union_scan(sh, E);
-  const uint32_t tbits = slot >= 0 ? sh.tokmask[tid] : 0u;
-  if (slot >= 0) r.union_list[slot] = tid;
-  // Work lists, in union order.  An expert with at most kTokGroup positions
-  // gets one token-group record of 8 words:
-  //   [expert, positions, (t*K + k) | t << 16 per position, 0 ...];
-  // one with more gets a dense record of kDenseRec words:
-  //   [expert, positions, 0 x 6, (t*K + k) | t << 16 per position].
-  // Both counts come from one exclusive scan (groups in the low half-word).
-  const int npos = __popc(tbits);
-  const bool dense = npos > kTokGroup;
-  const int cnt = dense ? 1 << 16 : (npos + kTokGroup - 1) / kTokGroup;
-  int incl = cnt;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int o = __shfl_up(incl, s);
-    if (lane >= s) incl += o;
-  }
-  if (lane == 63) sh.wtot[wave] = incl;
-  __syncthreads();
-  int off = incl - cnt, tot = 0;
-  for (int w = 0; w < kSelThreads / 64; ++w) {
-    if (w < wave) off += sh.wtot[w];
-    tot += sh.wtot[w];
-  }
-  const int gtot = tot & 0xffff, dtot = tot >> 16;
-  if (dense) {
-    int32_t *rec = r.dlist + (off >> 16) * kDenseRec;
-    rec[0] = tid;
-    rec[1] = npos;
-    uint32_t bits = tbits;
-    // eight positions at a time: their slot reads are independent
-    for (int j0 = 0; bits; j0 += 8) {
-      int tt[8], kq[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        tt[j] = bits ? __ffs(bits) - 1 : -1;
-        bits &= bits - 1u;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kq[j] = sh.kslot[tt[j] >= 0 ? tt[j] : 0][tid];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (tt[j] >= 0) rec[8 + j0 + j] = (tt[j] * K + kq[j]) | (tt[j] << 16);
+    __syncthreads();
+    if (!s_last) {
+      // after the acquire of the flag: plain loads
+      if (tid < kMaxE / 32) s_cb[tid] = tid < (E + 31) / 32 ? r.sync.cbits[tid] : 0u;
+      if (tid == 0) s_csize = r.sync.words[3];
     }
+    __syncthreads();
+    // re-routing: the first min(K, |C|) coreset members in this position's order
+    const int es = e_sorted & (kMaxE - 1);   // (padding lanes past E hold no expert)
+    const bool member = tid < E && ((s_cb[es >> 5] >> (es & 31)) & 1u);
+    int nmem = 0;
+    const int before = block_flag_scan(member, s_wave, &nmem);
+    kk = min(min(K, s_csize), nmem);
+    if (member && before < kk) s_pick[before] = e_sorted;
+    __syncthreads();
   } else {
-    const int goff = off & 0xffff;
-    uint32_t bits = tbits;
-    int j = 0;
-    while (bits) {
-      const int tt = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      int32_t *rec = r.glist + (goff + j / kTokGroup) * 8;
-      if (j % kTokGroup == 0) {
-        rec[0] = tid;
-        rec[1] = min(kTokGroup, npos - j);
-        for (int q = 2 + min(kTokGroup, npos - j); q < 8; ++q) rec[q] = 0;
-      }
-      rec[2 + j % kTokGroup] = (tt * K + sh.kslot[tt][tid]) | (tt << 16);
-      ++j;
+    if (tid < K) s_pick[tid] = e_sorted;
+    __syncthreads();
+  }
+  // ---- final picks: weights renormalised over the picks (slot order)
+  if (tid < K) {
+    const int e = tid < kk ? s_pick[tid] : -1;
+    float ssum = 0.f;
+    for (int j = 0; j < kk; ++j) ssum += s_p[s_pick[j]];
+    r.idx[(size_t)t * K + tid] = e;
+    r.wgt[(size_t)t * K + tid] = e >= 0 ? s_p[e] / ssum : 0.f;
+    if (e >= 0) {
+      atomicOr(r.sync.mask2 + e, 1u << t);
+      atomicOr(r.sync.kslot + e * (kMaxT / 4) + (t >> 2), (uint32_t)tid << (8 * (t & 3)));
     }
   }
-  if (tid == 0) {
-    r.meta[2] = gtot;
-    r.meta[3] = dtot;
-    r.meta[0] = sh.nu;
-    r.meta[1] = sh.csize;
-    if (r.n_distinct_out) *r.n_distinct_out = sh.nu;
-    if (r.coreset_size_out) *r.coreset_size_out = sh.csize;
-    publish(done_count, 0);
-  }
+  __syncthreads();
+  if (tid == 0) s_last = count_done(r.sync.words + 2) == T - 1;
+  __syncthreads();
+  if (!s_last) return;
+  union_records(r, T, E, K, coreset, s_wave);
 }
 
 // ------------------------------------------------------------------ coreset alone
@@ -808,36 +894,38 @@ hipError_t launch_rmsnorm(int wdtype, const float *in, float *copy_out, void *ou
 int router_slices(int H) { return H / kRouterSlice; }
 
 template <class W, int NT>
-static hipError_t router_launch(const void *xhat, int32_t *zero_word, const void *w_router, float *part,
-                                int T, int H, int E, const int32_t *gate, hipStream_t s) {
+static hipError_t router_launch(const void *xhat, uint32_t *zero_base, int zero_words, const void *w_router,
+                                float *part, int T, int H, int E, const int32_t *gate, hipStream_t s) {
   typedef typename W::T WT;
   const dim3 grid((E + 15) / 16, router_slices(H));
-  router_kernel<W, NT><<<grid, 64, 0, s>>>((const WT *)xhat, zero_word, (const WT *)w_router, part, T, H, E,
-                                           gate);
+  router_kernel<W, NT><<<grid, 64, 0, s>>>((const WT *)xhat, zero_base, zero_words, (const WT *)w_router, part, T,
+                                           H, E, gate);
   return hipGetLastError();
 }
 
-hipError_t launch_router(int wdtype, const void *xhat, int32_t *zero_word, const void *w_router,
+hipError_t launch_router(int wdtype, const void *xhat, uint32_t *zero_base, int zero_words, const void *w_router,
                          float *part, int T, int H, int E, const int32_t *gate, hipStream_t s) {
   if (wdtype == 1)
-    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_word, w_router, part, T, H, E, gate, s)
-                   : router_launch<WBf16, 2>(xhat, zero_word, w_router, part, T, H, E, gate, s);
-  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_word, w_router, part, T, H, E, gate, s)
-                 : router_launch<WF32, 2>(xhat, zero_word, w_router, part, T, H, E, gate, s);
+    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
+                   : router_launch<WBf16, 2>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s);
+  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
+                 : router_launch<WF32, 2>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s);
 }
 
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
-                               int32_t *sorted_ids, int32_t *done_count, int wdtype, const void *xpk,
-                               const void *ws_gate_up, void *act_shared, int Is, hipStream_t s) {
+                               int wdtype, const void *xpk, const void *ws_gate_up, void *act_shared, int Is,
+                               hipStream_t s) {
   const int grid = T + Is / 16;
-  if (wdtype == 1) {
+  if (wdtype == 2) {
+    // 4-bit shared expert: the packed matrix behind a bf16-typed pointer
+    const SharedGU<WI4> sg = {(const bf16_t *)xpk, (const bf16_t *)ws_gate_up, (char *)act_shared, H, Is};
+    select_kernel<WI4><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
+  } else if (wdtype == 1) {
     const SharedGU<WBf16> sg = {(const bf16_t *)xpk, (const bf16_t *)ws_gate_up, (char *)act_shared, H, Is};
-    select_kernel<WBf16><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids,
-                                                      done_count, sg);
+    select_kernel<WBf16><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
   } else {
     const SharedGU<WF32> sg = {(const float *)xpk, (const float *)ws_gate_up, (char *)act_shared, H, Is};
-    select_kernel<WF32><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sorted_ids,
-                                                     done_count, sg);
+    select_kernel<WF32><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
   }
   return hipGetLastError();
 }

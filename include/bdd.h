@@ -53,8 +53,13 @@ typedef enum {
   BDD_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
 } bdd_status;
 
-/* BDD_INT4: 4-bit weight-only LM head (bdd_lmhead_pack_int4); the MoE
- * layers and the full round take BDD_F32 or BDD_BF16 only. */
+/* BDD_INT4: 4-bit weight-only matrices ([P3] 10100.com article on
+ * Clover-35B-A3B-Preview, part 03: an INT4 deployment; the pages give no
+ * format, the one read here is): two codes per byte, the low nibble the even
+ * column, a nibble n standing for n - 8, one bf16 scale per row and
+ * 128-column group, w[r][c] = (n - 8) * scale[r][c / 128].  Packed by
+ * bdd_pack_int4 (expert matrices) or bdd_lmhead_pack_int4 (LM head).  In a
+ * 4-bit MoE layer the router and the activations stay bf16. */
 typedef enum { BDD_F32 = 0, BDD_BF16 = 1, BDD_INT4 = 2 } bdd_dtype;
 
 /* Shapes of one MoE layer and the block.  T block positions, H hidden, E
@@ -67,12 +72,16 @@ typedef struct {
 } bdd_moe_dims;
 
 /* Device pointers to one MoE layer's weights ([P1] section 四).
- *   w_router    [E][H]          router logits l = xhat W_r^T + b
+ *   w_router    [E][H]          router logits l = xhat W_r^T + b (bf16 when
+ *                               wdtype is BDD_INT4)
  *   router_bias [E] fp32        may be NULL (no bias)
  *   w_gate_up   [E][2I][H]      expert e: rows 0..I-1 gate, I..2I-1 up
  *   w_down      [E][H][I]
  *   ws_gate_up  [2I_shared][H]  shared expert (ignored when I_shared == 0)
- *   ws_down     [H][I_shared] */
+ *   ws_down     [H][I_shared]
+ * With wdtype BDD_INT4 the four expert tensors are packed by bdd_pack_int4
+ * (w_gate_up: E matrices of 2I x H, w_down: E matrices of H x I, the shared
+ * expert's one each); I and I_shared must then be multiples of 128. */
 typedef struct {
   const void *w_router;
   const float *router_bias;
@@ -157,6 +166,25 @@ size_t bdd_lmhead_packed_bytes(int32_t V, int32_t H, int32_t dtype);
 bdd_status bdd_lmhead_pack(const void *w_lm, int32_t V, int32_t H, int32_t dtype, void *w_packed,
                            void *stream);
 
+/* Bytes of n_mats packed 4-bit matrices of rows x cols (0 if invalid: rows a
+ * multiple of 16, cols of 128). */
+size_t bdd_int4_packed_bytes(int32_t n_mats, int32_t rows, int32_t cols);
+
+/* Packs n_mats 4-bit weight matrices (the BDD_INT4 format) for the 4-bit
+ * expert kernels, once, at load time:
+ *   codes   device [n_mats][rows][cols/2] uint8 (byte j: columns 2j, 2j + 1)
+ *   scales  device [n_mats][rows][cols/128] bf16
+ *   packed  device out, bdd_int4_packed_bytes(n_mats, rows, cols) bytes: the
+ *           matrices one after the other, each in 16-row tiles with, per
+ *           tile and 128-column group, one KiB of codes in the order the MFMA
+ *           lanes consume them (lane li + 16 g: row li, dword kk holding the
+ *           codes of columns 32 (4 group + kk) + 8 g + e, e = 0..7, code e at
+ *           bit 4 (e / 2) + 16 (e % 2)), then the scales as [tile][group][16].
+ * Errors: BDD_ERR_INVALID_ARG (NULL pointer, non-positive size),
+ * BDD_ERR_UNSUPPORTED (rows not a multiple of 16, cols not of 128). */
+bdd_status bdd_pack_int4(const void *codes, const void *scales, int32_t n_mats, int32_t rows, int32_t cols,
+                         void *packed, void *stream);
+
 /* Packs a 4-bit weight-only LM head ([P3] 10100.com article on
  * Clover-35B-A3B-Preview, part 03, memory and quantisation: the model is
  * deployed in INT4; the pages give no format, so this one is assumed):
@@ -201,7 +229,8 @@ bdd_status bdd_lmhead_confidence_commit(const void *hhat, const void *w_packed, 
                                         int32_t *choice, int32_t *round_info, void *ws,
                                         size_t ws_bytes, void *stream);
 
-/* Workspace bytes bdd_block_denoise_round needs. */
+/* Workspace bytes bdd_block_denoise_round needs.  (With wdtype BDD_INT4 the
+ * round's LM head is a 4-bit head packed by bdd_lmhead_pack_int4.) */
 size_t bdd_round_workspace_bytes(const bdd_moe_dims *d, int32_t V);
 
 /* One full denoising round ([P1] section 三 pseudocode, one pass of the inner
@@ -275,12 +304,18 @@ void bdd_round_graph_destroy(bdd_round_graph g);
  * whole).  The mixer and its history state are not built: the caller
  * supplies each round's block input (the re-embedding stub).
  *   max_steps      rounds allowed per block (>= 1)
- *   rounds_per_read  0: all of a block's rounds are enqueued back to back and
- *                  the host reads their results once per block; k > 0: the
- *                  host reads them every k rounds.  Every round commits at
- *                  least one masked position, so at most min(max_steps, T)
- *                  rounds are enqueued; each round's kernels return at once
- *                  when an earlier round of the block has resolved it.
+ *   rounds_per_read  how the host learns that a block is resolved.  Every
+ *                  round commits at least one masked position, so at most
+ *                  min(max_steps, T) rounds run, and each round's kernels
+ *                  return at once when an earlier round of the block has
+ *                  resolved it.  0: the host stays one round ahead (it
+ *                  enqueues round r + 1, then waits for round r's info,
+ *                  copied to pinned host memory), so the GPU never waits
+ *                  for the host and at most one extra (empty) round runs per
+ *                  block; k > 0: k rounds are enqueued back to back, then
+ *                  the host reads their info (k >= max_steps: once per
+ *                  block).  The library keeps one small pinned host buffer
+ *                  and two events per calling thread for mode 0.
  *   prompt_len, max_new_tokens  the request; it is rejected (BDD_ERR_INVALID_ARG,
  *                  nothing enqueued) when prompt_len + max_new_tokens rounded
  *                  up to whole blocks exceeds 131072 tokens ([P2] "What

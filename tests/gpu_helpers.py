@@ -148,3 +148,51 @@ def commit_check(tok_before, c_ref, ch_ref, excl, c_gpu, ch_gpu, tok_after_gpu, 
                 assert tok_after_gpu[t] == ch_gpu[t], t
         assert ri_gpu[1] == 0
     return None, False
+
+
+class Int4Rows:
+    """Rows of a dequantised 4-bit matrix (codes uint8 [R][C/2], bf16 scales
+    [R][C/128]), built slice by slice in float64 (the oracle's LM head reads
+    its weight in row blocks)."""
+
+    def __init__(self, codes, scales):
+        self.codes = codes.cpu().numpy()
+        self.scales = scales.float().cpu().numpy().astype(np.float64)
+        self.shape = (self.codes.shape[0], 2 * self.codes.shape[1])
+
+    def __getitem__(self, sl):
+        return O.int4_dequantize(self.codes[sl], self.scales[sl])
+
+
+class Int4Experts:
+    """e -> (dequantised gate/up [2I][H], down [H][I]) in float64, on first use."""
+
+    def __init__(self, w):
+        self.w, self.cache = w, {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            w = self.w
+            self.cache[e] = (O.int4_dequantize(w["gu_codes"][e].cpu().numpy(), f64(w["gu_scales"][e])),
+                             O.int4_dequantize(w["dn_codes"][e].cpu().numpy(), f64(w["dn_scales"][e])))
+        return self.cache[e]
+
+
+def oracle_layer_int4(w: dict) -> dict:
+    """The oracle's view of a 4-bit layer from workloads.layer_weights_int4:
+    the router as is, every expert matrix dequantised."""
+    return {"w_router": f64(w["w_router"]), "router_bias": f64(w["router_bias"]),
+            "ws_gate_up": O.int4_dequantize(w["sgu_codes"].cpu().numpy(), f64(w["sgu_scales"])),
+            "ws_down": O.int4_dequantize(w["sdn_codes"].cpu().numpy(), f64(w["sdn_scales"])),
+            "experts": Int4Experts(w)}
+
+
+def packed_layer_int4(w: dict, device) -> dict:
+    """The library's 4-bit layer: the router as is, the expert matrices packed
+    by bdd_pack_int4."""
+    def pk(c, s):
+        return bdd.pack_int4(w[c].to(device), w[s].to(device))
+    return {"w_router": w["w_router"].to(device), "router_bias": w["router_bias"].to(device),
+            "w_gate_up": pk("gu_codes", "gu_scales"), "w_down": pk("dn_codes", "dn_scales"),
+            "ws_gate_up": pk("sgu_codes", "sgu_scales"), "ws_down": pk("sdn_codes", "sdn_scales")}

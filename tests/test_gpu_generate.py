@@ -90,7 +90,7 @@ def _compare(got, ref, nb_expect):
         assert flat[:n] == out
 
 
-@pytest.mark.parametrize("rounds_per_read", [0, 1, 3])
+@pytest.mark.parametrize("rounds_per_read", [0, 1, 3, 32])   # 32: one read per block
 def test_generate_matches_the_oracle(setup, rounds_per_read):
     plan, xr, fwd, ref = setup
     got = bdd.generate(plan, xr, max_new_tokens=NB * D.T, max_steps=STEPS, eos_token=-7,

@@ -18,23 +18,10 @@ import torch
 import block_diffusion_decode_amd as bdd
 import oracle as O
 import workloads as W
-from gpu_helpers import BAND, TAU, assert_close, commit_in_band, f64, top2_gap
+from gpu_helpers import BAND, TAU, Int4Rows, assert_close, commit_in_band, f64, top2_gap
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-
-
-class _Dequantised:
-    """Rows of the dequantised head, built slice by slice (the oracle's LM
-    head reads its weight in row blocks)."""
-
-    def __init__(self, codes, scales):
-        self.codes = codes.cpu().numpy()
-        self.scales = scales.float().cpu().numpy().astype(np.float64)
-        self.shape = (self.codes.shape[0], 2 * self.codes.shape[1])
-
-    def __getitem__(self, sl):
-        return O.int4_dequantize(self.codes[sl], self.scales[sl])
 
 
 def _dims(T, H, V):
@@ -110,7 +97,7 @@ def test_int4_pack_layout_matches_the_stated_layout():
 def test_int4_lmhead_commit_multiround(T, V, seed):
     d = _dims(T, 384, V)                        # 3 groups of 128 columns
     codes, scales = W.lm_head_int4(seed, d)
-    wl = _Dequantised(codes, scales)
+    wl = Int4Rows(codes, scales)
     R = 8
     # the first draw of planted inputs (seed counting up by 1000) whose oracle
     # resolve has no commit or argmax decision inside the margin band
@@ -163,7 +150,7 @@ def test_int4_zero_codes_and_extreme_codes():
     tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=DEV)
     conf, choice, _ = bdd.lmhead_confidence_commit(h, bdd.pack_lm_head_int4(codes, scales), tok)
     torch.cuda.synchronize()
-    c_ref, ch_ref, z = O.lm_head_confidence(f64(h), _Dequantised(codes, scales))
+    c_ref, ch_ref, z = O.lm_head_confidence(f64(h), Int4Rows(codes, scales))
     assert_close(conf.cpu().numpy(), c_ref, "conf")
     ok = top2_gap(z) >= BAND
     assert np.array_equal(choice.cpu().numpy()[ok], ch_ref[ok])
@@ -182,7 +169,7 @@ def test_int4_lmhead_full_vocabulary():
     tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=DEV)
     conf, choice, ri = bdd.lmhead_confidence_commit(h, lm, tok)
     torch.cuda.synchronize()
-    c_ref, ch_ref, z = O.lm_head_confidence(f64(h), _Dequantised(codes, scales))
+    c_ref, ch_ref, z = O.lm_head_confidence(f64(h), Int4Rows(codes, scales))
     assert_close(conf.cpu().numpy(), c_ref, "conf")
     ok = top2_gap(z) >= BAND
     assert ok.sum() >= d.T - 2

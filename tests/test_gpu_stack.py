@@ -19,8 +19,8 @@ import torch
 import block_diffusion_decode_amd as bdd
 import oracle as O
 import workloads as W
-from gpu_helpers import (BAND, assert_close, bf16_ulp, commit_check, coreset_in_band, dims_of, f64,
-                         oracle_layer, top2_gap, topk_gap)
+from gpu_helpers import (BAND, Int4Rows, assert_close, bf16_ulp, commit_check, coreset_in_band, f64,
+                         oracle_layer, oracle_layer_int4, packed_layer_int4, top2_gap, topk_gap)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -32,14 +32,10 @@ def _phase1_idx(l, K):
     return np.argsort(-l, axis=1, kind="stable")[:, :K]
 
 
-def test_stack_40_layers_zipf_coreset():
-    seed, d, top_p = 0, W.C1, 0.9
+def _run_stack(d, layers, oracle_of, lm, wl, x, top_p, wdtype):
+    """One round through the layers; every layer checked teacher-forced."""
     T, K = d.T, d.K
-    layers = [W.layer_weights(seed, l, d, device=DEV, bias="zipf", gamma=1.0) for l in range(LAYERS)]
-    x, xinfo = W.planted_round_inputs(seed, d, rounds=1, p=0.3, amp_pass=40.0, amp_fail=(14.0, 22.0),
-                                      tag="stack")
-    w_lm = W.lm_head_weight(seed, d, device=DEV, unit_rows=xinfo["unit_rows"])
-    plan = bdd.RoundPlan(dims_of(d), layers, bdd.pack_lm_head(w_lm), top_p)
+    plan = bdd.RoundPlan(bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, wdtype), layers, lm, top_p)
     tok = torch.full((T,), bdd.MASK, dtype=torch.int32, device=DEV)
     conf = torch.empty(T, dtype=torch.float32, device=DEV)
     choice = torch.empty(T, dtype=torch.int32, device=DEV)
@@ -61,7 +57,7 @@ def test_stack_40_layers_zipf_coreset():
         # two bf16 ulps, plus an absolute term for the float32 residual sum
         # (entries near zero after cancellation carry its ~1e-6 rounding)
         assert np.all(np.abs(xg - xr) <= 2 * bf16_ulp(xr) + XTOL), f"layer {l}: normalised input"
-        ol = oracle_layer(layers[l])
+        ol = oracle_of(l)
         _, info = O.moe_layer(xg, ol, K, top_p)
         g = ltk_g[l]
         cband = coreset_in_band(info["p"], _phase1_idx(info["logits"], K), top_p)
@@ -87,7 +83,6 @@ def test_stack_40_layers_zipf_coreset():
     hg = f64(hh)
     assert np.all(np.abs(hg - hr) <= 2 * bf16_ulp(hr) + XTOL), "LM-head input"
 
-    wl = f64(w_lm)
     c_ref, ch_ref, z = O.lm_head_confidence(hg, wl)
     c_gpu, ch_gpu = conf.cpu().numpy(), choice.cpu().numpy()
     assert_close(c_gpu, c_ref, "conf")
@@ -97,3 +92,29 @@ def test_stack_40_layers_zipf_coreset():
     print(f"{LAYERS} layers: distinct experts per layer {nd_g.tolist()}, layers with a band decision "
           f"{band_layers}, round_info {ri.cpu().tolist()}, commit exact {exact}, "
           f"conf range {c_gpu.min():.3f}..{c_gpu.max():.3f}")
+
+
+def test_stack_40_layers_zipf_coreset():
+    seed, d, top_p = 0, W.C1, 0.9
+    layers = [W.layer_weights(seed, l, d, device=DEV, bias="zipf", gamma=1.0) for l in range(LAYERS)]
+    x, xinfo = W.planted_round_inputs(seed, d, rounds=1, p=0.3, amp_pass=40.0, amp_fail=(14.0, 22.0),
+                                      tag="stack")
+    w_lm = W.lm_head_weight(seed, d, device=DEV, unit_rows=xinfo["unit_rows"])
+    _run_stack(d, layers, lambda l: oracle_layer(layers[l]), bdd.pack_lm_head(w_lm), f64(w_lm), x, top_p,
+               bdd.BDD_BF16)
+
+
+def test_stack_40_layers_int4_zipf_coreset():
+    """The same round with 4-bit expert weights (every routed expert and the
+    shared expert; router bf16) and the 4-bit LM head (the planted tokens'
+    rows the 4-bit rounding of the bf16 head's): about 16 GB of packed
+    weights.  The oracle runs on the dequantised weights."""
+    seed, d, top_p = 0, W.C1, 0.9
+    raw = [W.layer_weights_int4(seed, l, d, device=DEV, bias="zipf", gamma=1.0) for l in range(LAYERS)]
+    layers = [packed_layer_int4(w, DEV) for w in raw]
+    x, xinfo = W.planted_round_inputs(seed, d, rounds=1, p=0.3, amp_pass=40.0, amp_fail=(14.0, 22.0),
+                                      tag="stack")
+    codes, scales = W.lm_head_int4(seed, d, device=DEV, unit_rows=xinfo["unit_rows"])
+    lm = bdd.pack_lm_head_int4(codes, scales)
+    _run_stack(d, layers, lambda l: oracle_layer_int4(raw[l]), lm, Int4Rows(codes, scales), x, top_p,
+               bdd.BDD_INT4)

@@ -18,9 +18,13 @@ from .gen import (  # noqa: F401
     counter_normal,
     key_of,
     layer_weights,
+    layer_weights_int4,
+    int4_matrix,
+    router_weights,
     lm_head_weight,
     lm_head_rows,
     lm_head_int4,
+    quantize_int4,
     block_hidden,
     zipf_router_bias,
     lmhead_stub_inputs,

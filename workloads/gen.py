@@ -162,6 +162,20 @@ def zipf_router_bias(seed: int, layer: int, E: int, s: float = 1.1,
     return torch.from_numpy(b.astype(np.float32))
 
 
+def router_weights(seed: int, layer: int, d: Dims, dtype, device="cpu", bias: str = "flat",
+                   gamma: float = 1.0) -> dict:
+    """A layer's router weight w_router [E][H] (N(0, w_std), stored as dtype)
+    and router_bias [E] float32 (zeros, or the Zipf bias)."""
+    out = {"w_router": _normal_tensor(key_of(seed, "router", layer), (d.E, d.H), d.w_std, dtype, device)}
+    if bias == "flat":
+        out["router_bias"] = torch.zeros(d.E, dtype=torch.float32, device=device)
+    elif bias == "zipf":
+        out["router_bias"] = zipf_router_bias(seed, layer, d.E, 1.1, gamma).to(device)
+    else:
+        raise ValueError(bias)
+    return out
+
+
 def layer_weights(seed: int, layer: int, d: Dims, device="cpu",
                   bias: str = "flat", gamma: float = 1.0,
                   experts=None) -> dict:
@@ -173,14 +187,7 @@ def layer_weights(seed: int, layer: int, d: Dims, device="cpu",
     With ``experts`` given, w_gate_up / w_down hold only those experts (in
     that order) and 'experts' lists them."""
     dt = d.torch_wdtype
-    out = {}
-    out["w_router"] = _normal_tensor(key_of(seed, "router", layer), (d.E, d.H), d.w_std, dt, device)
-    if bias == "flat":
-        out["router_bias"] = torch.zeros(d.E, dtype=torch.float32, device=device)
-    elif bias == "zipf":
-        out["router_bias"] = zipf_router_bias(seed, layer, d.E, 1.1, gamma).to(device)
-    else:
-        raise ValueError(bias)
+    out = router_weights(seed, layer, d, dt, device, bias, gamma)
     ex = list(range(d.E)) if experts is None else list(experts)
     gu = torch.empty((len(ex), 2 * d.I, d.H), dtype=dt, device=device)
     dn = torch.empty((len(ex), d.H, d.I), dtype=dt, device=device)
@@ -192,6 +199,47 @@ def layer_weights(seed: int, layer: int, d: Dims, device="cpu",
     out["experts"] = ex
     out["ws_gate_up"] = _normal_tensor(key_of(seed, "shared_gate_up", layer), (2 * d.I_s, d.H), d.w_std, dt, device)
     out["ws_down"] = _normal_tensor(key_of(seed, "shared_down", layer), (d.H, d.I_s), d.w_std, dt, device)
+    return out
+
+
+def int4_matrix(key: tuple, rows: int, cols: int, std: float, device="cpu", group: int = 128):
+    """Synthetic 4-bit weight matrix [rows][cols]: (codes uint8 [rows][cols/2],
+    scales bf16 [rows][cols/group]).  Byte j of a row holds columns 2j (low
+    nibble) and 2j + 1 (high nibble).  Codes are a rounded normal, n =
+    clamp(round(2.5 z), -8, 7) + 8; scales are std / 2.5 * U(0.8, 1.2), so the
+    weights (n - 8) * scale have about the given spread.  ``key`` is a tuple
+    of names and ints naming the matrix."""
+    assert cols % group == 0
+    k_codes, k_scales = key_of(*key, "codes"), key_of(*key, "scales")
+    n = torch.empty(rows * cols, dtype=torch.uint8, device=device)
+    for s_, e_ in _ranges(0, rows * cols):
+        z = counter_normal(k_codes, e_ - s_, 1.0, device, start=s_)
+        n[s_:e_] = (torch.round(z * 2.5).clamp_(-8, 7) + 8).to(torch.uint8)
+    n = n.reshape(rows, cols // 2, 2)
+    codes = (n[..., 0] | (n[..., 1] << 4)).contiguous()
+    u = counter_uniform(k_scales, rows * (cols // group), device)
+    scales = (std / 2.5 * (0.8 + 0.4 * u)).to(torch.bfloat16).reshape(rows, cols // group)
+    return codes, scales
+
+
+def layer_weights_int4(seed: int, layer: int, d: Dims, device="cpu", bias: str = "flat",
+                       gamma: float = 1.0) -> dict:
+    """One MoE layer with 4-bit expert weights (the format int4_matrix
+    describes): the router (bf16, the same tensor layer_weights draws) and
+    bias, and per expert matrix its codes and scales:
+      gu_codes [E][2I][H/2], gu_scales [E][2I][H/128]   (rows 0..I-1 gate)
+      dn_codes [E][H][I/2],  dn_scales [E][H][I/128]
+      sgu_codes / sgu_scales, sdn_codes / sdn_scales    (the shared expert)
+    The routed experts' matrices are drawn as one stacked matrix each (expert
+    e = rows e*R .. (e+1)*R - 1)."""
+    out = router_weights(seed, layer, d, torch.bfloat16, device, bias, gamma)
+    c, sc = int4_matrix((seed, "i4_gate_up", layer), d.E * 2 * d.I, d.H, d.w_std, device)
+    out["gu_codes"], out["gu_scales"] = c.reshape(d.E, 2 * d.I, d.H // 2), sc.reshape(d.E, 2 * d.I, d.H // 128)
+    c, sc = int4_matrix((seed, "i4_down", layer), d.E * d.H, d.I, d.w_std, device)
+    out["dn_codes"], out["dn_scales"] = c.reshape(d.E, d.H, d.I // 2), sc.reshape(d.E, d.H, d.I // 128)
+    out["sgu_codes"], out["sgu_scales"] = int4_matrix((seed, "i4_shared_gate_up", layer), 2 * d.I_s, d.H,
+                                                      d.w_std, device)
+    out["sdn_codes"], out["sdn_scales"] = int4_matrix((seed, "i4_shared_down", layer), d.H, d.I_s, d.w_std, device)
     return out
 
 
@@ -222,13 +270,15 @@ def lm_head_weight(seed: int, d: Dims, device="cpu", unit_rows=()) -> torch.Tens
     return w.to(d.torch_wdtype)
 
 
-def lm_head_int4(seed: int, d: Dims, device="cpu", group: int = 128):
+def lm_head_int4(seed: int, d: Dims, device="cpu", group: int = 128, unit_rows=()):
     """Synthetic 4-bit LM head of shape [V][H]: (codes uint8 [V][H/2], scales
     bf16 [V][H/group]).  Byte j of a row holds columns 2j (low nibble) and
     2j + 1 (high nibble).  Codes are a rounded normal, n = clamp(round(2.5 z),
     -8, 7) + 8, the histogram of quantised weights; scales are
     lm_std / 2.5 * U(0.8, 1.2), so the weights the codes stand for have
-    about the bf16 head's spread."""
+    about the bf16 head's spread.  Rows in ``unit_rows`` hold instead the
+    4-bit rounding (quantize_int4) of the bf16 head's planted unit rows, so
+    inputs planted along those rows peak on the same tokens."""
     assert d.H % group == 0
     n = torch.empty(d.V * d.H, dtype=torch.uint8, device=device)
     key = key_of(seed, "lm_int4_codes")
@@ -239,7 +289,26 @@ def lm_head_int4(seed: int, d: Dims, device="cpu", group: int = 128):
     codes = (n[..., 0] | (n[..., 1] << 4)).contiguous()
     u = counter_uniform(key_of(seed, "lm_int4_scales"), d.V * (d.H // group), device)
     scales = (d.lm_std / 2.5 * (0.8 + 0.4 * u)).to(torch.bfloat16).reshape(d.V, d.H // group)
+    if len(unit_rows):
+        idx = sorted(set(int(v) for v in unit_rows))
+        rows = lm_head_rows(seed, d, idx, "cpu", unit_rows=idx).float()
+        qc, qs = quantize_int4(rows, group)
+        it = torch.tensor(idx, dtype=torch.int64, device=device)
+        codes[it] = qc.to(device)
+        scales[it] = qs.to(device)
     return codes, scales
+
+
+def quantize_int4(w: torch.Tensor, group: int = 128):
+    """Round rows w [R][C] to the 4-bit format of int4_matrix: per row and
+    group, scale s = bf16(max |w| / 7) and code n = clamp(round(w / s), -8, 7)
+    + 8 (an input-preparation step; the method only reads the codes)."""
+    R, C = w.shape
+    g = w.double().reshape(R, C // group, group)
+    s = (g.abs().amax(dim=2) / 7.0).to(torch.bfloat16)
+    sd = s.double().clamp_min(1e-30).unsqueeze(2)
+    n = (torch.round(g / sd).clamp_(-8, 7) + 8).to(torch.uint8).reshape(R, C // 2, 2)
+    return (n[..., 0] | (n[..., 1] << 4)).contiguous(), s
 
 
 def block_hidden(seed: int, d: Dims, device="cpu", tag="h") -> torch.Tensor:
