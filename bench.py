@@ -75,9 +75,11 @@ def main():
     ap.add_argument("--int4-only", action="store_true",
                     help="only measure the 4-bit LM head + commit (for a kernel trace of it alone); prints one "
                          "JSON line with the 'lmhead_int4' object")
-    ap.add_argument("--counter-run", action="store_true",
+    ap.add_argument("--counter-run", nargs="?", const="flat", default=None, choices=["flat", "zipf", "int4"],
                     help="only run 3 rounds on inputs drawn with torch.randn (a handful of kernel launches "
-                         "besides the library's), for hardware-counter collection")
+                         "besides the library's), for hardware-counter collection: one Clover layer with flat "
+                         "routing (flat), with Zipf router bias and the coreset at top_p 0.9 (zipf), or the "
+                         "latter with 4-bit experts and LM head (int4)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -118,7 +120,7 @@ def main():
         print(json.dumps({"stack_int4": stack_round(args, W.C1, dev, int4=True)}), flush=True)
         return
     if args.counter_run:
-        counter_run(d, dev)
+        counter_run(d, dev, args.counter_run)
         return
     if args.int4_only:
         print(json.dumps({"lmhead_int4": lmhead_int4(args, d, dev)}), flush=True)
@@ -469,14 +471,17 @@ def sweep(args, d1, dev, blocks=4):
         torch.cuda.empty_cache()
 
 
-def counter_run(d, dev):
+def counter_run(d, dev, mode="flat"):
     """Three rounds of the benchmark's shape on torch.randn inputs.  The bytes
     each kernel moves do not depend on the values beyond the routing (the LM
     head streams its whole weight either way), and the seeded counter
-    generator's thousands of small launches stay out of the profiled process."""
+    generator's thousands of small launches stay out of the profiled process.
+    mode: flat routing (flat); Zipf router bias with the coreset at top_p 0.9
+    (zipf); the latter with 4-bit expert matrices and LM head (int4)."""
     import torch
 
     import block_diffusion_decode_amd as bdd
+    import workloads as W
 
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -485,20 +490,38 @@ def counter_run(d, dev):
     def rnd(shape, std):
         return (torch.randn(shape, generator=g, device=dev) * std).to(bf)
 
-    layer = {"w_router": rnd((d.E, d.H), d.w_std), "router_bias": torch.zeros(d.E, device=dev),
-             "w_gate_up": rnd((d.E, 2 * d.I, d.H), d.w_std), "w_down": rnd((d.E, d.H, d.I), d.w_std),
-             "ws_gate_up": rnd((2 * d.I_s, d.H), d.w_std), "ws_down": rnd((d.H, d.I_s), d.w_std)}
-    lm = bdd.pack_lm_head(rnd((d.V, d.H), d.lm_std))
-    plan = bdd.RoundPlan(bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16), [layer], lm, 1.0, 0.95)
+    def i4(n, rows, cols, std):
+        codes = torch.randint(0, 256, (n, rows, cols // 2), generator=g, device=dev, dtype=torch.uint8)
+        scales = (torch.rand((n, rows, cols // 128), generator=g, device=dev) * 0.4 + 0.8) * (std / 2.5)
+        return bdd.pack_int4(codes, scales.to(bf))
+
+    bias = W.zipf_router_bias(0, 0, d.E).to(dev) if mode != "flat" else torch.zeros(d.E, device=dev)
+    top_p = 0.9 if mode != "flat" else 1.0
+    if mode == "int4":
+        layer = {"w_router": rnd((d.E, d.H), d.w_std), "router_bias": bias,
+                 "w_gate_up": i4(d.E, 2 * d.I, d.H, d.w_std), "w_down": i4(d.E, d.H, d.I, d.w_std),
+                 "ws_gate_up": i4(1, 2 * d.I_s, d.H, d.w_std), "ws_down": i4(1, d.H, d.I_s, d.w_std)}
+        codes = torch.randint(0, 256, (d.V, d.H // 2), generator=g, device=dev, dtype=torch.uint8)
+        scales = ((torch.rand((d.V, d.H // 128), generator=g, device=dev) * 0.4 + 0.8) * (d.lm_std / 2.5)).to(bf)
+        lm = bdd.pack_lm_head_int4(codes, scales)
+        wdt = bdd.BDD_INT4
+    else:
+        layer = {"w_router": rnd((d.E, d.H), d.w_std), "router_bias": bias,
+                 "w_gate_up": rnd((d.E, 2 * d.I, d.H), d.w_std), "w_down": rnd((d.E, d.H, d.I), d.w_std),
+                 "ws_gate_up": rnd((2 * d.I_s, d.H), d.w_std), "ws_down": rnd((d.H, d.I_s), d.w_std)}
+        lm = bdd.pack_lm_head(rnd((d.V, d.H), d.lm_std))
+        wdt = bdd.BDD_BF16
+    plan = bdd.RoundPlan(bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, wdt), [layer], lm, top_p, 0.95)
     x = torch.randn((d.T, d.H), generator=g, device=dev)
     tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=dev)
     conf = torch.empty(d.T, dtype=torch.float32, device=dev)
     choice = torch.empty(d.T, dtype=torch.int32, device=dev)
     ri = torch.empty(4, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
     for _ in range(3):
-        plan(x, tok, conf, choice, ri)
+        plan(x, tok, conf, choice, ri, None, nd)
     torch.cuda.synchronize()
-    print(json.dumps({"counter_run_rounds": 3}), flush=True)
+    print(json.dumps({"counter_run_rounds": 3, "mode": mode, "distinct_experts": int(nd.item())}), flush=True)
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "lmhead_clover_v248320_hbm_counters.md")
