@@ -7,9 +7,9 @@
 namespace bdd {
 
 constexpr int kWave = 64;
-constexpr int kMaxT = 32;        // block positions handled per call
+constexpr int kMaxT = 64;        // block positions handled per call
 constexpr int kMaxE = 256;       // routed experts
-constexpr int kActSlotPerI = 128;  // bytes per intermediate unit of a packed activation slot
+constexpr int kActSlotPerI = 4 * kMaxT;  // bytes per intermediate unit of a packed activation slot (2 planes x kMaxT entries x bf16)
 constexpr int kTokGroup = 4;     // positions per pass of the routed-expert kernels
 
 typedef uint16_t bf16_t;

@@ -177,18 +177,18 @@ template <int MT>
 constexpr int dense_down_batch() { return MT <= 2 ? 4 : 2; }
 
 // Down projection of one dense expert, W_d [H][ie], for rows h0 .. h0 + 16 MT - 1
-// (MT row tiles) and up to 32 column entries, from the expert's packed
-// activation slot (see act_unit).  Lane (li, g) names entries li and 16 + li
-// by their rows row[n] in P (-1: no entry).  The four waves split the
+// (MT row tiles) and up to 16 NT column entries, from the expert's packed
+// activation slot (see act_unit).  Lane (li, g) names entries li + 16 n by
+// their rows row[n] in P (-1: no entry).  The four waves split the
 // intermediate dimension; each issues the loads of a batch of k-steps at
 // once, stages its weights through its own quarter of `red` (MT * 8 KiB), and
 // the partial tiles are then added through all of it.  With bf16
 // weights the activations enter as bf16 high parts and residuals (two MFMA
 // passes); every activation load serves MT weight tiles.
 // P[row][h] = A_entry . W_d[h].
-template <class W, int MT>
+template <class W, int MT, int NT>
 __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict__ w, int ie,
-                                                const char *__restrict__ act, int H, const int (&row)[2], int h0,
+                                                const char *__restrict__ act, int H, const int (&row)[NT], int h0,
                                                 int wave, int lane, float *__restrict__ P, f32x4 *red) {
   typedef typename W::T WT;
   constexpr bool BF = std::is_same<W, WBf16>::value;
@@ -199,11 +199,11 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
   const int cw0 = wave * ncw;
   const rsrc_t rw = make_rsrc(w, (uint32_t)(H * ie) * sizeof(WT));
   const rsrc_t ra = make_rsrc(act, (uint32_t)ie * kActSlotPerI);
-  f32x4 acc[MT][2];   // [row tile][column tile]
+  f32x4 acc[MT][NT];   // [row tile][column tile]
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kSdSteps = dense_down_batch<MT>();
   static_assert(kSdSteps % 2 == 0, "the dense down item streams whole units of 2 k-steps");
   constexpr int UB = kSdSteps / 2;          // units per load batch
@@ -213,9 +213,10 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
   // passes each unit through its own MT * 2 KiB of `red`
   const int sr = lane >> 3, sc = lane & 7;
   const uint32_t rowa = (uint32_t)((h0 + sr) * ie) * sizeof(WT), rows8 = (uint32_t)(8 * ie) * sizeof(WT);
-  f32x4 *stage = red + wave * MT * 128;
+  // (inside the span the wave's partial tiles take afterwards, MT * NT * 64)
+  f32x4 *stage = red + wave * MT * NT * 64;
   for (int u0 = 0; u0 < nunits; u0 += UB) {
-    uint4 wa[UB][2 * MT], xa[2 * UB][2][NP];
+    uint4 wa[UB][2 * MT], xa[2 * UB][NT][NP];
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
       const bool live_u = u0 + u < nunits;
@@ -229,7 +230,7 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
         const bool live = live_u && c < ncw;
         const int C = cw0 + c;
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
           for (int q = 0; q < NP; ++q)
             xa[2 * u + h][n][q] =
@@ -252,7 +253,7 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             const uint4 *x = xa[2 * u + h][n];
@@ -264,46 +265,48 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) red[((wave * MT + m) * 2 + n) * 64 + lane] = acc[m][n];
+    for (int n = 0; n < NT; ++n) red[((wave * MT + m) * NT + n) * 64 + lane] = acc[m][n];
   __syncthreads();
-  // wave v finishes output tiles v, v + 4, ... (tile q: row tile q >> 1, column tile q & 1)
+  // wave v finishes output tiles v, v + 4, ... (tile q: row tile q / NT, column tile q % NT)
 #pragma unroll
-  for (int q0 = 0; q0 < 2 * MT; q0 += 4) {
-    const int q = q0 + wave, m = q >> 1, n = q & 1;
+  for (int q0 = 0; q0 < NT * MT; q0 += 4) {
+    const int q = q0 + wave, m = q / NT, n = q % NT;
     f32x4 v = red[q * 64 + lane];
 #pragma unroll
-    for (int u = 1; u < 4; ++u) v += red[(u * MT * 2 + q) * 64 + lane];
-    const int rw_ = row[0] + n * (row[1] - row[0]);   // value arithmetic: no runtime-indexed array
+    for (int u = 1; u < 4; ++u) v += red[(u * MT * NT + q) * 64 + lane];
+    const int rw_ = pick_n<NT>(row, n);
     if (rw_ >= 0)
       *reinterpret_cast<float4 *>(P + (size_t)rw_ * H + h0 + 16 * m + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
   }
   __syncthreads();  // `red` is free for the next item
 }
 
-// Per-lane column entries of a dense record: entries li and 16 + li.  The
+// Per-lane column entries of a dense record: entries li + 16 c, c < NT.  The
 // record is read with wave-uniform loads (scalar loads where the compiler can
 // prove nothing in the kernel wrote it yet: a workgroup's first item), and
-// each lane picks its two entries.
-__device__ __forceinline__ void dense_entries(const int32_t *rec, int lane, int &e, int &n, int (&v)[2]) {
+// each lane picks its entries.
+template <int NT>
+__device__ __forceinline__ void dense_entries(const int32_t *rec, int lane, int &e, int &n, int (&v)[NT]) {
   e = uniform(rec[0]);
   n = uniform(rec[1]);
-  int ent[kMaxT];
+  int ent[16 * NT];
 #pragma unroll
-  for (int j = 0; j < kMaxT; ++j) ent[j] = uniform(rec[8 + j]);
+  for (int j = 0; j < 16 * NT; ++j) ent[j] = uniform(rec[8 + j]);
   const int li = lane & 15;
-  v[0] = ent[0];
-  v[1] = ent[16];
 #pragma unroll
-  for (int j = 1; j < 16; ++j) {
-    v[0] = li == j ? ent[j] : v[0];
-    v[1] = li == j ? ent[16 + j] : v[1];
+  for (int c = 0; c < NT; ++c) {
+    v[c] = ent[16 * c];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) v[c] = li == j ? ent[16 * c + j] : v[c];
   }
 }
 
 // Work list: the dense experts' items (expert, 16-row tile), then the token
 // groups' items (group, 16-row tile).
-template <class W>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void expert_gateup_kernel(
+// (four column tiles double the dense items' operands: fewer waves per SIMD,
+// so they stay in registers)
+template <class W, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 : 4))) void expert_gateup_kernel(
     const typename W::T *__restrict__ xhat, const typename W::T *__restrict__ xpk,
     const typename W::T *__restrict__ wgu, RouteBufs r, float *__restrict__ A, char *__restrict__ act, int T,
     int H, int I, int Imax) {
@@ -315,17 +318,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void e
   const int items = d_items + uniform(r.meta[2]) * tiles;
   const uint32_t x_bytes = (uint32_t)(T * H) * sizeof(WT);
   const size_t eb = (size_t)2 * I * H * sizeof(WT);
-  __shared__ f32x4 red[4 * 2 * 2 * 64];
+  __shared__ f32x4 red[4 * 2 * NT * 64];
   int item = blockIdx.x;
   for (; item < d_items; item += gridDim.x) {
     const int di = item / tiles, tile = item - di * tiles;
-    int e, n, v[2];
-    dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
-    int pos[2];
+    int e, n, v[NT];
+    dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
+    int pos[NT];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
+    for (int c = 0; c < NT; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
     // slot 0 holds the shared expert
-    dense_gateup_item<W, 2>(wgu + (size_t)e * 2 * I * H, I, xpk, T, H, pos, item, tile * 16, wave, lane,
+    dense_gateup_item<W, 2, NT>(wgu + (size_t)e * 2 * I * H, I, xpk, T, H, pos, item, tile * 16, wave, lane,
                             act + (size_t)(1 + di) * Imax * kActSlotPerI, red);
   }
   int tile_next = 0;
@@ -485,8 +488,8 @@ __device__ __forceinline__ void down_pass(const Group &g, const float *__restric
 
 // Work list: the shared expert's items (32 rows each), the dense experts'
 // items (expert, 32 rows), then the token groups' items (group, 128 rows).
-template <class W>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void expert_down_kernel(const float *__restrict__ A,
+template <class W, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 : 3))) void expert_down_kernel(const float *__restrict__ A,
                                                           const char *__restrict__ act,
                                                           const typename W::T *__restrict__ wd,
                                                           const typename W::T *__restrict__ wsd,
@@ -499,20 +502,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
   const int tiles = H / (4 * kDownRowsPerWave), dtiles = H / DR;
   const int s_items = Is > 0 ? dtiles : 0;
   const int d_end = s_items + uniform(r.meta[3]) * dtiles;
-  __shared__ f32x4 red[4 * kDenseRowTiles * 2 * 64];
+  __shared__ f32x4 red[4 * kDenseRowTiles * NT * 64];
   const int items = d_end + uniform(r.meta[2]) * tiles;
   const uint32_t a_bytes = (uint32_t)(T * K) * (uint32_t)Imax * 4u;
   const size_t eb = (size_t)H * I * sizeof(WT);
   const int stride = gridDim.x;
   int item = blockIdx.x;
   for (; item < d_end; item += stride) {
-    int row[2];
+    int row[NT];
     const WT *w;
     int ie, h0, slot;
     if (item < s_items) {
       // the shared expert (slot 0): column entry j is position j, row T*K + j
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NT; ++c) {
         const int j = c * 16 + (lane & 15);
         row[c] = j < T ? T * K + j : -1;
       }
@@ -522,16 +525,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
       slot = 0;
     } else {
       const int di = (item - s_items) / dtiles;
-      int e, n, v[2];
-      dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
+      int e, n, v[NT];
+      dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) row[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
+      for (int c = 0; c < NT; ++c) row[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
       w = wd + (size_t)e * H * I;
       ie = I;
       h0 = (item - s_items - di * dtiles) * DR;
       slot = 1 + di;
     }
-    dense_down_item<W, kDenseRowTiles>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, H, row, h0, wave, lane, P,
+    dense_down_item<W, kDenseRowTiles, NT>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, H, row, h0, wave, lane, P,
                                        red);
   }
   int tile_next = 0;
@@ -576,7 +579,8 @@ __device__ __forceinline__ void group_entry(const int32_t *rec, int lane, int &r
   pos = li < ng ? (v >> 16) : -1;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void expert_gateup_i4_kernel(
+template <int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 1 : 2))) void expert_gateup_i4_kernel(
     const bf16_t *__restrict__ xpk, const char *__restrict__ wgu, RouteBufs r, float *__restrict__ A,
     char *__restrict__ act, int T, int H, int I, int Imax) {
   if (gated_off(r.gate)) return;
@@ -585,17 +589,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   const int d_items = uniform(r.meta[3]) * tiles;
   const int items = d_items + uniform(r.meta[2]) * tiles;
   const size_t mb = i4_mat_bytes(2 * I, H);
-  __shared__ f32x4 red[4 * 2 * 2 * 64];
+  __shared__ f32x4 red[4 * 2 * NT * 64];
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     if (item < d_items) {
       const int di = item / tiles, tile = item - di * tiles;
-      int e, n, v[2];
-      dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
-      int pos[2];
+      int e, n, v[NT];
+      dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
+      int pos[NT];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
+      for (int c = 0; c < NT; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
       const I4Mat w = i4_mat(wgu + (size_t)e * mb, 2 * I, H);
-      i4_gateup_item<2>(w, I, xpk, T, pos, tile * 16, wave, lane, act + (size_t)(1 + di) * Imax * kActSlotPerI,
+      i4_gateup_item<NT>(w, I, xpk, T, pos, tile * 16, wave, lane, act + (size_t)(1 + di) * Imax * kActSlotPerI,
                         nullptr, nullptr, Imax, red);
     } else {
       const int j = item - d_items;
@@ -610,7 +614,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void e
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void expert_down_i4_kernel(
+template <int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 : 3))) void expert_down_i4_kernel(
     const float *__restrict__ A, const char *__restrict__ act, const char *__restrict__ wd,
     const char *__restrict__ wsd, RouteBufs r, float *__restrict__ P, int T, int H, int K, int I, int Is,
     int Imax) {
@@ -624,16 +629,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
   const int items = d_end + uniform(r.meta[2]) * gtiles;
   const uint32_t a_bytes = (uint32_t)(T * K) * (uint32_t)Imax * 4u;
   const size_t mb = i4_mat_bytes(H, I);
+  static_assert(kI4GroupDownTiles * 2 >= kDenseRowTiles * 4, "`red` holds a dense item's tiles for four column tiles");
   __shared__ f32x4 red[4 * kI4GroupDownTiles * 2 * 64];
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     if (item < d_end) {
-      int prow[2];
+      int prow[NT];
       I4Mat w;
       int ie, h0, slot;
       if (item < s_items) {
         // the shared expert (slot 0): column entry j is position j, row T*K + j
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NT; ++c) {
           const int j = c * 16 + (lane & 15);
           prow[c] = j < T ? T * K + j : -1;
         }
@@ -643,16 +649,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void e
         slot = 0;
       } else {
         const int di = (item - s_items) / dtiles;
-        int e, n, v[2];
-        dense_entries(r.dlist + di * kDenseRec, lane, e, n, v);
+        int e, n, v[NT];
+        dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) prow[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
+        for (int c = 0; c < NT; ++c) prow[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
         w = i4_mat(wd + (size_t)e * mb, H, I);
         ie = I;
         h0 = (item - s_items - di * dtiles) * DR;
         slot = 1 + di;
       }
-      i4_down_item<kDenseRowTiles, 2>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, nullptr, nullptr, 0, Imax, H,
+      i4_down_item<kDenseRowTiles, NT>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, nullptr, nullptr, 0, Imax, H,
                                       prow, h0, wave, lane, P, red);
     } else {
       const int j = item - d_end;
@@ -680,34 +686,51 @@ int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup, boo
   return (Is > 0 ? dtiles : 0) + dense * dtiles + groups * gtiles;
 }
 
-hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
+template <int NT>
+static hipError_t gateup_launch(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
                                 const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
                                 hipStream_t s) {
   if (wdtype == 2)
-    expert_gateup_i4_kernel<<<grid, 256, 0, s>>>((const bf16_t *)xpk, (const char *)w_gate_up, r, A, (char *)act, T,
-                                                 H, I, Imax);
+    expert_gateup_i4_kernel<NT><<<grid, 256, 0, s>>>((const bf16_t *)xpk, (const char *)w_gate_up, r, A,
+                                                     (char *)act, T, H, I, Imax);
   else if (wdtype == 1)
-    expert_gateup_kernel<WBf16><<<grid, 256, 0, s>>>((const bf16_t *)xhat, (const bf16_t *)xpk,
-                                                     (const bf16_t *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
+    expert_gateup_kernel<WBf16, NT><<<grid, 256, 0, s>>>((const bf16_t *)xhat, (const bf16_t *)xpk,
+                                                         (const bf16_t *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
   else
-    expert_gateup_kernel<WF32><<<grid, 256, 0, s>>>((const float *)xhat, (const float *)xpk,
-                                                    (const float *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
+    expert_gateup_kernel<WF32, NT><<<grid, 256, 0, s>>>((const float *)xhat, (const float *)xpk,
+                                                        (const float *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
+                                const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
+                                hipStream_t s) {
+  // two 16-entry column tiles cover a block of up to 32 positions, four up to 64
+  return T > 32 ? gateup_launch<4>(wdtype, xhat, xpk, w_gate_up, r, A, act, T, H, I, Imax, grid, s)
+                : gateup_launch<2>(wdtype, xhat, xpk, w_gate_up, r, A, act, T, H, I, Imax, grid, s);
+}
+
+template <int NT>
+static hipError_t down_launch(int wdtype, const float *A, const void *act, const void *w_down, const void *ws_down,
+                              const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
+                              int grid, hipStream_t s) {
+  if (wdtype == 2)
+    expert_down_i4_kernel<NT><<<grid, 256, 0, s>>>(A, (const char *)act, (const char *)w_down, (const char *)ws_down,
+                                                   r, P, T, H, K, I, Is, Imax);
+  else if (wdtype == 1)
+    expert_down_kernel<WBf16, NT><<<grid, 256, 0, s>>>(A, (const char *)act, (const bf16_t *)w_down,
+                                                       (const bf16_t *)ws_down, r, P, T, H, K, I, Is, Imax);
+  else
+    expert_down_kernel<WF32, NT><<<grid, 256, 0, s>>>(A, (const char *)act, (const float *)w_down,
+                                                      (const float *)ws_down, r, P, T, H, K, I, Is, Imax);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_down(int wdtype, const float *A, const void *act, const void *w_down, const void *ws_down,
                               const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
                               int grid, hipStream_t s) {
-  if (wdtype == 2)
-    expert_down_i4_kernel<<<grid, 256, 0, s>>>(A, (const char *)act, (const char *)w_down, (const char *)ws_down, r, P,
-                                               T, H, K, I, Is, Imax);
-  else if (wdtype == 1)
-    expert_down_kernel<WBf16><<<grid, 256, 0, s>>>(A, (const char *)act, (const bf16_t *)w_down,
-                                                   (const bf16_t *)ws_down, r, P, T, H, K, I, Is, Imax);
-  else
-    expert_down_kernel<WF32><<<grid, 256, 0, s>>>(A, (const char *)act, (const float *)w_down,
-                                                  (const float *)ws_down, r, P, T, H, K, I, Is, Imax);
-  return hipGetLastError();
+  return T > 32 ? down_launch<4>(wdtype, A, act, w_down, ws_down, r, P, T, H, K, I, Is, Imax, grid, s)
+                : down_launch<2>(wdtype, A, act, w_down, ws_down, r, P, T, H, K, I, Is, Imax, grid, s);
 }
 
 }  // namespace bdd

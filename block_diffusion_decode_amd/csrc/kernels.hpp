@@ -10,24 +10,27 @@ namespace bdd {
 
 // Cross-workgroup state of the selection kernel (one contiguous block of
 // sel_sync_bytes(E) in the workspace, cleared by the router kernel).
+typedef unsigned long long posmask_t;   // one bit per block position (kMaxT <= 64)
+static_assert(kMaxT <= 64, "position masks are 64-bit");
 struct SelSync {
-  unsigned long long *mass_fx;  // [E] block expert mass of the first picks, units of 2^-56
-  uint32_t *mask1;              // [E] positions whose first picks include the expert
-  uint32_t *mask2;              // [E] positions whose final picks include the expert
   uint32_t *kslot;              // [E][kMaxT / 4] slot of the expert among position t's final picks (byte t % 4)
+  unsigned long long *mass_fx;  // [E] block expert mass of the first picks, units of 2^-56
+  posmask_t *mask1;             // [E] positions whose first picks include the expert
+  posmask_t *mask2;             // [E] positions whose final picks include the expert
   uint32_t *cbits;              // [8] coreset membership, published for the positions
   int32_t *words;               // [0] coreset published, [1] first count, [2] second count, [3] coreset size
 };
-inline size_t sel_sync_bytes(int E) { return (size_t)E * (8 + 4 + 4 + kMaxT) + 32 + 64; }
+// (the slot words first: 16-byte aligned rows of kMaxT bytes per expert)
+inline size_t sel_sync_bytes(int E) { return (size_t)E * (kMaxT + 8 + 8 + 8) + 32 + 64; }
 inline SelSync sel_sync_at(void *base, int E) {
   char *b = static_cast<char *>(base);
   SelSync s;
-  s.mass_fx = reinterpret_cast<unsigned long long *>(b);
-  s.mask1 = reinterpret_cast<uint32_t *>(b + (size_t)E * 8);
-  s.mask2 = reinterpret_cast<uint32_t *>(b + (size_t)E * 12);
-  s.kslot = reinterpret_cast<uint32_t *>(b + (size_t)E * 16);
-  s.cbits = reinterpret_cast<uint32_t *>(b + (size_t)E * (16 + kMaxT));
-  s.words = reinterpret_cast<int32_t *>(b + (size_t)E * (16 + kMaxT) + 32);
+  s.kslot = reinterpret_cast<uint32_t *>(b);
+  s.mass_fx = reinterpret_cast<unsigned long long *>(b + (size_t)E * kMaxT);
+  s.mask1 = reinterpret_cast<posmask_t *>(b + (size_t)E * (kMaxT + 8));
+  s.mask2 = reinterpret_cast<posmask_t *>(b + (size_t)E * (kMaxT + 16));
+  s.cbits = reinterpret_cast<uint32_t *>(b + (size_t)E * (kMaxT + 24));
+  s.words = reinterpret_cast<int32_t *>(b + (size_t)E * (kMaxT + 24) + 32);
   return s;
 }
 
@@ -119,6 +122,9 @@ hipError_t launch_pack_lm_int4(const void *codes, const void *scales, int V, int
                                hipStream_t s);
 size_t lmhead_lds_bytes(int wdtype, int T, int H);
 // Commit fused into the LM head's last workgroup (done_count must be zero).
+// A block of more than 32 positions runs the head in two passes of at most
+// 32 positions (the staged block of 64 would not fit in LDS), each writing
+// its positions' partials, then the commit as its own kernel.
 struct LmCommit {
   int32_t *done_count;
   float threshold;
@@ -138,6 +144,7 @@ hipError_t launch_block_start(int32_t *tokens, int T, int32_t *info, int words, 
 
 hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,
                          int nparts, int T, float threshold, int32_t *tokens, float *conf,
-                         int32_t *choice, int32_t *round_info, hipStream_t s);
+                         int32_t *choice, int32_t *round_info, hipStream_t s, const int32_t *gate = nullptr,
+                         int32_t *resolved_flag = nullptr);
 
 }  // namespace bdd

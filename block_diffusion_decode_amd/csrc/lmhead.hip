@@ -179,8 +179,11 @@ __global__ __launch_bounds__(1024) void commit_kernel(const float *__restrict__ 
                                                       int32_t *__restrict__ tokens,
                                                       float *__restrict__ conf,
                                                       int32_t *__restrict__ choice,
-                                                      int32_t *__restrict__ round_info) {
-  commit_block(part_m, part_s, part_i, nparts, T, threshold, tokens, conf, choice, round_info, nullptr);
+                                                      int32_t *__restrict__ round_info,
+                                                      const int32_t *__restrict__ gate,
+                                                      int32_t *__restrict__ resolved_flag) {
+  if (gated_off(gate)) return;
+  commit_block(part_m, part_s, part_i, nparts, T, threshold, tokens, conf, choice, round_info, resolved_flag);
 }
 
 // Start of a block whose rounds are all enqueued at once: every position
@@ -221,8 +224,8 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
                                                       const int32_t *__restrict__ gate,
                                                       int32_t *__restrict__ resolved_flag) {
   extern __shared__ uint4 xs[];  // [H / kChunk][16 * NT]
-  __shared__ float sm[kLmWaves][kMaxT], ssum[kLmWaves][kMaxT];
-  __shared__ int si[kLmWaves][kMaxT];
+  __shared__ float sm[kLmWaves][16 * NT], ssum[kLmWaves][16 * NT];
+  __shared__ int si[kLmWaves][16 * NT];
   constexpr int CH = W::kChunk;
   constexpr int TP = 16 * NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -589,6 +592,21 @@ static hipError_t lmhead_launch(const void *hhat, const void *w_lm, int T, int H
 hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,
                          float *part_m, float *part_s, int32_t *part_i, int grid, const LmCommit *fused,
                          hipStream_t s) {
+  if (T > 32) {
+    // two passes over the vocabulary, positions 0..31 and 32..T-1 (partials
+    // [T][grid]: the second pass writes rows 32..), then the commit
+    const LmCommit gate_only = {nullptr, 0.f, nullptr, nullptr, nullptr, nullptr, fused ? fused->gate : nullptr,
+                                nullptr};
+    const size_t es = wdtype == 0 ? 4 : 2;
+    const size_t off = (size_t)32 * grid;
+    hipError_t err = launch_lmhead(wdtype, hhat, w_lm, 32, H, V, part_m, part_s, part_i, grid, &gate_only, s);
+    if (err != hipSuccess) return err;
+    err = launch_lmhead(wdtype, static_cast<const char *>(hhat) + (size_t)32 * H * es, w_lm, T - 32, H, V,
+                        part_m + off, part_s + off, part_i + off, grid, &gate_only, s);
+    if (err != hipSuccess || !fused || !fused->done_count) return err;
+    return launch_commit(part_m, part_s, part_i, grid, T, fused->threshold, fused->tokens, fused->conf,
+                         fused->choice, fused->round_info, s, fused->gate, fused->resolved_flag);
+  }
   if (wdtype == 2)
     return T <= 16 ? lmhead_launch<WI4, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
                    : lmhead_launch<WI4, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
@@ -606,9 +624,10 @@ hipError_t launch_block_start(int32_t *tokens, int T, int32_t *info, int words, 
 
 hipError_t launch_commit(const float *part_m, const float *part_s, const int32_t *part_i,
                          int nparts, int T, float threshold, int32_t *tokens, float *conf,
-                         int32_t *choice, int32_t *round_info, hipStream_t s) {
+                         int32_t *choice, int32_t *round_info, hipStream_t s, const int32_t *gate,
+                         int32_t *resolved_flag) {
   commit_kernel<<<1, 1024, 0, s>>>(part_m, part_s, part_i, nparts, T, threshold, tokens, conf,
-                                   choice, round_info);
+                                   choice, round_info, gate, resolved_flag);
   return hipGetLastError();
 }
 

@@ -171,7 +171,7 @@ __device__ __forceinline__ void wave_argbest(float &v, int &id) {
 struct SelShared {
   int32_t idx[kMaxT][kMaxK];    // picks of each position (-1: unused slot)
   float psel[kMaxT][kMaxK];     // their softmax scores
-  uint32_t tokmask[kMaxE];      // positions that picked each expert
+  posmask_t tokmask[kMaxE];     // positions that picked each expert
   uint8_t kslot[kMaxT][kMaxE];  // slot k of expert e among position t's picks
   double mass[kMaxE];           // block expert mass
   int32_t ulist[kMaxE];         // experts with a pick, ascending id
@@ -188,13 +188,13 @@ struct SelShared {
 // Rebuilds tokmask / kslot from sh.idx (all threads; ends with a barrier).
 __device__ void build_masks(SelShared &sh, int T, int E, int K) {
   const int tid = threadIdx.x;
-  if (tid < E) sh.tokmask[tid] = 0u;
+  if (tid < E) sh.tokmask[tid] = 0ull;
   __syncthreads();
   for (int i = tid; i < T * K; i += blockDim.x) {
     const int t = i / K, k = i - t * K;
     const int e = sh.idx[t][k];
     if (e >= 0) {
-      atomicOr(&sh.tokmask[e], 1u << t);
+      atomicOr(&sh.tokmask[e], 1ull << t);
       sh.kslot[t][e] = (uint8_t)k;
     }
   }
@@ -205,7 +205,7 @@ __device__ void build_masks(SelShared &sh, int T, int E, int K) {
 // threads; ends with a barrier).  Returns the caller's slot (or -1).
 __device__ int union_scan(SelShared &sh, int E) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int flag = (tid < E && sh.tokmask[tid] != 0u) ? 1 : 0;
+  const int flag = (tid < E && sh.tokmask[tid] != 0ull) ? 1 : 0;
   int incl = flag;
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) {
@@ -239,13 +239,13 @@ __device__ void coreset_core(SelShared &sh, int T, int E, int K, float top_p) {
   if (tid < E) {
     // ascending positions, eight at a time (their slot reads are independent)
     double m = 0.0;
-    uint32_t bits = sh.tokmask[tid];
+    posmask_t bits = sh.tokmask[tid];
     while (bits) {
       int tt[8], kq[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        tt[j] = bits ? __ffs(bits) - 1 : -1;
-        bits &= bits - 1u;
+        tt[j] = bits ? __ffsll((long long)bits) - 1 : -1;
+        bits &= bits - 1ull;
       }
       // unconditional reads (row 0 stands in for a missing position, whose
       // term is then +0.0), so the sixteen reads are not serialised by branches
@@ -471,14 +471,14 @@ __device__ void coreset_step(const RouteBufs &r, int E, float top_p, int *s_wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int te = min(tid, E - 1);
   const unsigned long long m_all = r.sync.mass_fx[te];
-  const uint32_t msk_all = r.sync.mask1[te];
+  const posmask_t msk_all = r.sync.mask1[te];
   const unsigned long long m = tid < E ? m_all : 0ull;
-  const uint32_t msk = tid < E ? msk_all : 0u;
+  const posmask_t msk = tid < E ? msk_all : 0ull;
   if (tid < kMaxE / 32) s_cb[tid] = 0u;
   if (tid == 0) s_below = 0;
   int nu = 0;
-  const int slot = block_flag_scan(msk != 0u, s_wave, &nu);
-  if (msk != 0u) {
+  const int slot = block_flag_scan(msk != 0ull, s_wave, &nu);
+  if (msk != 0ull) {
     s_um[slot] = m;
     s_ue[slot] = tid;
   }
@@ -572,7 +572,7 @@ __device__ void union_records(const RouteBufs &r, int T, int E, int K, bool core
   // position would be placed in scratch memory)
   __shared__ uint32_t s_kw[kSelThreads][KW + 1];
   const int te = min(tid, E - 1);
-  const uint32_t tb_all = r.sync.mask2[te];
+  const posmask_t tb_all = r.sync.mask2[te];
 #pragma unroll
   for (int j = 0; j < KW; j += 4) {
     const uint4 v = reinterpret_cast<const uint4 *>(r.sync.kslot + (size_t)te * KW)[j / 4];
@@ -581,28 +581,28 @@ __device__ void union_records(const RouteBufs &r, int T, int E, int K, bool core
     s_kw[tid][j + 2] = v.z;
     s_kw[tid][j + 3] = v.w;
   }
-  const uint32_t tbits = tid < E ? tb_all : 0u;
+  const posmask_t tbits = tid < E ? tb_all : 0ull;
   int nu = 0;
-  const int slot = block_flag_scan(tbits != 0u, s_wave, &nu);
-  if (tbits != 0u) r.union_list[slot] = tid;
+  const int slot = block_flag_scan(tbits != 0ull, s_wave, &nu);
+  if (tbits != 0ull) r.union_list[slot] = tid;
   if (!coreset) {
     // without the coreset every expert with a pick is reported as its member
-    const unsigned long long b = __ballot(tid < E && tbits != 0u);
+    const unsigned long long b = __ballot(tid < E && tbits != 0ull);
     if (lane == 0 && 64 * wave < E) r.cs_bits[2 * wave] = (uint32_t)b;
     if (lane == 32 && 64 * wave + 32 < E) r.cs_bits[2 * wave + 1] = (uint32_t)(b >> 32);
   }
-  // group and dense-record counts: exclusive prefix by bit-sliced ballots
-  // (an expert has at most kMaxT / kTokGroup groups, bits 0..3 of its count;
-  // the dense flag is bit 16, so the block's group total stays below it)
-  const int npos = __popc(tbits);
+  // group and dense-record counts: exclusive prefix by bit-sliced ballots (an
+  // expert with a pick has one token group, bit 0, when it has at most
+  // kTokGroup positions, else one dense record, bit 16; the block's group
+  // total stays below bit 16)
+  const int npos = __popcll(tbits);
   const bool dense = npos > kTokGroup;
-  const int ng = dense ? 0 : (npos + kTokGroup - 1) / kTokGroup;
-  static_assert(kMaxT / kTokGroup < 16, "group counts fit four bits");
+  const int ng = (npos > 0 && !dense) ? 1 : 0;
   const int cnt = ng | (dense ? 1 << 16 : 0);
   int pre = 0, wtot = 0;
 #pragma unroll
-  for (int bit = 0; bit < 5; ++bit) {
-    const int sh = bit < 4 ? bit : 16;
+  for (int bit = 0; bit < 2; ++bit) {
+    const int sh = bit == 0 ? 0 : 16;
     const unsigned long long bb = __ballot((cnt >> sh) & 1);
     pre += __popcll(bb & lanes_below(lane)) << sh;
     wtot += __popcll(bb) << sh;
@@ -621,18 +621,18 @@ __device__ void union_records(const RouteBufs &r, int T, int E, int K, bool core
     int32_t *rec = r.dlist + (off >> 16) * kDenseRec;
     rec[0] = tid;
     rec[1] = npos;
-    uint32_t bits = tbits;
+    posmask_t bits = tbits;
     for (int j = 0; bits; ++j) {
-      const int t = __ffs(bits) - 1;
-      bits &= bits - 1u;
+      const int t = __ffsll((long long)bits) - 1;
+      bits &= bits - 1ull;
       rec[8 + j] = (t * K + kslot_of(t)) | (t << 16);
     }
   } else if (npos > 0) {
     const int g0 = off & 0xffff;
-    uint32_t bits = tbits;
+    posmask_t bits = tbits;
     for (int j = 0; bits; ++j) {
-      const int t = __ffs(bits) - 1;
-      bits &= bits - 1u;
+      const int t = __ffsll((long long)bits) - 1;
+      bits &= bits - 1ull;
       int32_t *rec = r.glist + (g0 + j / kTokGroup) * 8;
       if (j % kTokGroup == 0) {
         rec[0] = tid;
@@ -652,7 +652,7 @@ __device__ void union_records(const RouteBufs &r, int T, int E, int K, bool core
   }
 }
 
-template <class W>
+template <class W, int NT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const float *__restrict__ bias,
                                                              int KS, int T, int E, int K, float top_p,
                                                              SharedGU<W> sg) {
@@ -667,19 +667,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   const int t = blockIdx.x;
   if (gated_off(r.gate)) return;
   if (t >= T) {
-    __shared__ f32x4 red[4 * 2 * 2 * 64];
+    __shared__ f32x4 red[4 * 2 * NT * 64];
     // column entry j is position j
-    int pos[2];
+    int pos[NT];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < NT; ++n) {
       const int j = n * 16 + (lane & 15);
       pos[n] = j < T ? j : -1;
     }
     if constexpr (std::is_same<W, WI4>::value)
-      i4_gateup_item<2>(i4_mat(sg.wsgu, 2 * sg.Is, sg.H), sg.Is, sg.xpk, T, pos, (t - T) * 16, wave, lane, sg.act,
-                        nullptr, nullptr, 0, red);
+      i4_gateup_item<NT>(i4_mat(sg.wsgu, 2 * sg.Is, sg.H), sg.Is, sg.xpk, T, pos, (t - T) * 16, wave, lane, sg.act,
+                         nullptr, nullptr, 0, red);
     else
-      dense_gateup_item<W, kSgSteps>(sg.wsgu, sg.Is, sg.xpk, T, sg.H, pos, t - T, (t - T) * 16, wave, lane, sg.act,
+      dense_gateup_item<W, kSgSteps, NT>(sg.wsgu, sg.Is, sg.xpk, T, sg.H, pos, t - T, (t - T) * 16, wave, lane, sg.act,
                                      red);
     return;
   }
@@ -726,7 +726,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
     // contribute the first picks to the block mass and the position masks
     if (tid < K) {
       atomicAdd(r.sync.mass_fx + e_sorted, (unsigned long long)((double)s_p[e_sorted] * kMassScale));
-      atomicOr(r.sync.mask1 + e_sorted, 1u << t);
+      atomicOr(r.sync.mask1 + e_sorted, 1ull << t);
     }
     __syncthreads();
     if (tid == 0) s_last = count_done(r.sync.words + 1) == T - 1;
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
     r.idx[(size_t)t * K + tid] = e;
     r.wgt[(size_t)t * K + tid] = e >= 0 ? s_p[e] / ssum : 0.f;
     if (e >= 0) {
-      atomicOr(r.sync.mask2 + e, 1u << t);
+      atomicOr(r.sync.mask2 + e, 1ull << t);
       atomicOr(r.sync.kslot + e * (kMaxT / 4) + (t >> 2), (uint32_t)tid << (8 * (t & 3)));
     }
   }
@@ -906,28 +906,39 @@ static hipError_t router_launch(const void *xhat, uint32_t *zero_base, int zero_
 hipError_t launch_router(int wdtype, const void *xhat, uint32_t *zero_base, int zero_words, const void *w_router,
                          float *part, int T, int H, int E, const int32_t *gate, hipStream_t s) {
   if (wdtype == 1)
-    return T <= 16 ? router_launch<WBf16, 1>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
-                   : router_launch<WBf16, 2>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s);
-  return T <= 16 ? router_launch<WF32, 1>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
-                 : router_launch<WF32, 2>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s);
+    return T <= 16   ? router_launch<WBf16, 1>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
+           : T <= 32 ? router_launch<WBf16, 2>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
+                     : router_launch<WBf16, 4>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s);
+  return T <= 16   ? router_launch<WF32, 1>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
+         : T <= 32 ? router_launch<WF32, 2>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s)
+                   : router_launch<WF32, 4>(xhat, zero_base, zero_words, w_router, part, T, H, E, gate, s);
+}
+
+template <int NT>
+static hipError_t select_launch(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
+                                int wdtype, const void *xpk, const void *ws_gate_up, void *act_shared, int Is,
+                                hipStream_t s) {
+  const int grid = T + Is / 16;
+  if (wdtype == 2) {
+    // 4-bit shared expert: the packed matrix behind a bf16-typed pointer
+    const SharedGU<WI4> sg = {(const bf16_t *)xpk, (const bf16_t *)ws_gate_up, (char *)act_shared, H, Is};
+    select_kernel<WI4, NT><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
+  } else if (wdtype == 1) {
+    const SharedGU<WBf16> sg = {(const bf16_t *)xpk, (const bf16_t *)ws_gate_up, (char *)act_shared, H, Is};
+    select_kernel<WBf16, NT><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
+  } else {
+    const SharedGU<WF32> sg = {(const float *)xpk, (const float *)ws_gate_up, (char *)act_shared, H, Is};
+    select_kernel<WF32, NT><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
                                int wdtype, const void *xpk, const void *ws_gate_up, void *act_shared, int Is,
                                hipStream_t s) {
-  const int grid = T + Is / 16;
-  if (wdtype == 2) {
-    // 4-bit shared expert: the packed matrix behind a bf16-typed pointer
-    const SharedGU<WI4> sg = {(const bf16_t *)xpk, (const bf16_t *)ws_gate_up, (char *)act_shared, H, Is};
-    select_kernel<WI4><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
-  } else if (wdtype == 1) {
-    const SharedGU<WBf16> sg = {(const bf16_t *)xpk, (const bf16_t *)ws_gate_up, (char *)act_shared, H, Is};
-    select_kernel<WBf16><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
-  } else {
-    const SharedGU<WF32> sg = {(const float *)xpk, (const float *)ws_gate_up, (char *)act_shared, H, Is};
-    select_kernel<WF32><<<grid, kSelThreads, 0, s>>>(r, bias, router_slices(H), T, E, K, top_p, sg);
-  }
-  return hipGetLastError();
+  // the shared expert's items cover the block in 16-entry column tiles
+  return T > 32 ? select_launch<4>(r, bias, T, H, E, K, top_p, wdtype, xpk, ws_gate_up, act_shared, Is, s)
+                : select_launch<2>(r, bias, T, H, E, K, top_p, wdtype, xpk, ws_gate_up, act_shared, Is, s);
 }
 
 hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, int K, float top_p,

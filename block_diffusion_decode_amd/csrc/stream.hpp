@@ -91,11 +91,23 @@ __device__ __forceinline__ uint32_t act_unit(int C, int plane, int e, int planes
 }
 
 constexpr int kSgSteps = 4;   // k-steps per load batch of the shared gate/up beside selection
-template <int STEPS>
+template <int STEPS, int NT>
 struct DgBufs {
   uint4 a[STEPS / 2][4];   // [unit of 2 k-steps][gate rows 0-7, 8-15, up rows 0-7, 8-15]
-  uint4 b[STEPS][2];       // [k-step][column tile]
+  uint4 b[STEPS][NT];      // [k-step][column tile]
 };
+
+// v[n] for a compile-time n range and a runtime n, by value arithmetic (a
+// runtime index into a register array would leave it in memory, which the
+// compiler places in LDS addressed through the dispatch packet: a slow first
+// load in every workgroup).
+template <int NT>
+__device__ __forceinline__ int pick_n(const int (&v)[NT], int n) {
+  int r = v[0];
+#pragma unroll
+  for (int j = 1; j < NT; ++j) r = n == j ? v[j] : r;
+  return r;
+}
 
 // Weight staging of the dense gate/up item.  A unit is 2 k-steps (8 chunks of
 // 16 bytes, 128 bytes of a row): one load instruction reads 8 rows of it
@@ -108,17 +120,17 @@ __device__ __forceinline__ int stage_swz(int r) { return (r & 7) ^ ((r >> 3) & 1
 __device__ __forceinline__ int stage_slot(int q, int r, int c) { return (q * 16 + r) * 8 + (c ^ stage_swz(r)); }
 
 // Gate/up rows i0 .. i0 + 15 (and ie + i0 ..) of one expert, W_gu [2 ie][H],
-// for up to 32 column entries (two tiles of 16).  Lane (li, g) names entries
-// li and 16 + li by their positions pos[n] (-1: no entry).  The four waves
-// split the hidden dimension, each starting its units `rot` units in (so
-// concurrent items spread their reads of the packed block); each wave stages
-// its weights through its own quarter of `red` (16 KiB) and afterwards adds
-// its partial tiles through all of it; waves 0 and 1 finish column tiles 0
-// and 1 and store silu(gate) * up into the packed activation slot.
-template <class W, int STEPS>
+// for up to 16 NT column entries (NT tiles of 16).  Lane (li, g) names entries
+// li + 16 n by their positions pos[n] (-1: no entry).  The four waves split
+// the hidden dimension, each starting its units `rot` units in (so concurrent
+// items spread their reads of the packed block); each wave stages its
+// weights through 4 KiB of its own span of `red` (4 * 2 * NT * 64 f32x4)
+// and afterwards adds its partial tiles through all of it; wave n < NT finishes
+// column tile n and stores silu(gate) * up into the packed activation slot.
+template <class W, int STEPS, int NT>
 __device__ __forceinline__ void dense_gateup_item(const typename W::T *__restrict__ w, int ie,
                                                   const typename W::T *__restrict__ xpk, int T, int H,
-                                                  const int (&pos)[2], int rot, int i0, int wave, int lane,
+                                                  const int (&pos)[NT], int rot, int i0, int wave, int lane,
                                                   char *__restrict__ act, f32x4 *red) {
   typedef typename W::T WT;
   constexpr int CH = W::kChunk;
@@ -137,13 +149,16 @@ __device__ __forceinline__ void dense_gateup_item(const typename W::T *__restric
   // wave-uniform offsets of gate rows 8-15 and of the up rows (scalar offsets;
   // an out-of-range vector offset still returns zeros)
   const uint32_t rows8 = (uint32_t)(8 * H) * sizeof(WT), upo = (uint32_t)(ie * H) * sizeof(WT);
-  f32x4 *stage = red + wave * 256;
-  f32x4 acc[2][2];   // [gate, up][column tile]
+  // the wave's staging area (256 f32x4) lies inside the span its partial
+  // tiles take in `red` afterwards (2 * NT * 64), so no other wave's
+  // accumulator store can land on a unit still being staged
+  f32x4 *stage = red + wave * 2 * NT * 64;
+  f32x4 acc[2][NT];   // [gate, up][column tile]
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int bt, DgBufs<STEPS> &b) {
+    for (int n = 0; n < NT; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int bt, DgBufs<STEPS, NT> &b) {
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
       const int us = UB * bt + u;
@@ -163,13 +178,13 @@ __device__ __forceinline__ void dense_gateup_item(const typename W::T *__restric
         const int c = 8 * ur + 4 * h + g;
         const bool live = live_u && c < ncw;
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < NT; ++n)
           b.b[2 * u + h][n] =
               buf_ld16(rx, live && pos[n] >= 0 ? xpack_unit(cw0 + c, pos[n], T) * 16u : kOutOfRange, 0);
       }
     }
   };
-  auto step = [&](int, const DgBufs<STEPS> &b) {
+  auto step = [&](int, const DgBufs<STEPS, NT> &b) {
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
       // Lanes read what other lanes of the wave wrote: a wave's LDS accesses
@@ -190,30 +205,27 @@ __device__ __forceinline__ void dense_gateup_item(const typename W::T *__restric
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-          for (int n = 0; n < 2; ++n) acc[q][n] = mfma_chunk<W>(a[h][q], b.b[2 * u + h][n], acc[q][n]);
+          for (int n = 0; n < NT; ++n) acc[q][n] = mfma_chunk<W>(a[h][q], b.b[2 * u + h][n], acc[q][n]);
     }
   };
-  DgBufs<STEPS> b0, b1;
+  DgBufs<STEPS, NT> b0, b1;
   pipeline((nunits + UB - 1) / UB, b0, b1, load, step);
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) red[((wave * 2 + q) * 2 + n) * 64 + lane] = acc[q][n];
+    for (int n = 0; n < NT; ++n) red[((wave * 2 + q) * NT + n) * 64 + lane] = acc[q][n];
   __syncthreads();
-  if (wave < 2) {
+  if (wave < NT) {
     // wave n finishes column tile n: rows i0 + 4g + r, entry 16n + li
     const int n = wave;
-    f32x4 gt = red[n * 64 + lane], up = red[(2 + n) * 64 + lane];
+    f32x4 gt = red[n * 64 + lane], up = red[(NT + n) * 64 + lane];
 #pragma unroll
     for (int v = 1; v < 4; ++v) {
-      const f32x4 a = red[((v * 2 + 0) * 2 + n) * 64 + lane], b = red[((v * 2 + 1) * 2 + n) * 64 + lane];
+      const f32x4 a = red[((v * 2 + 0) * NT + n) * 64 + lane], b = red[((v * 2 + 1) * NT + n) * 64 + lane];
       gt += a;
       up += b;
     }
-    // (value arithmetic, not pos[n]: a runtime index would leave the array in
-    // memory, which the compiler places in LDS addressed through the dispatch
-    // packet, a slow first load in every workgroup)
-    const int my_pos = pos[0] + (n & 1) * (pos[1] - pos[0]);
+    const int my_pos = pick_n<NT>(pos, n);
     if (my_pos >= 0) {
       float o[4];
 #pragma unroll

@@ -27,10 +27,12 @@
  *     launch failure returns BDD_ERR_HIP.  bdd_last_error() describes the
  *     last failure of the calling thread.  No exception crosses the ABI.
  *   - MASK is -1 and is never a vocabulary candidate.
- *   - Supported shapes: 1 <= T <= 32; 1 <= K <= min(E, 32); E <= 256; H a
+ *   - Supported shapes: 1 <= T <= 64; 1 <= K <= min(E, 32); E <= 256; H a
  *     multiple of 128 for the MoE layer (of 32 for the LM head alone); I,
  *     I_shared multiples of 32; H <= 2048 for the LM head when T > 16 (the
- *     block's normalised hidden states are kept in the 160 KiB LDS of one CU).
+ *     block's normalised hidden states are kept in the 160 KiB LDS of one CU;
+ *     a block of more than 32 positions is read in two passes of at most 32,
+ *     so the LM head streams its weight twice).
  */
 #ifndef BDD_H
 #define BDD_H

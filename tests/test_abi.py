@@ -51,9 +51,11 @@ def test_workspace_queries():
     assert m >= 32 * 8 * (512 + 2048) * 4
     assert bdd.round_workspace_bytes(d, 248320) > m
     assert bdd.lmhead_workspace_bytes(32, 2048, 248320) > 0
-    bad = bdd.MoEDims(33, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    assert bdd.moe_workspace_bytes(bdd.MoEDims(64, 2048, 256, 8, 512, 512, bdd.BDD_BF16)) > m
+    bad = bdd.MoEDims(65, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
     assert bdd.moe_workspace_bytes(bad) == 0
     assert bdd.lmhead_workspace_bytes(0, 2048, 10) == 0
+    assert bdd.lmhead_workspace_bytes(65, 2048, 10) == 0
 
 
 def _call_moe(d):
@@ -66,7 +68,7 @@ def _call_moe(d):
 
 @pytest.mark.parametrize("dims,status", [
     ((0, 256, 16, 4, 128, 128, 0), -1),       # T < 1
-    ((33, 256, 16, 4, 128, 128, 0), -2),      # T > 32
+    ((65, 256, 16, 4, 128, 128, 0), -2),      # T > 64
     ((8, 256, 16, 17, 128, 128, 0), -1),      # K > E
     ((8, 250, 16, 4, 128, 128, 0), -2),       # H not a multiple of 128
     ((8, 288, 16, 4, 128, 128, 0), -2),       # H multiple of 32, not of 128
@@ -181,7 +183,7 @@ def test_noalloc_round_rejects_dims_beyond_its_scratch():
     assert bdd.round_workspace_bytes(big, 1000) > bdd.NOALLOC_SCRATCH_BYTES
     assert L.bdd_block_denoise_round_noalloc(*args(big, 1000)) == -2
     assert b"static scratch" in L.bdd_last_error()
-    bad = bdd.MoEDims(33, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
+    bad = bdd.MoEDims(65, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
     assert L.bdd_block_denoise_round_noalloc(*args(bad, 1000)) == -2
     clover = bdd.MoEDims(32, 2048, 256, 8, 512, 512, bdd.BDD_BF16)
     assert 0 < bdd.round_workspace_bytes(clover, 248320) <= bdd.NOALLOC_SCRATCH_BYTES

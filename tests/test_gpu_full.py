@@ -2,6 +2,8 @@
 intermediate 512, vocab 248320, block 32), in the launch configuration the
 benchmark times, against the CPU oracle."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -21,11 +23,14 @@ def _phase1_idx(l, K):
     return np.argsort(-l, axis=1, kind="stable")[:, :K]
 
 
-@pytest.mark.parametrize("bias,top_p", [("flat", 1.0), ("zipf", 1.0), ("zipf", 0.9), ("zipf", 0.7)])
-def test_moe_layer_full_shape(bias, top_p):
-    """One Clover-shaped layer against the oracle.  With a coreset, a draw whose
-    top-K or coreset decision falls inside the margin band is replaced by the
-    next seed (the decision would be legitimately ambiguous)."""
+@pytest.mark.parametrize("bias,top_p,T", [("flat", 1.0, 32), ("zipf", 1.0, 32), ("zipf", 0.9, 32), ("zipf", 0.7, 32),
+                                          ("flat", 1.0, 64), ("zipf", 0.9, 64)])
+def test_moe_layer_full_shape(bias, top_p, T):
+    """One Clover-shaped layer against the oracle (block 32, and block 64:
+    four 16-position column tiles in the dense items).  With a coreset, a draw
+    whose top-K or coreset decision falls inside the margin band is replaced
+    by the next seed (the decision would be legitimately ambiguous)."""
+    C1 = W.C1 if T == 32 else dataclasses.replace(W.C1, name=f"clover_layer_block{T}", T=T)
     for seed in range(8):
         layer = W.layer_weights(seed, 0, C1, device=DEV, bias=bias, gamma=1.0)
         h = W.block_hidden(seed, C1, device=DEV)

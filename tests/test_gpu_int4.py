@@ -93,7 +93,8 @@ def test_int4_pack_layout_matches_the_stated_layout():
     assert np.array_equal(got[code_bytes:].view(np.uint16), ws.ravel())
 
 
-@pytest.mark.parametrize("T,V,seed", [(7, 5003, 0), (32, 5003, 1), (1, 4099, 2), (16, 16, 3)])
+@pytest.mark.parametrize("T,V,seed", [(7, 5003, 0), (32, 5003, 1), (1, 4099, 2), (16, 16, 3), (64, 5003, 4),
+                                      (40, 4099, 5)])
 def test_int4_lmhead_commit_multiround(T, V, seed):
     d = _dims(T, 384, V)                        # 3 groups of 128 columns
     codes, scales = W.lm_head_int4(seed, d)

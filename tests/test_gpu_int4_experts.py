@@ -12,6 +12,8 @@ bdd_pack_int4.  Tolerances are those of the bf16 layers.  Each draw is
 redrawn on the CPU until no routing or coreset decision lies inside a margin
 band, then routing, coreset, union and y are all compared."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -77,13 +79,15 @@ SMALL = W.Dims("i4_small", T=13, H=384, E=40, K=6, I=256, I_s=128, V=5003, wdtyp
                lm_std=384 ** -0.5)
 
 
-@pytest.mark.parametrize("bias,top_p,force", [("flat", 1.0, False), ("zipf", 0.7, False), ("flat", 1.0, True),
-                                              ("zipf", 0.9, True)])
-def test_int4_layer_small(bias, top_p, force):
+@pytest.mark.parametrize("bias,top_p,force,T", [("flat", 1.0, False, 13), ("zipf", 0.7, False, 13),
+                                                ("flat", 1.0, True, 13), ("zipf", 0.9, True, 13),
+                                                ("flat", 1.0, True, 64), ("zipf", 0.9, False, 50)])
+def test_int4_layer_small(bias, top_p, force, T):
     # hidden 384 (3 groups of 128: the waves' group shares are uneven), I 256,
     # I_s 128; `force` sends every position to experts 0..2 (dense experts
-    # with all 13 positions beside token groups)
-    d = SMALL
+    # with all T positions beside token groups); blocks of 50 and 64 positions
+    # take four column tiles
+    d = SMALL if T == SMALL.T else dataclasses.replace(SMALL, name=f"i4_small_block{T}", T=T)
     for s in range(3, 20003, 1000):
         w = W.layer_weights_int4(s, 0, d, bias=bias)
         if force:

@@ -112,21 +112,31 @@ def test_moe_forward_tiny_fp32(seed):
     assert nb == 0 and not gb
 
 
-@pytest.mark.parametrize("T,top_p", [(4, 1.0), (5, 1.0), (16, 1.0), (17, 1.0), (32, 1.0), (32, 0.7), (13, 0.7)])
+@pytest.mark.parametrize("T,top_p", [(4, 1.0), (5, 1.0), (16, 1.0), (17, 1.0), (32, 1.0), (32, 0.7), (13, 0.7),
+                                     (33, 1.0), (48, 0.7), (64, 1.0), (64, 0.7)])
 def test_moe_forward_dense_experts(T, top_p):
     # a large bias on experts 0..2 sends every position to them: experts with
     # exactly T positions (token-group path at T <= 4, one dense column tile at
-    # T <= 16, two above), next to the other picks' mix of groups and dense
-    # experts; at top_p 0.7 the coreset keeps only the forced experts
+    # T <= 16, two up to 32, three or four up to 64), next to the other picks'
+    # mix of groups and dense experts; at top_p 0.7 the coreset keeps only the
+    # forced experts.  The first seed from 10 (counting up by 1000) with no
+    # decision in a margin band is used.
     d = W.Dims(f"forced{T}", T=T, H=256, E=40, K=6, I=96, I_s=64, V=16, wdtype="bf16", w_std=0.05,
                lm_std=0.06)
-    layer = W.layer_weights(10, 0, d, device=DEV, bias="flat")   # seed 10: no decision in a margin band
-    layer["router_bias"][:3] = 10.0
-    h = W.block_hidden(10, d, device=DEV)
-    out = bdd.moe_block_forward(dims_of(d), layer, h, top_p)
+    for s in range(10, 40010, 1000):
+        layer = W.layer_weights(s, 0, d, device="cpu", bias="flat")
+        layer["router_bias"][:3] = 10.0
+        h = W.block_hidden(s, d)
+        xh = O.bf16_round(O.rmsnorm(f64(h)))
+        y_ref, info = O.moe_layer(xh, oracle_layer(layer), d.K, top_p)
+        band_tok, glob = _moe_band(d, info, top_p)
+        if not (glob or band_tok.any()):
+            break
+    else:
+        pytest.fail("no seed with every decision outside the margin band")
+    layer = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in layer.items()}
+    out = bdd.moe_block_forward(dims_of(d), layer, h.to(DEV), top_p)
     torch.cuda.synchronize()
-    xh = O.bf16_round(O.rmsnorm(f64(h)))
-    y_ref, info = O.moe_layer(xh, oracle_layer(layer), d.K, top_p)
     nb, gb = _check_moe(d, out, y_ref, info, xh, top_p)
     assert not gb and nb == 0
     n_e = np.bincount(np.asarray(info["idx"]).ravel()[np.asarray(info["idx"]).ravel() >= 0], minlength=d.E)
@@ -233,11 +243,14 @@ def _clear_lm_resolve(h, wl, tau, rounds):
     return True
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt,T", [("bf16", 7), ("f32", 7), ("bf16", 64), ("f32", 45)])
 @pytest.mark.parametrize("seed", [0, 1])
-def test_lmhead_commit_multiround_small(dt, seed):
-    d = _lm_dims(dt)
-    R = 8
+def test_lmhead_commit_multiround_small(dt, T, seed):
+    # T above 32: two passes of the head over position halves, then the commit
+    d = _lm_dims(dt, T=T)
+    # enough rounds for the block to resolve: a masked position passes with
+    # probability 0.3 per round (plus the forced commit)
+    R = 8 if T <= 8 else 24
     # conf = 0.95 sits near logit 12 at V=5003: passing peaks 14.5-16.5, failing 6-10;
     # a draw with a decision inside the margin band is replaced by the next seed
     for s in range(seed, seed + 20000, 1000):
@@ -356,6 +369,12 @@ ROUND_CASES = {
     # (failing amplitudes spread so that confidences straddle the threshold)
     "bf16_2layers_coreset_tau0.8": (None, 2, "zipf", 0.7, (40.0, (6.0, 16.0)), 0.8),
     "bf16_2layers_coreset_tau0.99": (None, 2, "zipf", 0.9, (40.0, (8.0, 24.0)), 0.99),
+    # blocks of 64 and of 45 positions (four column tiles, two LM-head passes)
+    "bf16_block64_2layers_coreset": (W.Dims("small_bf16_block64", T=64, H=256, E=40, K=6, I=96, I_s=64, V=5003,
+                                            wdtype="bf16", w_std=0.05, lm_std=256 ** -0.5),
+                                     2, "zipf", 0.7, (40.0, (4.0, 9.0)), 0.95),
+    "f32_block45_1layer": (W.Dims("tiny_fp32_block45", T=45, H=256, E=16, K=4, I=128, I_s=128, V=1024,
+                                  wdtype="f32", w_std=0.02, lm_std=0.02), 1, "flat", 1.0, (32.0, (3.0, 7.0)), 0.95),
 }
 
 
