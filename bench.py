@@ -70,7 +70,7 @@ def main():
     ap.add_argument("--int4-stack-only", type=int, default=0, metavar="L",
                     help="only run the 4-bit L-layer stack measurement; prints one JSON line with 'stack_int4'")
     ap.add_argument("--sweep", action="store_true",
-                    help="only run the block-size / threshold sweep (T in 8, 16, 32; threshold 0.8 .. 0.99) of "
+                    help="only run the block-size / threshold sweep (T in 8, 16, 32, 64; threshold 0.8 .. 0.99) of "
                          "block resolves on the round stub; prints one JSON line per (T, threshold)")
     ap.add_argument("--int4-only", action="store_true",
                     help="only measure the 4-bit LM head + commit (for a kernel trace of it alone); prints one "
@@ -403,7 +403,7 @@ def sweep(args, d1, dev, blocks=4):
     import block_diffusion_decode_amd as bdd
     import workloads as W
 
-    for T in (8, 16, 32):
+    for T in (8, 16, 32, 64):
         d = dataclasses.replace(d1, name=f"sweep_T{T}", T=T)
         dims = bdd.MoEDims(d.T, d.H, d.E, d.K, d.I, d.I_s, bdd.BDD_BF16)
         layer = W.layer_weights(args.seed, 0, d, device=dev)
