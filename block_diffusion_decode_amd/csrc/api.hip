@@ -116,7 +116,7 @@ bdd_status check_dims(const bdd_moe_dims *d) {
 }
 
 struct MoePlan {
-  size_t logits, idx, wgt, meta, ulist, glist, dlist, bits, mass, xhat, xpk, A, act, P;
+  size_t logits, idx, wgt, meta, bits, mass, xhat, xpk, A, act, P;
   size_t sync;
   size_t end;
 };
@@ -130,9 +130,6 @@ MoePlan plan_moe(const bdd_moe_dims &d, size_t base) {
   p.idx = take(T * K * 4);
   p.wgt = take(T * K * 4);
   p.meta = take(64);
-  p.ulist = take(E * 4);
-  p.glist = take((size_t)expert_groups_max(d.T, d.E, d.K) * 8 * 4);
-  p.dlist = take((size_t)(expert_dense_max(d.T, d.E, d.K) + 1) * kDenseRec * 4);
   p.bits = take(32);
   p.mass = take(E * 4);
   p.xhat = take(T * H * esize(d.wdtype));
@@ -205,14 +202,12 @@ RouteBufs route_bufs(void *ws, const MoePlan &p) {
   r.idx = at<int32_t>(ws, p.idx);
   r.wgt = at<float>(ws, p.wgt);
   r.meta = at<int32_t>(ws, p.meta);
-  r.union_list = at<int32_t>(ws, p.ulist);
-  r.glist = at<int32_t>(ws, p.glist);
-  r.dlist = at<int32_t>(ws, p.dlist);
   r.cs_bits = at<uint32_t>(ws, p.bits);
   r.mass = at<float>(ws, p.mass);
   r.n_distinct_out = nullptr;
   r.coreset_size_out = nullptr;
   r.gate = nullptr;
+  r.coreset = 0;
   return r;
 }
 
@@ -230,6 +225,7 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
   float *A = at<float>(ws, p.A), *P = at<float>(ws, p.P);
   void *xpk = at<void>(ws, p.xpk), *act = at<void>(ws, p.act);
   r.sync = sel_sync_at(at<void>(ws, p.sync), E);
+  r.coreset = top_p < 1.0f ? 1 : 0;
   const int adt = act_dtype(d.wdtype);
   if (h_in) LAUNCH("rmsnorm", s, launch_rmsnorm(adt, h_in, h_copy, xhat, xpk, T, H, lm_count, r.gate, s));
   LAUNCH("router_logits", s, launch_router(adt, xhat, reinterpret_cast<uint32_t *>(at<void>(ws, p.sync)),
@@ -240,9 +236,9 @@ bdd_status moe_layer(const bdd_moe_dims &d, const bdd_moe_weights &w, float top_
   int g1 = expert_items_max(T, H, E, K, I, Is, true, i4), g2 = expert_items_max(T, H, E, K, I, Is, false, i4);
   g1 = g1 < cus * kGateupWgPerCu ? g1 : cus * kGateupWgPerCu;
   g2 = g2 < cus * kDownWgPerCu ? g2 : cus * kDownWgPerCu;
-  LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, xpk, w.w_gate_up, r, A, act, T, H, I, Imax, g1,
-                                                  s));
-  LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, act, w.w_down, w.ws_down, r, P, T, H, K, I, Is, Imax,
+  LAUNCH("expert_gateup", s, launch_expert_gateup(d.wdtype, xhat, xpk, w.w_gate_up, r, A, act, T, H, E, K, I, Imax,
+                                                  g1, s));
+  LAUNCH("expert_down", s, launch_expert_down(d.wdtype, A, act, w.w_down, w.ws_down, r, P, T, H, E, K, I, Is, Imax,
                                               g2, s));
   LAUNCH("combine", s, launch_combine(adt, P, Is > 0 ? P + (size_t)T * K * H : nullptr, r.idx, r.wgt, h,
                                       y_out, xhat_next, xpk_next ? xpk : nullptr, T, H, K, r.gate, s));

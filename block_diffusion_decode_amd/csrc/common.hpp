@@ -66,6 +66,29 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) { return __builtin_b
 
 // Wave-uniform copy of a value (lets the compiler keep it in an SGPR).
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ unsigned long long uniform64(unsigned long long x) {
+  return ((unsigned long long)(uint32_t)uniform((int)(x >> 32)) << 32) | (uint32_t)uniform((int)(uint32_t)x);
+}
+
+// Mask of the lanes below `lane` in a wave.
+__device__ __forceinline__ unsigned long long lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Index of the j-th (from 0) set bit of m, for j < popcount(m): a binary
+// search on the population counts of m's low bits.
+__device__ __forceinline__ int nth_bit(unsigned long long m, int j) {
+  int p = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll((m >> p) & ((1ull << w) - 1ull));
+    if (j >= c) {
+      p += w;
+      j -= c;
+    }
+  }
+  return p;
+}
 
 // Raw buffer descriptor over [base, base + bytes): loads address it with a
 // per-lane byte offset (VGPR) plus a wave-uniform byte offset (SGPR), and

@@ -54,39 +54,125 @@ __device__ __forceinline__ float dot8bf(const uint4 &w, const uint4 &x, float c)
   return dot2bf(w.w, x.w, c);
 }
 
-// Routed token group of one work item (wave-uniform): one record of the
-// selection kernel's list, [expert, positions, (row | position << 16) x
-// kTokGroup, 0, 0], where the row of (position t, pick k) in A and P is
-// t * K + k.
+// ---------------------------------------------------------------------------
+// Work lists.  The selection leaves, per expert, the mask of the positions
+// whose final picks include it (sync.mask2) and each such pick's slot k
+// (sync.kslot); the row of (position t, slot k) in A and P is t * K + k.
+// Every workgroup of an expert kernel rebuilds the block's lists from the
+// masks in LDS: the experts with more than kTokGroup positions (dense, in
+// ascending id), then those with 1 .. kTokGroup (one token group each, in
+// ascending id).  An expert's entry j is its j-th position in ascending order.
+// ---------------------------------------------------------------------------
+struct ListShared {
+  posmask_t msk[kMaxE];   // position masks: dense experts, then token groups
+  int32_t exp[kMaxE];     // their expert ids
+  int wsum[4];            // per-wave counts (dense | groups << 16)
+};
+
+// Builds the lists (all 256 threads; ends with a barrier) and returns the
+// number of dense experts | token groups << 16.  With `report` (one
+// workgroup of the layer) it also writes the union size and, without a
+// coreset, the union as the coreset.
+__device__ __forceinline__ int build_lists(const RouteBufs &r, int E, ListShared &L, bool report) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const posmask_t m = tid < E ? r.sync.mask2[tid] : 0ull;
+  const int npos = __popcll(m);
+  const bool dense = npos > kTokGroup, grp = npos > 0 && !dense;
+  const unsigned long long bd = __ballot(dense), bg = __ballot(grp);
+  if (lane == 0) L.wsum[wave] = __popcll(bd) | __popcll(bg) << 16;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int v = L.wsum[w];
+    pre += w < wave ? v : 0;
+    tot += v;
+  }
+  const int nd = tot & 0xffff;
+  const unsigned long long below = lanes_below(lane);
+  if (dense) {
+    const int at = (pre & 0xffff) + __popcll(bd & below);
+    L.exp[at] = tid;
+    L.msk[at] = m;
+  }
+  if (grp) {
+    const int at = nd + (pre >> 16) + __popcll(bg & below);
+    L.exp[at] = tid;
+    L.msk[at] = m;
+  }
+  if (report) {
+    const int nu = nd + (tot >> 16);
+    if (tid == 0) {
+      r.meta[0] = nu;
+      if (r.n_distinct_out) *r.n_distinct_out = nu;
+      if (!r.coreset) {
+        r.meta[1] = nu;
+        if (r.coreset_size_out) *r.coreset_size_out = nu;
+      }
+    }
+    // without a coreset every expert with a pick is reported as its member
+    if (!r.coreset && lane == 0 && 64 * wave < E) r.cs_bits[2 * wave] = (uint32_t)(bd | bg);
+    if (!r.coreset && lane == 32 && 64 * wave + 32 < E) r.cs_bits[2 * wave + 1] = (uint32_t)((bd | bg) >> 32);
+  }
+  __syncthreads();
+  return tot;
+}
+
+// The pick slot of expert e in position t's final picks.
+__device__ __forceinline__ int pick_slot(const RouteBufs &r, int e, int t) {
+  return (int)((r.sync.kslot[e * (kMaxT / 4) + (t >> 2)] >> (8 * (t & 3))) & 0xffu);
+}
+
+// Routed token group of one work item (wave-uniform): up to kTokGroup
+// positions of one expert and the expert's slot words (lane l < kMaxT / 4
+// holds word l).  A row is formed only where it is used, so the slot load of
+// a prefetched group stays in flight until then.
 struct Group {
-  const void *w;           // the expert's weights
-  int ie;                  // its intermediate size
-  int ng;                  // positions in the group, 1..kTokGroup
-  int p[kTokGroup];        // row | position << 16 of the group's positions
-  const int32_t *rec;      // the record (for per-lane reads)
-  __device__ __forceinline__ int row(int t) const { return p[t] & 0xffff; }
-  __device__ __forceinline__ int pos(int t) const { return p[t] >> 16; }
-  // row of position t where t differs between lanes
-  __device__ __forceinline__ int lane_row(int t) const { return rec[2 + t] & 0xffff; }
+  const void *w;             // the expert's weights
+  int ie;                    // its intermediate size
+  int ng;                    // positions in the group, 1..kTokGroup
+  int K;                     // picks per position
+  int pp[kTokGroup];         // positions, ascending (0 past the group)
+  uint32_t wv;               // this lane's slot word of the expert
+  __device__ __forceinline__ int pos(int t) const { return pp[t]; }
+  __device__ __forceinline__ int row(int t) const {
+    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)wv, pp[t] >> 2);
+    return pp[t] * K + (int)((word >> (8 * (pp[t] & 3))) & 0xffu);
+  }
+  // row of entry t where t differs between lanes (value arithmetic: a
+  // runtime index would leave the arrays in memory)
+  __device__ __forceinline__ int lane_row(int t) const {
+    int v = row(0);
+#pragma unroll
+    for (int j = 1; j < kTokGroup; ++j) v = t == j ? row(j) : v;
+    return v;
+  }
 };
 
 // Resolves routed item j = group * tiles + tile.  Items of one group and
 // different tiles are `tiles` apart, so on a grid that is a multiple of 8
-// they run on one XCD.  Only scalar loads with no dependence between them, so
-// the next item's record can be fetched while the current item streams.
-__device__ __forceinline__ Group resolve(int j, int tiles, const RouteBufs &r, const void *w_routed,
-                                         size_t expert_bytes, int I, int &tile) {
+// they run on one XCD.  The group's mask comes from LDS and its slot words
+// from one vector load (a load at a wave-uniform address would be moved to a
+// scalar register at once, waiting for it there), so the next item's group
+// can be fetched while the current item streams.
+__device__ __forceinline__ Group resolve(int j, int tiles, const RouteBufs &r, const ListShared &L, int nd, int K,
+                                         const void *w_routed, size_t expert_bytes, int I, int &tile) {
   Group g;
   const int gi = j / tiles;
   tile = j - gi * tiles;
-  const int32_t *rec = r.glist + gi * 8;
-  const int e = uniform(rec[0]);
+  const int e = uniform(L.exp[nd + gi]);
+  posmask_t m = uniform64(L.msk[nd + gi]);
   g.w = static_cast<const char *>(w_routed) + (size_t)e * expert_bytes;
   g.ie = I;
-  g.ng = uniform(rec[1]);
+  g.ng = __popcll(m);
+  g.K = K;
 #pragma unroll
-  for (int t = 0; t < kTokGroup; ++t) g.p[t] = uniform(rec[2 + t]);
-  g.rec = rec;
+  for (int t = 0; t < kTokGroup; ++t) {
+    const int pt = m ? __ffsll((long long)m) - 1 : 0;
+    m &= m - 1ull;
+    g.pp[t] = pt;
+  }
+  g.wv = r.sync.kslot[e * (kMaxT / 4) + (__lane_id() & (kMaxT / 4 - 1))];
   return g;
 }
 
@@ -178,18 +264,21 @@ constexpr int dense_down_batch() { return MT <= 2 ? 4 : 2; }
 
 // Down projection of one dense expert, W_d [H][ie], for rows h0 .. h0 + 16 MT - 1
 // (MT row tiles) and up to 16 NT column entries, from the expert's packed
-// activation slot (see act_unit).  Lane (li, g) names entries li + 16 n by
-// their rows row[n] in P (-1: no entry).  The four waves split the
-// intermediate dimension; each issues the loads of a batch of k-steps at
-// once, stages its weights through its own quarter of `red` (MT * 8 KiB), and
-// the partial tiles are then added through all of it.  With bf16
+// activation slot (see act_unit).  Lane (li, g) names entries li + 16 n:
+// live[n] < 0 where there is no entry, and row[n] is the entry's row in P
+// (read only at the end, so it may still be in flight when the item
+// starts).  The four waves split the intermediate dimension; each issues the
+// loads of a batch of k-steps at once, stages its weights through its own
+// span of `red` (MT * 2 KiB), and the partial tiles are then added through
+// all of it.  With bf16
 // weights the activations enter as bf16 high parts and residuals (two MFMA
 // passes); every activation load serves MT weight tiles.
 // P[row][h] = A_entry . W_d[h].
 template <class W, int MT, int NT>
 __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict__ w, int ie,
-                                                const char *__restrict__ act, int H, const int (&row)[NT], int h0,
-                                                int wave, int lane, float *__restrict__ P, f32x4 *red) {
+                                                const char *__restrict__ act, int H, const int (&live)[NT],
+                                                const int (&row)[NT], int h0, int wave, int lane,
+                                                float *__restrict__ P, f32x4 *red) {
   typedef typename W::T WT;
   constexpr bool BF = std::is_same<W, WBf16>::value;
   constexpr int CH = W::kChunk;
@@ -227,14 +316,14 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = 8 * (u0 + u) + 4 * h + g;
-        const bool live = live_u && c < ncw;
+        const bool live_c = live_u && c < ncw;
         const int C = cw0 + c;
 #pragma unroll
         for (int n = 0; n < NT; ++n)
 #pragma unroll
           for (int q = 0; q < NP; ++q)
             xa[2 * u + h][n][q] =
-                buf_ld16(ra, live && row[n] >= 0 ? act_unit(C, q, 16 * n + li, NP) * 16u : kOutOfRange, 0);
+                buf_ld16(ra, live_c && live[n] >= 0 ? act_unit(C, q, 16 * n + li, NP) * 16u : kOutOfRange, 0);
       }
     }
 #pragma unroll
@@ -281,24 +370,26 @@ __device__ __forceinline__ void dense_down_item(const typename W::T *__restrict_
   __syncthreads();  // `red` is free for the next item
 }
 
-// Per-lane column entries of a dense record: entries li + 16 c, c < NT.  The
-// record is read with wave-uniform loads (scalar loads where the compiler can
-// prove nothing in the kernel wrote it yet: a workgroup's first item), and
-// each lane picks its entries.
+// Per-lane column entries of a dense expert with position mask m: entries
+// li + 16 c, c < NT, as positions (-1 past the expert's positions).
 template <int NT>
-__device__ __forceinline__ void dense_entries(const int32_t *rec, int lane, int &e, int &n, int (&v)[NT]) {
-  e = uniform(rec[0]);
-  n = uniform(rec[1]);
-  int ent[16 * NT];
-#pragma unroll
-  for (int j = 0; j < 16 * NT; ++j) ent[j] = uniform(rec[8 + j]);
-  const int li = lane & 15;
+__device__ __forceinline__ void dense_positions(posmask_t m, int lane, int (&pos)[NT]) {
+  const int n = __popcll(m);
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
-    v[c] = ent[16 * c];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) v[c] = li == j ? ent[16 * c + j] : v[c];
+    const int j = 16 * c + (lane & 15);
+    pos[c] = j < n ? nth_bit(m, j) : -1;
   }
+}
+
+// The same entries as positions and as rows t * K + k of P (-1 past the
+// expert's positions); the rows wait on a load of the pick slots.
+template <int NT>
+__device__ __forceinline__ void dense_rows(const RouteBufs &r, int e, posmask_t m, int K, int lane, int (&pos)[NT],
+                                           int (&row)[NT]) {
+  dense_positions<NT>(m, lane, pos);
+#pragma unroll
+  for (int c = 0; c < NT; ++c) row[c] = pos[c] >= 0 ? pos[c] * K + pick_slot(r, e, max(pos[c], 0)) : -1;
 }
 
 // Work list: the dense experts' items (expert, 16-row tile), then the token
@@ -309,36 +400,37 @@ template <class W, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 : 4))) void expert_gateup_kernel(
     const typename W::T *__restrict__ xhat, const typename W::T *__restrict__ xpk,
     const typename W::T *__restrict__ wgu, RouteBufs r, float *__restrict__ A, char *__restrict__ act, int T,
-    int H, int I, int Imax) {
+    int H, int E, int K, int I, int Imax) {
   typedef typename W::T WT;
   if (gated_off(r.gate)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ ListShared L;
+  const int cnt = build_lists(r, E, L, blockIdx.x == 0);
+  const int nd = cnt & 0xffff;
   const int tiles = I / 16;
-  const int d_items = uniform(r.meta[3]) * tiles;
-  const int items = d_items + uniform(r.meta[2]) * tiles;
+  const int d_items = nd * tiles;
+  const int items = d_items + (cnt >> 16) * tiles;
   const uint32_t x_bytes = (uint32_t)(T * H) * sizeof(WT);
   const size_t eb = (size_t)2 * I * H * sizeof(WT);
   __shared__ f32x4 red[4 * 2 * NT * 64];
   int item = blockIdx.x;
   for (; item < d_items; item += gridDim.x) {
     const int di = item / tiles, tile = item - di * tiles;
-    int e, n, v[NT];
-    dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
+    const int e = uniform(L.exp[di]);
     int pos[NT];
-#pragma unroll
-    for (int c = 0; c < NT; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
+    dense_positions<NT>(uniform64(L.msk[di]), lane, pos);
     // slot 0 holds the shared expert
     dense_gateup_item<W, 2, NT>(wgu + (size_t)e * 2 * I * H, I, xpk, T, H, pos, item, tile * 16, wave, lane,
                             act + (size_t)(1 + di) * Imax * kActSlotPerI, red);
   }
   int tile_next = 0;
   Group next;
-  if (item < items) next = resolve(item - d_items, tiles, r, wgu, eb, I, tile_next);
+  if (item < items) next = resolve(item - d_items, tiles, r, L, nd, K, wgu, eb, I, tile_next);
   for (; item < items; item += gridDim.x) {
     const int nitem = item + (int)gridDim.x;
     const Group g = next;
     const int tile = tile_next;
-    if (nitem < items) next = resolve(nitem - d_items, tiles, r, wgu, eb, I, tile_next);
+    if (nitem < items) next = resolve(nitem - d_items, tiles, r, L, nd, K, wgu, eb, I, tile_next);
     const int i0 = uniform(tile * 16 + wave * 4);
     if (g.ng <= 1)      gateup_group<W, 1>(g, xhat, x_bytes, H, Imax, i0, lane, A);
     else if (g.ng <= 2) gateup_group<W, 2>(g, xhat, x_bytes, H, Imax, i0, lane, A);
@@ -494,22 +586,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 
                                                           const typename W::T *__restrict__ wd,
                                                           const typename W::T *__restrict__ wsd,
                                                           RouteBufs r, float *__restrict__ P, int T,
-                                                          int H, int K, int I, int Is, int Imax) {
+                                                          int H, int E, int K, int I, int Is, int Imax) {
   typedef typename W::T WT;
   if (gated_off(r.gate)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ ListShared L;
+  const int cnt = build_lists(r, E, L, false);
+  const int nd = cnt & 0xffff;
   constexpr int DR = 16 * kDenseRowTiles;   // rows per dense item
   const int tiles = H / (4 * kDownRowsPerWave), dtiles = H / DR;
   const int s_items = Is > 0 ? dtiles : 0;
-  const int d_end = s_items + uniform(r.meta[3]) * dtiles;
+  const int d_end = s_items + nd * dtiles;
   __shared__ f32x4 red[4 * kDenseRowTiles * NT * 64];
-  const int items = d_end + uniform(r.meta[2]) * tiles;
+  const int items = d_end + (cnt >> 16) * tiles;
   const uint32_t a_bytes = (uint32_t)(T * K) * (uint32_t)Imax * 4u;
   const size_t eb = (size_t)H * I * sizeof(WT);
   const int stride = gridDim.x;
   int item = blockIdx.x;
   for (; item < d_end; item += stride) {
-    int row[NT];
+    int live[NT], row[NT];
     const WT *w;
     int ie, h0, slot;
     if (item < s_items) {
@@ -518,6 +613,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 
       for (int c = 0; c < NT; ++c) {
         const int j = c * 16 + (lane & 15);
         row[c] = j < T ? T * K + j : -1;
+        live[c] = row[c];
       }
       w = wsd;
       ie = Is;
@@ -525,26 +621,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 
       slot = 0;
     } else {
       const int di = (item - s_items) / dtiles;
-      int e, n, v[NT];
-      dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
-#pragma unroll
-      for (int c = 0; c < NT; ++c) row[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
+      const int e = uniform(L.exp[di]);
+      dense_rows<NT>(r, e, uniform64(L.msk[di]), K, lane, live, row);
       w = wd + (size_t)e * H * I;
       ie = I;
       h0 = (item - s_items - di * dtiles) * DR;
       slot = 1 + di;
     }
-    dense_down_item<W, kDenseRowTiles, NT>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, H, row, h0, wave, lane, P,
-                                       red);
+    dense_down_item<W, kDenseRowTiles, NT>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, H, live, row, h0, wave,
+                                           lane, P, red);
   }
   int tile_next = 0;
   Group next;
-  if (item < items) next = resolve(item - d_end, tiles, r, wd, eb, I, tile_next);
+  if (item < items) next = resolve(item - d_end, tiles, r, L, nd, K, wd, eb, I, tile_next);
   for (; item < items; item += stride) {
     const int nitem = item + stride;
     const Group g = next;
     const int tile = tile_next;
-    if (nitem < items) next = resolve(nitem - d_end, tiles, r, wd, eb, I, tile_next);
+    if (nitem < items) next = resolve(nitem - d_end, tiles, r, L, nd, K, wd, eb, I, tile_next);
     const int h0 = uniform(tile * 4 * kDownRowsPerWave + wave * kDownRowsPerWave);
     if (g.ie <= 64 * W::kChunk) {
       // one pass over the whole group: the activations sit in registers
@@ -569,45 +663,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 
 
 constexpr int kI4GroupDownTiles = 4;   // 16-row tiles per token-group down item (64 rows)
 
-// Per-lane entry of a token-group record: entry li (< positions) of the
-// group, as (row t*K + k, position t); -1, -1 past the group.
-__device__ __forceinline__ void group_entry(const int32_t *rec, int lane, int &row, int &pos) {
+// Per-lane entry of token group gi: entry li (< positions) of the group, as
+// (row t*K + k, position t); -1, -1 past the group.  Returns the expert.
+__device__ __forceinline__ int group_entry(const RouteBufs &r, const ListShared &L, int nd, int gi, int K, int lane,
+                                           int &row, int &pos) {
+  const int e = uniform(L.exp[nd + gi]);
+  const posmask_t m = uniform64(L.msk[nd + gi]);
   const int li = lane & 15;
-  const int ng = uniform(rec[1]);
-  const int v = rec[2 + min(li, kTokGroup - 1)];
-  row = li < ng ? (v & 0xffff) : -1;
-  pos = li < ng ? (v >> 16) : -1;
+  pos = li < __popcll(m) ? nth_bit(m, li) : -1;
+  row = pos >= 0 ? pos * K + pick_slot(r, e, max(pos, 0)) : -1;
+  return e;
 }
 
 template <int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 1 : 2))) void expert_gateup_i4_kernel(
     const bf16_t *__restrict__ xpk, const char *__restrict__ wgu, RouteBufs r, float *__restrict__ A,
-    char *__restrict__ act, int T, int H, int I, int Imax) {
+    char *__restrict__ act, int T, int H, int E, int K, int I, int Imax) {
   if (gated_off(r.gate)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ ListShared L;
+  const int cnt = build_lists(r, E, L, blockIdx.x == 0);
+  const int nd = cnt & 0xffff;
   const int tiles = I / 16;
-  const int d_items = uniform(r.meta[3]) * tiles;
-  const int items = d_items + uniform(r.meta[2]) * tiles;
+  const int d_items = nd * tiles;
+  const int items = d_items + (cnt >> 16) * tiles;
   const size_t mb = i4_mat_bytes(2 * I, H);
   __shared__ f32x4 red[4 * 2 * NT * 64];
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     if (item < d_items) {
       const int di = item / tiles, tile = item - di * tiles;
-      int e, n, v[NT];
-      dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
+      const int e = uniform(L.exp[di]);
       int pos[NT];
-#pragma unroll
-      for (int c = 0; c < NT; ++c) pos[c] = c * 16 + (lane & 15) < n ? v[c] >> 16 : -1;
+      dense_positions<NT>(uniform64(L.msk[di]), lane, pos);
       const I4Mat w = i4_mat(wgu + (size_t)e * mb, 2 * I, H);
       i4_gateup_item<NT>(w, I, xpk, T, pos, tile * 16, wave, lane, act + (size_t)(1 + di) * Imax * kActSlotPerI,
                         nullptr, nullptr, Imax, red);
     } else {
       const int j = item - d_items;
       const int gi = j / tiles, tile = j - gi * tiles;
-      const int32_t *rec = r.glist + gi * 8;
-      const int e = uniform(rec[0]);
       int row[1], pos[1];
-      group_entry(rec, lane, row[0], pos[0]);
+      const int e = group_entry(r, L, nd, gi, K, lane, row[0], pos[0]);
       const I4Mat w = i4_mat(wgu + (size_t)e * mb, 2 * I, H);
       i4_gateup_item<1>(w, I, xpk, T, pos, tile * 16, wave, lane, nullptr, A, row, Imax, red);
     }
@@ -617,23 +712,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 1 
 template <int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 : 3))) void expert_down_i4_kernel(
     const float *__restrict__ A, const char *__restrict__ act, const char *__restrict__ wd,
-    const char *__restrict__ wsd, RouteBufs r, float *__restrict__ P, int T, int H, int K, int I, int Is,
+    const char *__restrict__ wsd, RouteBufs r, float *__restrict__ P, int T, int H, int E, int K, int I, int Is,
     int Imax) {
   if (gated_off(r.gate)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ ListShared L;
+  const int cnt = build_lists(r, E, L, false);
+  const int nd = cnt & 0xffff;
   constexpr int DR = 16 * kDenseRowTiles;              // rows per dense item
   constexpr int GR = 16 * kI4GroupDownTiles;           // rows per token-group item
   const int dtiles = H / DR, gtiles = H / GR;
   const int s_items = Is > 0 ? dtiles : 0;
-  const int d_end = s_items + uniform(r.meta[3]) * dtiles;
-  const int items = d_end + uniform(r.meta[2]) * gtiles;
+  const int d_end = s_items + nd * dtiles;
+  const int items = d_end + (cnt >> 16) * gtiles;
   const uint32_t a_bytes = (uint32_t)(T * K) * (uint32_t)Imax * 4u;
   const size_t mb = i4_mat_bytes(H, I);
   static_assert(kI4GroupDownTiles * 2 >= kDenseRowTiles * 4, "`red` holds a dense item's tiles for four column tiles");
   __shared__ f32x4 red[4 * kI4GroupDownTiles * 2 * 64];
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     if (item < d_end) {
-      int prow[NT];
+      int live[NT], prow[NT];
       I4Mat w;
       int ie, h0, slot;
       if (item < s_items) {
@@ -642,6 +740,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 
         for (int c = 0; c < NT; ++c) {
           const int j = c * 16 + (lane & 15);
           prow[c] = j < T ? T * K + j : -1;
+          live[c] = prow[c];
         }
         w = i4_mat(wsd, H, Is);
         ie = Is;
@@ -649,27 +748,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT > 2 ? 2 
         slot = 0;
       } else {
         const int di = (item - s_items) / dtiles;
-        int e, n, v[NT];
-        dense_entries<NT>(r.dlist + di * kDenseRec, lane, e, n, v);
-#pragma unroll
-        for (int c = 0; c < NT; ++c) prow[c] = c * 16 + (lane & 15) < n ? (v[c] & 0xffff) : -1;
+        const int e = uniform(L.exp[di]);
+        dense_rows<NT>(r, e, uniform64(L.msk[di]), K, lane, live, prow);
         w = i4_mat(wd + (size_t)e * mb, H, I);
         ie = I;
         h0 = (item - s_items - di * dtiles) * DR;
         slot = 1 + di;
       }
       i4_down_item<kDenseRowTiles, NT>(w, ie, act + (size_t)slot * Imax * kActSlotPerI, nullptr, nullptr, 0, Imax, H,
-                                      prow, h0, wave, lane, P, red);
+                                      live, prow, h0, wave, lane, P, red);
     } else {
       const int j = item - d_end;
       const int gi = j / gtiles, tile = j - gi * gtiles;
-      const int32_t *rec = r.glist + gi * 8;
-      const int e = uniform(rec[0]);
       int row[1], pos[1];
-      group_entry(rec, lane, row[0], pos[0]);
+      const int e = group_entry(r, L, nd, gi, K, lane, row[0], pos[0]);
       const I4Mat w = i4_mat(wd + (size_t)e * mb, H, I);
-      i4_down_item<kI4GroupDownTiles, 1>(w, I, nullptr, A, row, a_bytes, Imax, H, row, tile * GR, wave, lane, P,
-                                         red);
+      i4_down_item<kI4GroupDownTiles, 1>(w, I, nullptr, A, row, a_bytes, Imax, H, row, row, tile * GR, wave, lane,
+                                         P, red);
     }
   }
 }
@@ -688,49 +783,51 @@ int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup, boo
 
 template <int NT>
 static hipError_t gateup_launch(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
-                                const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
-                                hipStream_t s) {
+                                const RouteBufs &r, float *A, void *act, int T, int H, int E, int K, int I, int Imax,
+                                int grid, hipStream_t s) {
   if (wdtype == 2)
     expert_gateup_i4_kernel<NT><<<grid, 256, 0, s>>>((const bf16_t *)xpk, (const char *)w_gate_up, r, A,
-                                                     (char *)act, T, H, I, Imax);
+                                                     (char *)act, T, H, E, K, I, Imax);
   else if (wdtype == 1)
     expert_gateup_kernel<WBf16, NT><<<grid, 256, 0, s>>>((const bf16_t *)xhat, (const bf16_t *)xpk,
-                                                         (const bf16_t *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
+                                                         (const bf16_t *)w_gate_up, r, A, (char *)act, T, H, E, K, I,
+                                                         Imax);
   else
     expert_gateup_kernel<WF32, NT><<<grid, 256, 0, s>>>((const float *)xhat, (const float *)xpk,
-                                                        (const float *)w_gate_up, r, A, (char *)act, T, H, I, Imax);
+                                                        (const float *)w_gate_up, r, A, (char *)act, T, H, E, K, I,
+                                                        Imax);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
-                                const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
-                                hipStream_t s) {
+                                const RouteBufs &r, float *A, void *act, int T, int H, int E, int K, int I,
+                                int Imax, int grid, hipStream_t s) {
   // two 16-entry column tiles cover a block of up to 32 positions, four up to 64
-  return T > 32 ? gateup_launch<4>(wdtype, xhat, xpk, w_gate_up, r, A, act, T, H, I, Imax, grid, s)
-                : gateup_launch<2>(wdtype, xhat, xpk, w_gate_up, r, A, act, T, H, I, Imax, grid, s);
+  return T > 32 ? gateup_launch<4>(wdtype, xhat, xpk, w_gate_up, r, A, act, T, H, E, K, I, Imax, grid, s)
+                : gateup_launch<2>(wdtype, xhat, xpk, w_gate_up, r, A, act, T, H, E, K, I, Imax, grid, s);
 }
 
 template <int NT>
 static hipError_t down_launch(int wdtype, const float *A, const void *act, const void *w_down, const void *ws_down,
-                              const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
+                              const RouteBufs &r, float *P, int T, int H, int E, int K, int I, int Is, int Imax,
                               int grid, hipStream_t s) {
   if (wdtype == 2)
     expert_down_i4_kernel<NT><<<grid, 256, 0, s>>>(A, (const char *)act, (const char *)w_down, (const char *)ws_down,
-                                                   r, P, T, H, K, I, Is, Imax);
+                                                   r, P, T, H, E, K, I, Is, Imax);
   else if (wdtype == 1)
     expert_down_kernel<WBf16, NT><<<grid, 256, 0, s>>>(A, (const char *)act, (const bf16_t *)w_down,
-                                                       (const bf16_t *)ws_down, r, P, T, H, K, I, Is, Imax);
+                                                       (const bf16_t *)ws_down, r, P, T, H, E, K, I, Is, Imax);
   else
     expert_down_kernel<WF32, NT><<<grid, 256, 0, s>>>(A, (const char *)act, (const float *)w_down,
-                                                      (const float *)ws_down, r, P, T, H, K, I, Is, Imax);
+                                                      (const float *)ws_down, r, P, T, H, E, K, I, Is, Imax);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_down(int wdtype, const float *A, const void *act, const void *w_down, const void *ws_down,
-                              const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
+                              const RouteBufs &r, float *P, int T, int H, int E, int K, int I, int Is, int Imax,
                               int grid, hipStream_t s) {
-  return T > 32 ? down_launch<4>(wdtype, A, act, w_down, ws_down, r, P, T, H, K, I, Is, Imax, grid, s)
-                : down_launch<2>(wdtype, A, act, w_down, ws_down, r, P, T, H, K, I, Is, Imax, grid, s);
+  return T > 32 ? down_launch<4>(wdtype, A, act, w_down, ws_down, r, P, T, H, E, K, I, Is, Imax, grid, s)
+                : down_launch<2>(wdtype, A, act, w_down, ws_down, r, P, T, H, E, K, I, Is, Imax, grid, s);
 }
 
 }  // namespace bdd

@@ -188,11 +188,13 @@ __device__ __forceinline__ void i4_gateup_item(const I4Mat &w, int ie, const bf1
 // residuals; per group the correction is 136 times the group's sum of both.
 // The four waves take the groups round-robin and add their partial tiles in
 // `red` (4 * MT * NT * 64 f32x4); P[prow[n]][h] receives the unweighted rows.
+// From the packed slot, entries with live[n] < 0 are absent (prow is read
+// only at the end).
 template <int MT, int NT>
 __device__ __forceinline__ void i4_down_item(const I4Mat &w, int ie, const char *__restrict__ act,
                                              const float *__restrict__ A, const int *arow, uint32_t a_bytes,
-                                             int Imax, int H, const int (&prow)[NT], int h0, int wave, int lane,
-                                             float *__restrict__ P, f32x4 *red) {
+                                             int Imax, int H, const int (&live)[NT], const int (&prow)[NT], int h0,
+                                             int wave, int lane, float *__restrict__ P, f32x4 *red) {
   const int li = lane & 15, g = lane >> 4;
   const int t0 = h0 / 16;
   const int G = w.G;
@@ -229,12 +231,12 @@ __device__ __forceinline__ void i4_down_item(const I4Mat &w, int ie, const char 
                               __uint_as_float(x1.z), __uint_as_float(x1.w)};
           split_hi_lo(f, hi[kk][n], lo[kk][n]);
         } else {
-          int my_row = prow[0];
+          int my_live = live[0];
 #pragma unroll
-          for (int j = 1; j < NT; ++j) my_row = n == j ? prow[j] : my_row;
-          const bool live = my_row >= 0;
-          hi[kk][n] = buf_ld16(ra, live ? act_unit(C, 0, 16 * n + li, 2) * 16u : kOutOfRange, 0);
-          lo[kk][n] = buf_ld16(ra, live ? act_unit(C, 1, 16 * n + li, 2) * 16u : kOutOfRange, 0);
+          for (int j = 1; j < NT; ++j) my_live = n == j ? live[j] : my_live;
+          const bool ok = my_live >= 0;
+          hi[kk][n] = buf_ld16(ra, ok ? act_unit(C, 0, 16 * n + li, 2) * 16u : kOutOfRange, 0);
+          lo[kk][n] = buf_ld16(ra, ok ? act_unit(C, 1, 16 * n + li, 2) * 16u : kOutOfRange, 0);
         }
       }
     float xs[NT];

@@ -18,7 +18,7 @@ struct SelSync {
   posmask_t *mask1;             // [E] positions whose first picks include the expert
   posmask_t *mask2;             // [E] positions whose final picks include the expert
   uint32_t *cbits;              // [8] coreset membership, published for the positions
-  int32_t *words;               // [0] coreset published, [1] first count, [2] second count, [3] coreset size
+  int32_t *words;               // [0] coreset published, [1] first count, [2] unused, [3] coreset size
 };
 // (the slot words first: 16-byte aligned rows of kMaxT bytes per expert)
 inline size_t sel_sync_bytes(int E) { return (size_t)E * (kMaxT + 8 + 8 + 8) + 32 + 64; }
@@ -39,30 +39,25 @@ struct RouteBufs {
   float *logits;       // [H/128][T][E] router logit slices (bias not added)
   int32_t *idx;        // [T][K]   picked experts (-1 = unused slot)
   float *wgt;          // [T][K]   their renormalised weights
-  int32_t *meta;       // [0] union size, [1] coreset size, [2] token groups, [3] dense experts,
-                       // [4] set if a wait for the coreset timed out
-  int32_t *union_list; // [E]      union experts, ascending id
-  int32_t *glist;      // [expert_groups_max][8] token-group records (see the expert kernels)
-  int32_t *dlist;      // [expert_dense_max][kDenseRec] dense-expert records
+  int32_t *meta;       // [0] union size, [1] coreset size, [4] set if a wait for the coreset timed out
   uint32_t *cs_bits;   // [8]      coreset membership bitset
   float *mass;         // [E]      block expert mass (with the coreset)
   SelSync sync;        // selection kernel's cross-workgroup state
   int32_t *n_distinct_out;    // [1] union size copy (may be null)
   int32_t *coreset_size_out;  // [1] coreset size copy (may be null)
   const int32_t *gate;        // block resolved flag (may be null): the layer's kernels return when set
+  int coreset;                // the selection took a coreset (else the gate/up kernel reports the union
+                              // as the coreset)
 };
 
-// Upper bound of the routed token groups (kTokGroup positions of one expert)
-// of a block: sum over union experts of ceil(n_e / kTokGroup).
+// Upper bound of the routed token groups of a block: one per expert picked by
+// 1 .. kTokGroup positions.
 inline int expert_groups_max(int T, int E, int K) {
   const int picks = T * K;
-  return (E < picks ? E : picks) + (picks + kTokGroup - 1) / kTokGroup;
+  return E < picks ? E : picks;
 }
 
-// Upper bound of the dense experts (more than kTokGroup positions) of a block,
-// and the words of one dense record: expert, positions, 6 spare words, then
-// one word per position.
-constexpr int kDenseRec = 8 + kMaxT;
+// Upper bound of the dense experts (more than kTokGroup positions) of a block.
 inline int expert_dense_max(int T, int E, int K) {
   const int d = T * K / (kTokGroup + 1);
   return d < E ? d : E;
@@ -81,10 +76,12 @@ hipError_t launch_router(int wdtype, const void *xhat, uint32_t *zero_base, int 
                          float *part, int T, int H, int E, const int32_t *gate, hipStream_t s);
 
 // Selection: one workgroup per position (logits = slices summed in order +
-// bias), the coreset and the work lists (r.sync must have been cleared by the
-// router kernel); workgroups past the positions compute the shared expert's
-// gate/up from the packed block `xpk` into its packed activation slot
-// `act_shared`.
+// bias) and the coreset (r.sync must have been cleared by the router kernel);
+// it leaves the final picks in r.idx / r.wgt and, per expert, the positions
+// that picked it (sync.mask2) with the pick slots (sync.kslot), from which
+// the expert kernels build their work lists.  Workgroups past the positions
+// compute the shared expert's gate/up from the packed block `xpk` into its
+// packed activation slot `act_shared`.
 hipError_t launch_route_select(const RouteBufs &r, const float *bias, int T, int H, int E, int K, float top_p,
                                int wdtype, const void *xpk, const void *ws_gate_up, void *act_shared, int Is,
                                hipStream_t s);
@@ -94,15 +91,17 @@ hipError_t launch_coreset(const float *prob, const int32_t *idx, int T, int E, i
 
 // Expert FFNs.  Token groups: A [T*K][Imax] fp32 activations (row t*K + k);
 // dense experts and the shared expert: packed activation slots in `act`
-// (Imax * 128 bytes each; slot 0 the shared expert, slot 1 + d dense record
-// d).  P [T*K + T][H] fp32 unweighted outputs (rows t*K + k routed, T*K + t
-// shared).
+// (Imax * kActSlotPerI bytes each; slot 0 the shared expert, slot 1 + d the
+// d-th dense expert in ascending id).  P [T*K + T][H] fp32 unweighted
+// outputs (rows t*K + k routed, T*K + t shared).  The gate/up kernel's first
+// workgroup reports the union size (and, without a coreset, the union as the
+// coreset).
 int expert_items_max(int T, int H, int E, int K, int I, int Is, bool gateup, bool int4);
 hipError_t launch_expert_gateup(int wdtype, const void *xhat, const void *xpk, const void *w_gate_up,
-                                const RouteBufs &r, float *A, void *act, int T, int H, int I, int Imax, int grid,
-                                hipStream_t s);
+                                const RouteBufs &r, float *A, void *act, int T, int H, int E, int K, int I,
+                                int Imax, int grid, hipStream_t s);
 hipError_t launch_expert_down(int wdtype, const float *A, const void *act, const void *w_down, const void *ws_down,
-                              const RouteBufs &r, float *P, int T, int H, int K, int I, int Is, int Imax,
+                              const RouteBufs &r, float *P, int T, int H, int E, int K, int I, int Is, int Imax,
                               int grid, hipStream_t s);
 
 // y_t = sum_k wgt[t*K+k] * P[t*K+k] (slots with idx >= 0) + P_s[t] (if non-null).  Then

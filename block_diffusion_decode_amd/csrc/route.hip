@@ -1,4 +1,4 @@
-// Normalisation, router, top-K selection, block coreset and expert work lists.
+// Normalisation, router, top-K selection and block coreset.
 //
 // Pages: [P1] aitujian.cn article on Clover-35B-A3B-Preview, section 四 (256
 // routed experts, top-8, one shared expert) and section 五 (a block of 32
@@ -398,8 +398,10 @@ __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
 //     each re-takes its position's first min(K, |C|) coreset members in its
 //     own sorted order;
 //   - each writes its final picks and weights, and adds its bit and pick slot
-//     to each picked expert's mask and slot word; the workgroup counted last
-//     then builds the union and the experts' work lists from them.
+//     to each picked expert's mask and slot word.  The expert kernels build
+//     the union and their work lists from these (after the kernel boundary),
+//     so the selection ends with its positions: no workgroup waits for the
+//     last one to finish the block.
 // The waiting workgroups have all been counted, so the one they wait for is
 // running: the wait needs no co-residency.  It is bounded all the same (every
 // wave leaves it), and a timeout is reported in meta[4].
@@ -431,10 +433,6 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
   const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
   return ((unsigned long long)(uint32_t)__shfl_xor((int)hi, m) << 32) | (uint32_t)__shfl_xor((int)lo, m);
-}
-
-__device__ __forceinline__ unsigned long long lanes_below(int lane) {
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
 // Exclusive prefix over the workgroup of flags (0/1), via ballots; returns
@@ -554,102 +552,6 @@ __device__ void coreset_step(const RouteBufs &r, int E, float top_p, int *s_wave
   }
   __syncthreads();   // every published word is ordered before the flag
   if (tid == 0) __hip_atomic_store(r.sync.words, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The union of the final picks and the experts' work lists, by the workgroup
-// counted last after every position published its final picks.  An expert
-// with at most kTokGroup positions gets token-group records of 8 words:
-//   [expert, positions, (t*K + k) | t << 16 per position, 0 ...];
-// one with more gets a dense record of kDenseRec words:
-//   [expert, positions, 0 x 6, (t*K + k) | t << 16 per position],
-// positions ascending, records in union (ascending expert) order.
-__device__ void union_records(const RouteBufs &r, int T, int E, int K, bool coreset, int *s_wave) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int KW = kMaxT / 4;   // slot words per expert
-  static_assert(KW % 4 == 0, "slot words load as 16-byte vectors");
-  // after the workgroup's acquire: plain loads, all in flight together; the
-  // expert's slot words go to its own LDS row (a register array indexed by
-  // position would be placed in scratch memory)
-  __shared__ uint32_t s_kw[kSelThreads][KW + 1];
-  const int te = min(tid, E - 1);
-  const posmask_t tb_all = r.sync.mask2[te];
-#pragma unroll
-  for (int j = 0; j < KW; j += 4) {
-    const uint4 v = reinterpret_cast<const uint4 *>(r.sync.kslot + (size_t)te * KW)[j / 4];
-    s_kw[tid][j] = v.x;
-    s_kw[tid][j + 1] = v.y;
-    s_kw[tid][j + 2] = v.z;
-    s_kw[tid][j + 3] = v.w;
-  }
-  const posmask_t tbits = tid < E ? tb_all : 0ull;
-  int nu = 0;
-  const int slot = block_flag_scan(tbits != 0ull, s_wave, &nu);
-  if (tbits != 0ull) r.union_list[slot] = tid;
-  if (!coreset) {
-    // without the coreset every expert with a pick is reported as its member
-    const unsigned long long b = __ballot(tid < E && tbits != 0ull);
-    if (lane == 0 && 64 * wave < E) r.cs_bits[2 * wave] = (uint32_t)b;
-    if (lane == 32 && 64 * wave + 32 < E) r.cs_bits[2 * wave + 1] = (uint32_t)(b >> 32);
-  }
-  // group and dense-record counts: exclusive prefix by bit-sliced ballots (an
-  // expert with a pick has one token group, bit 0, when it has at most
-  // kTokGroup positions, else one dense record, bit 16; the block's group
-  // total stays below bit 16)
-  const int npos = __popcll(tbits);
-  const bool dense = npos > kTokGroup;
-  const int ng = (npos > 0 && !dense) ? 1 : 0;
-  const int cnt = ng | (dense ? 1 << 16 : 0);
-  int pre = 0, wtot = 0;
-#pragma unroll
-  for (int bit = 0; bit < 2; ++bit) {
-    const int sh = bit == 0 ? 0 : 16;
-    const unsigned long long bb = __ballot((cnt >> sh) & 1);
-    pre += __popcll(bb & lanes_below(lane)) << sh;
-    wtot += __popcll(bb) << sh;
-  }
-  if (lane == 0) s_wave[wave] = wtot;
-  __syncthreads();
-  int off = pre, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) {
-    off += w < wave ? s_wave[w] : 0;
-    tot += s_wave[w];
-  }
-  // the pick slot of position t: byte t % 4 of the expert's word t / 4
-  auto kslot_of = [&](int t) { return (int)((s_kw[tid][t >> 2] >> (8 * (t & 3))) & 0xffu); };
-  if (dense) {
-    int32_t *rec = r.dlist + (off >> 16) * kDenseRec;
-    rec[0] = tid;
-    rec[1] = npos;
-    posmask_t bits = tbits;
-    for (int j = 0; bits; ++j) {
-      const int t = __ffsll((long long)bits) - 1;
-      bits &= bits - 1ull;
-      rec[8 + j] = (t * K + kslot_of(t)) | (t << 16);
-    }
-  } else if (npos > 0) {
-    const int g0 = off & 0xffff;
-    posmask_t bits = tbits;
-    for (int j = 0; bits; ++j) {
-      const int t = __ffsll((long long)bits) - 1;
-      bits &= bits - 1ull;
-      int32_t *rec = r.glist + (g0 + j / kTokGroup) * 8;
-      if (j % kTokGroup == 0) {
-        rec[0] = tid;
-        rec[1] = min(kTokGroup, npos - j);
-        for (int q = 2 + min(kTokGroup, npos - j); q < 8; ++q) rec[q] = 0;
-      }
-      rec[2 + j % kTokGroup] = (t * K + kslot_of(t)) | (t << 16);
-    }
-  }
-  if (tid == 0) {
-    r.meta[2] = tot & 0xffff;
-    r.meta[3] = tot >> 16;
-    r.meta[0] = nu;
-    if (!coreset) r.meta[1] = nu;
-    if (r.n_distinct_out) *r.n_distinct_out = nu;
-    if (!coreset && r.coreset_size_out) *r.coreset_size_out = nu;
-  }
 }
 
 template <class W, int NT>
@@ -774,11 +676,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
       atomicOr(r.sync.kslot + e * (kMaxT / 4) + (t >> 2), (uint32_t)tid << (8 * (t & 3)));
     }
   }
-  __syncthreads();
-  if (tid == 0) s_last = count_done(r.sync.words + 2) == T - 1;
-  __syncthreads();
-  if (!s_last) return;
-  union_records(r, T, E, K, coreset, s_wave);
 }
 
 // ------------------------------------------------------------------ coreset alone
