@@ -288,14 +288,23 @@ __device__ __forceinline__ uint2 buf_ld8(rsrc_t r, uint32_t voff, uint32_t soff)
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
   return make_uint2(v.x, v.y);
 }
-// (a & m) | c for a c with no bit inside m: a bitfield insert of a's m bits
-// into c, which the compiler issues as one v_bfi_b32.  (Plain code, so the
-// compiler's hazard tracking sees every instruction next to the MFMAs.)
+// a's m bits inserted into c: one v_bfi_b32.  (Plain code, so the compiler's
+// hazard tracking sees every instruction next to the MFMAs.)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | (c & ~m); }
+// The expansion's mask and bias, held in vector registers: v_bfi_b32 takes
+// no literal operand on this target, so with literal constants each insert
+// became an and plus an or.  (mbcnt over an empty lane mask returns its
+// addend; the compiler does not fold it into a literal.)
+struct I4Bits {
+  uint32_t m, c;
+};
+__device__ __forceinline__ I4Bits i4_bits() {
+  return {__builtin_amdgcn_mbcnt_lo(0u, 0x000f000fu), __builtin_amdgcn_mbcnt_lo(0u, 0x43004300u)};
+}
 // codes 2d and 2d + 1 of a dword (see WI4) as the bf16 pair 128 + n
-__device__ __forceinline__ uint4 i4_expand(uint32_t x) {
-  const uint32_t m = 0x000f000fu, c = 0x43004300u;
-  return make_uint4(and_or(x, m, c), and_or(x >> 4, m, c), and_or(x >> 8, m, c), and_or(x >> 12, m, c));
+__device__ __forceinline__ uint4 i4_expand(uint32_t x, const I4Bits &k) {
+  return make_uint4(and_or(x, k.m, k.c), and_or(x >> 4, k.m, k.c), and_or(x >> 8, k.m, k.c),
+                    and_or(x >> 12, k.m, k.c));
 }
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }

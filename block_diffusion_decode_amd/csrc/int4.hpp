@@ -73,6 +73,7 @@ __device__ __forceinline__ void i4_gateup_item(const I4Mat &w, int ie, const bf1
   const int li = lane & 15, g = lane >> 4;
   const int tg = i0 / 16, tu = (ie + i0) / 16;
   const int G = w.G;
+  const I4Bits kb = i4_bits();
   const rsrc_t rc = make_rsrc(w.codes, w.code_bytes);
   const rsrc_t rs = make_rsrc(w.scl, w.code_bytes / 32u);   // scales: 32 bytes per tile and group
   const rsrc_t rx = make_rsrc(xpk, (uint32_t)(T * G * kI4Group) * 2u);
@@ -117,7 +118,7 @@ __device__ __forceinline__ void i4_gateup_item(const I4Mat &w, int ie, const bf1
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const uint4 &aq = b.a[q];
-        const uint4 e = i4_expand(kk == 0 ? aq.x : kk == 1 ? aq.y : kk == 2 ? aq.z : aq.w);
+        const uint4 e = i4_expand(kk == 0 ? aq.x : kk == 1 ? aq.y : kk == 2 ? aq.z : aq.w, kb);
 #pragma unroll
         for (int n = 0; n < NT; ++n) p[q][n] = mfma_bf16(e, b.b[kk][n], p[q][n]);
       }
@@ -198,6 +199,7 @@ __device__ __forceinline__ void i4_down_item(const I4Mat &w, int ie, const char 
   const int li = lane & 15, g = lane >> 4;
   const int t0 = h0 / 16;
   const int G = w.G;
+  const I4Bits kb = i4_bits();
   const rsrc_t rc = make_rsrc(w.codes, w.code_bytes);
   const rsrc_t rs = make_rsrc(w.scl, w.code_bytes / 32u);
   const rsrc_t ra = A ? make_rsrc(A, a_bytes) : make_rsrc(act, (uint32_t)ie * kActSlotPerI);
@@ -254,7 +256,7 @@ __device__ __forceinline__ void i4_down_item(const I4Mat &w, int ie, const char 
       for (int n = 0; n < NT; ++n) p[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const uint4 e = i4_expand(kk == 0 ? a[m].x : kk == 1 ? a[m].y : kk == 2 ? a[m].z : a[m].w);
+        const uint4 e = i4_expand(kk == 0 ? a[m].x : kk == 1 ? a[m].y : kk == 2 ? a[m].z : a[m].w, kb);
 #pragma unroll
         for (int n = 0; n < NT; ++n) p[n] = mfma_bf16(e, lo[kk][n], mfma_bf16(e, hi[kk][n], p[n]));
       }

@@ -241,6 +241,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   // form one flat sequence of load steps, so the next tile's first batch is in
   // flight during a tile's epilogue, and the first batch during the staging.
   constexpr bool I4 = std::is_same<W, WI4>::value;
+  const I4Bits kb = i4_bits();
   constexpr int LB = lm_batch<W>();
   constexpr int TW = lm_tiles<W>();
   const int ntiles = (V + 15) / 16;
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
 #pragma unroll
           for (int q = 0; q < TW; ++q) {
             const uint4 &aq = bf.a[q][j];
-            const uint4 e = i4_expand(kk == 0 ? aq.x : kk == 1 ? aq.y : kk == 2 ? aq.z : aq.w);
+            const uint4 e = i4_expand(kk == 0 ? aq.x : kk == 1 ? aq.y : kk == 2 ? aq.z : aq.w, kb);
 #pragma unroll
             for (int n = 0; n < NT; ++n) ag[q][n] = mfma_bf16(e, bv[n], ag[q][n]);
           }
