@@ -121,9 +121,6 @@ hipError_t launch_pack_lm_int4(const void *codes, const void *scales, int V, int
                                hipStream_t s);
 size_t lmhead_lds_bytes(int wdtype, int T, int H);
 // Commit fused into the LM head's last workgroup (done_count must be zero).
-// A block of more than 32 positions runs the head in two passes of at most
-// 32 positions (the staged block of 64 would not fit in LDS), each writing
-// its positions' partials, then the commit as its own kernel.
 struct LmCommit {
   int32_t *done_count;
   float threshold;

@@ -57,17 +57,32 @@ __device__ __forceinline__ void sm_merge(float &m, float &s, int &i, float m2, f
 // multiplies by the row's scale once per group.  Scales: 16 bf16 per (tile,
 // group), after all the codes; lane (li, g) reads those of its output rows
 // 4g .. 4g + 3.
-// units per tile per load batch, and tiles a wave streams side by side: a
-// 4-bit wave works on two tiles at once, so every block operand it reads from
-// LDS feeds both tiles' MFMAs (a bf16 tile is HBM-bound on its own)
-template <class W>
-constexpr int lm_batch() { return std::is_same<W, WI4>::value ? 2 : 8; }
-template <class W>
-constexpr int lm_tiles() { return std::is_same<W, WI4>::value ? 2 : 1; }
-template <class W>
+//
+// Units per tile per load batch, and tiles a wave streams side by side: a
+// 4-bit wave of a block of up to 32 positions works on two tiles at once, so
+// every block operand it reads from LDS feeds both tiles' MFMAs (a bf16 tile
+// is HBM-bound on its own).
+//
+// H phases: a block of up to 32 positions is staged whole (one phase).  A
+// wider one (64 positions: 256 KiB of bf16 at H = 2048) would not fit in
+// LDS, so the block is staged half of H at a time: each wave takes its tiles
+// in groups of lm_group() tile steps, runs the group's k-steps over the
+// staged half into per-tile accumulators, the workgroup restages the other
+// half, and the group's k-steps over that half finish its tiles.  The next
+// group starts with the half that is staged, so a workgroup restages once
+// per group, and every weight still streams once.
+template <class W, int NT>
+constexpr int lm_phases() { return NT > 2 ? 2 : 1; }
+template <class W, int NT>
+constexpr int lm_batch() { return std::is_same<W, WI4>::value ? 2 : (NT > 2 ? 4 : 8); }
+template <class W, int NT>
+constexpr int lm_tiles() { return std::is_same<W, WI4>::value && NT <= 2 ? 2 : 1; }
+template <class W, int NT>
+constexpr int lm_group() { return NT > 2 ? 2 : 1; }
+template <class W, int NT>
 struct LmBufs {
-  uint4 a[lm_tiles<W>()][lm_batch<W>()];
-  uint2 sc[lm_tiles<W>()][std::is_same<W, WI4>::value ? lm_batch<W>() : 1];
+  uint4 a[lm_tiles<W, NT>()][lm_batch<W, NT>()];
+  uint2 sc[lm_tiles<W, NT>()][std::is_same<W, WI4>::value ? lm_batch<W, NT>() : 1];
 };
 // A buffer offset past every LM-head tile: such a load returns zeros without
 // a memory access (pads the prefetches past a wave's last step).
@@ -242,54 +257,100 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   // flight during a tile's epilogue, and the first batch during the staging.
   constexpr bool I4 = std::is_same<W, WI4>::value;
   const I4Bits kb = i4_bits();
-  constexpr int LB = lm_batch<W>();
-  constexpr int TW = lm_tiles<W>();
+  constexpr int LB = lm_batch<W, NT>();
+  constexpr int TW = lm_tiles<W, NT>();
+  constexpr int PH = lm_phases<W, NT>();
+  constexpr int TG = lm_group<W, NT>();
+  static_assert(PH == 1 || TP == 64, "a phased block is staged one position per lane");
   const int ntiles = (V + 15) / 16;
   const int ksteps = NC / 4;                    // MFMA k-steps per tile
   const int lsteps = I4 ? ksteps / 4 : ksteps;  // KiB load units per tile
-  const int nb = (lsteps + LB - 1) / LB;
-  float *hs = reinterpret_cast<float *>(xs + NC * TP);   // [H / 128][16 NT]: group sums of h (WI4)
+  // phase 0 takes the first ceil(lsteps / PH) units of a tile, phase 1 the rest
+  const int lph0 = (lsteps + PH - 1) / PH;
+  const int cpu = NC / lsteps;                  // staged chunks per unit
+  const int NCP = lph0 * cpu;                   // staged chunks (the larger phase)
+  const int nb = (lph0 + LB - 1) / LB;          // load batches per tile and phase
+  float *hs = reinterpret_cast<float *>(xs + NCP * TP);   // [H / 128][16 NT]: group sums of h (WI4)
   const int first = uniform(wave * (int)gridDim.x + (int)blockIdx.x);
   const int stride = gridDim.x * kLmWaves;
   const int my_tiles = first < ntiles ? (ntiles - 1 - first) / stride + 1 : 0;
-  const int steps = (my_tiles + TW - 1) / TW * nb;   // TW tiles per step sequence
+  // with phases every wave runs the same steps (the restages are workgroup
+  // barriers): as many groups as the workgroup's first wave, which has the
+  // most tiles; a wave's steps past its own tiles load and fold nothing
+  const int tiles0 = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / stride + 1 : 0;
+  const int ngroups = ((tiles0 + TW - 1) / TW + TG - 1) / TG;
+  const int gsteps = PH * TG * nb;              // steps per group
+  const int steps = PH == 1 ? (my_tiles + TW - 1) / TW * nb : ngroups * gsteps;
+  // A step: tile step k (tiles TW k .. TW k + TW - 1 of the wave), batch b,
+  // the H phase hph it covers, its tile step kin within the group and
+  // whether it belongs to the group's second phase (which finishes the
+  // tiles).  Two cursors walk the steps by increments (no divisions): one for
+  // the MFMAs, one for the loads two steps ahead.
+  struct Step {
+    int k, b, hph, kin, pi, grp;
+    __device__ bool second() const { return pi == PH - 1; }
+    __device__ int u0(int l0) const { return hph * l0; }                       // the phase's first unit
+    __device__ int units(int l0, int ls) const { return hph ? ls - l0 : l0; }   // and its units
+    __device__ void next(int nbatch) {
+      if (++b < nbatch) return;
+      b = 0;
+      if (++kin < TG) {
+        ++k;
+        return;
+      }
+      kin = 0;
+      if (++pi < PH) {
+        k -= TG - 1;
+      } else {
+        pi = 0;
+        ++grp;
+        ++k;
+      }
+      hph = (grp & 1) ? PH - 1 - pi : pi;
+    }
+  };
   const uint32_t vbase = (uint32_t)lane * 16u;
   const uint32_t tile_bytes = I4 ? (uint32_t)(8 * H) : (uint32_t)(16 * H * (int)sizeof(typename W::T));
-  auto load = [&](int st, LmBufs<W> &bf) {
+  auto load = [&](int st, const Step &d, LmBufs<W, NT> &bf) {
     const bool live = st < steps;
-    const int k = live ? st / nb : 0, b = st - (st / nb) * nb;
 #pragma unroll
     for (int q = 0; q < TW; ++q) {
-      const int kt = TW * k + q;   // the wave's tile number (past my_tiles: no access)
+      const int kt = TW * d.k + q;   // the wave's tile number (past my_tiles: no access)
       const bool lq = live && kt < my_tiles;
       const size_t tile = (size_t)(first + (lq ? kt : 0) * stride);
       // descriptor over the tile's packed rows (rows past V were packed as zeros)
       const rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(wlm) + tile * tile_bytes, tile_bytes);
 #pragma unroll
-      for (int j = 0; j < LB; ++j)   // units past the tile or the stream: no access
-        bf.a[q][j] = buf_ld16(rs, lq && b * LB + j < lsteps ? vbase : kLmOutOfRange,
-                              (uint32_t)min(b * LB + j, lsteps - 1) * 1024u);
+      for (int j = 0; j < LB; ++j) {  // units past the phase or the stream: no access
+        const int u = d.b * LB + j;
+        bf.a[q][j] = buf_ld16(rs, lq && u < d.units(lph0, lsteps) ? vbase : kLmOutOfRange,
+                              (uint32_t)min(d.u0(lph0) + u, lsteps - 1) * 1024u);
+      }
       if constexpr (I4) {
         const rsrc_t rq = make_rsrc(scl + tile * (size_t)lsteps * 16, (uint32_t)lsteps * 32u);
 #pragma unroll
-        for (int j = 0; j < LB; ++j)
-          bf.sc[q][j] = buf_ld8(rq, lq && b * LB + j < lsteps ? (uint32_t)g * 8u : kLmOutOfRange,
-                                (uint32_t)min(b * LB + j, lsteps - 1) * 32u);
+        for (int j = 0; j < LB; ++j) {
+          const int u = d.b * LB + j;
+          bf.sc[q][j] = buf_ld8(rq, lq && u < d.units(lph0, lsteps) ? (uint32_t)g * 8u : kLmOutOfRange,
+                                (uint32_t)min(d.u0(lph0) + u, lsteps - 1) * 32u);
+        }
       }
     }
   };
-  f32x4 acc[TW][NT];
+  f32x4 acc[TG][TW][NT];
 #pragma unroll
-  for (int q = 0; q < TW; ++q)
+  for (int i = 0; i < TG; ++i)
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](int st, const LmBufs<W> &bf) {
-    const int b = st % nb;
+    for (int q = 0; q < TW; ++q)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[i][q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one step's MFMAs into the accumulators of tile step i of the group
+  auto mma_into = [&](f32x4 (&ac)[TW][NT], const Step &d, const LmBufs<W, NT> &bf) {
     if constexpr (I4) {
 #pragma unroll
       for (int j = 0; j < LB; ++j) {
-        const int grp = b * LB + j;
-        if (grp >= lsteps) break;
+        const int grp = d.b * LB + j;   // the group within the phase
+        if (grp >= d.units(lph0, lsteps)) break;
         f32x4 ag[TW][NT];
 #pragma unroll
         for (int q = 0; q < TW; ++q)
@@ -310,7 +371,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
         }
         float off[NT];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) off[n] = kI4Offset * hs[grp * TP + n * 16 + li];
+        for (int n = 0; n < NT; ++n) off[n] = kI4Offset * hs[(d.u0(lph0) + grp) * TP + n * 16 + li];
 #pragma unroll
         for (int q = 0; q < TW; ++q) {
           const uint2 sq = bf.sc[q][j];
@@ -318,7 +379,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
 #pragma unroll
           for (int n = 0; n < NT; ++n)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[q][n][r] = fmaf(sr[r], ag[q][n][r] - off[n], acc[q][n][r]);
+            for (int r = 0; r < 4; ++r) ac[q][n][r] = fmaf(sr[r], ag[q][n][r] - off[n], ac[q][n][r]);
         }
       }
       return;
@@ -326,30 +387,30 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
     const uint4(&a)[LB] = bf.a[0];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
-      const int ks = b * LB + j;
-      if (ks >= ksteps) break;
+      const int ks = d.b * LB + j;   // the k-step within the phase
+      if (ks >= d.units(lph0, lsteps)) break;
       const int c = ks * 4 + g;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const uint4 bv = xs[c * TP + n * 16 + li];
         if constexpr (std::is_same<W, WBf16>::value) {
-          acc[0][n] = mfma_bf16(a[j], bv, acc[0][n]);
+          ac[0][n] = mfma_bf16(a[j], bv, ac[0][n]);
         } else {
-          acc[0][n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), acc[0][n]);
-          acc[0][n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), acc[0][n]);
-          acc[0][n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), acc[0][n]);
-          acc[0][n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), acc[0][n]);
+          ac[0][n] = mfma_f32(__uint_as_float(a[j].x), __uint_as_float(bv.x), ac[0][n]);
+          ac[0][n] = mfma_f32(__uint_as_float(a[j].y), __uint_as_float(bv.y), ac[0][n]);
+          ac[0][n] = mfma_f32(__uint_as_float(a[j].z), __uint_as_float(bv.z), ac[0][n]);
+          ac[0][n] = mfma_f32(__uint_as_float(a[j].w), __uint_as_float(bv.w), ac[0][n]);
         }
       }
     }
   };
-  // epilogue of a finished tile: lane holds rows row0 + 4g + r (r = 0..3) of
-  // column li + 16n; fold them into the running (max, sum, argmax)
-  auto epilogue = [&](int st) {
+  // epilogue of a finished tile step: lane holds rows row0 + 4g + r (r =
+  // 0..3) of column li + 16n; fold them into the running (max, sum, argmax)
+  auto fold = [&](f32x4 (&ac)[TW][NT], int k) {
 #pragma unroll
     for (int q = 0; q < TW; ++q) {
     // (a tile past the wave's last has row0 >= V: it folds nothing)
-    const int row0 = (first + (TW * (st / nb) + q) * stride) * 16;
+    const int row0 = (first + (TW * k + q) * stride) * 16;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       float tmax = -FLT_MAX;
@@ -357,7 +418,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = row0 + 4 * g + r;
-        if (v < V && (targ == INT_MAX || acc[q][n][r] > tmax)) { tmax = acc[q][n][r]; targ = v; }
+        if (v < V && (targ == INT_MAX || ac[q][n][r] > tmax)) { tmax = ac[q][n][r]; targ = v; }
       }
       {
         const float m2 = partner_f32<16>(tmax, lane);
@@ -379,63 +440,128 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = row0 + 4 * g + r;
-        if (v < V) tsum += __expf(acc[q][n][r] - tmax);
+        if (v < V) tsum += __expf(ac[q][n][r] - tmax);
       }
       tsum += partner_f32<16>(tsum, lane);
       tsum += partner_f32<32>(tsum, lane);
       sm_merge(m[n], s[n], am[n], tmax, tsum, targ);
-      acc[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ac[q][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     }
   };
+  // a step's MFMAs (into the accumulators of its tile step in the group)
+  auto run = [&](const Step &d, const LmBufs<W, NT> &bf) {
+#pragma unroll
+    for (int i = 0; i < TG; ++i)
+      if (d.kin == i) mma_into(acc[i], d, bf);
+  };
+  // Phased staging: one wave instruction gathers chunk c of the half into
+  // xs[c][*] straight from memory (lane t: position t, 16 bytes; positions
+  // past T read as zeros), so no registers hold the block while the weight
+  // loads stay in flight.
+  const rsrc_t rh = make_rsrc(hhat, (uint32_t)(T * H) * (uint32_t)sizeof(typename W::T));
+  auto stage_half = [&](int hph) {
+    const uint32_t vo = lane < T ? (uint32_t)lane * (uint32_t)H * (uint32_t)sizeof(typename W::T) : kLmOutOfRange;
+    const int nc = (hph ? lsteps - lph0 : lph0) * cpu;
+    for (int c = wave; c < nc; c += kLmWaves)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rh, (__attribute__((address_space(3))) void *)(xs + c * TP), 16, (int)vo,
+          (int)((uint32_t)((hph * NCP + c) * CH) * (uint32_t)sizeof(typename W::T)), 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);   // (the lgkm/vm counts: the gathers have landed)
+  };
 
-  LmBufs<W> a0, a1;
-  load(0, a0);
-  load(1, a1);
-  // stage the block: batches of 8 independent loads per thread
-  for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
-    uint4 v[8];
+  Step cc = {0, 0, 0, 0, 0, 0}, cl = cc;   // compute and load cursors
+  LmBufs<W, NT> a0, a1;
+  load(0, cl, a0);
+  cl.next(nb);
+  load(1, cl, a1);
+  cl.next(nb);
+  if constexpr (PH == 1) {
+    // stage the block: batches of 8 independent loads per thread
+    for (int base = tid; base < TP * NC; base += 8 * (int)blockDim.x) {
+      uint4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const int t = idx / NC, c = idx - t * NC;
-      v[j] = (idx < TP * NC && t < T) ? ld16(hhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
-    }
+      for (int j = 0; j < 8; ++j) {
+        const int idx = base + j * (int)blockDim.x;
+        const int t = idx / NC, c = idx - t * NC;
+        v[j] = (idx < TP * NC && t < T) ? ld16(hhat + (size_t)t * H + (size_t)c * CH) : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int idx = base + j * (int)blockDim.x;
-      const int t = idx / NC, c = idx - t * NC;
-      if (idx < TP * NC) xs[c * TP + t] = v[j];
+      for (int j = 0; j < 8; ++j) {
+        const int idx = base + j * (int)blockDim.x;
+        const int t = idx / NC, c = idx - t * NC;
+        if (idx < TP * NC) xs[c * TP + t] = v[j];
+      }
     }
+  } else {
+    stage_half(0);
   }
-  __syncthreads();
   if constexpr (I4) {
-    // per (group, position): the sum of the group's 128 values of h
+    // per (group, position): the sum of the group's 128 values of h, from
+    // the staged block, or with phases (the staged block holds half of H)
+    // from memory, its 16 loads in flight together; the same sum order
+    if constexpr (PH == 1) __syncthreads();
     for (int idx = tid; idx < (H / kI4Group) * TP; idx += (int)blockDim.x) {
       const int grp = idx / TP, t = idx - grp * TP;
       float sum = 0.f;
-      for (int c = grp * (kI4Group / 8); c < (grp + 1) * (kI4Group / 8); ++c) {
-        float f[8];
-        unpack8(xs[c * TP + t], f);
+      if constexpr (PH == 1) {
+        for (int c = grp * (kI4Group / 8); c < (grp + 1) * (kI4Group / 8); ++c) {
+          float f[8];
+          unpack8(xs[c * TP + t], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum += f[e];
+          for (int e = 0; e < 8; ++e) sum += f[e];
+        }
+      } else if (t < T) {
+        uint4 v[kI4Group / 8];
+#pragma unroll
+        for (int c = 0; c < kI4Group / 8; ++c) v[c] = ld16(hhat + (size_t)t * H + (size_t)(grp * (kI4Group / 8) + c) * 8);
+#pragma unroll
+        for (int c = 0; c < kI4Group / 8; ++c) {
+          float f[8];
+          unpack8(v[c], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum += f[e];
+        }
       }
       hs[idx] = sum;
     }
-    __syncthreads();
   }
+  __syncthreads();
   // A buffer is refilled as soon as its MFMAs have read it, before a tile's
   // epilogue, so two batches stay in flight through the epilogue.  Loads past
   // the last step are out of range (no access): the loop always has the same
   // loads in flight and the compiler's in-order wait counts stay exact.
+  // After a step: the tile step's epilogue after its last batch of the
+  // group's second phase, or the restage after the group's first phase (the
+  // same step in every wave).
+  auto after = [&](const Step &d) {
+    if (d.b != nb - 1) return;
+    if (d.second()) {
+#pragma unroll
+      for (int i = 0; i < TG; ++i)
+        if (d.kin == i) fold(acc[i], d.k);
+    } else {
+      if constexpr (PH > 1) {
+        if (d.kin == TG - 1) {
+          __syncthreads();   // every wave is done with the staged half
+          stage_half(1 - d.hph);
+          __syncthreads();
+        }
+      }
+    }
+  };
   for (int st = 0; st < steps; st += 2) {
-    mma(st, a0);
-    load(st + 2, a0);
-    if (st % nb == nb - 1) epilogue(st);
+    run(cc, a0);
+    load(st + 2, cl, a0);
+    cl.next(nb);
+    after(cc);
+    cc.next(nb);
     if (st + 1 >= steps) break;
-    mma(st + 1, a1);
-    load(st + 3, a1);
-    if ((st + 1) % nb == nb - 1) epilogue(st + 1);
+    run(cc, a1);
+    load(st + 3, cl, a1);
+    cl.next(nb);
+    after(cc);
+    cc.next(nb);
   }
 
   if (lane < 16) {
@@ -559,9 +685,15 @@ int lmhead_grid(int cus, int V) {
 }
 
 size_t lmhead_lds_bytes(int wdtype, int T, int H) {
-  const int tp = T <= 16 ? 16 : 32;
+  // (above 32 positions the staged block holds the first ceil(units / 2)
+  // load units' columns: two phases)
+  const int tp = T <= 16 ? 16 : T <= 32 ? 32 : 64;
+  const int ph = T <= 32 ? 1 : 2;
   const int ch = wdtype == 0 ? 4 : 8;
-  return (size_t)(H / ch) * tp * 16 + (wdtype == 2 ? (size_t)(H / kI4Group) * tp * 4 : 0);
+  const int unit_cols = wdtype == 2 ? kI4Group : 4 * ch;    // columns of one load unit
+  const int units = H / unit_cols;
+  const size_t chunks = (size_t)((units + ph - 1) / ph) * (unit_cols / ch);
+  return chunks * tp * 16 + (wdtype == 2 ? (size_t)(H / kI4Group) * tp * 4 : 0);
 }
 
 template <typename F>
@@ -593,29 +725,19 @@ static hipError_t lmhead_launch(const void *hhat, const void *w_lm, int T, int H
 hipError_t launch_lmhead(int wdtype, const void *hhat, const void *w_lm, int T, int H, int V,
                          float *part_m, float *part_s, int32_t *part_i, int grid, const LmCommit *fused,
                          hipStream_t s) {
-  if (T > 32) {
-    // two passes over the vocabulary, positions 0..31 and 32..T-1 (partials
-    // [T][grid]: the second pass writes rows 32..), then the commit
-    const LmCommit gate_only = {nullptr, 0.f, nullptr, nullptr, nullptr, nullptr, fused ? fused->gate : nullptr,
-                                nullptr};
-    const size_t es = wdtype == 0 ? 4 : 2;
-    const size_t off = (size_t)32 * grid;
-    hipError_t err = launch_lmhead(wdtype, hhat, w_lm, 32, H, V, part_m, part_s, part_i, grid, &gate_only, s);
-    if (err != hipSuccess) return err;
-    err = launch_lmhead(wdtype, static_cast<const char *>(hhat) + (size_t)32 * H * es, w_lm, T - 32, H, V,
-                        part_m + off, part_s + off, part_i + off, grid, &gate_only, s);
-    if (err != hipSuccess || !fused || !fused->done_count) return err;
-    return launch_commit(part_m, part_s, part_i, grid, T, fused->threshold, fused->tokens, fused->conf,
-                         fused->choice, fused->round_info, s, fused->gate, fused->resolved_flag);
-  }
+  // one, two or four 16-position column tiles (four: the block staged half
+  // of H at a time)
   if (wdtype == 2)
-    return T <= 16 ? lmhead_launch<WI4, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
-                   : lmhead_launch<WI4, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
+    return T <= 16   ? lmhead_launch<WI4, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+           : T <= 32 ? lmhead_launch<WI4, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+                     : lmhead_launch<WI4, 4>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
   if (wdtype == 1)
-    return T <= 16 ? lmhead_launch<WBf16, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
-                   : lmhead_launch<WBf16, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
-  return T <= 16 ? lmhead_launch<WF32, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
-                 : lmhead_launch<WF32, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
+    return T <= 16   ? lmhead_launch<WBf16, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+           : T <= 32 ? lmhead_launch<WBf16, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+                     : lmhead_launch<WBf16, 4>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
+  return T <= 16   ? lmhead_launch<WF32, 1>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+         : T <= 32 ? lmhead_launch<WF32, 2>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s)
+                   : lmhead_launch<WF32, 4>(hhat, w_lm, T, H, V, part_m, part_s, part_i, grid, fused, s);
 }
 
 hipError_t launch_block_start(int32_t *tokens, int T, int32_t *info, int words, int32_t *flag, hipStream_t s) {

@@ -31,8 +31,8 @@
  *     multiple of 128 for the MoE layer (of 32 for the LM head alone); I,
  *     I_shared multiples of 32; H <= 2048 for the LM head when T > 16 (the
  *     block's normalised hidden states are kept in the 160 KiB LDS of one CU;
- *     a block of more than 32 positions is read in two passes of at most 32,
- *     so the LM head streams its weight twice).
+ *     a block of more than 32 positions is kept half of H at a time, and the
+ *     LM head still streams its weight once).
  */
 #ifndef BDD_H
 #define BDD_H

@@ -246,7 +246,7 @@ def _clear_lm_resolve(h, wl, tau, rounds):
 @pytest.mark.parametrize("dt,T", [("bf16", 7), ("f32", 7), ("bf16", 64), ("f32", 45)])
 @pytest.mark.parametrize("seed", [0, 1])
 def test_lmhead_commit_multiround_small(dt, T, seed):
-    # T above 32: two passes of the head over position halves, then the commit
+    # T above 32: the head stages the block half of H at a time (two phases)
     d = _lm_dims(dt, T=T)
     # enough rounds for the block to resolve: a masked position passes with
     # probability 0.3 per round (plus the forced commit)
@@ -369,7 +369,7 @@ ROUND_CASES = {
     # (failing amplitudes spread so that confidences straddle the threshold)
     "bf16_2layers_coreset_tau0.8": (None, 2, "zipf", 0.7, (40.0, (6.0, 16.0)), 0.8),
     "bf16_2layers_coreset_tau0.99": (None, 2, "zipf", 0.9, (40.0, (8.0, 24.0)), 0.99),
-    # blocks of 64 and of 45 positions (four column tiles, two LM-head passes)
+    # blocks of 64 and of 45 positions (four column tiles, the LM head in two H phases)
     "bf16_block64_2layers_coreset": (W.Dims("small_bf16_block64", T=64, H=256, E=40, K=6, I=96, I_s=64, V=5003,
                                             wdtype="bf16", w_std=0.05, lm_std=256 ** -0.5),
                                      2, "zipf", 0.7, (40.0, (4.0, 9.0)), 0.95),
