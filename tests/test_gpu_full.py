@@ -116,6 +116,33 @@ def test_lmhead_commit_full_resolve(lm_full, p, tau):
     print(f"p={p} threshold {tau}: resolved in {rounds} rounds with {fallbacks} fallback rounds")
 
 
+def test_lmhead_commit_full_vocabulary_block64(lm_full):
+    """Three rounds of the LM head + commit over a block of 64 positions at the
+    full vocabulary: the head stages the block half of H at a time, and with
+    248320 tokens every workgroup runs several tile groups and restages."""
+    seed, lm, wl = lm_full
+    d = dataclasses.replace(C1, name="clover_block64", T=64)
+    R, tau = 3, 0.95
+    h, _ = W.lmhead_stub_inputs(seed, d, R, p=0.3, pass_logit=LEVELS[tau][0], fail_logit=LEVELS[tau][1])
+    tok = torch.full((d.T,), bdd.MASK, dtype=torch.int32, device=DEV)
+    tok_ref = np.full(d.T, O.MASK)
+    ws = torch.empty(bdd.lmhead_workspace_bytes(d.T, d.H, d.V), dtype=torch.uint8, device=DEV)
+    for r in range(R):
+        hr = h[r].contiguous().to(DEV)
+        conf, choice, ri = bdd.lmhead_confidence_commit(hr, lm, tok, threshold=tau, ws=ws)
+        torch.cuda.synchronize()
+        c_ref, ch_ref, z = O.lm_head_confidence(f64(hr), wl)
+        assert_close(conf.cpu().numpy(), c_ref, f"conf round {r}")
+        ok = top2_gap(z) >= BAND
+        assert ok.sum() >= d.T - 2
+        assert np.array_equal(choice.cpu().numpy()[ok], ch_ref[ok])
+        assert not commit_in_band(tok_ref, c_ref, tau), f"round {r}: stub landed in the margin band"
+        tok_ref, acc, fb, left, done = O.commit(tok_ref, c_ref, ch_ref, tau)
+        assert np.array_equal(tok.cpu().numpy(), tok_ref), r
+        assert ri.cpu().tolist() == [len(acc), int(fb), left, int(done)]
+    assert (tok_ref != O.MASK).sum() > 0
+
+
 def test_full_round_clover_layer_plus_lm_head(lm_full):
     """The benchmark's round: one Clover-shaped MoE layer (flat routing), final
     RMSNorm, the full LM head and the commit; two rounds checked."""
