@@ -13,7 +13,7 @@
 // flat routing, so its contraction is a matrix-vector product: VALU dot
 // products on weights streamed with 16-byte buffer loads.  Work items are
 // (token group, row tile); a token group is up to kTokGroup positions of one
-// expert (the selection kernel lists them).  A wave owns 8 weight rows of its
+// expert (see the work lists below).  A wave owns 8 weight rows of its
 // item; lane l covers 16-byte chunks l, l + 64, ... of every row, so a load
 // instruction reads one contiguous 1 KiB segment of a row.  The positions'
 // activations are read per chunk straight from L2 next to the weights, so the
