@@ -1,8 +1,8 @@
 """GPU check of bdd_block_denoise_round_noalloc (the round without a
 workspace, on the library's static per-GPU scratch): through the C ABI, its
 outputs equal those of bdd_block_denoise_round on the same inputs, bit for
-bit (the same kernels in the same order), for two calls in a row, the second
-on a smaller block and layer stack than the first."""
+bit (the same kernels in the same order), for calls in a row, each on a
+smaller block or layer stack than the one before (64, 32, then 13 positions)."""
 
 import numpy as np
 import pytest
@@ -15,6 +15,8 @@ from gpu_helpers import dims_of
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
+WIDE = W.Dims("noalloc_wide", T=64, H=1024, E=64, K=8, I=256, I_s=256, V=20011, wdtype="bf16", w_std=0.03,
+              lm_std=1024 ** -0.5)
 BIG = W.Dims("noalloc_big", T=32, H=1024, E=64, K=8, I=256, I_s=256, V=20011, wdtype="bf16", w_std=0.03,
              lm_std=1024 ** -0.5)
 SMALL = W.Dims("noalloc_small", T=13, H=256, E=40, K=6, I=96, I_s=64, V=5003, wdtype="bf16", w_std=0.05,
@@ -54,6 +56,10 @@ def _run_both(d, x, plan, L, rounds):
 
 
 def test_noalloc_round_matches_the_workspace_round_twice_in_a_row():
+    print("noalloc: wide case (T 64, H 1024, 2 layers, coreset 0.9)", flush=True)
+    x0, plan0 = _case(WIDE, 2, 2, 0.9, 3)
+    assert bdd.round_workspace_bytes(plan0.d, plan0.V) <= bdd.NOALLOC_SCRATCH_BYTES
+    n0 = _run_both(WIDE, x0, plan0, 2, 3)
     print("noalloc: big case (T 32, H 1024, 2 layers, coreset 0.9)", flush=True)
     x, plan = _case(BIG, 0, 2, 0.9, 4)
     assert bdd.round_workspace_bytes(plan.d, plan.V) <= bdd.NOALLOC_SCRATCH_BYTES
@@ -61,4 +67,4 @@ def test_noalloc_round_matches_the_workspace_round_twice_in_a_row():
     print("noalloc: small case (T 13, H 256, 1 layer, no coreset)", flush=True)
     x2, plan2 = _case(SMALL, 1, 1, 1.0, 3)
     n2 = _run_both(SMALL, x2, plan2, 1, 3)
-    assert n1 > 0 and n2 > 0
+    assert n0 > 0 and n1 > 0 and n2 > 0
