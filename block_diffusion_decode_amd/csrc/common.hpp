@@ -109,20 +109,43 @@ __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff
 // agent-scope atomics, so on this multi-XCD part they are not kept in a
 // per-XCD L2.  The publishing workgroup's waves meet at a barrier (whose
 // workgroup-scope release orders every wave's stores before it), then one
-// thread increments the workgroup counter with an agent-scope acquire-release
-// read-modify-write.  The workgroup whose increment returns the last count
-// has acquired every earlier increment, hence every value published before
-// it; a barrier then passes that on to its other waves.
+// thread increments the workgroup counter with an agent-scope release
+// read-modify-write.  Only the workgroup whose increment returns the last
+// count takes an agent-scope acquire fence: its increment read the end of the
+// counter's release sequence, so the fence makes every value published before
+// any earlier increment visible to it, and a barrier then passes that on to
+// its other waves.  (An agent-scope acquire invalidates the XCD's L2 and a
+// release writes it back; the workgroups that are not last take neither the
+// invalidate nor an acquire they do not use.)
 template <typename T>
 __device__ __forceinline__ void publish(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 template <typename T>
 __device__ __forceinline__ T fetch_published(const T *p) {
   return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Counts this workgroup as done (release of what it published, acquire of
-// what the workgroups counted before it) and returns the previous count.
-__device__ __forceinline__ int count_done(int32_t *counter) {
-  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// Counts this workgroup as done (release of what it published) and returns
+// whether it is the last of n; the last one has acquired what all the others
+// published.
+__device__ __forceinline__ bool count_done_last(int32_t *counter, int n) {
+  const bool last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+// Waits until *flag (set by an agent-scope release store) is nonzero, with
+// relaxed loads, then acquires once; gives up after max_spins sleeps and
+// returns false.
+__device__ __forceinline__ bool wait_flag(const int32_t *flag, int max_spins) {
+  int n = 0;
+  bool ok = true;
+  while (__hip_atomic_load(const_cast<int32_t *>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+    if (++n > max_spins) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
 }
 
 // ---------------------------------------------------------------- block-resident rounds

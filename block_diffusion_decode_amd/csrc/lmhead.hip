@@ -221,7 +221,8 @@ __global__ __launch_bounds__(256) void block_start_kernel(int32_t *__restrict__ 
 // multiplies them by the staged positions on MFMA, and folds the 16 x 32
 // logits into its running (max, sum, argmax).
 // With `done_count` given, the workgroup that finishes last (agent-scope
-// acquire-release counter over partials published as agent-scope atomics)
+// release counter over partials published as agent-scope atomics; the last
+// one acquires)
 // also merges the partials and runs the commit, then clears the counter.  The
 // counter must be zero when the kernel starts.
 template <class W, int NT>
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
   if (done_count == nullptr) return;
   __shared__ int s_last;
   __syncthreads();   // the published partials are ordered before the count
-  if (tid == 0) s_last = count_done(done_count) == (int)gridDim.x - 1;
+  if (tid == 0) s_last = count_done_last(done_count, (int)gridDim.x);
   __syncthreads();   // the last workgroup's waves read after its acquire
   if (!s_last) return;
   commit_block(part_m, part_s, part_i, gridDim.x, T, threshold, tokens, conf, choice, round_info, resolved_flag);

@@ -631,19 +631,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
       atomicOr(r.sync.mask1 + e_sorted, 1ull << t);
     }
     __syncthreads();
-    if (tid == 0) s_last = count_done(r.sync.words + 1) == T - 1;
+    if (tid == 0) s_last = count_done_last(r.sync.words + 1, T);
     __syncthreads();
     if (s_last) {
       coreset_step(r, E, top_p, s_wave, s_cb, &s_csize);
     } else if (tid == 0) {
-      int n = 0;
-      while (__hip_atomic_load(r.sync.words, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-        if (++n > kSelSpinMax) {
-          r.meta[4] = 1;    // the coreset was never published: reported, and the wait ends
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
+      // the coreset never published: reported, and the wait ends
+      if (!wait_flag(r.sync.words, kSelSpinMax)) r.meta[4] = 1;
     }
     __syncthreads();
     if (!s_last) {
