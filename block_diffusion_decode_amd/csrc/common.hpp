@@ -131,14 +131,18 @@ __device__ __forceinline__ bool count_done_last(int32_t *counter, int n) {
   if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return last;
 }
-// Waits until *flag (set by an agent-scope release store) is nonzero, with
-// relaxed loads, then acquires once; gives up after max_spins sleeps and
-// returns false.
-__device__ __forceinline__ bool wait_flag(const int32_t *flag, int max_spins) {
-  int n = 0;
+// Counts this workgroup (agent-scope release increment), then waits until
+// the counter reaches n, with relaxed loads, and acquires once: after it,
+// every value the n counted workgroups published before their increments is
+// visible.  Gives up after max_spins sleeps and returns false.  (It waits for
+// workgroups that may not have started, so n must not exceed the workgroups
+// the device runs at once.)
+__device__ __forceinline__ bool count_and_wait_all(int32_t *counter, int n, int max_spins) {
+  __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  int spins = 0;
   bool ok = true;
-  while (__hip_atomic_load(const_cast<int32_t *>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-    if (++n > max_spins) {
+  while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+    if (++spins > max_spins) {
       ok = false;
       break;
     }

@@ -17,11 +17,10 @@ struct SelSync {
   unsigned long long *mass_fx;  // [E] block expert mass of the first picks, units of 2^-56
   posmask_t *mask1;             // [E] positions whose first picks include the expert
   posmask_t *mask2;             // [E] positions whose final picks include the expert
-  uint32_t *cbits;              // [8] coreset membership, published for the positions
-  int32_t *words;               // [0] coreset published, [1] first count, [2] unused, [3] coreset size
+  int32_t *words;               // [0] positions counted (coreset)
 };
 // (the slot words first: 16-byte aligned rows of kMaxT bytes per expert)
-inline size_t sel_sync_bytes(int E) { return (size_t)E * (kMaxT + 8 + 8 + 8) + 32 + 64; }
+inline size_t sel_sync_bytes(int E) { return (size_t)E * (kMaxT + 8 + 8 + 8) + 64; }
 inline SelSync sel_sync_at(void *base, int E) {
   char *b = static_cast<char *>(base);
   SelSync s;
@@ -29,8 +28,7 @@ inline SelSync sel_sync_at(void *base, int E) {
   s.mass_fx = reinterpret_cast<unsigned long long *>(b + (size_t)E * kMaxT);
   s.mask1 = reinterpret_cast<posmask_t *>(b + (size_t)E * (kMaxT + 8));
   s.mask2 = reinterpret_cast<posmask_t *>(b + (size_t)E * (kMaxT + 16));
-  s.cbits = reinterpret_cast<uint32_t *>(b + (size_t)E * (kMaxT + 24));
-  s.words = reinterpret_cast<int32_t *>(b + (size_t)E * (kMaxT + 24) + 32);
+  s.words = reinterpret_cast<int32_t *>(b + (size_t)E * (kMaxT + 24));
   return s;
 }
 
@@ -39,7 +37,7 @@ struct RouteBufs {
   float *logits;       // [H/128][T][E] router logit slices (bias not added)
   int32_t *idx;        // [T][K]   picked experts (-1 = unused slot)
   float *wgt;          // [T][K]   their renormalised weights
-  int32_t *meta;       // [0] union size, [1] coreset size, [4] set if a wait for the coreset timed out
+  int32_t *meta;       // [0] union size, [1] coreset size, [4] set if the wait for the positions' counts timed out
   uint32_t *cs_bits;   // [8]      coreset membership bitset
   float *mass;         // [E]      block expert mass (with the coreset)
   SelSync sync;        // selection kernel's cross-workgroup state

@@ -387,31 +387,31 @@ __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
 
 // ------------------------------------------------------------------ route + select
 // One workgroup of kSelThreads per position: softmax over the position's E
-// router logits and a bitonic sort of (logit desc, expert id asc), so its
-// top-K is the prefix of its sorted list.  The block-level steps run mostly
-// in these workgroups, in parallel:
+// router logits and its expert order (logit desc, expert id asc), the rank of
+// each expert counted over all keys, so its top-K are ranks 0 .. K-1.  The
+// block-level steps run in these workgroups, in parallel:
 //   - with the coreset, each adds its first picks' softmax scores to the block
 //     mass (64-bit fixed-point atomics: the sums are exact, so their order
-//     does not matter) and its bit to each picked expert's position mask; the
-//     workgroup counted last ranks the experts, cuts the coreset and publishes
-//     it behind a release flag; the others wait for the flag (acquire) and
-//     each re-takes its position's first min(K, |C|) coreset members in its
-//     own sorted order;
+//     does not matter) and its bit to each picked expert's position mask,
+//     counts itself, and waits until all T positions are counted; then each
+//     ranks the experts and cuts the coreset itself (the same exact sums give
+//     every workgroup the same coreset, so nothing is handed back) and
+//     re-takes its position's first min(K, |C|) coreset members in its own
+//     order;
 //   - each writes its final picks and weights, and adds its bit and pick slot
 //     to each picked expert's mask and slot word.  The expert kernels build
-//     the union and their work lists from these (after the kernel boundary),
-//     so the selection ends with its positions: no workgroup waits for the
-//     last one to finish the block.
-// The waiting workgroups have all been counted, so the one they wait for is
-// running: the wait needs no co-residency.  It is bounded all the same (every
-// wave leaves it), and a timeout is reported in meta[4].
+//     the union and their work lists from these (after the kernel boundary).
+// The wait is for the other positions' workgroups, which the dispatcher
+// starts first (T <= 64 of them, far fewer than the device runs at once).  It
+// is bounded all the same (every wave leaves it), and a timeout is reported in
+// meta[4].
 // Workgroups past the T positions compute the shared expert's gate/up (it
 // needs only the normalised block), so its weights stream while selection
 // runs: workgroup T + j takes intermediate units 16 j .. 16 j + 15.
 constexpr int kSelThreads = 256;
 static_assert(kSelThreads == 256, "the shared gate/up item runs on four waves");
 static_assert(kSelThreads >= kMaxE, "one thread per expert in the block steps");
-constexpr int kSelSpinMax = 1 << 21;          // bound of the wait for the coreset (~0.1 s)
+constexpr int kSelSpinMax = 1 << 21;          // bound of the wait for the positions' counts (~0.1 s)
 constexpr double kMassScale = 72057594037927936.0;   // 2^56: fixed-point unit of the block mass
 
 // Shared-expert operands for the workgroups past the positions.
@@ -428,11 +428,6 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   const uint32_t u = __float_as_uint(v);
   const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ~asc;
-}
-
-__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  return ((unsigned long long)(uint32_t)__shfl_xor((int)hi, m) << 32) | (uint32_t)__shfl_xor((int)lo, m);
 }
 
 // Exclusive prefix over the workgroup of flags (0/1), via ballots; returns
@@ -453,14 +448,17 @@ __device__ __forceinline__ int block_flag_scan(bool flag, int *s_wave, int *tota
   return off + __popcll(b & lanes_below(lane));
 }
 
-// The coreset step ([P2] coreset section), by the workgroup counted last:
-// experts with a first pick, ranked by (mass desc, id asc) from the exact
-// fixed-point masses; the shortest ranked prefix whose cumulative mass reaches
-// top_p of the total; its bitset published for the other positions.
-// It runs after the workgroup's acquire (count and barrier), so the other
-// workgroups' atomics are visible to plain loads, all issued at once.  The
-// coreset is left in s_cb / *s_csize for the caller.
-__device__ void coreset_step(const RouteBufs &r, int E, float top_p, int *s_wave, uint32_t *s_cb, int *s_csize) {
+// The coreset step ([P2] coreset section), in every position's workgroup
+// once all positions are counted: experts with a first pick, ranked by (mass
+// desc, id asc) from the exact fixed-point masses; the shortest ranked prefix
+// whose cumulative mass reaches top_p of the total.  The masses are exact
+// integer sums, so every workgroup finds the same coreset; it is left in
+// s_cb / *s_csize, and the workgroup with `report` also writes the bitset,
+// the masses and the size out.  It runs after the workgroup's acquire (the
+// count and a barrier), so the other workgroups' atomics are visible to plain
+// loads, all issued at once.
+__device__ void coreset_step(const RouteBufs &r, int E, float top_p, int *s_wave, uint32_t *s_cb, int *s_csize,
+                             bool report) {
   __shared__ unsigned long long s_um[kMaxE];
   __shared__ int s_ue[kMaxE], s_rank[kMaxE], s_sorted[kMaxE];
   __shared__ unsigned long long s_cum[kMaxE];
@@ -538,33 +536,30 @@ __device__ void coreset_step(const RouteBufs &r, int E, float top_p, int *s_wave
   __syncthreads();
   const int k = max(1, min(s_below + 1, nu));
   if (tid < k) atomicOr(&s_cb[s_sorted[tid] >> 5], 1u << (s_sorted[tid] & 31));
+  if (tid == 0) *s_csize = k;
   __syncthreads();
-  if (tid < (E + 31) / 32) {
-    publish(r.sync.cbits + tid, s_cb[tid]);
-    r.cs_bits[tid] = s_cb[tid];
+  if (report) {
+    if (tid < (E + 31) / 32) r.cs_bits[tid] = s_cb[tid];
+    if (tid < E) r.mass[tid] = (float)((double)m / kMassScale);
+    if (tid == 0) {
+      r.meta[1] = k;
+      if (r.coreset_size_out) *r.coreset_size_out = k;
+    }
   }
-  if (tid < E) r.mass[tid] = (float)((double)m / kMassScale);
-  if (tid == 0) {
-    publish(r.sync.words + 3, k);
-    *s_csize = k;
-    r.meta[1] = k;
-    if (r.coreset_size_out) *r.coreset_size_out = k;
-  }
-  __syncthreads();   // every published word is ordered before the flag
-  if (tid == 0) __hip_atomic_store(r.sync.words, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class W, int NT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const float *__restrict__ bias,
                                                              int KS, int T, int E, int K, float top_p,
                                                              SharedGU<W> sg) {
-  __shared__ unsigned long long s_key[kSelThreads];
+  __shared__ __align__(16) unsigned long long s_key[kSelThreads];
+  __shared__ int s_order[kSelThreads];
   __shared__ float s_p[kSelThreads];
   __shared__ float s_red[kSelThreads / 64];
   __shared__ int s_wave[kSelThreads / 64];
   __shared__ int s_pick[kMaxK];
   __shared__ uint32_t s_cb[kMaxE / 32];
-  __shared__ int s_last, s_csize;
+  __shared__ int s_csize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
   if (gated_off(r.gate)) return;
@@ -604,24 +599,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
   __syncthreads();
   sum = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
   s_p[tid] = ex / sum;
-  // bitonic sort, ascending on (order_key(logit), id); padding sorts last
-  unsigned long long key = tid < E ? (((unsigned long long)order_key(l) << 32) | (uint32_t)tid) : ~0ull;
-  for (int k = 2; k <= kSelThreads; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      unsigned long long other;
-      if (j >= 64) {
-        __syncthreads();
-        s_key[tid] = key;
-        __syncthreads();
-        other = s_key[tid ^ j];
-      } else {
-        other = shfl_xor64(key, j);
-      }
-      const bool lower = (tid & j) == 0, asc = (tid & k) == 0;
-      key = (lower == asc) ? (key < other ? key : other) : (key < other ? other : key);
+  // the position's expert order, ascending on (order_key(logit), id): each
+  // expert's rank is the number of keys below its own (the keys are distinct),
+  // counted over the keys in LDS with broadcast reads
+  const unsigned long long key = tid < E ? (((unsigned long long)order_key(l) << 32) | (uint32_t)tid) : ~0ull;
+  s_key[tid] = key;
+  __syncthreads();
+  int rank = tid;   // (padding past E keeps its own slot)
+  if (tid < E) {
+    const ulonglong2 *kp = reinterpret_cast<const ulonglong2 *>(s_key);
+    int below = 0;
+#pragma unroll 8
+    for (int j = 0; j < (E + 1) / 2; ++j) {   // (an odd E reads padding key E, which is never below)
+      const ulonglong2 v = kp[j];
+      below += (int)(v.x < key) + (int)(v.y < key);
     }
+    rank = below;
   }
-  const int e_sorted = (int32_t)(uint32_t)key;   // rank tid of the position's sorted list
+  s_order[rank] = tid;
+  __syncthreads();
+  const int e_sorted = tid < E ? s_order[tid] : -1;   // the expert of rank tid
   const bool coreset = top_p < 1.0f;
   int kk = K;
   if (coreset) {
@@ -631,21 +628,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(RouteBufs r, const 
       atomicOr(r.sync.mask1 + e_sorted, 1ull << t);
     }
     __syncthreads();
-    if (tid == 0) s_last = count_done_last(r.sync.words + 1, T);
+    // the positions' timeout is reported, and the wait ends
+    if (tid == 0 && !count_and_wait_all(r.sync.words, T, kSelSpinMax)) r.meta[4] = 1;
     __syncthreads();
-    if (s_last) {
-      coreset_step(r, E, top_p, s_wave, s_cb, &s_csize);
-    } else if (tid == 0) {
-      // the coreset never published: reported, and the wait ends
-      if (!wait_flag(r.sync.words, kSelSpinMax)) r.meta[4] = 1;
-    }
-    __syncthreads();
-    if (!s_last) {
-      // after the acquire of the flag: plain loads
-      if (tid < kMaxE / 32) s_cb[tid] = tid < (E + 31) / 32 ? r.sync.cbits[tid] : 0u;
-      if (tid == 0) s_csize = r.sync.words[3];
-    }
-    __syncthreads();
+    coreset_step(r, E, top_p, s_wave, s_cb, &s_csize, t == 0);
     // re-routing: the first min(K, |C|) coreset members in this position's order
     const int es = e_sorted & (kMaxE - 1);   // (padding lanes past E hold no expert)
     const bool member = tid < E && ((s_cb[es >> 5] >> (es & 31)) & 1u);
