@@ -411,7 +411,7 @@ __device__ void write_bits(const SelShared &sh, int E, uint32_t *bits) {
 constexpr int kSelThreads = 256;
 static_assert(kSelThreads == 256, "the shared gate/up item runs on four waves");
 static_assert(kSelThreads >= kMaxE, "one thread per expert in the block steps");
-constexpr int kSelSpinMax = 1 << 21;          // bound of the wait for the positions' counts (~0.1 s)
+constexpr int kSelSpinMax = 1 << 17;          // bound of the wait for the positions' counts: polls of ~1 us, ~0.1-0.2 s
 constexpr double kMassScale = 72057594037927936.0;   // 2^56: fixed-point unit of the block mass
 
 // Shared-expert operands for the workgroups past the positions.
