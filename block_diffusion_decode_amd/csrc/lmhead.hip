@@ -551,13 +551,18 @@ __global__ __launch_bounds__(1024) void lmhead_kernel(const typename W::T *__res
       }
     }
   };
+  // Always two steps per trip (an odd count runs one step past the end: its
+  // loads were out of range, so its MFMAs add zeros, and a tile past the
+  // wave's last folds nothing).  An exit between the two steps would join
+  // the loop's load-count state with the exit path's, and the compiler then
+  // waits at the first step for the second buffer's loads as well: one batch
+  // in flight instead of two.
   for (int st = 0; st < steps; st += 2) {
     run(cc, a0);
     load(st + 2, cl, a0);
     cl.next(nb);
     after(cc);
     cc.next(nb);
-    if (st + 1 >= steps) break;
     run(cc, a1);
     load(st + 3, cl, a1);
     cl.next(nb);
