@@ -17,16 +17,23 @@ constexpr uint32_t kOutOfRange = 0x7ff00000u;
 // arithmetic.  The prefetch past the last step is an out-of-range load (no
 // memory access), so the loop always has the same loads in flight and the
 // compiler's in-order wait counts stay exact (a conditional prefetch makes it
-// drain every load).
+// drain every load).  The loop body runs whole pairs of steps and an odd
+// last step follows the loop: an exit between the two steps of a pair would
+// join the loop's wait counts with the exit path's, and the compiler would
+// then wait at the first step for the second buffer's loads as well.
 template <class Bufs, class Load, class Step>
 __device__ __forceinline__ void pipeline(int steps, Bufs &b0, Bufs &b1, Load load, Step step) {
   load(0, b0);
-  for (int s = 0; s < steps; s += 2) {
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {
     load(s + 1, b1);
     step(s, b0);
-    if (s + 1 >= steps) break;
     load(s + 2, b0);
     step(s + 1, b1);
+  }
+  if (s < steps) {
+    load(s + 1, b1);
+    step(s, b0);
   }
 }
 
@@ -37,14 +44,19 @@ template <class Bufs, class Load, class Step, class Post>
 __device__ __forceinline__ void pipeline_post(int steps, Bufs &b0, Bufs &b1, Load load, Step step, Post post) {
   load(0, b0);
   load(1, b1);
-  for (int s = 0; s < steps; s += 2) {
+  int s = 0;
+  for (; s + 1 < steps; s += 2) {   // (whole pairs, as above)
     step(s, b0);
     load(s + 2, b0);
     post(s);
-    if (s + 1 >= steps) break;
     step(s + 1, b1);
     load(s + 3, b1);
     post(s + 1);
+  }
+  if (s < steps) {
+    step(s, b0);
+    load(s + 2, b0);
+    post(s);
   }
 }
 
